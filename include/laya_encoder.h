@@ -1,0 +1,299 @@
+/*
+ * laya_encoder.h -- C ABI of the MI355X (gfx950) BF16 encoder forward pass.
+ *
+ * What the library computes: the forward pass of an encoder-only transformer,
+ * "28 encoder layers and two decision transformer layers" after a token
+ * embedding, in BF16, with the final hidden states left in device memory for
+ * a scorer (page "Run Laya encoder and decision layers on CUDA", section
+ * Purpose).  Each layer is pre-LayerNorm (no bias) with rotary position
+ * embedding, bidirectional attention that is global on every 3rd encoder
+ * layer and a 128-token sliding window otherwise, and a GeGLU FFN; separate
+ * QKV, RoPE and attention steps ("[RFC]: Native Laya inference with Rust and
+ * CUDA #14", section Design).  Optionally the last decision layer runs only
+ * for a list of marker rows, with keys and values still computed for every
+ * token (page "perf(model): exact Metal speed-ups of the forward pass").
+ *
+ * Conventions (the "ops.h"-style C ABI of the RFC's build discussion: an ABI
+ * version query, int return codes, work queued on a caller-supplied stream so
+ * that it can be captured into a graph, resolved handles reused):
+ *   - every function returns LAYA_OK (0) or a negative LAYA_E_* code;
+ *   - `stream` arguments are hipStream_t values passed as void* (NULL = the
+ *     null stream); all device work is queued on that stream and nothing
+ *     synchronises the host unless a function says so;
+ *   - pointers documented "host" are ordinary host memory and are only read
+ *     during the call; pointers documented "device" are device memory on the
+ *     handle's device;
+ *   - BF16 tensors are row-major arrays of 16-bit bfloat16 values;
+ *   - validation happens before any device call: an invalid argument returns
+ *     LAYA_E_INVALID (or LAYA_E_UNSUPPORTED) and touches no device state;
+ *   - a HIP failure returns LAYA_E_DEVICE and poisons the handle: every later
+ *     call on it returns LAYA_E_POISONED; laya_encoder_destroy still works.
+ * Limits follow the worker's input limits: at most 16 rows ("questions"),
+ * 512 tokens per row and 2048 markers (page "Laya native CUDA worker",
+ * section Start and check).
+ */
+#ifndef LAYA_ENCODER_H
+#define LAYA_ENCODER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LAYA_ABI_VERSION 1
+
+#define LAYA_OK 0
+#define LAYA_E_INVALID -1     /* bad ids, lengths, markers, sizes, NULL pointers */
+#define LAYA_E_UNSUPPORTED -2 /* configuration outside the kernels' supported shapes */
+#define LAYA_E_NOMEM -3       /* device or host allocation failed */
+#define LAYA_E_DEVICE -4      /* a HIP call failed; the handle is poisoned */
+#define LAYA_E_POISONED -5    /* the handle saw a device failure earlier */
+#define LAYA_E_ABI -6         /* laya_config.abi_version != LAYA_ABI_VERSION */
+
+/* laya_encoder_run flags */
+#define LAYA_RUN_EAGER 1u          /* launch kernels directly instead of replaying a graph */
+#define LAYA_RUN_CAPTURE_LAYERS 2u /* keep every layer's output (implies eager) */
+#define LAYA_RUN_RESIDENT 4u       /* rerun on the indices already uploaded by the previous
+                                      run of the same (B, S, R): no packing, no upload;
+                                      token_ids/lengths/markers are not read */
+
+/* Model and limit configuration.  laya_config_init() fills the 421M-parameter
+ * shape: vocab 50368, hidden 1024, 16 heads of 64, GeGLU inner width 2624,
+ * 28 encoder + 2 decision layers, global attention on encoder layers with
+ * l % 3 == 0 (RoPE theta 160000), a 128-token window elsewhere (theta 10000),
+ * LayerNorm eps 1e-5, limits 16 rows x 512 tokens, 2048 markers. */
+typedef struct laya_config {
+    int32_t abi_version;   /* must be LAYA_ABI_VERSION */
+    int32_t vocab;
+    int32_t hidden;        /* n_heads * head_dim; multiple of 128, <= 2048 */
+    int32_t n_heads;
+    int32_t head_dim;      /* must be 64 */
+    int32_t ffn;           /* GeGLU inner width F: W_i has 2F rows, W_o2 has F columns; multiple of 64 */
+    int32_t n_enc_layers;
+    int32_t n_dec_layers;  /* >= 1 */
+    int32_t global_every;  /* encoder layer l is global iff l % global_every == 0 */
+    int32_t window;        /* local layers see keys with |i - j| <= window / 2; even */
+    float theta_global;
+    float theta_local;
+    float ln_eps;
+    int32_t max_batch;     /* <= 16 */
+    int32_t max_seq;       /* <= 512; also the number of rotary-table positions */
+    int32_t max_markers;   /* <= 2048 */
+} laya_config;
+
+/* Device-resident result of a run.  Owned by the handle; valid until the next
+ * laya_encoder_run with the same (B, S, R) shape, or laya_encoder_destroy. */
+typedef struct laya_output {
+    const void *hidden;     /* device BF16 [rows][dim] */
+    int32_t rows;           /* T = sum of lengths (full run) or R (marker run) */
+    int32_t dim;            /* hidden */
+    const int32_t *row_off; /* device int32 [B + 1]: row b's tokens are rows row_off[b] ..
+                               row_off[b+1]-1 (full run); NULL for a marker run */
+} laya_output;
+
+typedef struct laya_stats {
+    double create_ms;        /* weights generated, tables built, workspace allocated */
+    double last_capture_ms;  /* last graph miss: 2 eager warmups + capture + instantiate */
+    int32_t graphs_cached;   /* instantiated graphs held by the handle */
+    int32_t launches_last_run; /* kernel launches of the last eager run (or captured graph) */
+    int64_t weight_bytes;    /* device bytes of resident weights */
+    int64_t workspace_bytes; /* device bytes of the activation workspace */
+} laya_stats;
+
+typedef struct laya_encoder laya_encoder;
+
+/* Returns LAYA_ABI_VERSION. */
+int laya_abi_version(void);
+
+/* Fills *cfg with the model shape and limits listed above.  Host only. */
+void laya_config_init(laya_config *cfg);
+
+/* Checks a configuration without touching the device.  Returns LAYA_OK,
+ * LAYA_E_ABI, LAYA_E_INVALID (non-positive or inconsistent sizes) or
+ * LAYA_E_UNSUPPORTED (head_dim != 64, hidden not a multiple of 128 or above
+ * 2048, ffn not a multiple of 64, limits above 16 x 512 / 2048). */
+int laya_validate_config(const laya_config *cfg);
+
+/* Checks run arguments without touching the device (the host half of
+ * laya_encoder_run's validation).  token_ids: host int32 [B][S] row-major,
+ * right-padded, each valid id in [0, vocab); lengths: host int32 [B], each in
+ * [1, S]; markers: host int32 [R][2] (row, position) pairs with position <
+ * lengths[row], or NULL when R == 0.  B == 0 is valid (empty batch).  Limits:
+ * B <= max_batch, S <= max_seq, R <= max_markers.  Returns LAYA_OK or
+ * LAYA_E_INVALID. */
+int laya_validate_run_args(const laya_config *cfg, const int32_t *token_ids,
+                           const int32_t *lengths, int32_t B, int32_t S,
+                           const int32_t *markers, int32_t R);
+
+/* Creates a handle on HIP device `device`: validates cfg, allocates the
+ * weights (vocab x hidden embedding plus four matrices per layer, all BF16)
+ * and fills them on the device from weight_seed with the counter-based
+ * generator below, builds the four rotary tables, and allocates the
+ * activation workspace for max_batch x max_seq tokens.  Synchronous.
+ *
+ * Weight generator (there is no checkpoint; the pages load "English 421M",
+ * page "[Performance]: Optimize native Rust/CUDA Laya inference #66", section
+ * Recorded baseline and environment): element idx (nn.Linear [out][in]
+ * order) of tensor tensor_id takes three SplitMix64 outputs
+ *   r_j = mix64(seed + ((tensor_id << 40 | 3*idx + j) + 1) * 0x9e3779b97f4a7c15)
+ * sums their twelve 16-bit fields s, and stores bf16_rne(0.02f * ((s - 393210)
+ * / 65536.0f)).  Tensor ids: 0 embedding [vocab][hidden]; for layer L
+ * (encoder layers first, then decision layers) 1+4L W_qkv [3*hidden][hidden]
+ * with rows [Q | K | V], 2+4L W_o [hidden][hidden], 3+4L W_i [2*ffn][hidden]
+ * with rows [GELU half | gate half], 4+4L W_o2 [hidden][ffn].  Every
+ * LayerNorm gain is 1; there are no biases.
+ *
+ * Rotary tables ("reproduce official BF16 rotary-table rounding", page "Laya
+ * native CUDA worker", section Prepare the checkpoint and bundle; "both
+ * global/local tables", page "[Performance]...#66", section Starting
+ * evidence): cos and sin of p * theta^(-2i/head_dim), p < max_seq,
+ * i < head_dim/2, evaluated in double and rounded once to BF16.
+ *
+ * On success *out owns all device memory it allocated.  Errors: LAYA_E_ABI,
+ * LAYA_E_INVALID, LAYA_E_UNSUPPORTED, LAYA_E_NOMEM, LAYA_E_DEVICE (no handle is
+ * returned; laya_last_error() explains). */
+int laya_encoder_create(const laya_config *cfg, uint64_t weight_seed, int device,
+                        laya_encoder **out);
+
+/* Runs the forward pass on B right-padded rows of S token ids.
+ *
+ * Inputs (host, read before the call returns, so the caller may free them
+ * at once): token_ids int32 [B][S], lengths int32 [B], markers int32 [R][2]
+ * or NULL.  They are validated as laya_validate_run_args does, packed into
+ * pinned staging memory and uploaded with one asynchronous copy on `stream`
+ * (the host waits only if the previous run's upload from the same staging
+ * memory is still in flight).  Padded positions are never computed: valid
+ * tokens of all rows are packed and each query sees only its own row's keys.
+ *
+ * R == 0: the full pass; out->hidden is [T][hidden], T = sum(lengths), rows in
+ * batch order, out->row_off the device row offsets.
+ * R > 0: the last decision layer computes keys/values for every token but
+ * queries, attention, output projection and FFN only for the R marker rows;
+ * out->hidden is [R][hidden] in marker-list order (duplicates allowed).
+ *
+ * Without LAYA_RUN_EAGER the launch sequence for the shape key (B, S, R) is
+ * captured once into a hipGraph (two eager warmups, then capture; the cost is
+ * reported by laya_encoder_stats) and replayed on `stream` afterwards; the
+ * kernels read T and the row layout from device memory, so one graph serves
+ * every length pattern of its key.  Eager and graph runs give bitwise equal
+ * outputs.  B == 0 returns LAYA_OK with out->rows == 0 and launches nothing.
+ *
+ * With LAYA_RUN_RESIDENT the pass reruns on the device copy of the previous
+ * run's indices (same B, S, R; LAYA_E_INVALID otherwise): inputs already in
+ * device memory, nothing crosses the host link ("repeat each workspace
+ * without intermediate readbacks", page "Run Laya encoder and decision layers
+ * on CUDA", section Test Plan).
+ *
+ * The caller synchronises `stream` before reading out->hidden, and must not
+ * run the same handle concurrently on two streams. */
+int laya_encoder_run(laya_encoder *enc, void *stream, const int32_t *token_ids,
+                     const int32_t *lengths, int32_t B, int32_t S,
+                     const int32_t *markers, int32_t R, uint32_t flags,
+                     laya_output *out);
+
+/* Frees every resource of the handle (waits for its device work).  NULL is a
+ * no-op.  Works on a poisoned handle. */
+int laya_encoder_destroy(laya_encoder *enc);
+
+/* Message of the last failure on this handle ("" if none).  The string is
+ * owned by the handle. */
+const char *laya_encoder_last_error(const laya_encoder *enc);
+
+/* Message of the last failure in this thread that had no handle to attach
+ * to (laya_encoder_create, laya_validate_*, laya_op_*). */
+const char *laya_last_error(void);
+
+/* After a run with LAYA_RUN_CAPTURE_LAYERS: layer output `index` (0 = "emb",
+ * then "enc00".."enc<n_enc-1>" (residual stream after each encoder layer),
+ * "enc_final", "dec0".., and "out"), as a device BF16 [rows][hidden] view
+ * owned by the handle and valid until the next run.  name_out (host, may be
+ * NULL) receives the NUL-terminated name.  Returns LAYA_E_INVALID for an
+ * index out of range or when the last run did not capture. */
+int laya_encoder_layer_output(laya_encoder *enc, int32_t index, laya_output *out,
+                              char *name_out, size_t name_cap);
+
+/* FNV-1a-64 over the BF16 bytes (little-endian, logical [out][in] order) of
+ * weight tensor `tensor_id` (numbering as in laya_encoder_create).  Copies
+ * the tensor to the host; synchronous; diagnostic only. */
+int laya_encoder_weight_digest(laya_encoder *enc, int32_t tensor_id, uint64_t *fnv64);
+
+/* Device pointer (BF16, [rows][cols]) and shape of weight tensor `tensor_id`;
+ * diagnostic only. */
+int laya_encoder_weight(laya_encoder *enc, int32_t tensor_id, const void **dev,
+                        int32_t *rows, int32_t *cols);
+
+int laya_encoder_stats(const laya_encoder *enc, laya_stats *stats);
+
+/* Rotary table of laya_encoder_create, on the host: cos_bits/sin_bits receive
+ * max_pos * head_dim/2 BF16 bit patterns ([p][i] row-major).  Host only. */
+int laya_rope_table(float theta, int32_t max_pos, int32_t head_dim,
+                    uint16_t *cos_bits, uint16_t *sin_bits);
+
+/* Copies `bytes` between host and device memory on `stream` and waits for
+ * the copy.  kind: 0 device->host, 1 host->device, 2 device->device. */
+int laya_memcpy(void *dst, const void *src, size_t bytes, int32_t kind, void *stream);
+
+/* ----------------------------------------------------------------------------
+ * Single-step entry points.  Each queues one step of the pass on `stream`,
+ * on device buffers the caller owns; they are the same kernels the handle
+ * launches.  Return LAYA_E_INVALID for inconsistent sizes or NULL pointers.
+ * ------------------------------------------------------------------------- */
+
+/* Embedding gather: out[t][:] = emb[ids[t]][:] for t < T (bit-exact copy).
+ * emb device BF16 [vocab][hidden]; ids device int32 [T], each < vocab;
+ * out device BF16 [T][hidden]. */
+int laya_op_gather(void *stream, const void *emb, int32_t vocab, int32_t hidden,
+                   const int32_t *ids, int32_t T, void *out);
+
+/* Fused residual add + LayerNorm over T rows of `hidden` values:
+ *   if r != NULL:  x[t] <- bf16(x[t] + r[t])   (written back to x)
+ *   n[t] <- bf16((x[t] - mean) / sqrt(var + eps) * gamma)
+ * with mean and biased variance of row t in float32, no bias.  x, r, n device
+ * BF16 [T][hidden] (n must not alias x or r); gamma device float32 [hidden]. */
+int laya_op_layernorm(void *stream, void *x, const void *r, void *n, const float *gamma,
+                      int32_t T, int32_t hidden, float eps);
+
+/* C[m][n] = bf16(sum_k A[m][k] * W[n][k]) for m < M, n < N (float32
+ * accumulation; nn.Linear without bias).  epilogue 0: plain.  epilogue 1
+ * (GeGLU): W has 2N rows; with u = A W[0:N]^T and g = A W[N:2N]^T in float32,
+ * C = bf16(GELU(u) * g), GELU(z) = 0.5 z (1 + erf(z / sqrt 2)).  A device BF16
+ * [M][lda], W device BF16 [N or 2N][ldw], C device BF16 [M][ldc]; K a multiple
+ * of 64, N a multiple of 64, lda/ldw/ldc multiples of 8 (16-byte rows). */
+int laya_op_gemm(void *stream, const void *A, int32_t lda, const void *W, int32_t ldw,
+                 void *C, int32_t ldc, int32_t M, int32_t N, int32_t K, int32_t epilogue);
+
+/* RoPE in place on `n_heads_rot` consecutive 64-wide heads starting at column
+ * 0 of each of `rows` rows of buf (device BF16, row stride ld): with
+ * (x, y) = (v[i], v[i+32]) and (c, s) = table[pos[row]][i],
+ *   v[i] <- bf16(fl32(x c - y s)),  v[i+32] <- bf16(fl32(y c + x s)).
+ * Columns beyond the rotated heads (the V block) are not read or written.
+ * pos device int32 [rows], each < max_pos; cos_tab/sin_tab device BF16
+ * [max_pos][32]. */
+int laya_op_rope(void *stream, void *buf, int32_t ld, int32_t n_heads_rot, int32_t rows,
+                 const int32_t *pos, const void *cos_tab, const void *sin_tab,
+                 int32_t max_pos);
+
+/* Attention with a key-padding row and an optional sliding window, for a
+ * packed batch.  Keys/values of row b are tokens row_off[b] .. row_off[b+1]-1
+ * of k and v (device BF16, row stride ldkv, head h at columns 64h..64h+63).
+ * Queries: if q_tok == NULL, every token t is a query, at q row t;
+ * otherwise q row r is the query of token q_tok[r] (host int32 [n_q],
+ * grouped so that queries of one row are consecutive).  Query of token t in
+ * row b at position p sees key j of the same row iff half_window < 0 or
+ * |p - j| <= half_window; scores (q . k) / 8 in float32, softmax in float32,
+ * o = sum p v stored as BF16 at o row r (device BF16, row stride ldo).
+ * row_off host int32 [B + 1].  Index metadata is built on the host and
+ * uploaded into a buffer this call allocates and frees (diagnostic entry;
+ * synchronises the stream). */
+int laya_op_attention(void *stream, const void *q, int32_t ldq, const void *k,
+                      const void *v, int32_t ldkv, void *o, int32_t ldo, int32_t n_heads,
+                      const int32_t *row_off, int32_t B, const int32_t *q_tok, int32_t n_q,
+                      int32_t half_window);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LAYA_ENCODER_H */

@@ -1,0 +1,128 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol its header
+declares, and its host-only logic (validation, rotary tables) is right.  No
+device compute happens here."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from transformer_encoder_bf16_amd import binding as b
+from transformer_encoder_bf16_amd.inputs import MODEL, TINY, WORKLOADS, make_batch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(b.LIB_PATH):
+        from transformer_encoder_bf16_amd import build_lib
+        build_lib.build()
+    return b.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    hdr = open(os.path.join(ROOT, "include", "laya_encoder.h")).read()
+    declared = set(re.findall(r"^\s*(?:int|void|const char \*)\s*(laya_\w+)\s*\(", hdr, re.M))
+    assert declared == set(b.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert lib.laya_abi_version() == b.LAYA_ABI_VERSION == 1
+
+
+def test_default_config_is_the_model(lib):
+    d = b.default_config()
+    for k, v in MODEL.items():
+        assert d[k] == pytest.approx(v), k
+
+
+@pytest.mark.parametrize("cfg", [MODEL, TINY])
+def test_valid_configs(lib, cfg):
+    assert b.validate_config(cfg) == b.LAYA_OK
+
+
+@pytest.mark.parametrize("change,code", [
+    (dict(head_dim=32, n_heads=32), b.LAYA_E_UNSUPPORTED),
+    (dict(hidden=1000), b.LAYA_E_INVALID),
+    (dict(hidden=960, n_heads=15), b.LAYA_E_UNSUPPORTED),
+    (dict(ffn=2600), b.LAYA_E_UNSUPPORTED),
+    (dict(max_batch=17), b.LAYA_E_UNSUPPORTED),
+    (dict(max_seq=513), b.LAYA_E_UNSUPPORTED),
+    (dict(max_markers=4096), b.LAYA_E_UNSUPPORTED),
+    (dict(n_dec_layers=0), b.LAYA_E_INVALID),
+    (dict(window=127), b.LAYA_E_UNSUPPORTED),
+    (dict(vocab=0), b.LAYA_E_INVALID),
+    (dict(ln_eps=0.0), b.LAYA_E_INVALID),
+])
+def test_invalid_configs(lib, change, code):
+    cfg = dict(MODEL)
+    cfg.update(change)
+    assert b.validate_config(cfg) == code
+
+
+def test_abi_mismatch(lib):
+    c = b.Config.from_dict(MODEL)
+    c.abi_version = 2
+    assert lib.laya_validate_config(ctypes.byref(c)) == b.LAYA_E_ABI
+
+
+def test_run_args_validation(lib):
+    batch = make_batch(MODEL, WORKLOADS["short_3"])
+    ok = b.validate_run_args(MODEL, batch.ids, batch.lengths)
+    assert ok == b.LAYA_OK
+    # padding positions are not validated (any id there is fine)
+    ids = batch.ids.copy()
+    ids[0, batch.lengths[0]:] = -5
+    if batch.lengths[0] < ids.shape[1]:
+        assert b.validate_run_args(MODEL, ids, batch.lengths) == b.LAYA_OK
+    bad = batch.ids.copy()
+    bad[1, 0] = MODEL["vocab"]
+    assert b.validate_run_args(MODEL, bad, batch.lengths) == b.LAYA_E_INVALID
+    bad[1, 0] = -1
+    assert b.validate_run_args(MODEL, bad, batch.lengths) == b.LAYA_E_INVALID
+    ln = batch.lengths.copy()
+    ln[2] = 0
+    assert b.validate_run_args(MODEL, batch.ids, ln) == b.LAYA_E_INVALID
+    ln[2] = batch.ids.shape[1] + 1
+    assert b.validate_run_args(MODEL, batch.ids, ln) == b.LAYA_E_INVALID
+    # markers
+    mk = np.array([[0, 0], [3, int(batch.lengths[3]) - 1]], np.int32)
+    assert b.validate_run_args(MODEL, batch.ids, batch.lengths, mk) == b.LAYA_OK
+    mk2 = np.array([[0, int(batch.lengths[0])]], np.int32)
+    assert b.validate_run_args(MODEL, batch.ids, batch.lengths, mk2) == b.LAYA_E_INVALID
+    mk3 = np.array([[4, 0]], np.int32)
+    assert b.validate_run_args(MODEL, batch.ids, batch.lengths, mk3) == b.LAYA_E_INVALID
+    # limits: 16 rows, 512 tokens, 2048 markers
+    big = np.zeros((17, 8), np.int32)
+    assert b.validate_run_args(MODEL, big, np.full(17, 8)) == b.LAYA_E_INVALID
+    long = np.zeros((1, 513), np.int32)
+    assert b.validate_run_args(MODEL, long, np.array([513])) == b.LAYA_E_INVALID
+    many = np.zeros((2049, 2), np.int32)
+    assert b.validate_run_args(MODEL, np.zeros((1, 4), np.int32), np.array([4]), many) == b.LAYA_E_INVALID
+    # the empty batch is valid
+    assert b.validate_run_args(MODEL, np.zeros((0, 4), np.int32), np.zeros(0, np.int32)) == b.LAYA_OK
+
+
+@pytest.mark.parametrize("theta", [MODEL["theta_global"], MODEL["theta_local"]])
+def test_rope_tables_match_oracle(lib, theta):
+    c_bits, s_bits = b.rope_table(theta, 512, 64)
+    oc, os_ = oracle.rope_tables(theta, 512, 64)
+    assert np.array_equal(c_bits, oracle.f32_to_bf16_bits(oc))
+    assert np.array_equal(s_bits, oracle.f32_to_bf16_bits(os_))
+
+
+def test_create_without_gpu_fails_cleanly(lib):
+    try:
+        import torch
+        if torch.cuda.is_available():
+            pytest.skip("a GPU is visible")
+    except ImportError:
+        pass
+    c = b.Config.from_dict(TINY)
+    h = ctypes.c_void_p()
+    rc = lib.laya_encoder_create(ctypes.byref(c), 1, 0, ctypes.byref(h))
+    assert rc == b.LAYA_E_DEVICE
+    assert not h.value
+    assert lib.laya_encoder_destroy(None) == b.LAYA_OK

@@ -1,0 +1,294 @@
+"""Single-step parity of the HIP kernels against the CPU oracle (GPU only).
+
+Each kernel is called through the C ABI (laya_op_*) on seeded inputs and
+compared with the oracle element by element: bit-exact for the gather and
+for RoPE, within one BF16 ulp (float32 summation order) for LayerNorm and the
+GEMMs, within a small nRMS for attention (whose P is rounded to BF16 before
+the P V product, the one interior rounding the oracle does not mirror).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from tests.gpu_helpers import bits_of, ensure_built, from_dev, report, to_dev, ulp_diff
+from transformer_encoder_bf16_amd.inputs import random_gamma, random_normal
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def B():
+    ensure_built()
+    import torch
+    torch.cuda.init()
+    from transformer_encoder_bf16_amd import binding
+    return binding
+
+
+def _sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------ gather ---
+
+@pytest.mark.parametrize("T", [1, 37, 4096])
+def test_gather_bit_exact(B, T):
+    import torch
+    emb_h = oracle.bf16_round(random_normal((1000, 1024), 1, 0.02))
+    ids_h = np.random.default_rng(T).integers(0, 1000, T).astype(np.int32)
+    ids_h[0] = 999
+    emb = to_dev(emb_h)
+    ids = torch.from_numpy(ids_h).cuda()
+    out = torch.full((T, 1024), float("nan"), dtype=torch.bfloat16, device="cuda")
+    B.op_gather(emb, ids, out)
+    _sync()
+    assert np.array_equal(bits_of(from_dev(out)), bits_of(emb_h[ids_h]))
+
+
+def test_gather_empty(B):
+    import torch
+    emb = torch.zeros((8, 128), dtype=torch.bfloat16, device="cuda")
+    ids = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = torch.zeros((1, 128), dtype=torch.bfloat16, device="cuda")
+    B.op_gather(emb, ids[:0], out[:0])
+    _sync()
+
+
+# --------------------------------------------------------------- layernorm ---
+
+@pytest.mark.parametrize("T,H,resid", [(1, 1024, True), (7, 128, False), (130, 1024, True),
+                                       (1000, 2048, True), (257, 384, False), (64, 1024, False)])
+def test_layernorm(B, T, H, resid):
+    import torch
+    x_h = oracle.bf16_round(random_normal((T, H), T + H, 2.0) + np.float32(0.3))
+    r_h = oracle.bf16_round(random_normal((T, H), T + H + 1, 0.5)) if resid else None
+    g_h = oracle.bf16_round(random_gamma(H, H))
+    x = to_dev(x_h)
+    r = to_dev(r_h) if resid else None
+    n = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    g = torch.from_numpy(g_h).cuda()
+    B.op_layernorm(x, r, n, g, 1e-5)
+    _sync()
+    xs = oracle.bf16_round(x_h + r_h) if resid else x_h
+    assert np.array_equal(bits_of(from_dev(x)), bits_of(xs))  # residual sum: exact
+    want = oracle.bf16_round(oracle.layer_norm(xs, g_h, 1e-5))
+    got = from_dev(n)
+    d = ulp_diff(got, want)
+    assert d.max() <= 1
+    assert (d > 0).mean() < 0.005
+    report("layernorm", {"T": T, "H": H, "resid": resid, "max_ulp": int(d.max()),
+                         "frac_diff": float((d > 0).mean())})
+
+
+# -------------------------------------------------------------------- gemm ---
+
+GEMM_SHAPES = [(1, 64, 64), (48, 1024, 1024), (130, 3072, 1024), (300, 1024, 2624),
+               (257, 384, 128), (4096, 1024, 1024)]
+
+
+@pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
+def test_gemm_plain(B, M, N, K):
+    import torch
+    a_h = oracle.bf16_round(random_normal((M, K), M + K))
+    w_h = oracle.bf16_round(random_normal((N, K), N + K, 0.02))
+    a, w = to_dev(a_h), to_dev(w_h)
+    c = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    B.op_gemm(a, w, c, M, N, K, 0)
+    _sync()
+    want = oracle.bf16_round(oracle.linear(a_h, w_h))
+    got = from_dev(c)
+    d = ulp_diff(got, want)
+    assert d.max() <= 1, (M, N, K)
+    assert (d > 0).mean() < 0.01
+    report("gemm", {"M": M, "N": N, "K": K, "max_ulp": int(d.max()),
+                    "frac_diff": float((d > 0).mean()), "nrms": oracle.nrms(got, want)})
+
+
+@pytest.mark.parametrize("M,F,K", [(1, 192, 128), (48, 2624, 1024), (333, 2624, 1024),
+                                   (70, 64, 64)])
+def test_gemm_geglu(B, M, F, K):
+    import torch
+    a_h = oracle.bf16_round(random_normal((M, K), M + F))
+    w_h = oracle.bf16_round(random_normal((2 * F, K), F + K, 0.05))
+    a, w = to_dev(a_h), to_dev(w_h)
+    c = torch.full((M, F), float("nan"), dtype=torch.bfloat16, device="cuda")
+    B.op_gemm(a, w, c, M, F, K, 1)
+    _sync()
+    ug = oracle.linear(a_h, w_h)
+    want = oracle.bf16_round(oracle.gelu(ug[:, :F]) * ug[:, F:])
+    got = from_dev(c)
+    d = ulp_diff(got, want)
+    assert d.max() <= 2, (M, F, K)
+    assert (d > 0).mean() < 0.02
+    assert oracle.nrms(got, want) < 2e-3
+    report("gemm_geglu", {"M": M, "F": F, "K": K, "max_ulp": int(d.max()),
+                          "frac_diff": float((d > 0).mean()), "nrms": oracle.nrms(got, want)})
+
+
+def test_gemm_rejects_bad_shapes(B):
+    import torch
+    a = torch.zeros((4, 96), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((64, 96), dtype=torch.bfloat16, device="cuda")
+    c = torch.zeros((4, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(B.LayaError):
+        B.op_gemm(a, w, c, 4, 64, 96, 0)  # K not a multiple of 64
+
+
+# -------------------------------------------------------------------- rope ---
+
+ROPE_ROWS = [1, 2, 3, 5, 7, 8, 13, 16, 31, 32, 33, 48, 63, 64, 65, 100, 127, 128, 129, 160,
+             187, 200, 255, 256, 257, 300, 333, 400, 464, 500, 511, 512, 600, 777, 1024, 1496,
+             1715, 2048, 4050, 8192]
+ROPE_HEADS = [1, 2, 16, 32]
+
+
+@pytest.mark.parametrize("theta", [160000.0, 10000.0])
+def test_rope_bit_exact_160_shapes(B, theta):
+    """160 shapes (40 row counts x 4 head counts) per table, both tables: 320
+    bit-exact comparisons, with the V block's bytes checked unchanged."""
+    import torch
+    cb, sb = B.rope_table(theta, 512, 64)
+    ct = torch.from_numpy(cb.view(np.int16)).cuda()
+    st = torch.from_numpy(sb.view(np.int16)).cuda()
+    oc, os_ = oracle.rope_tables(theta, 512, 64)
+    n_cmp = 0
+    for rows in ROPE_ROWS:
+        pos_h = np.random.default_rng(rows).integers(0, 512, rows).astype(np.int32)
+        pos_h[0] = 0
+        pos = torch.from_numpy(pos_h).cuda()
+        for nrot in ROPE_HEADS:
+            width = nrot * 64 + 128  # rotated heads, then an untouched "V" block
+            buf_h = oracle.bf16_round(random_normal((rows, width), rows * 7 + nrot))
+            buf = to_dev(buf_h)
+            B.op_rope(buf, nrot, pos, ct, st)
+            _sync()
+            got = from_dev(buf)
+            want = oracle.rope_apply(buf_h[:, :nrot * 64].reshape(rows, nrot, 64), pos_h, oc, os_)
+            assert np.array_equal(bits_of(got[:, :nrot * 64]), bits_of(want.reshape(rows, -1))), \
+                (theta, rows, nrot)
+            assert np.array_equal(bits_of(got[:, nrot * 64:]), bits_of(buf_h[:, nrot * 64:]))
+            n_cmp += 1
+    assert n_cmp == 160
+    report("rope", {"theta": theta, "shapes": n_cmp, "bit_exact": True})
+
+
+# --------------------------------------------------------------- attention ---
+
+KEY_LENGTHS = [1, 37, 48, 64, 65, 129, 187, 400, 464, 512]
+
+
+def _attn_inputs(lengths, nh, seed):
+    T = int(sum(lengths))
+    row_off = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    q = oracle.bf16_round(random_normal((T, nh * 64), seed))
+    kv = oracle.bf16_round(random_normal((T, 2 * nh * 64), seed + 1))
+    return T, row_off, q, kv
+
+
+def _attn_oracle(q, kv, row_off, nh, hw, q_tok=None):
+    H = nh * 64
+    k, v = kv[:, :H], kv[:, H:]
+    B_ = len(row_off) - 1
+    if q_tok is None:
+        out = np.zeros_like(q)
+        for b in range(B_):
+            s = slice(row_off[b], row_off[b + 1])
+            pos = np.arange(row_off[b + 1] - row_off[b])
+            out[s] = oracle.attention(q[s], k[s], v[s], pos, pos, nh, 64, hw)
+        return out
+    out = np.zeros((len(q_tok), H), np.float32)
+    for r, t in enumerate(q_tok):
+        b = np.searchsorted(row_off, t, side="right") - 1
+        s = slice(row_off[b], row_off[b + 1])
+        pos = np.arange(row_off[b + 1] - row_off[b])
+        out[r:r + 1] = oracle.attention(q[t:t + 1], k[s], v[s], np.array([t - row_off[b]]), pos,
+                                        nh, 64, hw)
+    return out
+
+
+@pytest.mark.parametrize("hw", [-1, 64])
+def test_attention_against_oracle(B, hw):
+    import torch
+    nh = 4
+    T, row_off, q_h, kv_h = _attn_inputs(KEY_LENGTHS, nh, 20 + hw)
+    q, kv = to_dev(q_h), to_dev(kv_h)
+    o = torch.full((T, nh * 64), float("nan"), dtype=torch.bfloat16, device="cuda")
+    B.op_attention(q, kv[:, :nh * 64], kv[:, nh * 64:], o, nh, row_off, None, hw)
+    _sync()
+    got = from_dev(o)
+    want = _attn_oracle(q_h, kv_h, row_off, nh, None if hw < 0 else hw)
+    worst = 0.0
+    for b in range(len(KEY_LENGTHS)):
+        s = slice(row_off[b], row_off[b + 1])
+        e = oracle.nrms(got[s], want[s])
+        worst = max(worst, e)
+        assert e < 4e-3, (KEY_LENGTHS[b], e)
+    assert np.isfinite(got).all()
+    report("attention", {"half_window": hw, "lengths": KEY_LENGTHS, "worst_row_nrms": worst})
+
+
+@pytest.mark.parametrize("hw", [-1, 64])
+@pytest.mark.parametrize("n_rows", [1, 2, 3, 96])
+def test_attention_subset_rows_equal_full_rows(B, hw, n_rows):
+    """Attention over a subset of query rows equals the matching rows of full
+    attention bit for bit, with the key-padding row (and window) applied."""
+    import torch
+    nh = 2
+    lens = [187, 37, 512, 64]
+    T, row_off, q_h, kv_h = _attn_inputs(lens, nh, 40)
+    q, kv = to_dev(q_h), to_dev(kv_h)
+    k, v = kv[:, :nh * 64], kv[:, nh * 64:]
+    full = torch.empty((T, nh * 64), dtype=torch.bfloat16, device="cuda")
+    B.op_attention(q, k, v, full, nh, row_off, None, hw)
+    rng = np.random.default_rng(n_rows)
+    per_row = []
+    for b in range(len(lens)):
+        cnt = min(lens[b], max(1, n_rows // len(lens) + (b < n_rows % len(lens))))
+        per_row.append(np.sort(rng.choice(lens[b], cnt, replace=False)) + row_off[b])
+    q_tok = np.concatenate(per_row)[:n_rows].astype(np.int32)
+    qsub = q[torch.from_numpy(q_tok.astype(np.int64)).cuda()].contiguous()
+    osub = torch.full((len(q_tok), nh * 64), float("nan"), dtype=torch.bfloat16, device="cuda")
+    B.op_attention(qsub, k, v, osub, nh, row_off, q_tok, hw)
+    _sync()
+    got = from_dev(osub)
+    assert np.array_equal(bits_of(got), bits_of(from_dev(full)[q_tok]))
+    want = _attn_oracle(q_h, kv_h, row_off, nh, None if hw < 0 else hw, q_tok)
+    assert oracle.nrms(got, want) < 4e-3
+
+
+def test_attention_single_row_honours_padding(B):
+    """One query row of a short sequence in a batch of long ones only sees its
+    own row's keys (the pages' fused single-query kernel ignored the mask)."""
+    import torch
+    nh = 2
+    lens = [512, 37, 512]
+    T, row_off, q_h, kv_h = _attn_inputs(lens, nh, 50)
+    q, kv = to_dev(q_h), to_dev(kv_h)
+    t = int(row_off[1] + 5)
+    osub = torch.empty((1, nh * 64), dtype=torch.bfloat16, device="cuda")
+    B.op_attention(q[t:t + 1].contiguous(), kv[:, :nh * 64], kv[:, nh * 64:], osub, nh, row_off,
+                   np.array([t], np.int32), -1)
+    _sync()
+    want = _attn_oracle(q_h, kv_h, row_off, nh, None, [t])
+    assert oracle.nrms(from_dev(osub), want) < 4e-3
+
+
+def test_attention_keys_outside_window_do_not_matter(B):
+    import torch
+    nh = 1
+    lens = [400]
+    T, row_off, q_h, kv_h = _attn_inputs(lens, nh, 60)
+    q = to_dev(q_h)
+    o1 = torch.empty((T, 64), dtype=torch.bfloat16, device="cuda")
+    o2 = torch.empty((T, 64), dtype=torch.bfloat16, device="cuda")
+    kv = to_dev(kv_h)
+    B.op_attention(q, kv[:, :64], kv[:, 64:], o1, nh, row_off, None, 64)
+    kv2_h = kv_h.copy()
+    kv2_h[300:] = 5.0  # keys/values at positions >= 300
+    kv2 = to_dev(kv2_h)
+    B.op_attention(q, kv2[:, :64], kv2[:, 64:], o2, nh, row_off, None, 64)
+    _sync()
+    a, b = from_dev(o1), from_dev(o2)
+    assert np.array_equal(bits_of(a[:236]), bits_of(b[:236]))  # queries < 236 never see key 300
+    assert not np.array_equal(bits_of(a[236:]), bits_of(b[236:]))

@@ -1,0 +1,1087 @@
+// Host engine of the encoder pass: the C ABI of include/laya_encoder.h.
+//
+// The engine owns resident weights, the rotary tables, one activation
+// workspace sized for max_batch x max_seq tokens, pinned staging memory for
+// the per-run index upload, and a cache of per-shape hipGraphs ("The executor
+// owns resident weights and bounded shape workspaces", page "Laya native CUDA
+// worker", section Prepare the checkpoint and bundle; "A new shape allocates
+// buffers, runs two warmups, and captures synchronously", "[RFC]: Native Laya
+// inference with Rust and CUDA #14", section Design).  A run packs the valid
+// tokens of all rows on the host, uploads the packed indices with one copy
+// ("group uploads with safe host-buffer lifetimes", "[Performance]: Optimize
+// native Rust/CUDA Laya inference #66", section Implementation priorities),
+// then queues the layer schedule: gather; per layer LayerNorm(+residual),
+// QKV GEMM, RoPE, attention, output GEMM, LayerNorm(+residual), GeGLU-up
+// GEMM, down GEMM; final LayerNorms.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <chrono>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <new>
+#include <string>
+#include <tuple>
+#include <vector>
+
+#include "kernels.h"
+#include "laya_encoder.h"
+
+using laya::AttnBlock;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int set_global_error(int code, const std::string &msg) {
+    g_last_error = msg;
+    return code;
+}
+
+// ---------------------------------------------------------------------------
+// Rotary tables: cos/sin of p * theta^(-2i/d) in double, rounded once to BF16
+// (nearest, ties to even) straight from the double's bit pattern.
+// ---------------------------------------------------------------------------
+uint16_t double_to_bf16_rne(double x) {
+    uint64_t u;
+    std::memcpy(&u, &x, 8);
+    const uint64_t sign = u >> 63;
+    const int e = (int)((u >> 52) & 0x7ff);
+    const uint64_t mant = u & ((1ull << 52) - 1);
+    if (e == 0 && mant == 0) return (uint16_t)(sign << 15);
+    if (e == 0x7ff) return (uint16_t)((sign << 15) | 0x7f80u | (mant ? 0x40u : 0u));
+    const int eb = e - 1023 + 127;  // BF16 biased exponent
+    if (eb <= 0 || eb >= 255) {
+        // outside the normal BF16 range: go through float (not reached by tables)
+        float f = (float)x;
+        uint32_t b;
+        std::memcpy(&b, &f, 4);
+        return (uint16_t)((b + 0x7fffu + ((b >> 16) & 1u)) >> 16);
+    }
+    // keep the top 7 mantissa bits; the 45 dropped bits decide the rounding
+    uint64_t keep = mant >> 45;
+    const uint64_t rest = mant & ((1ull << 45) - 1);
+    const uint64_t half = 1ull << 44;
+    uint32_t bits = ((uint32_t)eb << 7) | (uint32_t)keep;
+    if (rest > half || (rest == half && (keep & 1))) bits += 1;  // may carry into exponent
+    return (uint16_t)((sign << 15) | bits);
+}
+
+void build_rope_table(double theta, int max_pos, int head_dim, uint16_t *c, uint16_t *s) {
+    const int half = head_dim / 2;
+    for (int i = 0; i < half; ++i) {
+        const double inv_freq = std::pow(theta, -2.0 * (double)i / (double)head_dim);
+        for (int p = 0; p < max_pos; ++p) {
+            const double ang = (double)p * inv_freq;
+            c[p * half + i] = double_to_bf16_rne(std::cos(ang));
+            s[p * half + i] = double_to_bf16_rne(std::sin(ang));
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Attention work list: blocks of <= 64 queries of one row.  Full pass: each
+// row's tokens in chunks of 64.  Marker pass: runs of consecutive marker
+// entries from the same row, chunked at 64.  Key range per block: the whole
+// row on global layers; [min pos - hw, max pos + hw] clipped to the row on
+// local layers (one list per window width is built).  The first key is
+// rounded down to a multiple of the 64-key tile, so every query meets its keys
+// in the same tiles whichever block it sits in: a query's result is then
+// bitwise the same in the full pass and in the marker pass (extra fully
+// masked keys leave the online softmax exactly unchanged).
+// ---------------------------------------------------------------------------
+int align_down(int k) { return k - k % 64; }
+
+void build_blocks_full(const int32_t *row_off, int B, int half_window, AttnBlock *out,
+                       int *n_out) {
+    int n = 0;
+    for (int b = 0; b < B; ++b) {
+        const int kt0 = row_off[b], len = row_off[b + 1] - row_off[b];
+        for (int i0 = 0; i0 < len; i0 += laya::kAttnQueries) {
+            const int cnt = std::min(laya::kAttnQueries, len - i0);
+            AttnBlock a{};
+            a.kt0 = kt0;
+            a.klen = len;
+            if (half_window < 0) {
+                a.k_lo = 0;
+                a.k_hi = len;
+            } else {
+                a.k_lo = align_down(std::max(0, i0 - half_window));
+                a.k_hi = std::min(len, i0 + cnt - 1 + half_window + 1);
+            }
+            a.q_first = kt0 + i0;
+            a.q_count = cnt;
+            out[n++] = a;
+        }
+    }
+    *n_out = n;
+}
+
+// q_row[r] = row of query r, q_pos[r] = its position.
+void build_blocks_list(const int32_t *row_off, const int32_t *q_row, const int32_t *q_pos,
+                       int n_q, int half_window, AttnBlock *out, int *n_out) {
+    int n = 0;
+    int r = 0;
+    while (r < n_q) {
+        const int row = q_row[r];
+        int e = r;
+        while (e < n_q && q_row[e] == row && e - r < laya::kAttnQueries) ++e;
+        int pmin = q_pos[r], pmax = q_pos[r];
+        for (int j = r; j < e; ++j) {
+            pmin = std::min(pmin, q_pos[j]);
+            pmax = std::max(pmax, q_pos[j]);
+        }
+        const int len = row_off[row + 1] - row_off[row];
+        AttnBlock a{};
+        a.kt0 = row_off[row];
+        a.klen = len;
+        if (half_window < 0) {
+            a.k_lo = 0;
+            a.k_hi = len;
+        } else {
+            a.k_lo = align_down(std::max(0, pmin - half_window));
+            a.k_hi = std::min(len, pmax + half_window + 1);
+        }
+        a.q_first = r;
+        a.q_count = e - r;
+        out[n++] = a;
+        r = e;
+    }
+    *n_out = n;
+}
+
+int config_check(const laya_config *c, std::string *why) {
+    if (!c) {
+        *why = "config is NULL";
+        return LAYA_E_INVALID;
+    }
+    if (c->abi_version != LAYA_ABI_VERSION) {
+        *why = "abi_version mismatch";
+        return LAYA_E_ABI;
+    }
+    if (c->vocab <= 0 || c->hidden <= 0 || c->n_heads <= 0 || c->head_dim <= 0 || c->ffn <= 0 ||
+        c->n_enc_layers <= 0 || c->n_dec_layers <= 0 || c->global_every <= 0 || c->window < 0 ||
+        c->max_batch <= 0 || c->max_seq <= 0 || c->max_markers < 0 || !(c->ln_eps > 0.f) ||
+        !(c->theta_global > 1.f) || !(c->theta_local > 1.f)) {
+        *why = "non-positive size or parameter in config";
+        return LAYA_E_INVALID;
+    }
+    if (c->n_heads * c->head_dim != c->hidden) {
+        *why = "hidden != n_heads * head_dim";
+        return LAYA_E_INVALID;
+    }
+    if (c->head_dim != 64) {
+        *why = "head_dim must be 64";
+        return LAYA_E_UNSUPPORTED;
+    }
+    if (c->hidden % 128 != 0 || c->hidden > 2048) {
+        *why = "hidden must be a multiple of 128 and <= 2048";
+        return LAYA_E_UNSUPPORTED;
+    }
+    if (c->ffn % 64 != 0) {
+        *why = "ffn must be a multiple of 64";
+        return LAYA_E_UNSUPPORTED;
+    }
+    if (c->window % 2 != 0) {
+        *why = "window must be even";
+        return LAYA_E_UNSUPPORTED;
+    }
+    if (c->max_batch > 16 || c->max_seq > 512 || c->max_markers > 2048) {
+        *why = "limits above 16 rows x 512 tokens / 2048 markers";
+        return LAYA_E_UNSUPPORTED;
+    }
+    if ((int64_t)c->vocab * c->hidden >= (1ll << 31)) {
+        *why = "embedding too large for 32-bit indexing";
+        return LAYA_E_UNSUPPORTED;
+    }
+    return LAYA_OK;
+}
+
+int run_args_check(const laya_config *c, const int32_t *ids, const int32_t *lengths, int32_t B,
+                   int32_t S, const int32_t *markers, int32_t R, std::string *why) {
+    if (B < 0 || S < 0 || R < 0) {
+        *why = "negative B, S or R";
+        return LAYA_E_INVALID;
+    }
+    if (B > c->max_batch) {
+        *why = "B exceeds max_batch";
+        return LAYA_E_INVALID;
+    }
+    if (S > c->max_seq) {
+        *why = "S exceeds max_seq";
+        return LAYA_E_INVALID;
+    }
+    if (R > c->max_markers) {
+        *why = "R exceeds max_markers";
+        return LAYA_E_INVALID;
+    }
+    if (B == 0) {
+        if (R != 0) {
+            *why = "markers given for an empty batch";
+            return LAYA_E_INVALID;
+        }
+        return LAYA_OK;
+    }
+    if (!ids || !lengths) {
+        *why = "token_ids or lengths is NULL";
+        return LAYA_E_INVALID;
+    }
+    if (S == 0) {
+        *why = "S == 0 with B > 0";
+        return LAYA_E_INVALID;
+    }
+    for (int b = 0; b < B; ++b) {
+        if (lengths[b] < 1 || lengths[b] > S) {
+            *why = "length of row " + std::to_string(b) + " outside [1, S]";
+            return LAYA_E_INVALID;
+        }
+        for (int p = 0; p < lengths[b]; ++p) {
+            const int32_t id = ids[(int64_t)b * S + p];
+            if (id < 0 || id >= c->vocab) {
+                *why = "token id out of range at row " + std::to_string(b) + ", position " +
+                       std::to_string(p);
+                return LAYA_E_INVALID;
+            }
+        }
+    }
+    if (R > 0) {
+        if (!markers) {
+            *why = "markers is NULL with R > 0";
+            return LAYA_E_INVALID;
+        }
+        for (int r = 0; r < R; ++r) {
+            const int32_t row = markers[2 * r], pos = markers[2 * r + 1];
+            if (row < 0 || row >= B || pos < 0 || pos >= lengths[row]) {
+                *why = "marker " + std::to_string(r) + " outside its row";
+                return LAYA_E_INVALID;
+            }
+        }
+    }
+    return LAYA_OK;
+}
+
+struct GraphEntry {
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+    int launches = 0;
+};
+
+// Offsets (in int32) of the per-run index upload for shape key (B, S, R).
+struct MetaLayout {
+    int64_t hdr, row_off, blk_g, blk_l, blk_sub, mrk_tok, mrk_pos, pos, ids, total;
+    int nblk_full_max, nblk_sub_max;
+    static int64_t up8(int64_t v) { return (v + 7) & ~int64_t(7); }
+    MetaLayout(int B, int S, int R) {
+        nblk_full_max = B * ((S + laya::kAttnQueries - 1) / laya::kAttnQueries);
+        nblk_sub_max = R;
+        int64_t o = 0;
+        hdr = o;
+        o += 8;
+        row_off = o;
+        o = up8(o + B + 1);
+        blk_g = o;
+        o += (int64_t)nblk_full_max * 8;
+        blk_l = o;
+        o += (int64_t)nblk_full_max * 8;
+        blk_sub = o;
+        o += (int64_t)nblk_sub_max * 8;
+        mrk_tok = o;
+        o = up8(o + R);
+        mrk_pos = o;
+        o = up8(o + R);
+        pos = o;
+        o = up8(o + (int64_t)B * S);
+        ids = o;
+        o = up8(o + (int64_t)B * S);
+        total = o;
+    }
+};
+
+// header fields
+enum { H_T = 0, H_B = 1, H_R = 2, H_NBLK = 3, H_NBLK_L = 4, H_NBLK_SUB = 5 };
+
+}  // namespace
+
+struct laya_encoder {
+    laya_config cfg{};
+    int device = 0;
+    bool poisoned = false;
+    std::string err;
+    laya_stats stats{};
+
+    // weights
+    void *wmem = nullptr;
+    size_t wbytes = 0;
+    bf16_t *emb = nullptr;
+    std::vector<bf16_t *> wqkv, wo, wi, wo2;
+    float *gamma_ones = nullptr;
+    bf16_t *cos_g = nullptr, *sin_g = nullptr, *cos_l = nullptr, *sin_l = nullptr;
+
+    // workspace
+    void *ws = nullptr;
+    size_t ws_bytes = 0;
+    int64_t tcap = 0;
+    bf16_t *xa = nullptr, *xb = nullptr, *nrm = nullptr, *qkv = nullptr, *att = nullptr,
+           *proj = nullptr, *hid = nullptr, *out = nullptr;
+    bf16_t *x_sub = nullptr, *n_sub = nullptr, *q_sub = nullptr;
+    int32_t *meta_dev = nullptr;
+    int32_t *meta_host = nullptr;
+    int64_t meta_cap = 0;
+    hipEvent_t upload_done = nullptr;
+    bool upload_pending = false;
+    hipStream_t cap_stream = nullptr;
+
+    std::map<std::tuple<int, int, int>, GraphEntry> graphs;
+
+    // per-layer captures
+    void *cap_mem = nullptr;
+    size_t cap_bytes = 0;
+    std::vector<std::string> cap_names;
+    std::vector<int32_t> cap_rows;
+    std::vector<bf16_t *> cap_ptrs;
+    bool have_caps = false;
+
+    // indices currently in meta_dev (for LAYA_RUN_RESIDENT)
+    bool have_upload = false;
+    int up_B = 0, up_S = 0, up_R = 0, up_T = 0;
+
+    int launches = 0;
+};
+
+namespace {
+
+int fail(laya_encoder *e, int code, const std::string &msg) {
+    if (e) {
+        e->err = msg;
+        if (code == LAYA_E_DEVICE) e->poisoned = true;
+    }
+    g_last_error = msg;
+    return code;
+}
+
+#define HIPCHK(expr)                                                                      \
+    do {                                                                                  \
+        hipError_t _e = (expr);                                                           \
+        if (_e != hipSuccess)                                                             \
+            return fail(enc, LAYA_E_DEVICE,                                               \
+                        std::string(#expr) + ": " + hipGetErrorString(_e));               \
+    } while (0)
+
+// Everything a recorded schedule needs about the run shape.
+struct RunShape {
+    int B, S, R;
+    int T;  // actual tokens (host value; used only for captures in eager mode)
+    bool capture_layers;
+};
+
+int layer_count(const laya_config &c) { return c.n_enc_layers + c.n_dec_layers; }
+
+// Queue the whole pass on stream s.  Reads T, the row layout and the
+// attention work lists from the device copy of the index upload.
+int record(laya_encoder *enc, hipStream_t s, const RunShape &rs) {
+    const laya_config &c = enc->cfg;
+    const int H = c.hidden, F = c.ffn, nh = c.n_heads;
+    const int NL = layer_count(c);
+    const int Tmax = rs.B * rs.S;
+    const MetaLayout ml(rs.B, rs.S, rs.R);
+    const int32_t *md = enc->meta_dev;
+    const int32_t *T_dev = md + ml.hdr + H_T;
+    const int32_t *ids = md + ml.ids;
+    const int32_t *pos = md + ml.pos;
+    const AttnBlock *blk_g = reinterpret_cast<const AttnBlock *>(md + ml.blk_g);
+    const AttnBlock *blk_l = reinterpret_cast<const AttnBlock *>(md + ml.blk_l);
+    const AttnBlock *blk_s = reinterpret_cast<const AttnBlock *>(md + ml.blk_sub);
+    const int32_t *nblk_g = md + ml.hdr + H_NBLK;
+    const int32_t *nblk_l = md + ml.hdr + H_NBLK_L;
+    const int32_t *nblk_s = md + ml.hdr + H_NBLK_SUB;
+    const int32_t *mrk_tok = md + ml.mrk_tok;
+    const int32_t *mrk_pos = md + ml.mrk_pos;
+    const int hw = c.window / 2;
+    enc->launches = 0;
+
+    size_t ci = 0;
+    auto cap = [&](const char *name, const bf16_t *src, int rows) -> int {
+        if (!rs.capture_layers) return LAYA_OK;
+        if (ci >= enc->cap_ptrs.size()) return fail(enc, LAYA_E_INVALID, "capture overflow");
+        enc->cap_names[ci] = name;
+        enc->cap_rows[ci] = rows;
+        HIPCHK(hipMemcpyAsync(enc->cap_ptrs[ci], src, (size_t)rows * H * 2,
+                              hipMemcpyDeviceToDevice, s));
+        ++ci;
+        return LAYA_OK;
+    };
+#define L_CHK(expr)                                                                   \
+    do {                                                                              \
+        hipError_t _e = (expr);                                                       \
+        ++enc->launches;                                                              \
+        if (_e != hipSuccess)                                                         \
+            return fail(enc, LAYA_E_DEVICE, std::string(#expr) + ": " + hipGetErrorString(_e)); \
+    } while (0)
+#define C_CHK(expr)                      \
+    do {                                 \
+        int _r = (expr);                 \
+        if (_r != LAYA_OK) return _r;    \
+    } while (0)
+
+    bf16_t *xr = enc->xa, *xalt = enc->xb;
+    L_CHK(laya::launch_gather(s, enc->emb, ids, T_dev, Tmax, H, xr));
+    C_CHK(cap("emb", xr, rs.T));
+    bool pending = false;  // the down projection of the previous layer waits in proj
+    char name[32];
+    for (int L = 0; L < NL; ++L) {
+        const bool is_enc = L < c.n_enc_layers;
+        const bool glob = !is_enc || (L % c.global_every) == 0;
+        const bf16_t *ctab = glob ? enc->cos_g : enc->cos_l;
+        const bf16_t *stab = glob ? enc->sin_g : enc->sin_l;
+        const int half = glob ? -1 : hw;
+        const AttnBlock *blk = glob ? blk_g : blk_l;
+        const int32_t *nblk = glob ? nblk_g : nblk_l;
+        const bool subset = (L == NL - 1) && rs.R > 0;
+        const bf16_t *Wqkv = enc->wqkv[L], *Wo = enc->wo[L], *Wi = enc->wi[L],
+                     *Wo2 = enc->wo2[L];
+        const float *g1 = enc->gamma_ones;
+
+        // attention sublayer: n = LN(x [+ f of the previous layer])
+        L_CHK(laya::launch_layernorm(s, xr, pending ? enc->proj : nullptr, enc->nrm, g1, T_dev,
+                                     Tmax, H, c.ln_eps));
+        if (pending) {
+            std::snprintf(name, sizeof name, (L - 1) < c.n_enc_layers ? "enc%02d" : "dec%d",
+                          (L - 1) < c.n_enc_layers ? L - 1 : L - 1 - c.n_enc_layers);
+            C_CHK(cap(name, xr, rs.T));
+        }
+        pending = false;
+        if (!subset) {
+            L_CHK(laya::launch_gemm(s, enc->nrm, H, Wqkv, H, enc->qkv, 3 * H, T_dev, Tmax, 3 * H,
+                                    H, 0));
+            L_CHK(laya::launch_rope(s, enc->qkv, 3 * H, 2 * nh, T_dev, Tmax, pos, ctab, stab));
+            L_CHK(laya::launch_attention(s, enc->qkv, 3 * H, enc->qkv + H, enc->qkv + 2 * H,
+                                         3 * H, enc->att, H, blk, nblk, ml.nblk_full_max, pos,
+                                         nh, half));
+            L_CHK(laya::launch_gemm(s, enc->att, H, Wo, H, enc->proj, H, T_dev, Tmax, H, H, 0));
+            L_CHK(laya::launch_layernorm(s, xr, enc->proj, enc->nrm, g1, T_dev, Tmax, H,
+                                         c.ln_eps));
+            L_CHK(laya::launch_gemm(s, enc->nrm, H, Wi, H, enc->hid, F, T_dev, Tmax, F, H, 1));
+            L_CHK(laya::launch_gemm(s, enc->hid, F, Wo2, F, enc->proj, H, T_dev, Tmax, H, F, 0));
+            pending = true;
+            if (L == c.n_enc_layers - 1) {
+                // x += f; the encoder's final LayerNorm output becomes the decision stream
+                L_CHK(laya::launch_layernorm(s, xr, enc->proj, xalt, g1, T_dev, Tmax, H,
+                                             c.ln_eps));
+                std::snprintf(name, sizeof name, "enc%02d", L);
+                C_CHK(cap(name, xr, rs.T));
+                C_CHK(cap("enc_final", xalt, rs.T));
+                std::swap(xr, xalt);
+                pending = false;
+            }
+        } else {
+            const int R = rs.R;
+            // keys/values for every token, queries only for the marker rows
+            L_CHK(laya::launch_gemm(s, enc->nrm, H, Wqkv + (size_t)H * H, H, enc->qkv, 2 * H,
+                                    T_dev, Tmax, 2 * H, H, 0));
+            L_CHK(laya::launch_gather_rows(s, enc->nrm, H, mrk_tok, R, H, enc->n_sub, H));
+            L_CHK(laya::launch_gather_rows(s, xr, H, mrk_tok, R, H, enc->x_sub, H));
+            L_CHK(laya::launch_gemm(s, enc->n_sub, H, Wqkv, H, enc->q_sub, H, nullptr, R, H, H,
+                                    0));
+            L_CHK(laya::launch_rope(s, enc->qkv, 2 * H, nh, T_dev, Tmax, pos, ctab, stab));
+            L_CHK(laya::launch_rope(s, enc->q_sub, H, nh, nullptr, R, mrk_pos, ctab, stab));
+            L_CHK(laya::launch_attention(s, enc->q_sub, H, enc->qkv, enc->qkv + H, 2 * H,
+                                         enc->att, H, blk_s, nblk_s, ml.nblk_sub_max, mrk_pos,
+                                         nh, half));
+            L_CHK(laya::launch_gemm(s, enc->att, H, Wo, H, enc->proj, H, nullptr, R, H, H, 0));
+            L_CHK(laya::launch_layernorm(s, enc->x_sub, enc->proj, enc->n_sub, g1, nullptr, R, H,
+                                         c.ln_eps));
+            L_CHK(laya::launch_gemm(s, enc->n_sub, H, Wi, H, enc->hid, F, nullptr, R, F, H, 1));
+            L_CHK(laya::launch_gemm(s, enc->hid, F, Wo2, F, enc->proj, H, nullptr, R, H, F, 0));
+            L_CHK(laya::launch_layernorm(s, enc->x_sub, enc->proj, enc->out, g1, nullptr, R, H,
+                                         c.ln_eps));
+            std::snprintf(name, sizeof name, L < c.n_enc_layers ? "enc%02d" : "dec%d",
+                          L < c.n_enc_layers ? L : L - c.n_enc_layers);
+            C_CHK(cap(name, enc->x_sub, R));
+            C_CHK(cap("out", enc->out, R));
+            return LAYA_OK;
+        }
+    }
+    // closing LayerNorm over the decision stream
+    L_CHK(laya::launch_layernorm(s, xr, pending ? enc->proj : nullptr, enc->out, enc->gamma_ones,
+                                 T_dev, Tmax, H, c.ln_eps));
+    if (pending) {
+        std::snprintf(name, sizeof name, (NL - 1) < c.n_enc_layers ? "enc%02d" : "dec%d",
+                      (NL - 1) < c.n_enc_layers ? NL - 1 : NL - 1 - c.n_enc_layers);
+        C_CHK(cap(name, xr, rs.T));
+    }
+    C_CHK(cap("out", enc->out, rs.T));
+    return LAYA_OK;
+#undef L_CHK
+#undef C_CHK
+}
+
+int ensure_captures(laya_encoder *enc) {
+    const laya_config &c = enc->cfg;
+    const size_t n = (size_t)layer_count(c) + 4;
+    const size_t per = (size_t)enc->tcap * c.hidden * 2;
+    if (enc->cap_mem) return LAYA_OK;
+    void *p = nullptr;
+    if (hipMalloc(&p, n * per) != hipSuccess)
+        return fail(enc, LAYA_E_NOMEM, "capture buffers: hipMalloc failed");
+    enc->cap_mem = p;
+    enc->cap_bytes = n * per;
+    enc->cap_ptrs.resize(n);
+    enc->cap_names.assign(n, "");
+    enc->cap_rows.assign(n, 0);
+    for (size_t i = 0; i < n; ++i)
+        enc->cap_ptrs[i] = reinterpret_cast<bf16_t *>(static_cast<char *>(p) + i * per);
+    return LAYA_OK;
+}
+
+}  // namespace
+
+// ============================================================================
+// C ABI
+// ============================================================================
+extern "C" {
+
+int laya_abi_version(void) { return LAYA_ABI_VERSION; }
+
+void laya_config_init(laya_config *c) {
+    if (!c) return;
+    c->abi_version = LAYA_ABI_VERSION;
+    c->vocab = 50368;
+    c->hidden = 1024;
+    c->n_heads = 16;
+    c->head_dim = 64;
+    c->ffn = 2624;
+    c->n_enc_layers = 28;
+    c->n_dec_layers = 2;
+    c->global_every = 3;
+    c->window = 128;
+    c->theta_global = 160000.0f;
+    c->theta_local = 10000.0f;
+    c->ln_eps = 1e-5f;
+    c->max_batch = 16;
+    c->max_seq = 512;
+    c->max_markers = 2048;
+}
+
+const char *laya_last_error(void) { return g_last_error.c_str(); }
+
+int laya_validate_config(const laya_config *cfg) {
+    std::string why;
+    int rc = config_check(cfg, &why);
+    if (rc != LAYA_OK) g_last_error = why;
+    return rc;
+}
+
+int laya_validate_run_args(const laya_config *cfg, const int32_t *ids, const int32_t *lengths,
+                           int32_t B, int32_t S, const int32_t *markers, int32_t R) {
+    std::string why;
+    int rc = config_check(cfg, &why);
+    if (rc == LAYA_OK) rc = run_args_check(cfg, ids, lengths, B, S, markers, R, &why);
+    if (rc != LAYA_OK) g_last_error = why;
+    return rc;
+}
+
+int laya_rope_table(float theta, int32_t max_pos, int32_t head_dim, uint16_t *cos_bits,
+                    uint16_t *sin_bits) {
+    if (!(theta > 1.f) || max_pos <= 0 || head_dim <= 0 || head_dim % 2 || !cos_bits ||
+        !sin_bits)
+        return set_global_error(LAYA_E_INVALID, "laya_rope_table: bad arguments");
+    build_rope_table((double)theta, max_pos, head_dim, cos_bits, sin_bits);
+    return LAYA_OK;
+}
+
+int laya_encoder_create(const laya_config *cfg, uint64_t seed, int device, laya_encoder **out) {
+    auto t_start = std::chrono::steady_clock::now();
+    if (!out) return set_global_error(LAYA_E_INVALID, "out is NULL");
+    *out = nullptr;
+    std::string why;
+    int rc = config_check(cfg, &why);
+    if (rc != LAYA_OK) return set_global_error(rc, why);
+
+    laya_encoder *enc = new (std::nothrow) laya_encoder();
+    if (!enc) return set_global_error(LAYA_E_NOMEM, "host allocation failed");
+    enc->cfg = *cfg;
+    enc->device = device;
+    auto bail = [&](int code) {
+        laya_encoder_destroy(enc);
+        return code;
+    };
+    const laya_config &c = *cfg;
+    const int H = c.hidden, F = c.ffn, NL = layer_count(c);
+
+    if (hipSetDevice(device) != hipSuccess)
+        return bail(set_global_error(LAYA_E_DEVICE, "hipSetDevice failed"));
+
+    // --- weights: one allocation, 256-byte aligned tensors -----------------
+    auto al = [](size_t v) { return (v + 255) & ~size_t(255); };
+    std::vector<std::pair<size_t, size_t>> tensors;  // (offset, elements)
+    size_t off = 0;
+    auto add = [&](size_t elems) {
+        tensors.push_back({off, elems});
+        off += al(elems * 2);
+    };
+    add((size_t)c.vocab * H);
+    for (int L = 0; L < NL; ++L) {
+        add((size_t)3 * H * H);
+        add((size_t)H * H);
+        add((size_t)2 * F * H);
+        add((size_t)H * F);
+    }
+    const size_t gamma_off = off;
+    off += al((size_t)H * 4);
+    const size_t tab_off = off;
+    const size_t tab_elems = (size_t)c.max_seq * (c.head_dim / 2);
+    off += 4 * al(tab_elems * 2);
+    enc->wbytes = off;
+    if (hipMalloc(&enc->wmem, off) != hipSuccess)
+        return bail(set_global_error(LAYA_E_NOMEM, "weights: hipMalloc failed"));
+    char *wb = static_cast<char *>(enc->wmem);
+    enc->emb = reinterpret_cast<bf16_t *>(wb + tensors[0].first);
+    for (int L = 0; L < NL; ++L) {
+        enc->wqkv.push_back(reinterpret_cast<bf16_t *>(wb + tensors[1 + 4 * L].first));
+        enc->wo.push_back(reinterpret_cast<bf16_t *>(wb + tensors[2 + 4 * L].first));
+        enc->wi.push_back(reinterpret_cast<bf16_t *>(wb + tensors[3 + 4 * L].first));
+        enc->wo2.push_back(reinterpret_cast<bf16_t *>(wb + tensors[4 + 4 * L].first));
+    }
+    enc->gamma_ones = reinterpret_cast<float *>(wb + gamma_off);
+    enc->cos_g = reinterpret_cast<bf16_t *>(wb + tab_off);
+    enc->sin_g = reinterpret_cast<bf16_t *>(wb + tab_off + al(tab_elems * 2));
+    enc->cos_l = reinterpret_cast<bf16_t *>(wb + tab_off + 2 * al(tab_elems * 2));
+    enc->sin_l = reinterpret_cast<bf16_t *>(wb + tab_off + 3 * al(tab_elems * 2));
+
+    hipStream_t s = nullptr;
+    if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess)
+        return bail(set_global_error(LAYA_E_DEVICE, "hipStreamCreate failed"));
+    enc->cap_stream = s;
+    for (size_t t = 0; t < tensors.size(); ++t) {
+        if (laya::launch_init_weights(s, reinterpret_cast<bf16_t *>(wb + tensors[t].first),
+                                      tensors[t].second, seed, (uint32_t)t) != hipSuccess)
+            return bail(set_global_error(LAYA_E_DEVICE, "weight init launch failed"));
+    }
+    if (laya::launch_fill_f32(s, enc->gamma_ones, H, 1.0f) != hipSuccess)
+        return bail(set_global_error(LAYA_E_DEVICE, "gamma fill failed"));
+    {
+        std::vector<uint16_t> tc(tab_elems), ts(tab_elems);
+        build_rope_table(c.theta_global, c.max_seq, c.head_dim, tc.data(), ts.data());
+        if (hipMemcpyAsync(enc->cos_g, tc.data(), tab_elems * 2, hipMemcpyHostToDevice, s) ||
+            hipMemcpyAsync(enc->sin_g, ts.data(), tab_elems * 2, hipMemcpyHostToDevice, s) ||
+            hipStreamSynchronize(s))
+            return bail(set_global_error(LAYA_E_DEVICE, "rope table upload failed"));
+        build_rope_table(c.theta_local, c.max_seq, c.head_dim, tc.data(), ts.data());
+        if (hipMemcpyAsync(enc->cos_l, tc.data(), tab_elems * 2, hipMemcpyHostToDevice, s) ||
+            hipMemcpyAsync(enc->sin_l, ts.data(), tab_elems * 2, hipMemcpyHostToDevice, s) ||
+            hipStreamSynchronize(s))
+            return bail(set_global_error(LAYA_E_DEVICE, "rope table upload failed"));
+    }
+
+    // --- workspace for max_batch x max_seq tokens ---------------------------
+    const int64_t tcap = (int64_t)c.max_batch * c.max_seq;
+    const int64_t rcap = std::max(1, c.max_markers);
+    enc->tcap = tcap;
+    size_t wsz = 0;
+    std::vector<std::pair<bf16_t **, size_t>> bufs = {
+        {&enc->xa, (size_t)tcap * H},      {&enc->xb, (size_t)tcap * H},
+        {&enc->nrm, (size_t)tcap * H},     {&enc->qkv, (size_t)tcap * 3 * H},
+        {&enc->att, (size_t)tcap * H},     {&enc->proj, (size_t)tcap * H},
+        {&enc->hid, (size_t)tcap * F},     {&enc->out, (size_t)tcap * H},
+        {&enc->x_sub, (size_t)rcap * H},   {&enc->n_sub, (size_t)rcap * H},
+        {&enc->q_sub, (size_t)rcap * H}};
+    for (auto &b : bufs) wsz += al(b.second * 2);
+    const MetaLayout mlmax(c.max_batch, c.max_seq, c.max_markers);
+    enc->meta_cap = mlmax.total;
+    const size_t meta_off = wsz;
+    wsz += al((size_t)enc->meta_cap * 4);
+    enc->ws_bytes = wsz;
+    if (hipMalloc(&enc->ws, wsz) != hipSuccess)
+        return bail(set_global_error(LAYA_E_NOMEM, "workspace: hipMalloc failed"));
+    if (hipMemsetAsync(enc->ws, 0, wsz, s) != hipSuccess || hipStreamSynchronize(s) != hipSuccess)
+        return bail(set_global_error(LAYA_E_DEVICE, "workspace clear failed"));
+    {
+        char *p = static_cast<char *>(enc->ws);
+        size_t o = 0;
+        for (auto &b : bufs) {
+            *b.first = reinterpret_cast<bf16_t *>(p + o);
+            o += al(b.second * 2);
+        }
+        enc->meta_dev = reinterpret_cast<int32_t *>(p + meta_off);
+    }
+    if (hipHostMalloc((void **)&enc->meta_host, (size_t)enc->meta_cap * 4, hipHostMallocDefault) !=
+        hipSuccess)
+        return bail(set_global_error(LAYA_E_NOMEM, "pinned staging: hipHostMalloc failed"));
+    if (hipEventCreateWithFlags(&enc->upload_done, hipEventDisableTiming) != hipSuccess)
+        return bail(set_global_error(LAYA_E_DEVICE, "hipEventCreate failed"));
+    if (hipStreamSynchronize(s) != hipSuccess)
+        return bail(set_global_error(LAYA_E_DEVICE, "weight generation failed"));
+
+    enc->stats.weight_bytes = (int64_t)enc->wbytes;
+    enc->stats.workspace_bytes = (int64_t)enc->ws_bytes;
+    enc->stats.create_ms =
+        std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t_start)
+            .count();
+    *out = enc;
+    return LAYA_OK;
+}
+
+int laya_encoder_destroy(laya_encoder *enc) {
+    if (!enc) return LAYA_OK;
+    hipSetDevice(enc->device);
+    if (enc->cap_stream) hipStreamSynchronize(enc->cap_stream);
+    hipDeviceSynchronize();
+    for (auto &kv : enc->graphs) {
+        if (kv.second.exec) hipGraphExecDestroy(kv.second.exec);
+        if (kv.second.graph) hipGraphDestroy(kv.second.graph);
+    }
+    if (enc->upload_done) hipEventDestroy(enc->upload_done);
+    if (enc->meta_host) hipHostFree(enc->meta_host);
+    if (enc->cap_mem) hipFree(enc->cap_mem);
+    if (enc->ws) hipFree(enc->ws);
+    if (enc->wmem) hipFree(enc->wmem);
+    if (enc->cap_stream) hipStreamDestroy(enc->cap_stream);
+    delete enc;
+    return LAYA_OK;
+}
+
+const char *laya_encoder_last_error(const laya_encoder *enc) {
+    return enc ? enc->err.c_str() : g_last_error.c_str();
+}
+
+int laya_encoder_run(laya_encoder *enc, void *stream, const int32_t *ids,
+                     const int32_t *lengths, int32_t B, int32_t S, const int32_t *markers,
+                     int32_t R, uint32_t flags, laya_output *out) {
+    if (!enc) return set_global_error(LAYA_E_INVALID, "handle is NULL");
+    if (enc->poisoned) return fail(enc, LAYA_E_POISONED, "handle poisoned by an earlier device failure");
+    if (!out) return fail(enc, LAYA_E_INVALID, "out is NULL");
+    const bool resident = (flags & LAYA_RUN_RESIDENT) != 0;
+    std::string why;
+    int rc = LAYA_OK;
+    if (resident) {
+        if (!enc->have_upload || B != enc->up_B || S != enc->up_S || R != enc->up_R)
+            return fail(enc, LAYA_E_INVALID,
+                        "LAYA_RUN_RESIDENT: no previous upload with this (B, S, R)");
+    } else {
+        rc = run_args_check(&enc->cfg, ids, lengths, B, S, markers, R, &why);
+        if (rc != LAYA_OK) return fail(enc, rc, why);
+    }
+    out->hidden = nullptr;
+    out->rows = 0;
+    out->dim = enc->cfg.hidden;
+    out->row_off = nullptr;
+    enc->have_caps = false;
+    if (B == 0) return LAYA_OK;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    HIPCHK(hipSetDevice(enc->device));
+    const MetaLayout ml(B, S, R);
+    const laya_config &c = enc->cfg;
+    int T = enc->up_T;
+    if (!resident) {
+
+    // --- pack into pinned staging (wait for the previous upload to drain) ---
+    if (enc->upload_pending) {
+        HIPCHK(hipEventSynchronize(enc->upload_done));
+        enc->upload_pending = false;
+    }
+    int32_t *mh = enc->meta_host;
+    T = 0;
+    mh[ml.row_off] = 0;
+    for (int b = 0; b < B; ++b) {
+        for (int p = 0; p < lengths[b]; ++p) {
+            mh[ml.ids + T] = ids[(int64_t)b * S + p];
+            mh[ml.pos + T] = p;
+            ++T;
+        }
+        mh[ml.row_off + b + 1] = T;
+    }
+    int nbg = 0, nbl = 0, nbs = 0;
+    build_blocks_full(mh + ml.row_off, B, -1, reinterpret_cast<AttnBlock *>(mh + ml.blk_g), &nbg);
+    build_blocks_full(mh + ml.row_off, B, c.window / 2,
+                      reinterpret_cast<AttnBlock *>(mh + ml.blk_l), &nbl);
+    if (R > 0) {
+        std::vector<int32_t> qrow(R);
+        for (int r = 0; r < R; ++r) {
+            qrow[r] = markers[2 * r];
+            mh[ml.mrk_pos + r] = markers[2 * r + 1];
+            mh[ml.mrk_tok + r] = mh[ml.row_off + markers[2 * r]] + markers[2 * r + 1];
+        }
+        // the marker pass's attention runs on the last layer, which is global
+        // unless the model has no decision layers and its last encoder layer is local
+        const int Llast = layer_count(c) - 1;
+        const bool glob = Llast >= c.n_enc_layers || (Llast % c.global_every) == 0;
+        build_blocks_list(mh + ml.row_off, qrow.data(), mh + ml.mrk_pos, R,
+                          glob ? -1 : c.window / 2,
+                          reinterpret_cast<AttnBlock *>(mh + ml.blk_sub), &nbs);
+    }
+    mh[ml.hdr + H_T] = T;
+    mh[ml.hdr + H_B] = B;
+    mh[ml.hdr + H_R] = R;
+    mh[ml.hdr + H_NBLK] = nbg;
+    mh[ml.hdr + H_NBLK_L] = nbl;
+    mh[ml.hdr + H_NBLK_SUB] = nbs;
+    const int64_t span = ml.ids + T;
+    HIPCHK(hipMemcpyAsync(enc->meta_dev, mh, (size_t)span * 4, hipMemcpyHostToDevice, s));
+    HIPCHK(hipEventRecord(enc->upload_done, s));
+    enc->upload_pending = true;
+    enc->have_upload = true;
+    enc->up_B = B;
+    enc->up_S = S;
+    enc->up_R = R;
+    enc->up_T = T;
+    }  // !resident
+
+    const bool capture = (flags & LAYA_RUN_CAPTURE_LAYERS) != 0;
+    const bool eager = capture || (flags & LAYA_RUN_EAGER) != 0;
+    RunShape rs{B, S, R, T, capture};
+    if (capture) {
+        int r2 = ensure_captures(enc);
+        if (r2 != LAYA_OK) return r2;
+    }
+
+    if (eager) {
+        int r2 = record(enc, s, rs);
+        if (r2 != LAYA_OK) return r2;
+        enc->stats.launches_last_run = enc->launches;
+        enc->have_caps = capture;
+    } else {
+        auto key = std::make_tuple((int)B, (int)S, (int)R);
+        auto it = enc->graphs.find(key);
+        if (it == enc->graphs.end()) {
+            auto t0 = std::chrono::steady_clock::now();
+            RunShape warm{B, S, R, T, false};
+            for (int w = 0; w < 2; ++w) {
+                int r2 = record(enc, s, warm);
+                if (r2 != LAYA_OK) return r2;
+            }
+            HIPCHK(hipStreamSynchronize(s));
+            GraphEntry ge;
+            HIPCHK(hipStreamBeginCapture(enc->cap_stream, hipStreamCaptureModeThreadLocal));
+            int r2 = record(enc, enc->cap_stream, warm);
+            hipGraph_t g = nullptr;
+            hipError_t ec = hipStreamEndCapture(enc->cap_stream, &g);
+            if (r2 != LAYA_OK) {
+                if (g) hipGraphDestroy(g);
+                return r2;
+            }
+            if (ec != hipSuccess)
+                return fail(enc, LAYA_E_DEVICE, std::string("hipStreamEndCapture: ") + hipGetErrorString(ec));
+            ge.graph = g;
+            ge.launches = enc->launches;
+            hipError_t ei = hipGraphInstantiate(&ge.exec, g, nullptr, nullptr, 0);
+            if (ei != hipSuccess) {
+                hipGraphDestroy(g);
+                return fail(enc, LAYA_E_DEVICE, std::string("hipGraphInstantiate: ") + hipGetErrorString(ei));
+            }
+            it = enc->graphs.emplace(key, ge).first;
+            enc->stats.last_capture_ms =
+                std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0)
+                    .count();
+            enc->stats.graphs_cached = (int32_t)enc->graphs.size();
+        }
+        HIPCHK(hipGraphLaunch(it->second.exec, s));
+        enc->stats.launches_last_run = it->second.launches;
+    }
+
+    out->hidden = enc->out;
+    out->rows = R > 0 ? R : T;
+    out->dim = c.hidden;
+    out->row_off = R > 0 ? nullptr : enc->meta_dev + ml.row_off;
+    return LAYA_OK;
+}
+
+int laya_encoder_layer_output(laya_encoder *enc, int32_t index, laya_output *out, char *name,
+                              size_t cap) {
+    if (!enc || !out) return set_global_error(LAYA_E_INVALID, "NULL argument");
+    if (!enc->have_caps) return fail(enc, LAYA_E_INVALID, "last run did not capture layers");
+    if (index < 0 || (size_t)index >= enc->cap_ptrs.size() || enc->cap_names[index].empty())
+        return fail(enc, LAYA_E_INVALID, "layer index out of range");
+    out->hidden = enc->cap_ptrs[index];
+    out->rows = enc->cap_rows[index];
+    out->dim = enc->cfg.hidden;
+    out->row_off = nullptr;
+    if (name && cap) {
+        std::strncpy(name, enc->cap_names[index].c_str(), cap - 1);
+        name[cap - 1] = 0;
+    }
+    return LAYA_OK;
+}
+
+int laya_encoder_weight(laya_encoder *enc, int32_t tid, const void **dev, int32_t *rows,
+                        int32_t *cols) {
+    if (!enc || !dev || !rows || !cols) return set_global_error(LAYA_E_INVALID, "NULL argument");
+    const laya_config &c = enc->cfg;
+    const int NL = layer_count(c);
+    if (tid < 0 || tid > 4 * NL) return fail(enc, LAYA_E_INVALID, "tensor id out of range");
+    const int H = c.hidden, F = c.ffn;
+    if (tid == 0) {
+        *dev = enc->emb;
+        *rows = c.vocab;
+        *cols = H;
+        return LAYA_OK;
+    }
+    const int L = (tid - 1) / 4, kind = (tid - 1) % 4;
+    switch (kind) {
+        case 0: *dev = enc->wqkv[L]; *rows = 3 * H; *cols = H; break;
+        case 1: *dev = enc->wo[L]; *rows = H; *cols = H; break;
+        case 2: *dev = enc->wi[L]; *rows = 2 * F; *cols = H; break;
+        default: *dev = enc->wo2[L]; *rows = H; *cols = F; break;
+    }
+    return LAYA_OK;
+}
+
+int laya_encoder_weight_digest(laya_encoder *enc, int32_t tid, uint64_t *fnv) {
+    if (!enc || !fnv) return set_global_error(LAYA_E_INVALID, "NULL argument");
+    if (enc->poisoned) return fail(enc, LAYA_E_POISONED, "handle poisoned");
+    const void *dev;
+    int32_t rows, cols;
+    int rc = laya_encoder_weight(enc, tid, &dev, &rows, &cols);
+    if (rc != LAYA_OK) return rc;
+    std::vector<uint8_t> hbuf((size_t)rows * cols * 2);
+    HIPCHK(hipSetDevice(enc->device));
+    HIPCHK(hipMemcpy(hbuf.data(), dev, hbuf.size(), hipMemcpyDeviceToHost));
+    uint64_t h = 14695981039346656037ull;
+    for (uint8_t byte : hbuf) {
+        h ^= byte;
+        h *= 1099511628211ull;
+    }
+    *fnv = h;
+    return LAYA_OK;
+}
+
+int laya_encoder_stats(const laya_encoder *enc, laya_stats *st) {
+    if (!enc || !st) return set_global_error(LAYA_E_INVALID, "NULL argument");
+    *st = enc->stats;
+    return LAYA_OK;
+}
+
+int laya_memcpy(void *dst, const void *src, size_t bytes, int32_t kind, void *stream) {
+    if (bytes == 0) return LAYA_OK;
+    if (!dst || !src || kind < 0 || kind > 2)
+        return set_global_error(LAYA_E_INVALID, "laya_memcpy: bad arguments");
+    const hipMemcpyKind k = kind == 0 ? hipMemcpyDeviceToHost
+                            : kind == 1 ? hipMemcpyHostToDevice
+                                        : hipMemcpyDeviceToDevice;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpyAsync(dst, src, bytes, k, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess)
+        return set_global_error(LAYA_E_DEVICE, std::string("laya_memcpy: ") + hipGetErrorString(e));
+    return LAYA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// single-step entry points
+// ---------------------------------------------------------------------------
+#define OPCHK(expr)                                                                       \
+    do {                                                                                  \
+        hipError_t _e = (expr);                                                           \
+        if (_e != hipSuccess)                                                             \
+            return set_global_error(LAYA_E_DEVICE, std::string(#expr) + ": " +            \
+                                                       hipGetErrorString(_e));            \
+    } while (0)
+
+int laya_op_gather(void *stream, const void *emb, int32_t vocab, int32_t hidden,
+                   const int32_t *ids, int32_t T, void *out) {
+    if (T < 0 || vocab <= 0 || hidden <= 0 || hidden % 8 || (T > 0 && (!emb || !ids || !out)))
+        return set_global_error(LAYA_E_INVALID, "laya_op_gather: bad arguments");
+    OPCHK(laya::launch_gather(static_cast<hipStream_t>(stream), static_cast<const bf16_t *>(emb),
+                              ids, nullptr, T, hidden, static_cast<bf16_t *>(out)));
+    return LAYA_OK;
+}
+
+int laya_op_layernorm(void *stream, void *x, const void *r, void *n, const float *gamma,
+                      int32_t T, int32_t hidden, float eps) {
+    if (T < 0 || hidden <= 0 || hidden % 8 || hidden > 2048 || !(eps > 0.f) ||
+        (T > 0 && (!x || !n || !gamma)) || n == x || (r && n == r))
+        return set_global_error(LAYA_E_INVALID, "laya_op_layernorm: bad arguments");
+    OPCHK(laya::launch_layernorm(static_cast<hipStream_t>(stream), static_cast<bf16_t *>(x),
+                                 static_cast<const bf16_t *>(r), static_cast<bf16_t *>(n), gamma,
+                                 nullptr, T, hidden, eps));
+    return LAYA_OK;
+}
+
+int laya_op_gemm(void *stream, const void *A, int32_t lda, const void *W, int32_t ldw, void *C,
+                 int32_t ldc, int32_t M, int32_t N, int32_t K, int32_t epilogue) {
+    if (M < 0 || N <= 0 || K <= 0 || K % 64 || N % 64 || lda % 8 || ldw % 8 || ldc % 8 ||
+        lda < K || ldw < K || ldc < N || (epilogue != 0 && epilogue != 1) ||
+        (M > 0 && (!A || !W || !C)))
+        return set_global_error(LAYA_E_INVALID, "laya_op_gemm: bad arguments");
+    OPCHK(laya::launch_gemm(static_cast<hipStream_t>(stream), static_cast<const bf16_t *>(A), lda,
+                            static_cast<const bf16_t *>(W), ldw, static_cast<bf16_t *>(C), ldc,
+                            nullptr, M, N, K, epilogue));
+    return LAYA_OK;
+}
+
+int laya_op_rope(void *stream, void *buf, int32_t ld, int32_t n_heads_rot, int32_t rows,
+                 const int32_t *pos, const void *cos_tab, const void *sin_tab, int32_t max_pos) {
+    if (rows < 0 || n_heads_rot <= 0 || ld % 8 || ld < n_heads_rot * 64 || max_pos <= 0 ||
+        (rows > 0 && (!buf || !pos || !cos_tab || !sin_tab)))
+        return set_global_error(LAYA_E_INVALID, "laya_op_rope: bad arguments");
+    OPCHK(laya::launch_rope(static_cast<hipStream_t>(stream), static_cast<bf16_t *>(buf), ld,
+                            n_heads_rot, nullptr, rows, pos, static_cast<const bf16_t *>(cos_tab),
+                            static_cast<const bf16_t *>(sin_tab)));
+    return LAYA_OK;
+}
+
+int laya_op_attention(void *stream, const void *q, int32_t ldq, const void *k, const void *v,
+                      int32_t ldkv, void *o, int32_t ldo, int32_t n_heads,
+                      const int32_t *row_off, int32_t B, const int32_t *q_tok, int32_t n_q,
+                      int32_t half_window) {
+    if (B < 0 || n_heads <= 0 || ldq % 8 || ldkv % 8 || ldo % 8 || ldq < n_heads * 64 ||
+        ldkv < n_heads * 64 || ldo < n_heads * 64 || !row_off)
+        return set_global_error(LAYA_E_INVALID, "laya_op_attention: bad arguments");
+    if (row_off[0] != 0)
+        return set_global_error(LAYA_E_INVALID, "laya_op_attention: row_off[0] != 0");
+    for (int b = 0; b < B; ++b)
+        if (row_off[b + 1] <= row_off[b])
+            return set_global_error(LAYA_E_INVALID, "laya_op_attention: empty or decreasing row");
+    const int T = B ? row_off[B] : 0;
+    if (T == 0) return LAYA_OK;
+    if (!q || !k || !v || !o)
+        return set_global_error(LAYA_E_INVALID, "laya_op_attention: NULL buffer");
+    std::vector<int32_t> qpos;
+    std::vector<AttnBlock> blocks;
+    int nb = 0;
+    if (!q_tok) {
+        qpos.resize(T);
+        for (int b = 0; b < B; ++b)
+            for (int t = row_off[b]; t < row_off[b + 1]; ++t) qpos[t] = t - row_off[b];
+        blocks.resize((size_t)B * (512 / laya::kAttnQueries + T / laya::kAttnQueries + 1));
+        build_blocks_full(row_off, B, half_window, blocks.data(), &nb);
+    } else {
+        if (n_q <= 0) return LAYA_OK;
+        qpos.resize(n_q);
+        std::vector<int32_t> qrow(n_q);
+        for (int r = 0; r < n_q; ++r) {
+            const int t = q_tok[r];
+            if (t < 0 || t >= T)
+                return set_global_error(LAYA_E_INVALID, "laya_op_attention: q_tok out of range");
+            const int b = (int)(std::upper_bound(row_off, row_off + B + 1, t) - row_off) - 1;
+            qrow[r] = b;
+            qpos[r] = t - row_off[b];
+        }
+        blocks.resize(n_q);
+        build_blocks_list(row_off, qrow.data(), qpos.data(), n_q, half_window, blocks.data(), &nb);
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void *dmem = nullptr;
+    const size_t bbytes = (size_t)nb * sizeof(AttnBlock);
+    OPCHK(hipMalloc(&dmem, bbytes + qpos.size() * 4));
+    hipError_t e = hipMemcpyAsync(dmem, blocks.data(), bbytes, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(static_cast<char *>(dmem) + bbytes, qpos.data(), qpos.size() * 4,
+                           hipMemcpyHostToDevice, s);
+    if (e == hipSuccess)
+        e = laya::launch_attention(s, static_cast<const bf16_t *>(q), ldq,
+                                   static_cast<const bf16_t *>(k), static_cast<const bf16_t *>(v),
+                                   ldkv, static_cast<bf16_t *>(o), ldo,
+                                   static_cast<const AttnBlock *>(dmem), nullptr, nb,
+                                   reinterpret_cast<const int32_t *>(static_cast<char *>(dmem) + bbytes),
+                                   n_heads, half_window);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    hipFree(dmem);
+    if (e != hipSuccess)
+        return set_global_error(LAYA_E_DEVICE, std::string("laya_op_attention: ") + hipGetErrorString(e));
+    return LAYA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,59 @@
+// Internal launch functions of the gfx950 kernels.  Every launch queues on
+// the given stream and returns the launch status; none synchronises.
+//
+// Row counts: where a kernel takes (count_dev, count_max), it processes
+// *count_dev rows when count_dev != nullptr (read on the device, so a captured
+// graph serves any count <= count_max) and count_max rows otherwise.  Grids
+// are always sized for count_max; surplus workgroups exit at once.
+#pragma once
+
+#include "common.h"
+
+namespace laya {
+
+// Attention work item: up to 64 queries of one batch row, one head per
+// workgroup.  Keys of the row are tokens kt0 .. kt0+klen-1 (positions
+// 0..klen-1); the block only visits key positions [k_lo, k_hi).  Queries are
+// rows q_first .. q_first+q_count-1 of the query/output buffers, with
+// positions qpos[q_first + i].
+struct AttnBlock {
+    int32_t kt0, klen, k_lo, k_hi, q_first, q_count, pad0, pad1;
+};
+static_assert(sizeof(AttnBlock) == 32, "AttnBlock is 8 int32");
+
+constexpr int kAttnQueries = 64;  // queries per block
+
+hipError_t launch_init_weights(hipStream_t s, bf16_t *dst, uint64_t n, uint64_t seed,
+                               uint32_t tensor_id);
+
+hipError_t launch_fill_f32(hipStream_t s, float *dst, int32_t n, float value);
+
+hipError_t launch_gather(hipStream_t s, const bf16_t *emb, const int32_t *ids,
+                         const int32_t *count_dev, int32_t count_max, int32_t hidden,
+                         bf16_t *out);
+
+// dst[r][0:cols] = src[idx[r]][0:cols] for r < n (bit-exact).
+hipError_t launch_gather_rows(hipStream_t s, const bf16_t *src, int32_t ld_src,
+                              const int32_t *idx, int32_t n, int32_t cols, bf16_t *dst,
+                              int32_t ld_dst);
+
+hipError_t launch_layernorm(hipStream_t s, bf16_t *x, const bf16_t *r, bf16_t *n,
+                            const float *gamma, const int32_t *count_dev, int32_t count_max,
+                            int32_t hidden, float eps);
+
+// C = bf16(A W^T), epilogue 0 plain, 1 GeGLU (W has 2N rows).
+hipError_t launch_gemm(hipStream_t s, const bf16_t *A, int32_t lda, const bf16_t *W,
+                       int32_t ldw, bf16_t *C, int32_t ldc, const int32_t *M_dev,
+                       int32_t M_max, int32_t N, int32_t K, int epilogue);
+
+hipError_t launch_rope(hipStream_t s, bf16_t *buf, int32_t ld, int32_t n_heads_rot,
+                       const int32_t *count_dev, int32_t rows_max, const int32_t *pos,
+                       const bf16_t *cos_tab, const bf16_t *sin_tab);
+
+hipError_t launch_attention(hipStream_t s, const bf16_t *q, int32_t ldq, const bf16_t *k,
+                            const bf16_t *v, int32_t ldkv, bf16_t *o, int32_t ldo,
+                            const AttnBlock *blocks, const int32_t *nblk_dev,
+                            int32_t nblk_max, const int32_t *qpos, int32_t n_heads,
+                            int32_t half_window);
+
+}  // namespace laya
