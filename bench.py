@@ -31,6 +31,13 @@ METRIC = "encoder calls/s + p50 ms (28+2 layers, BF16) at 1×48 and 16×512, 1 G
 # run 1), quoted for context: 38.7 req/s at 16x512, 358.9 req/s at 1x48.
 PAGES_CALLS_PER_S = {"mixed_16": 38.7, "short_1": 358.9, "short_3": 311.0, "long_3": 132.9}
 
+# kernel symbol that runs each op class (for matching rocprofv3 summaries)
+DOMINANT_KERNEL_SYMBOL = {
+    "up_geglu_gemm": "gemm_bf16_kernel<1>", "qkv_gemm": "gemm_bf16_kernel<0>",
+    "down_gemm": "gemm_bf16_kernel<0>", "out_proj_gemm": "gemm_bf16_kernel<0>",
+    "attention": "attention_kernel", "layernorm": "layernorm_kernel<2>", "rope": "rope_kernel",
+}
+
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense BF16 MFMA
 PEAK_HBM_GBS = 8000.0
 
@@ -42,37 +49,39 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="mixed_16")
     p.add_argument("--latency-calls", type=int, default=50)
-    p.add_argument("--kernel-iters", type=int, default=20)
+    p.add_argument("--profile-passes", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-rows", type=int, default=4)
     return p.parse_args()
 
 
-def gemm_shapes(cfg, T):
-    H, F = cfg["hidden"], cfg["ffn"]
-    # (name, M, N, K, epilogue, algorithmic FLOPs)
-    return [("qkv", T, 3 * H, H, 0, 2.0 * T * 3 * H * H),
-            ("o", T, H, H, 0, 2.0 * T * H * H),
-            ("up_geglu", T, F, H, 1, 2.0 * T * 2 * F * H),
-            ("down", T, H, F, 0, 2.0 * T * H * F)]
-
-
-def time_kernel(binding, torch, M, N, K, epi, iters):
-    """Average duration (s) of one GEMM launch, HIP events on its stream."""
-    a = torch.randn((M, K), device="cuda").to(torch.bfloat16)
-    w = (0.02 * torch.randn((2 * N if epi else N, K), device="cuda")).to(torch.bfloat16)
-    c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-    stream = torch.cuda.current_stream()
-    for _ in range(3):
-        binding.op_gemm(a, w, c, M, N, K, epi)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(iters):
-        binding.op_gemm(a, w, c, M, N, K, epi)
-    e1.record(stream)
-    e1.synchronize()
-    return e0.elapsed_time(e1) / 1000.0 / iters
+def op_table(enc, batch, mk, repeats):
+    """Per-op-class average of `repeats` event-bracketed eager passes."""
+    acc, tot = {}, 0.0
+    for _ in range(repeats):
+        ops, t = enc.profile(batch.ids, batch.lengths, markers=mk)
+        tot += t
+        for k, v in ops.items():
+            a = acc.setdefault(k, {"calls": 0, "ms": 0.0, "flops": 0.0, "bytes": 0.0})
+            for f in a:
+                a[f] += v[f]
+    table = {}
+    for k, v in acc.items():
+        sec = v["ms"] / 1e3
+        per_launch_us = v["ms"] / v["calls"] * 1e3
+        row = {"launches_per_pass": v["calls"] // repeats,
+               "ms_per_pass": round(v["ms"] / repeats, 4),
+               "share": round(v["ms"] / sum(x["ms"] for x in acc.values()), 4),
+               "avg_launch_us": round(per_launch_us, 2)}
+        if v["flops"] > 0:
+            row["tflops"] = round(v["flops"] / sec / 1e12, 1)
+            row["mfma_frac"] = round(v["flops"] / sec / 1e12 / PEAK_BF16_TFLOPS, 4)
+        row["hbm_gbs"] = round(v["bytes"] / sec / 1e9, 1)
+        row["hbm_frac"] = round(v["bytes"] / sec / 1e9 / PEAK_HBM_GBS, 4)
+        row["_flops"], row["_bytes"], row["_calls"], row["_sec"] = (v["flops"], v["bytes"],
+                                                                    v["calls"], sec)
+        table[k] = row
+    return table, tot / repeats
 
 
 def cpu_baseline(cfg, batch, rows):
@@ -160,18 +169,28 @@ def main():
         eager.append((time.perf_counter() - t) * 1e3)
     launches = enc.stats()["launches_last_run"]
 
-    # dominant kernel: GEMMs, timed per launch with HIP events
-    T = batch.T
-    shapes = gemm_shapes(MODEL, T)
-    ktimes = {}
-    for name, M, N, K, epi, flops in shapes:
-        ktimes[name] = time_kernel(binding, torch, M, N, K, epi, args.kernel_iters)
-    gemm_flops = sum(s[5] for s in shapes)
-    gemm_time = sum(ktimes.values())
-    dom = "up_geglu"
-    dom_flops = [s[5] for s in shapes if s[0] == dom][0]
-    achieved = dom_flops / ktimes[dom] / 1e12
+    # per-op table from event-bracketed eager passes (HIP events on the launch stream)
+    table, pass_ms = op_table(enc, batch, mk, args.profile_passes)
     enc.close()
+    dom = max(table, key=lambda k: table[k]["ms_per_pass"])
+    d = table[dom]
+    if d["_flops"] > 0:
+        roof = {"bound": "mfma", "achieved": round(d["_flops"] / d["_sec"] / 1e12, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(d["_bytes"] / d["_sec"] / 1e9, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = None
+    roof["op"] = dom
+    roof["kernel"] = DOMINANT_KERNEL_SYMBOL.get(dom, dom)
+    roof["avg_launch_us"] = d["avg_launch_us"]
+    roof["per_launch_algorithmic"] = (d["_flops"] if d["_flops"] > 0 else d["_bytes"]) / d["_calls"]
+    gemm_ops = [k for k in table if k.endswith("_gemm")]
+    gemm_frac = (sum(table[k]["_flops"] for k in gemm_ops) /
+                 sum(table[k]["_sec"] for k in gemm_ops) / 1e12 / PEAK_BF16_TFLOPS)
+    ops_out = {k: {f: v for f, v in row.items() if not f.startswith("_")}
+               for k, row in sorted(table.items(), key=lambda kv: -kv[1]["ms_per_pass"])}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -205,13 +224,10 @@ def main():
         "capture_ms": round(capture_ms, 2),
         "create_ms": round(st0["create_ms"], 1),
         "launches_per_call": launches,
-        "roofline": {"bound": "mfma", "kernel": "GeGLU-up GEMM (gemm_bf16_kernel<1>)",
-                     "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None,
-                     "avg_launch_us": round(ktimes[dom] * 1e6, 2)},
-        "gemm_mfma_frac": round(gemm_flops / gemm_time / 1e12 / PEAK_BF16_TFLOPS, 4),
-        "gemm_kernel_us": {k: round(v * 1e6, 2) for k, v in ktimes.items()},
+        "roofline": roof,
+        "gemm_mfma_frac": round(gemm_frac, 4),
+        "profiled_pass_ms": round(pass_ms, 4),
+        "ops": ops_out,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

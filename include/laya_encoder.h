@@ -226,6 +226,28 @@ int laya_encoder_weight(laya_encoder *enc, int32_t tensor_id, const void **dev,
 
 int laya_encoder_stats(const laya_encoder *enc, laya_stats *stats);
 
+/* Per-op time of one eager pass (the pages' per-op share table of the
+ * "profile_forward" tool, page "perf(model): exact Metal speed-ups of the
+ * forward pass"): the same launches as laya_encoder_run, each bracketed by
+ * HIP events on `stream`, aggregated by op class.  flops and bytes are the
+ * algorithmic work of the class's launches (GEMMs 2*M*N*K; attention
+ * 4*64*heads per visible (query, key) pair; bytes = the tensors each launch
+ * must read and write once, in BF16).  Arguments as laya_encoder_run;
+ * synchronous; out receives up to `cap` classes, *n_out how many, *total_ms
+ * (may be NULL) the event span of the whole pass.  Diagnostic only. */
+typedef struct laya_op_time {
+    char name[24];
+    int32_t calls;
+    double total_ms;
+    double flops;
+    double bytes;
+} laya_op_time;
+
+int laya_encoder_profile(laya_encoder *enc, void *stream, const int32_t *token_ids,
+                         const int32_t *lengths, int32_t B, int32_t S,
+                         const int32_t *markers, int32_t R, laya_op_time *out, int32_t cap,
+                         int32_t *n_out, double *total_ms);
+
 /* Rotary table of laya_encoder_create, on the host: cos_bits/sin_bits receive
  * max_pos * head_dim/2 BF16 bit patterns ([p][i] row-major).  Host only. */
 int laya_rope_table(float theta, int32_t max_pos, int32_t head_dim,

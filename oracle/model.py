@@ -68,8 +68,14 @@ def layer_norm(x: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
     return (d / np.sqrt(var + np.float32(eps)) * gamma).astype(np.float32)
 
 
-def linear(a: np.ndarray, w: np.ndarray) -> np.ndarray:
-    """a [T, K] times w [N, K] transposed, in float32 (nn.Linear without bias)."""
+def linear(a: np.ndarray, w: np.ndarray, accumulate: str = "float32") -> np.ndarray:
+    """a [T, K] times w [N, K] transposed (nn.Linear without bias), returned in
+    float32.  The sum is accumulated in float32 (the pass's stated precision)
+    or, with accumulate="float64", in float64 and rounded once to float32: the
+    same definition with a different accumulation error, used to measure how
+    far two valid implementations of the BF16 pass drift apart."""
+    if accumulate == "float64":
+        return np.matmul(np.asarray(a, np.float64), np.asarray(w, np.float64).T).astype(np.float32)
     return np.matmul(np.asarray(a, np.float32), np.asarray(w, np.float32).T)
 
 
@@ -106,16 +112,20 @@ def layer_kinds(cfg: dict):
 class Oracle:
     """The CPU oracle for one model configuration and one set of weights."""
 
-    def __init__(self, cfg: dict, weights, rounding: bool = True):
+    def __init__(self, cfg: dict, weights, rounding: bool = True, accumulate: str = "float32"):
         self.cfg = dict(cfg)
         self.w = weights
         self.rounding = rounding
+        self.accumulate = accumulate
         hd = cfg["head_dim"]
         self.tables = {th: rope_tables(th, cfg["max_seq"], hd)
                        for th in {cfg["theta_global"], cfg["theta_local"]}}
 
     def R(self, x):
         return bf16_round(x) if self.rounding else np.asarray(x, dtype=np.float32)
+
+    def lin(self, a, w):
+        return linear(a, w, self.accumulate)
 
     # -- one layer -----------------------------------------------------------
     def layer(self, L: int, x: np.ndarray, pos: np.ndarray, row_off: np.ndarray,
@@ -136,15 +146,15 @@ class Oracle:
         n = R(layer_norm(x, g_attn, eps))
         T = x.shape[0]
         if q_tok is None:
-            qkv = R(linear(n, wqkv))
+            qkv = R(self.lin(n, wqkv))
             q = qkv[:, :H]
             kv = qkv[:, H:]
             q_pos = pos
             rows_q = [np.arange(row_off[b], row_off[b + 1]) for b in range(len(row_off) - 1)]
             x_q = x
         else:
-            kv = R(linear(n, wqkv[H:]))
-            q = R(linear(n[q_tok], wqkv[:H]))
+            kv = R(self.lin(n, wqkv[H:]))
+            q = R(self.lin(n[q_tok], wqkv[:H]))
             q_pos = pos[q_tok]
             x_q = x[q_tok]
             rows_q = []
@@ -163,22 +173,25 @@ class Oracle:
             o[qi] = attention(q[qi], k[ks], v[ks], q_pos[qi], pos[ks], nh, hd, hw,
                               self.rounding)
 
-        a = R(linear(o, self.w.f32(f"L{L}.wo")))
+        a = R(self.lin(o, self.w.f32(f"L{L}.wo")))
         x1 = R(x_q + a)
         n2 = R(layer_norm(x1, g_ffn, eps))
-        ug = linear(n2, self.w.f32(f"L{L}.wi"))
+        ug = self.lin(n2, self.w.f32(f"L{L}.wi"))
         h = R(gelu(ug[:, :F]) * ug[:, F:])
-        f = R(linear(h, self.w.f32(f"L{L}.wo2")))
+        f = R(self.lin(h, self.w.f32(f"L{L}.wo2")))
         return R(x1 + f)
+
+    def final_norm(self, x: np.ndarray, which: str) -> np.ndarray:
+        """R(LN(x)) with the gain of "ln_enc_final" or "ln_dec_final"."""
+        return self.R(layer_norm(x, self.w.gamma[which], self.cfg["ln_eps"]))
 
     # -- the whole pass ------------------------------------------------------
     def forward(self, ids, lengths, markers=None, capture: bool = False):
         """Returns {'out': [T or R, H] float32 BF16 values, 'row_off', 'pos',
         'layers': [(name, array)] when capture}."""
-        cfg, R = self.cfg, self.R
+        cfg = self.cfg
         tok, pos, row_off = pack(ids, lengths)
         n_enc, n_dec = cfg["n_enc_layers"], cfg["n_dec_layers"]
-        eps = cfg["ln_eps"]
         layers = []
         x = self.w.f32("emb")[tok]
         if capture:
@@ -195,11 +208,45 @@ class Oracle:
                 name = f"enc{L:02d}" if L < n_enc else f"dec{L - n_enc}"
                 layers.append((name, x.copy()))
             if L == n_enc - 1:
-                x = R(layer_norm(x, self.w.gamma["ln_enc_final"], eps))
+                x = self.final_norm(x, "ln_enc_final")
                 if capture:
                     layers.append(("enc_final", x.copy()))
-        out = R(layer_norm(x, self.w.gamma["ln_dec_final"], eps))
+        out = self.final_norm(x, "ln_dec_final")
         if capture:
             layers.append(("out", out.copy()))
         return {"out": out, "row_off": row_off, "pos": pos, "tok": tok,
                 "q_tok": q_tok, "layers": layers}
+
+    def layer_names(self):
+        n_enc, n_dec = self.cfg["n_enc_layers"], self.cfg["n_dec_layers"]
+        names = ["emb"] + [f"enc{L:02d}" for L in range(n_enc)] + ["enc_final"]
+        return names + [f"dec{L}" for L in range(n_dec)] + ["out"]
+
+    def forward_layerwise(self, ids, lengths, inputs: dict, markers=None) -> dict:
+        """Each step of the pass applied to a GIVEN input instead of the
+        oracle's own previous output: for every captured name except "emb",
+        the oracle's result of that one layer (or closing LayerNorm) when fed
+        inputs[previous name].  Isolates the error each layer adds."""
+        cfg = self.cfg
+        tok, pos, row_off = pack(ids, lengths)
+        n_enc, n_dec = cfg["n_enc_layers"], cfg["n_dec_layers"]
+        q_tok = None
+        if markers is not None:
+            m = np.asarray(markers, dtype=np.int64).reshape(-1, 2)
+            q_tok = row_off[m[:, 0]] + m[:, 1]
+        names = self.layer_names()
+        out = {}
+        prev = "emb"
+        L = 0
+        for name in names[1:]:
+            x = np.asarray(inputs[prev], dtype=np.float32)
+            if name == "enc_final":
+                out[name] = self.final_norm(x, "ln_enc_final")
+            elif name == "out":
+                out[name] = self.final_norm(x, "ln_dec_final")
+            else:
+                last = L == n_enc + n_dec - 1
+                out[name] = self.layer(L, x, pos, row_off, q_tok if last else None)
+                L += 1
+            prev = name
+        return out

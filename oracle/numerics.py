@@ -49,12 +49,13 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
 
 def gelu(u: np.ndarray) -> np.ndarray:
     """GELU(z) = z * Phi(z) = 0.5 * z * (1 + erf(z / sqrt 2)), the exact (erf)
-    form; evaluated in float64 (torch's CPU erf) and returned as the nearest
-    float32."""
+    form, written as 0.5 * z * erfc(-z / sqrt 2) so that the negative tail
+    keeps its relative accuracy; evaluated in float64 (torch's CPU erfc) and
+    returned as the nearest float32."""
     import torch
 
     z = torch.from_numpy(np.asarray(u, dtype=np.float64))
-    g = 0.5 * z * (1.0 + torch.special.erf(z * (1.0 / math.sqrt(2.0))))
+    g = 0.5 * z * torch.special.erfc(z * (-1.0 / math.sqrt(2.0)))
     return g.numpy().astype(np.float32)
 
 

@@ -31,6 +31,25 @@ def ulp_diff(a: np.ndarray, b: np.ndarray) -> np.ndarray:
     return np.abs(ordered(a) - ordered(b))
 
 
+def bf16_close(got: np.ndarray, want: np.ndarray, ulps: float = 1.0,
+               floor_rel: float = 2.0 ** -16):
+    """Element-wise check for float32-accumulated results stored as BF16.
+
+    An element passes if it is within `ulps` BF16 ulps of the reference, or
+    within floor_rel * rms(reference) of it: near zero the BF16 ulp shrinks
+    without bound while the float32 summation error does not.  Returns
+    (number of failing elements, fraction of elements not bitwise equal)."""
+    g = np.asarray(got, np.float64)
+    w = np.asarray(want, np.float64)
+    rms = float(np.sqrt(np.mean(w * w))) if w.size else 0.0
+    mag = np.maximum(np.abs(w), 1e-38)
+    ulp = np.exp2(np.floor(np.log2(mag)) - 7)
+    allowed = np.maximum(ulps * ulp, floor_rel * rms)
+    bad = int((np.abs(g - w) > allowed).sum())
+    frac = float((bits_of(got) != bits_of(want)).mean()) if w.size else 0.0
+    return bad, frac
+
+
 def report(name: str, payload: dict):
     """Append a parity record to <report dir>/parity_report.jsonl when the
     report directory exists (gpurun_out/ on a GPU run)."""

@@ -3,14 +3,14 @@
 Each kernel is called through the C ABI (laya_op_*) on seeded inputs and
 compared with the oracle element by element: bit-exact for the gather and
 for RoPE, within one BF16 ulp (float32 summation order) for LayerNorm and the
-GEMMs, within a small nRMS for attention (whose P is rounded to BF16 before
-the P V product, the one interior rounding the oracle does not mirror).
+GEMMs, within a small nRMS for attention (online softmax, and P carried into
+the P V product as a BF16 head plus a BF16 tail).
 """
 import numpy as np
 import pytest
 
 import oracle
-from tests.gpu_helpers import bits_of, ensure_built, from_dev, report, to_dev, ulp_diff
+from tests.gpu_helpers import bf16_close, bits_of, ensure_built, from_dev, report, to_dev, ulp_diff
 from transformer_encoder_bf16_amd.inputs import random_gamma, random_normal
 
 pytestmark = pytest.mark.gpu
@@ -98,11 +98,12 @@ def test_gemm_plain(B, M, N, K):
     _sync()
     want = oracle.bf16_round(oracle.linear(a_h, w_h))
     got = from_dev(c)
-    d = ulp_diff(got, want)
-    assert d.max() <= 1, (M, N, K)
-    assert (d > 0).mean() < 0.01
-    report("gemm", {"M": M, "N": N, "K": K, "max_ulp": int(d.max()),
-                    "frac_diff": float((d > 0).mean()), "nrms": oracle.nrms(got, want)})
+    bad, frac = bf16_close(got, want)
+    e = oracle.nrms(got, want)
+    report("gemm", {"M": M, "N": N, "K": K, "bad": bad, "frac_diff": frac, "nrms": e})
+    assert bad == 0, (M, N, K)
+    assert frac < 0.01
+    assert e < 1e-4
 
 
 @pytest.mark.parametrize("M,F,K", [(1, 192, 128), (48, 2624, 1024), (333, 2624, 1024),
@@ -118,12 +119,12 @@ def test_gemm_geglu(B, M, F, K):
     ug = oracle.linear(a_h, w_h)
     want = oracle.bf16_round(oracle.gelu(ug[:, :F]) * ug[:, F:])
     got = from_dev(c)
-    d = ulp_diff(got, want)
-    assert d.max() <= 2, (M, F, K)
-    assert (d > 0).mean() < 0.02
-    assert oracle.nrms(got, want) < 2e-3
-    report("gemm_geglu", {"M": M, "F": F, "K": K, "max_ulp": int(d.max()),
-                          "frac_diff": float((d > 0).mean()), "nrms": oracle.nrms(got, want)})
+    bad, frac = bf16_close(got, want)
+    e = oracle.nrms(got, want)
+    report("gemm_geglu", {"M": M, "F": F, "K": K, "bad": bad, "frac_diff": frac, "nrms": e})
+    assert bad == 0, (M, F, K)
+    assert frac < 0.02
+    assert e < 1e-4
 
 
 def test_gemm_rejects_bad_shapes(B):

@@ -304,6 +304,17 @@ def test_marker_subset_equals_full_rows(tiny_weights):
     assert oracle.nrms(sub["out"], full["out"][rows]) < 1e-3
 
 
+def test_layerwise_on_own_captures_reproduces_forward(tiny_weights):
+    b = random_batch(TINY, 3, 24, seed=8, len_lo=4, markers_per_row=3)
+    o = oracle.Oracle(TINY, tiny_weights)
+    for mk in (None, b.markers):
+        caps = dict(o.forward(b.ids, b.lengths, markers=mk, capture=True)["layers"])
+        lw = o.forward_layerwise(b.ids, b.lengths, caps, markers=mk)
+        assert list(lw) == o.layer_names()[1:]
+        for name, y in lw.items():
+            assert np.array_equal(y, caps[name]), name
+
+
 def test_reversed_rows_and_padding_ids_do_not_change_outputs(tiny_weights):
     b = random_batch(TINY, 4, 20, seed=7, len_lo=3)
     o = oracle.Oracle(TINY, tiny_weights)

@@ -40,7 +40,7 @@ EXPORTS = [
     "laya_encoder_create", "laya_encoder_run", "laya_encoder_destroy",
     "laya_encoder_last_error", "laya_last_error", "laya_encoder_layer_output",
     "laya_encoder_weight_digest", "laya_encoder_weight", "laya_encoder_stats",
-    "laya_rope_table", "laya_memcpy", "laya_op_gather", "laya_op_layernorm", "laya_op_gemm",
+    "laya_encoder_profile", "laya_rope_table", "laya_memcpy", "laya_op_gather", "laya_op_layernorm", "laya_op_gemm",
     "laya_op_rope", "laya_op_attention",
 ]
 
@@ -76,6 +76,12 @@ class Config(ctypes.Structure):
 class Output(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_void_p), ("rows", ctypes.c_int32),
                 ("dim", ctypes.c_int32), ("row_off", ctypes.c_void_p)]
+
+
+class OpTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 24), ("calls", ctypes.c_int32),
+                ("total_ms", ctypes.c_double), ("flops", ctypes.c_double),
+                ("bytes", ctypes.c_double)]
 
 
 class Stats(ctypes.Structure):
@@ -120,6 +126,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         "laya_encoder_weight": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.POINTER(_P), _I32P,
                                                _I32P]),
         "laya_encoder_stats": (ctypes.c_int, [_P, ctypes.POINTER(Stats)]),
+        "laya_encoder_profile": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32,
+                                                _P, ctypes.c_int32, ctypes.POINTER(OpTime),
+                                                ctypes.c_int32, _I32P,
+                                                ctypes.POINTER(ctypes.c_double)]),
         "laya_rope_table": (ctypes.c_int, [ctypes.c_float, ctypes.c_int32, ctypes.c_int32, _P,
                                            _P]),
         "laya_memcpy": (ctypes.c_int, [_P, _P, ctypes.c_size_t, ctypes.c_int32, _P]),
@@ -290,6 +300,30 @@ class Encoder:
                "laya_encoder_weight", self.handle)
         return copy_to_host(p.value, r.value * c.value * 2, 0).view(np.uint16).reshape(
             r.value, c.value)
+
+    def profile(self, ids, lengths, markers=None, stream: Optional[int] = None):
+        """Per-op-class event times of one eager pass: ({name: {calls, ms, flops,
+        bytes}}, total_ms)."""
+        ids = _i32(ids)
+        lengths = _i32(lengths)
+        B = int(lengths.shape[0])
+        S = int(ids.shape[1]) if ids.ndim == 2 and B else 0
+        mk = None if markers is None else _i32(markers).reshape(-1, 2)
+        R = 0 if mk is None else int(mk.shape[0])
+        arr = (OpTime * 32)()
+        n = ctypes.c_int32()
+        tot = ctypes.c_double()
+        st = current_stream() if stream is None else stream
+        _check(self.lib.laya_encoder_profile(self.handle, st, _ptr(ids), _ptr(lengths), B, S,
+                                             _ptr(mk), R, arr, 32, ctypes.byref(n),
+                                             ctypes.byref(tot)),
+               "laya_encoder_profile", self.handle)
+        res = {}
+        for i in range(n.value):
+            a = arr[i]
+            res[a.name.decode()] = {"calls": a.calls, "ms": a.total_ms, "flops": a.flops,
+                                    "bytes": a.bytes}
+        return res, tot.value
 
     def stats(self) -> dict:
         s = Stats()

@@ -374,13 +374,35 @@ struct RunShape {
     int B, S, R;
     int T;  // actual tokens (host value; used only for captures in eager mode)
     bool capture_layers;
+    // host-side algorithmic counts, used only when profiling
+    double pairs_global = 0, pairs_local = 0, pairs_subset = 0;
+};
+
+// Op classes of the per-launch profile (laya_encoder_profile).
+enum OpKind {
+    OP_GATHER, OP_LAYERNORM, OP_QKV, OP_ROPE, OP_ATTENTION, OP_OUT_PROJ, OP_UP_GEGLU, OP_DOWN,
+    OP_ROW_GATHER, OP_KV, OP_Q, OP_COUNT
+};
+const char *const kOpNames[OP_COUNT] = {
+    "gather", "layernorm", "qkv_gemm", "rope", "attention", "out_proj_gemm",
+    "up_geglu_gemm", "down_gemm", "row_gather", "kv_gemm", "q_gemm"};
+
+struct ProfRec {
+    int op;
+    double flops, bytes;
+};
+
+struct Profiler {
+    std::vector<hipEvent_t> ev;  // two per launch
+    std::vector<ProfRec> recs;
+    size_t n = 0;
 };
 
 int layer_count(const laya_config &c) { return c.n_enc_layers + c.n_dec_layers; }
 
 // Queue the whole pass on stream s.  Reads T, the row layout and the
 // attention work lists from the device copy of the index upload.
-int record(laya_encoder *enc, hipStream_t s, const RunShape &rs) {
+int record(laya_encoder *enc, hipStream_t s, const RunShape &rs, Profiler *prof = nullptr) {
     const laya_config &c = enc->cfg;
     const int H = c.hidden, F = c.ffn, nh = c.n_heads;
     const int NL = layer_count(c);
@@ -412,12 +434,24 @@ int record(laya_encoder *enc, hipStream_t s, const RunShape &rs) {
         ++ci;
         return LAYA_OK;
     };
-#define L_CHK(expr)                                                                   \
+    // Every launch goes through L_OP: op class, algorithmic FLOPs and HBM
+    // bytes (for the profile), and the launch itself.
+#define L_OP(op, fl, by, expr)                                                        \
     do {                                                                              \
+        if (prof) {                                                                   \
+            if (prof->n >= prof->recs.size())                                         \
+                return fail(enc, LAYA_E_INVALID, "profile event pool too small");     \
+            prof->recs[prof->n] = ProfRec{(op), (fl), (by)};                          \
+            HIPCHK(hipEventRecord(prof->ev[2 * prof->n], s));                         \
+        }                                                                             \
         hipError_t _e = (expr);                                                       \
         ++enc->launches;                                                              \
         if (_e != hipSuccess)                                                         \
             return fail(enc, LAYA_E_DEVICE, std::string(#expr) + ": " + hipGetErrorString(_e)); \
+        if (prof) {                                                                   \
+            HIPCHK(hipEventRecord(prof->ev[2 * prof->n + 1], s));                     \
+            ++prof->n;                                                                \
+        }                                                                             \
     } while (0)
 #define C_CHK(expr)                      \
     do {                                 \
@@ -425,8 +459,17 @@ int record(laya_encoder *enc, hipStream_t s, const RunShape &rs) {
         if (_r != LAYA_OK) return _r;    \
     } while (0)
 
+    const double T = rs.T, R = rs.R, b2 = 2.0;
+    auto gemm_fl = [](double M, double N, double K) { return 2.0 * M * N * K; };
+    auto gemm_by = [&](double M, double Nw, double N, double K) {
+        return b2 * (M * K + Nw * K + M * N);
+    };
+    const double ln_res_by = 4 * T * H * b2, ln_by = 2 * T * H * b2;
+    const double attn_fl_per_pair = 4.0 * c.head_dim * nh;
+
     bf16_t *xr = enc->xa, *xalt = enc->xb;
-    L_CHK(laya::launch_gather(s, enc->emb, ids, T_dev, Tmax, H, xr));
+    L_OP(OP_GATHER, 0, 2 * T * H * b2 + 4 * T,
+         laya::launch_gather(s, enc->emb, ids, T_dev, Tmax, H, xr));
     C_CHK(cap("emb", xr, rs.T));
     bool pending = false;  // the down projection of the previous layer waits in proj
     char name[32];
@@ -444,8 +487,9 @@ int record(laya_encoder *enc, hipStream_t s, const RunShape &rs) {
         const float *g1 = enc->gamma_ones;
 
         // attention sublayer: n = LN(x [+ f of the previous layer])
-        L_CHK(laya::launch_layernorm(s, xr, pending ? enc->proj : nullptr, enc->nrm, g1, T_dev,
-                                     Tmax, H, c.ln_eps));
+        L_OP(OP_LAYERNORM, 0, pending ? ln_res_by : ln_by,
+             laya::launch_layernorm(s, xr, pending ? enc->proj : nullptr, enc->nrm, g1, T_dev,
+                                    Tmax, H, c.ln_eps));
         if (pending) {
             std::snprintf(name, sizeof name, (L - 1) < c.n_enc_layers ? "enc%02d" : "dec%d",
                           (L - 1) < c.n_enc_layers ? L - 1 : L - 1 - c.n_enc_layers);
@@ -453,22 +497,31 @@ int record(laya_encoder *enc, hipStream_t s, const RunShape &rs) {
         }
         pending = false;
         if (!subset) {
-            L_CHK(laya::launch_gemm(s, enc->nrm, H, Wqkv, H, enc->qkv, 3 * H, T_dev, Tmax, 3 * H,
-                                    H, 0));
-            L_CHK(laya::launch_rope(s, enc->qkv, 3 * H, 2 * nh, T_dev, Tmax, pos, ctab, stab));
-            L_CHK(laya::launch_attention(s, enc->qkv, 3 * H, enc->qkv + H, enc->qkv + 2 * H,
-                                         3 * H, enc->att, H, blk, nblk, ml.nblk_full_max, pos,
-                                         nh, half));
-            L_CHK(laya::launch_gemm(s, enc->att, H, Wo, H, enc->proj, H, T_dev, Tmax, H, H, 0));
-            L_CHK(laya::launch_layernorm(s, xr, enc->proj, enc->nrm, g1, T_dev, Tmax, H,
-                                         c.ln_eps));
-            L_CHK(laya::launch_gemm(s, enc->nrm, H, Wi, H, enc->hid, F, T_dev, Tmax, F, H, 1));
-            L_CHK(laya::launch_gemm(s, enc->hid, F, Wo2, F, enc->proj, H, T_dev, Tmax, H, F, 0));
+            L_OP(OP_QKV, gemm_fl(T, 3 * H, H), gemm_by(T, 3 * H, 3 * H, H),
+                 laya::launch_gemm(s, enc->nrm, H, Wqkv, H, enc->qkv, 3 * H, T_dev, Tmax, 3 * H,
+                                   H, 0));
+            L_OP(OP_ROPE, 0, 2 * T * 2 * H * b2,
+                 laya::launch_rope(s, enc->qkv, 3 * H, 2 * nh, T_dev, Tmax, pos, ctab, stab));
+            L_OP(OP_ATTENTION, attn_fl_per_pair * (glob ? rs.pairs_global : rs.pairs_local),
+                 4 * T * H * b2,
+                 laya::launch_attention(s, enc->qkv, 3 * H, enc->qkv + H, enc->qkv + 2 * H,
+                                        3 * H, enc->att, H, blk, nblk, ml.nblk_full_max, pos,
+                                        nh, half));
+            L_OP(OP_OUT_PROJ, gemm_fl(T, H, H), gemm_by(T, H, H, H),
+                 laya::launch_gemm(s, enc->att, H, Wo, H, enc->proj, H, T_dev, Tmax, H, H, 0));
+            L_OP(OP_LAYERNORM, 0, ln_res_by,
+                 laya::launch_layernorm(s, xr, enc->proj, enc->nrm, g1, T_dev, Tmax, H,
+                                        c.ln_eps));
+            L_OP(OP_UP_GEGLU, gemm_fl(T, 2 * F, H), gemm_by(T, 2 * F, F, H),
+                 laya::launch_gemm(s, enc->nrm, H, Wi, H, enc->hid, F, T_dev, Tmax, F, H, 1));
+            L_OP(OP_DOWN, gemm_fl(T, H, F), gemm_by(T, H, H, F),
+                 laya::launch_gemm(s, enc->hid, F, Wo2, F, enc->proj, H, T_dev, Tmax, H, F, 0));
             pending = true;
             if (L == c.n_enc_layers - 1) {
                 // x += f; the encoder's final LayerNorm output becomes the decision stream
-                L_CHK(laya::launch_layernorm(s, xr, enc->proj, xalt, g1, T_dev, Tmax, H,
-                                             c.ln_eps));
+                L_OP(OP_LAYERNORM, 0, ln_res_by,
+                     laya::launch_layernorm(s, xr, enc->proj, xalt, g1, T_dev, Tmax, H,
+                                            c.ln_eps));
                 std::snprintf(name, sizeof name, "enc%02d", L);
                 C_CHK(cap(name, xr, rs.T));
                 C_CHK(cap("enc_final", xalt, rs.T));
@@ -476,36 +529,49 @@ int record(laya_encoder *enc, hipStream_t s, const RunShape &rs) {
                 pending = false;
             }
         } else {
-            const int R = rs.R;
             // keys/values for every token, queries only for the marker rows
-            L_CHK(laya::launch_gemm(s, enc->nrm, H, Wqkv + (size_t)H * H, H, enc->qkv, 2 * H,
-                                    T_dev, Tmax, 2 * H, H, 0));
-            L_CHK(laya::launch_gather_rows(s, enc->nrm, H, mrk_tok, R, H, enc->n_sub, H));
-            L_CHK(laya::launch_gather_rows(s, xr, H, mrk_tok, R, H, enc->x_sub, H));
-            L_CHK(laya::launch_gemm(s, enc->n_sub, H, Wqkv, H, enc->q_sub, H, nullptr, R, H, H,
-                                    0));
-            L_CHK(laya::launch_rope(s, enc->qkv, 2 * H, nh, T_dev, Tmax, pos, ctab, stab));
-            L_CHK(laya::launch_rope(s, enc->q_sub, H, nh, nullptr, R, mrk_pos, ctab, stab));
-            L_CHK(laya::launch_attention(s, enc->q_sub, H, enc->qkv, enc->qkv + H, 2 * H,
-                                         enc->att, H, blk_s, nblk_s, ml.nblk_sub_max, mrk_pos,
-                                         nh, half));
-            L_CHK(laya::launch_gemm(s, enc->att, H, Wo, H, enc->proj, H, nullptr, R, H, H, 0));
-            L_CHK(laya::launch_layernorm(s, enc->x_sub, enc->proj, enc->n_sub, g1, nullptr, R, H,
-                                         c.ln_eps));
-            L_CHK(laya::launch_gemm(s, enc->n_sub, H, Wi, H, enc->hid, F, nullptr, R, F, H, 1));
-            L_CHK(laya::launch_gemm(s, enc->hid, F, Wo2, F, enc->proj, H, nullptr, R, H, F, 0));
-            L_CHK(laya::launch_layernorm(s, enc->x_sub, enc->proj, enc->out, g1, nullptr, R, H,
-                                         c.ln_eps));
+            const int Ri = rs.R;
+            L_OP(OP_KV, gemm_fl(T, 2 * H, H), gemm_by(T, 2 * H, 2 * H, H),
+                 laya::launch_gemm(s, enc->nrm, H, Wqkv + (size_t)H * H, H, enc->qkv, 2 * H,
+                                   T_dev, Tmax, 2 * H, H, 0));
+            L_OP(OP_ROW_GATHER, 0, 2 * R * H * b2,
+                 laya::launch_gather_rows(s, enc->nrm, H, mrk_tok, Ri, H, enc->n_sub, H));
+            L_OP(OP_ROW_GATHER, 0, 2 * R * H * b2,
+                 laya::launch_gather_rows(s, xr, H, mrk_tok, Ri, H, enc->x_sub, H));
+            L_OP(OP_Q, gemm_fl(R, H, H), gemm_by(R, H, H, H),
+                 laya::launch_gemm(s, enc->n_sub, H, Wqkv, H, enc->q_sub, H, nullptr, Ri, H, H,
+                                   0));
+            L_OP(OP_ROPE, 0, 2 * T * H * b2,
+                 laya::launch_rope(s, enc->qkv, 2 * H, nh, T_dev, Tmax, pos, ctab, stab));
+            L_OP(OP_ROPE, 0, 2 * R * H * b2,
+                 laya::launch_rope(s, enc->q_sub, H, nh, nullptr, Ri, mrk_pos, ctab, stab));
+            L_OP(OP_ATTENTION, attn_fl_per_pair * rs.pairs_subset, (2 * R + 2 * T) * H * b2,
+                 laya::launch_attention(s, enc->q_sub, H, enc->qkv, enc->qkv + H, 2 * H,
+                                        enc->att, H, blk_s, nblk_s, ml.nblk_sub_max, mrk_pos,
+                                        nh, half));
+            L_OP(OP_OUT_PROJ, gemm_fl(R, H, H), gemm_by(R, H, H, H),
+                 laya::launch_gemm(s, enc->att, H, Wo, H, enc->proj, H, nullptr, Ri, H, H, 0));
+            L_OP(OP_LAYERNORM, 0, 4 * R * H * b2,
+                 laya::launch_layernorm(s, enc->x_sub, enc->proj, enc->n_sub, g1, nullptr, Ri,
+                                        H, c.ln_eps));
+            L_OP(OP_UP_GEGLU, gemm_fl(R, 2 * F, H), gemm_by(R, 2 * F, F, H),
+                 laya::launch_gemm(s, enc->n_sub, H, Wi, H, enc->hid, F, nullptr, Ri, F, H, 1));
+            L_OP(OP_DOWN, gemm_fl(R, H, F), gemm_by(R, H, H, F),
+                 laya::launch_gemm(s, enc->hid, F, Wo2, F, enc->proj, H, nullptr, Ri, H, F, 0));
+            L_OP(OP_LAYERNORM, 0, 4 * R * H * b2,
+                 laya::launch_layernorm(s, enc->x_sub, enc->proj, enc->out, g1, nullptr, Ri, H,
+                                        c.ln_eps));
             std::snprintf(name, sizeof name, L < c.n_enc_layers ? "enc%02d" : "dec%d",
                           L < c.n_enc_layers ? L : L - c.n_enc_layers);
-            C_CHK(cap(name, enc->x_sub, R));
-            C_CHK(cap("out", enc->out, R));
+            C_CHK(cap(name, enc->x_sub, Ri));
+            C_CHK(cap("out", enc->out, Ri));
             return LAYA_OK;
         }
     }
     // closing LayerNorm over the decision stream
-    L_CHK(laya::launch_layernorm(s, xr, pending ? enc->proj : nullptr, enc->out, enc->gamma_ones,
-                                 T_dev, Tmax, H, c.ln_eps));
+    L_OP(OP_LAYERNORM, 0, pending ? ln_res_by : ln_by,
+         laya::launch_layernorm(s, xr, pending ? enc->proj : nullptr, enc->out, enc->gamma_ones,
+                                T_dev, Tmax, H, c.ln_eps));
     if (pending) {
         std::snprintf(name, sizeof name, (NL - 1) < c.n_enc_layers ? "enc%02d" : "dec%d",
                       (NL - 1) < c.n_enc_layers ? NL - 1 : NL - 1 - c.n_enc_layers);
@@ -513,7 +579,7 @@ int record(laya_encoder *enc, hipStream_t s, const RunShape &rs) {
     }
     C_CHK(cap("out", enc->out, rs.T));
     return LAYA_OK;
-#undef L_CHK
+#undef L_OP
 #undef C_CHK
 }
 
@@ -966,6 +1032,79 @@ int laya_memcpy(void *dst, const void *src, size_t bytes, int32_t kind, void *st
     if (e != hipSuccess)
         return set_global_error(LAYA_E_DEVICE, std::string("laya_memcpy: ") + hipGetErrorString(e));
     return LAYA_OK;
+}
+
+int laya_encoder_profile(laya_encoder *enc, void *stream, const int32_t *ids,
+                         const int32_t *lengths, int32_t B, int32_t S, const int32_t *markers,
+                         int32_t R, laya_op_time *out, int32_t cap, int32_t *n_out,
+                         double *total_ms) {
+    if (!enc || !out || !n_out || cap < 0) return set_global_error(LAYA_E_INVALID, "NULL argument");
+    if (enc->poisoned) return fail(enc, LAYA_E_POISONED, "handle poisoned");
+    laya_output o;
+    // upload the indices (and validate) with an ordinary eager run first
+    int rc = laya_encoder_run(enc, stream, ids, lengths, B, S, markers, R, LAYA_RUN_EAGER, &o);
+    if (rc != LAYA_OK) return rc;
+    *n_out = 0;
+    if (total_ms) *total_ms = 0;
+    if (B == 0) return LAYA_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const laya_config &c = enc->cfg;
+    RunShape rs{B, S, R, enc->up_T, false};
+    const int hw = c.window / 2;
+    for (int b = 0; b < B; ++b) {
+        const double len = lengths[b];
+        rs.pairs_global += len * len;
+        for (int i = 0; i < lengths[b]; ++i)
+            rs.pairs_local += std::min(lengths[b] - 1, i + hw) - std::max(0, i - hw) + 1;
+    }
+    for (int r = 0; r < R; ++r) rs.pairs_subset += lengths[markers[2 * r]];
+    Profiler prof;
+    const size_t n_launch = (size_t)layer_count(c) * 16 + 16;
+    prof.recs.resize(n_launch);
+    prof.ev.assign(2 * n_launch, nullptr);
+    int result = LAYA_OK;
+    for (auto &e : prof.ev) {
+        if (hipEventCreate(&e) != hipSuccess) {
+            result = fail(enc, LAYA_E_DEVICE, "hipEventCreate failed");
+            break;
+        }
+    }
+    if (result == LAYA_OK) result = record(enc, s, rs, &prof);
+    if (result == LAYA_OK && hipStreamSynchronize(s) != hipSuccess)
+        result = fail(enc, LAYA_E_DEVICE, "hipStreamSynchronize failed");
+    if (result == LAYA_OK) {
+        std::vector<laya_op_time> agg(OP_COUNT);
+        for (int k = 0; k < OP_COUNT; ++k) {
+            std::memset(&agg[k], 0, sizeof(laya_op_time));
+            std::strncpy(agg[k].name, kOpNames[k], sizeof(agg[k].name) - 1);
+        }
+        double tot = 0;
+        for (size_t i = 0; i < prof.n; ++i) {
+            float ms = 0;
+            if (hipEventElapsedTime(&ms, prof.ev[2 * i], prof.ev[2 * i + 1]) != hipSuccess) {
+                result = fail(enc, LAYA_E_DEVICE, "hipEventElapsedTime failed");
+                break;
+            }
+            laya_op_time &a = agg[prof.recs[i].op];
+            a.calls += 1;
+            a.total_ms += ms;
+            a.flops += prof.recs[i].flops;
+            a.bytes += prof.recs[i].bytes;
+            tot += ms;
+        }
+        if (prof.n >= 2 && total_ms) {
+            float span = 0;
+            if (hipEventElapsedTime(&span, prof.ev[0], prof.ev[2 * prof.n - 1]) == hipSuccess)
+                *total_ms = span;
+        }
+        int n = 0;
+        for (int k = 0; k < OP_COUNT && result == LAYA_OK; ++k)
+            if (agg[k].calls > 0 && n < cap) out[n++] = agg[k];
+        *n_out = n;
+    }
+    for (auto &e : prof.ev)
+        if (e) hipEventDestroy(e);
+    return result;
 }
 
 // ---------------------------------------------------------------------------

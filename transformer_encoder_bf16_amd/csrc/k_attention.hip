@@ -13,10 +13,12 @@
 //
 // Per workgroup: one block x one head, four waves of 16 queries.  For each
 // 64-key tile: S = Q K^T with MFMA 16x16x32 (queries as rows), scale,
-// mask, online softmax in float32 (max subtracted, exp2 domain), P rounded
-// to BF16 and staged in LDS, O += P V with MFMA 16x16x32 reading V from a
-// transposed LDS copy.  The row sum accumulates the same BF16-rounded P that
-// multiplies V, so the result is an exact weighted mean of V's rows.
+// mask, online softmax in float32 (max subtracted, exp2 domain), then
+// O += P V with MFMA 16x16x32 reading V from a transposed LDS copy.  The
+// matrix cores take BF16 operands, so the float32 P is split into a BF16 head
+// and a BF16 tail (p = hi + lo to about 16 significant bits) and both halves
+// are multiplied with V: rounding P to BF16 alone would perturb every output
+// by up to 2^-9 relative, a first-order departure from float32 softmax.
 #include "kernels.h"
 
 namespace laya {
@@ -45,7 +47,7 @@ __global__ __launch_bounds__(256) void attention_kernel(
 
     __shared__ __attribute__((aligned(16))) bf16_t sK[KT * LDK];
     __shared__ __attribute__((aligned(16))) bf16_t sVt[64 * LDV];
-    __shared__ __attribute__((aligned(16))) bf16_t sP[4][16 * LDP];
+    __shared__ __attribute__((aligned(16))) bf16_t sP[4][2][16 * LDP];  // [wave][hi, lo]
 
     const int tid = threadIdx.x;
     const int w = tid >> 6, lane = tid & 63;
@@ -133,7 +135,8 @@ __global__ __launch_bounds__(256) void attention_kernel(
             mx[i] = group16_max(mx[i]);
         }
 
-        bf16_t *pw = sP[w];
+        bf16_t *pw = sP[w][0];
+        bf16_t *pwl = sP[w][1];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const float mnew = fmaxf(m[i], mx[i]);
@@ -143,9 +146,11 @@ __global__ __launch_bounds__(256) void attention_kernel(
             for (int b = 0; b < 4; ++b) {
                 const float t = s[b][i];
                 const float p = (t == -INFINITY) ? 0.f : exp2f(t - mnew);
-                const uint32_t pb = f32_to_bf16(p);
-                rs += bf16_to_f32(pb);
-                pw[(g * 4 + i) * LDP + b * 16 + c16] = (bf16_t)pb;
+                const uint32_t ph = f32_to_bf16(p);
+                const uint32_t pl = f32_to_bf16(p - bf16_to_f32(ph));  // p - hi is exact
+                rs += p;
+                pw[(g * 4 + i) * LDP + b * 16 + c16] = (bf16_t)ph;
+                pwl[(g * 4 + i) * LDP + b * 16 + c16] = (bf16_t)pl;
             }
             l[i] = l[i] * alpha + group16_sum(rs);
             m[i] = mnew;
@@ -154,16 +159,19 @@ __global__ __launch_bounds__(256) void attention_kernel(
         }
         __syncthreads();  // P visible to the whole wave (and V tile still valid)
 
-        // O += P V: A = P [16 queries][keys], B = V [keys][d] read from V^T.
+        // O += (P_hi + P_lo) V: A = P [16 queries][keys], B = V [keys][d] from V^T.
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             const bf16x8_t pa =
                 *reinterpret_cast<const bf16x8_t *>(&pw[c16 * LDP + ks * 32 + g * 8]);
+            const bf16x8_t pal =
+                *reinterpret_cast<const bf16x8_t *>(&pwl[c16 * LDP + ks * 32 + g * 8]);
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
                 const bf16x8_t vb = *reinterpret_cast<const bf16x8_t *>(
                     &sVt[(d * 16 + c16) * LDV + ks * 32 + g * 8]);
                 oacc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, oacc[d], 0, 0, 0);
+                oacc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pal, vb, oacc[d], 0, 0, 0);
             }
         }
     }

@@ -36,8 +36,10 @@ __device__ __forceinline__ int swz(int row, int chunk) {
     return row * BK + ((chunk ^ ((row >> 1) & 7)) << 3);
 }
 
+// GELU(z) = z Phi(z) = 0.5 z erfc(-z / sqrt 2).  erfc keeps full relative
+// accuracy in the negative tail, where 1 + erf(z / sqrt 2) would cancel.
 __device__ __forceinline__ float gelu_erf(float z) {
-    return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));
+    return 0.5f * z * erfcf(-z * 0.70710678118654752f);
 }
 
 template <int EPI>
