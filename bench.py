@@ -31,11 +31,13 @@ METRIC = "encoder calls/s + p50 ms (28+2 layers, BF16) at 1×48 and 16×512, 1 G
 # run 1), quoted for context: 38.7 req/s at 16x512, 358.9 req/s at 1x48.
 PAGES_CALLS_PER_S = {"mixed_16": 38.7, "short_1": 358.9, "short_3": 311.0, "long_3": 132.9}
 
-# kernel symbol that runs each op class (for matching rocprofv3 summaries)
+# kernel that runs each op class (prefix of its symbol in rocprofv3 summaries;
+# the GEMM tile configuration and K split follow the plan for the batch shape)
 DOMINANT_KERNEL_SYMBOL = {
-    "up_geglu_gemm": "gemm_bf16_kernel<1>", "qkv_gemm": "gemm_bf16_kernel<0>",
-    "down_gemm": "gemm_bf16_kernel<0>", "out_proj_gemm": "gemm_bf16_kernel<0>",
-    "attention": "attention_kernel", "layernorm": "layernorm_kernel<2>", "rope": "rope_kernel",
+    "up_geglu_gemm": "gemm_kernel<Cfg<...>, 1, ...> (GeGLU epilogue)",
+    "qkv_gemm": "gemm_kernel<Cfg<...>, 0, ...>", "down_gemm": "gemm_kernel<Cfg<...>, 0, ...>",
+    "out_proj_gemm": "gemm_kernel<Cfg<...>, 0, ...>", "attention": "attention_kernel",
+    "layernorm": "layernorm_kernel", "rope": "rope_kernel",
 }
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense BF16 MFMA

@@ -282,9 +282,17 @@ int laya_op_layernorm(void *stream, void *x, const void *r, void *n, const float
  * (GeGLU): W has 2N rows; with u = A W[0:N]^T and g = A W[N:2N]^T in float32,
  * C = bf16(GELU(u) * g), GELU(z) = 0.5 z (1 + erf(z / sqrt 2)).  A device BF16
  * [M][lda], W device BF16 [N or 2N][ldw], C device BF16 [M][ldc]; K a multiple
- * of 64, N a multiple of 64, lda/ldw/ldc multiples of 8 (16-byte rows). */
+ * of 64, N a multiple of 64, lda/ldw/ldc multiples of 8 (16-byte rows).
+ * config -1 picks the tile shape and K split the pass itself would use for M
+ * rows; config 0..5 (tile shapes 32x64, 64x64, 128x64, 128x128, 256x128,
+ * 256x256 weight rows x tokens) with `splits` K ranges forces one (split K
+ * only on shapes 0..3; GeGLU not on shape 0).  Each output is the sum, in
+ * order, of one MFMA chain per K range, so results depend only on `splits`.
+ * With splits > 1 the call allocates its scratch and synchronises the
+ * stream. */
 int laya_op_gemm(void *stream, const void *A, int32_t lda, const void *W, int32_t ldw,
-                 void *C, int32_t ldc, int32_t M, int32_t N, int32_t K, int32_t epilogue);
+                 void *C, int32_t ldc, int32_t M, int32_t N, int32_t K, int32_t epilogue,
+                 int32_t config, int32_t splits);
 
 /* RoPE in place on `n_heads_rot` consecutive 64-wide heads starting at column
  * 0 of each of `rows` rows of buf (device BF16, row stride ld): with

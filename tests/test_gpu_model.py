@@ -185,15 +185,28 @@ def test_reversed_rows_and_padding_are_bitwise_invariant(binding, enc):
     for b in range(batch.B):
         r = batch.B - 1 - b
         assert np.array_equal(base[ro[b]:ro[b + 1]], rbits[rro[r]:rro[r + 1]])
-    # different padding ids and a longer padded S with the same lengths
-    ids2 = np.full((batch.B, 96), 7, np.int32)
+    # different padding ids, same padded width: bitwise
+    ids2 = batch.ids.copy()
     for b in range(batch.B):
-        ids2[b, :batch.lengths[b]] = batch.ids[b, :batch.lengths[b]]
+        ids2[b, batch.lengths[b]:] = 7 + b
     pad = type(batch)(ids=ids2, lengths=batch.lengths.copy())
     pbits, _ = _run_bits(binding, enc, pad, binding.RUN_EAGER)
     assert np.array_equal(base, pbits)
     gbits, _ = _run_bits(binding, enc, pad, 0)
     assert np.array_equal(base, gbits)
+    # a wider padded S with the same lengths: B*S picks the GEMMs' K split, so
+    # the result is bitwise equal while the split is unchanged and otherwise
+    # within the drift of a different summation order
+    ids3 = np.full((batch.B, 96), 7, np.int32)
+    for b in range(batch.B):
+        ids3[b, :batch.lengths[b]] = batch.ids[b, :batch.lengths[b]]
+    wide = type(batch)(ids=ids3, lengths=batch.lengths.copy())
+    wbits, _ = _run_bits(binding, enc, wide, binding.RUN_EAGER)
+    to_f = lambda u: (u.astype(np.uint32) << 16).view(np.float32)
+    e = oracle.nrms(to_f(wbits), to_f(base))
+    report("wider_padding", {"S": [batch.S, 96], "bitwise": bool(np.array_equal(base, wbits)),
+                             "nrms": e})
+    assert e < 0.03
 
 
 def test_one_graph_serves_every_length_pattern(binding, enc):

@@ -293,3 +293,51 @@ def test_attention_keys_outside_window_do_not_matter(B):
     a, b = from_dev(o1), from_dev(o2)
     assert np.array_equal(bits_of(a[:236]), bits_of(b[:236]))  # queries < 236 never see key 300
     assert not np.array_equal(bits_of(a[236:]), bits_of(b[236:]))
+
+
+# ------------------------------------------------- gemm tile shapes / split K --
+
+@pytest.mark.parametrize("M,N,K,epi", [(48, 1024, 2624, 0), (200, 3072, 1024, 0),
+                                       (97, 2624, 1024, 1), (300, 1024, 1024, 0)])
+def test_gemm_every_tile_shape_and_split(B, M, N, K, epi):
+    """All tile shapes give bitwise the same result for the same K split, and
+    every split matches the oracle."""
+    import torch
+    a_h = oracle.bf16_round(random_normal((M, K), 7 * M + K))
+    rows = 2 * N if epi else N
+    w_h = oracle.bf16_round(random_normal((rows, K), 3 * N + K, 0.03))
+    a, w = to_dev(a_h), to_dev(w_h)
+    if epi:
+        ug = oracle.linear(a_h, w_h)
+        want = oracle.bf16_round(oracle.gelu(ug[:, :N]) * ug[:, N:])
+    else:
+        want = oracle.bf16_round(oracle.linear(a_h, w_h))
+    for splits in (1, 2, 5):
+        outs = []
+        for cfg in range(6):
+            if (epi and cfg == 0) or (splits > 1 and cfg > 3):
+                continue
+            c = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+            B.op_gemm(a, w, c, M, N, K, epi, config=cfg, splits=splits)
+            _sync()
+            outs.append((cfg, bits_of(from_dev(c))))
+        for cfg, o in outs[1:]:
+            assert np.array_equal(o, outs[0][1]), (splits, cfg)
+        got = (outs[0][1].astype(np.uint32) << 16).view(np.float32)
+        bad, frac = bf16_close(got, want)
+        assert bad == 0 and frac < 0.02, (splits, bad, frac)
+
+
+def test_gemm_split_k_repeats_bitwise(B):
+    """The split-K counters reset themselves: repeated launches agree bit for bit."""
+    import torch
+    M, N, K = 48, 3072, 1024
+    a = to_dev(oracle.bf16_round(random_normal((M, K), 1)))
+    w = to_dev(oracle.bf16_round(random_normal((N, K), 2, 0.02)))
+    outs = []
+    for _ in range(3):
+        c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        B.op_gemm(a, w, c, M, N, K, 0, config=0, splits=8)
+        _sync()
+        outs.append(bits_of(from_dev(c)))
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[1], outs[2])

@@ -139,7 +139,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
                                              ctypes.c_float]),
         "laya_op_gemm": (ctypes.c_int, [_P, _P, ctypes.c_int32, _P, ctypes.c_int32, _P,
                                         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
-                                        ctypes.c_int32, ctypes.c_int32]),
+                                        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_int32]),
         "laya_op_rope": (ctypes.c_int, [_P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                         _P, _P, _P, ctypes.c_int32]),
         "laya_op_attention": (ctypes.c_int, [_P, _P, ctypes.c_int32, _P, _P, ctypes.c_int32, _P,
@@ -348,10 +349,11 @@ def op_layernorm(x, r, n, gamma, eps: float, stream: Optional[int] = None):
                                     x.shape[1], eps), "laya_op_layernorm")
 
 
-def op_gemm(A, W, C, M: int, N: int, K: int, epilogue: int = 0, stream: Optional[int] = None):
+def op_gemm(A, W, C, M: int, N: int, K: int, epilogue: int = 0, config: int = -1,
+            splits: int = 1, stream: Optional[int] = None):
     st = current_stream() if stream is None else stream
     _check(load().laya_op_gemm(st, _dp(A), A.stride(0), _dp(W), W.stride(0), _dp(C),
-                               C.stride(0), M, N, K, epilogue), "laya_op_gemm")
+                               C.stride(0), M, N, K, epilogue, config, splits), "laya_op_gemm")
 
 
 def op_rope(buf, n_heads_rot: int, pos, cos_tab, sin_tab, rows: Optional[int] = None,

@@ -326,6 +326,8 @@ struct laya_encoder {
     bf16_t *xa = nullptr, *xb = nullptr, *nrm = nullptr, *qkv = nullptr, *att = nullptr,
            *proj = nullptr, *hid = nullptr, *out = nullptr;
     bf16_t *x_sub = nullptr, *n_sub = nullptr, *q_sub = nullptr;
+    float *gemm_partial = nullptr;    // split-K partial tiles
+    uint32_t *gemm_counter = nullptr;  // split-K tile counters (zero between launches)
     int32_t *meta_dev = nullptr;
     int32_t *meta_host = nullptr;
     int64_t meta_cap = 0;
@@ -400,6 +402,89 @@ struct Profiler {
 
 int layer_count(const laya_config &c) { return c.n_enc_layers + c.n_dec_layers; }
 
+// GEMM plans of one pass.  The four projections over the packed tokens are
+// planned from B*S; the marker layer's GEMMs over R rows keep the K split of
+// the matching full-pass GEMM (so marker rows are bitwise the full pass's
+// rows) and choose their own tile shape.
+struct PassPlans {
+    laya::GemmPlan qkv, o, up, down;              // M = B*S
+    laya::GemmPlan kv_sub, q_sub, o_sub, up_sub, down_sub;  // marker layer
+};
+
+laya::GemmPlan subset_plan(const laya::GemmPlan &full, int R, int N, int K, int epi) {
+    laya::GemmPlan g;
+    g.splits = full.splits;
+    if (R <= 64)
+        g.config = epi ? 1 : 0;
+    else if (R <= 256 || full.splits > 1)
+        g.config = 2;  // split-capable
+    else
+        g.config = laya::plan_gemm(R, N, K, epi).config;  // R > 256: K is whole anyway
+    return g;
+}
+
+// K splits follow B*S (so eager and graph runs of one key add in the same
+// order); with whole K, the tile shape follows the tokens T of the run that
+// records the launches (any shape gives the same result).
+laya::GemmPlan full_plan(int Tmax, int T, int N, int K, int epi) {
+    laya::GemmPlan g = laya::plan_gemm(Tmax, N, K, epi);
+    if (g.splits == 1 && T > 0 && T < Tmax) g = laya::plan_gemm_tiles(T, N, K, epi);
+    return g;
+}
+
+PassPlans make_plans(const laya_config &c, int Tmax, int T, int R) {
+    const int H = c.hidden, F = c.ffn;
+    PassPlans p{};
+    p.qkv = full_plan(Tmax, T, 3 * H, H, 0);
+    p.o = full_plan(Tmax, T, H, H, 0);
+    p.up = full_plan(Tmax, T, F, H, 1);
+    p.down = full_plan(Tmax, T, H, F, 0);
+    if (R > 0) {
+        p.kv_sub = full_plan(Tmax, T, 2 * H, H, 0);
+        p.kv_sub.splits = p.qkv.splits;
+        if (p.kv_sub.splits > laya::gemm_max_splits(p.kv_sub.config)) p.kv_sub.config = 2;
+        p.q_sub = subset_plan(p.qkv, R, H, H, 0);
+        p.o_sub = subset_plan(p.o, R, H, H, 0);
+        p.up_sub = subset_plan(p.up, R, F, H, 1);
+        p.down_sub = subset_plan(p.down, R, H, F, 0);
+    }
+    return p;
+}
+
+// Largest split-K partial buffer (bytes) and counter count over every shape
+// the handle accepts.
+void gemm_scratch_bound(const laya_config &c, size_t *bytes, size_t *counters) {
+    const int H = c.hidden, F = c.ffn;
+    const int tcap = c.max_batch * c.max_seq;
+    size_t b = 0, n = 0;
+    auto acc = [&](const laya::GemmPlan &g, int M, int N, int epi) {
+        b = std::max(b, laya::gemm_workspace_bytes(g, M, N, epi));
+        n = std::max(n, laya::gemm_counter_count(g, M, N, epi));
+    };
+    int last_splits[4] = {-1, -1, -1, -1};
+    for (int T = 1; T <= tcap; ++T) {
+        const PassPlans p = make_plans(c, T, T, 0);
+        acc(p.qkv, T, 3 * H, 0);
+        acc(p.o, T, H, 0);
+        acc(p.up, T, F, 1);
+        acc(p.down, T, H, 0);
+        // marker layer: its plans depend on T only through the K splits
+        const int sp[4] = {p.qkv.splits, p.o.splits, p.up.splits, p.down.splits};
+        if (std::equal(sp, sp + 4, last_splits)) continue;
+        std::copy(sp, sp + 4, last_splits);
+        for (int R = 1; R <= c.max_markers; ++R) {
+            const PassPlans q = make_plans(c, T, T, R);
+            acc(q.kv_sub, T, 2 * H, 0);
+            acc(q.q_sub, R, H, 0);
+            acc(q.o_sub, R, H, 0);
+            acc(q.up_sub, R, F, 1);
+            acc(q.down_sub, R, H, 0);
+        }
+    }
+    *bytes = b;
+    *counters = n;
+}
+
 // Queue the whole pass on stream s.  Reads T, the row layout and the
 // attention work lists from the device copy of the index upload.
 int record(laya_encoder *enc, hipStream_t s, const RunShape &rs, Profiler *prof = nullptr) {
@@ -421,6 +506,9 @@ int record(laya_encoder *enc, hipStream_t s, const RunShape &rs, Profiler *prof 
     const int32_t *mrk_tok = md + ml.mrk_tok;
     const int32_t *mrk_pos = md + ml.mrk_pos;
     const int hw = c.window / 2;
+    const PassPlans plans = make_plans(c, Tmax, rs.T, rs.R);
+    float *gp = enc->gemm_partial;
+    uint32_t *gc = enc->gemm_counter;
     enc->launches = 0;
 
     size_t ci = 0;
@@ -499,7 +587,7 @@ int record(laya_encoder *enc, hipStream_t s, const RunShape &rs, Profiler *prof 
         if (!subset) {
             L_OP(OP_QKV, gemm_fl(T, 3 * H, H), gemm_by(T, 3 * H, 3 * H, H),
                  laya::launch_gemm(s, enc->nrm, H, Wqkv, H, enc->qkv, 3 * H, T_dev, Tmax, 3 * H,
-                                   H, 0));
+                                   H, 0, plans.qkv, gp, gc));
             L_OP(OP_ROPE, 0, 2 * T * 2 * H * b2,
                  laya::launch_rope(s, enc->qkv, 3 * H, 2 * nh, T_dev, Tmax, pos, ctab, stab));
             L_OP(OP_ATTENTION, attn_fl_per_pair * (glob ? rs.pairs_global : rs.pairs_local),
@@ -508,14 +596,17 @@ int record(laya_encoder *enc, hipStream_t s, const RunShape &rs, Profiler *prof 
                                         3 * H, enc->att, H, blk, nblk, ml.nblk_full_max, pos,
                                         nh, half));
             L_OP(OP_OUT_PROJ, gemm_fl(T, H, H), gemm_by(T, H, H, H),
-                 laya::launch_gemm(s, enc->att, H, Wo, H, enc->proj, H, T_dev, Tmax, H, H, 0));
+                 laya::launch_gemm(s, enc->att, H, Wo, H, enc->proj, H, T_dev, Tmax, H, H, 0,
+                                   plans.o, gp, gc));
             L_OP(OP_LAYERNORM, 0, ln_res_by,
                  laya::launch_layernorm(s, xr, enc->proj, enc->nrm, g1, T_dev, Tmax, H,
                                         c.ln_eps));
             L_OP(OP_UP_GEGLU, gemm_fl(T, 2 * F, H), gemm_by(T, 2 * F, F, H),
-                 laya::launch_gemm(s, enc->nrm, H, Wi, H, enc->hid, F, T_dev, Tmax, F, H, 1));
+                 laya::launch_gemm(s, enc->nrm, H, Wi, H, enc->hid, F, T_dev, Tmax, F, H, 1,
+                                   plans.up, gp, gc));
             L_OP(OP_DOWN, gemm_fl(T, H, F), gemm_by(T, H, H, F),
-                 laya::launch_gemm(s, enc->hid, F, Wo2, F, enc->proj, H, T_dev, Tmax, H, F, 0));
+                 laya::launch_gemm(s, enc->hid, F, Wo2, F, enc->proj, H, T_dev, Tmax, H, F, 0,
+                                   plans.down, gp, gc));
             pending = true;
             if (L == c.n_enc_layers - 1) {
                 // x += f; the encoder's final LayerNorm output becomes the decision stream
@@ -533,14 +624,14 @@ int record(laya_encoder *enc, hipStream_t s, const RunShape &rs, Profiler *prof 
             const int Ri = rs.R;
             L_OP(OP_KV, gemm_fl(T, 2 * H, H), gemm_by(T, 2 * H, 2 * H, H),
                  laya::launch_gemm(s, enc->nrm, H, Wqkv + (size_t)H * H, H, enc->qkv, 2 * H,
-                                   T_dev, Tmax, 2 * H, H, 0));
+                                   T_dev, Tmax, 2 * H, H, 0, plans.kv_sub, gp, gc));
             L_OP(OP_ROW_GATHER, 0, 2 * R * H * b2,
                  laya::launch_gather_rows(s, enc->nrm, H, mrk_tok, Ri, H, enc->n_sub, H));
             L_OP(OP_ROW_GATHER, 0, 2 * R * H * b2,
                  laya::launch_gather_rows(s, xr, H, mrk_tok, Ri, H, enc->x_sub, H));
             L_OP(OP_Q, gemm_fl(R, H, H), gemm_by(R, H, H, H),
                  laya::launch_gemm(s, enc->n_sub, H, Wqkv, H, enc->q_sub, H, nullptr, Ri, H, H,
-                                   0));
+                                   0, plans.q_sub, gp, gc));
             L_OP(OP_ROPE, 0, 2 * T * H * b2,
                  laya::launch_rope(s, enc->qkv, 2 * H, nh, T_dev, Tmax, pos, ctab, stab));
             L_OP(OP_ROPE, 0, 2 * R * H * b2,
@@ -550,14 +641,17 @@ int record(laya_encoder *enc, hipStream_t s, const RunShape &rs, Profiler *prof 
                                         enc->att, H, blk_s, nblk_s, ml.nblk_sub_max, mrk_pos,
                                         nh, half));
             L_OP(OP_OUT_PROJ, gemm_fl(R, H, H), gemm_by(R, H, H, H),
-                 laya::launch_gemm(s, enc->att, H, Wo, H, enc->proj, H, nullptr, Ri, H, H, 0));
+                 laya::launch_gemm(s, enc->att, H, Wo, H, enc->proj, H, nullptr, Ri, H, H, 0,
+                                   plans.o_sub, gp, gc));
             L_OP(OP_LAYERNORM, 0, 4 * R * H * b2,
                  laya::launch_layernorm(s, enc->x_sub, enc->proj, enc->n_sub, g1, nullptr, Ri,
                                         H, c.ln_eps));
             L_OP(OP_UP_GEGLU, gemm_fl(R, 2 * F, H), gemm_by(R, 2 * F, F, H),
-                 laya::launch_gemm(s, enc->n_sub, H, Wi, H, enc->hid, F, nullptr, Ri, F, H, 1));
+                 laya::launch_gemm(s, enc->n_sub, H, Wi, H, enc->hid, F, nullptr, Ri, F, H, 1,
+                                   plans.up_sub, gp, gc));
             L_OP(OP_DOWN, gemm_fl(R, H, F), gemm_by(R, H, H, F),
-                 laya::launch_gemm(s, enc->hid, F, Wo2, F, enc->proj, H, nullptr, Ri, H, F, 0));
+                 laya::launch_gemm(s, enc->hid, F, Wo2, F, enc->proj, H, nullptr, Ri, H, F, 0,
+                                   plans.down_sub, gp, gc));
             L_OP(OP_LAYERNORM, 0, 4 * R * H * b2,
                  laya::launch_layernorm(s, enc->x_sub, enc->proj, enc->out, g1, nullptr, Ri, H,
                                         c.ln_eps));
@@ -758,6 +852,12 @@ int laya_encoder_create(const laya_config *cfg, uint64_t seed, int device, laya_
     enc->meta_cap = mlmax.total;
     const size_t meta_off = wsz;
     wsz += al((size_t)enc->meta_cap * 4);
+    size_t gp_bytes = 0, gc_count = 0;
+    gemm_scratch_bound(c, &gp_bytes, &gc_count);
+    const size_t gp_off = wsz;
+    wsz += al(gp_bytes);
+    const size_t gc_off = wsz;
+    wsz += al(gc_count * 4);
     enc->ws_bytes = wsz;
     if (hipMalloc(&enc->ws, wsz) != hipSuccess)
         return bail(set_global_error(LAYA_E_NOMEM, "workspace: hipMalloc failed"));
@@ -771,6 +871,8 @@ int laya_encoder_create(const laya_config *cfg, uint64_t seed, int device, laya_
             o += al(b.second * 2);
         }
         enc->meta_dev = reinterpret_cast<int32_t *>(p + meta_off);
+        enc->gemm_partial = gp_bytes ? reinterpret_cast<float *>(p + gp_off) : nullptr;
+        enc->gemm_counter = gc_count ? reinterpret_cast<uint32_t *>(p + gc_off) : nullptr;
     }
     if (hipHostMalloc((void **)&enc->meta_host, (size_t)enc->meta_cap * 4, hipHostMallocDefault) !=
         hipSuccess)
@@ -1139,14 +1241,40 @@ int laya_op_layernorm(void *stream, void *x, const void *r, void *n, const float
 }
 
 int laya_op_gemm(void *stream, const void *A, int32_t lda, const void *W, int32_t ldw, void *C,
-                 int32_t ldc, int32_t M, int32_t N, int32_t K, int32_t epilogue) {
+                 int32_t ldc, int32_t M, int32_t N, int32_t K, int32_t epilogue, int32_t config,
+                 int32_t splits) {
     if (M < 0 || N <= 0 || K <= 0 || K % 64 || N % 64 || lda % 8 || ldw % 8 || ldc % 8 ||
         lda < K || ldw < K || ldc < N || (epilogue != 0 && epilogue != 1) ||
-        (M > 0 && (!A || !W || !C)))
+        (M > 0 && (!A || !W || !C)) || config < -1 || config >= laya::kGemmConfigs)
         return set_global_error(LAYA_E_INVALID, "laya_op_gemm: bad arguments");
-    OPCHK(laya::launch_gemm(static_cast<hipStream_t>(stream), static_cast<const bf16_t *>(A), lda,
+    if (M == 0) return LAYA_OK;
+    laya::GemmPlan plan = laya::plan_gemm(M, N, K, epilogue);
+    if (config >= 0) plan = laya::GemmPlan{config, splits < 1 ? 1 : splits};
+    if (plan.splits > K / 64 || (plan.splits > 1 && plan.config > 3) ||
+        (epilogue && plan.config == 0))
+        return set_global_error(LAYA_E_INVALID, "laya_op_gemm: unsupported config/splits");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const size_t pb = laya::gemm_workspace_bytes(plan, M, N, epilogue);
+    const size_t pc = laya::gemm_counter_count(plan, M, N, epilogue);
+    void *scratch = nullptr;
+    if (pb) {
+        OPCHK(hipMalloc(&scratch, pb + pc * 4));
+        hipError_t e = hipMemsetAsync(static_cast<char *>(scratch) + pb, 0, pc * 4, s);
+        if (e == hipSuccess)
+            e = laya::launch_gemm(s, static_cast<const bf16_t *>(A), lda,
+                                  static_cast<const bf16_t *>(W), ldw, static_cast<bf16_t *>(C),
+                                  ldc, nullptr, M, N, K, epilogue, plan,
+                                  static_cast<float *>(scratch),
+                                  reinterpret_cast<uint32_t *>(static_cast<char *>(scratch) + pb));
+        if (e == hipSuccess) e = hipStreamSynchronize(s);
+        hipFree(scratch);
+        if (e != hipSuccess)
+            return set_global_error(LAYA_E_DEVICE, std::string("laya_op_gemm: ") + hipGetErrorString(e));
+        return LAYA_OK;
+    }
+    OPCHK(laya::launch_gemm(s, static_cast<const bf16_t *>(A), lda,
                             static_cast<const bf16_t *>(W), ldw, static_cast<bf16_t *>(C), ldc,
-                            nullptr, M, N, K, epilogue));
+                            nullptr, M, N, K, epilogue, plan, nullptr, nullptr));
     return LAYA_OK;
 }
 

@@ -2,38 +2,100 @@
 // with float32 accumulation (the QKV, output-projection, GeGLU-up and down
 // projections, which take most of the pass's time: 72-74% of traced kernel
 // time on the pages' Hopper build, "[Performance]: Optimize native Rust/CUDA
-// Laya inference #66", section Implementation priorities).
+// Laya inference #66", section Implementation priorities, which also asks
+// for small-shape tiles that keep accumulation and BF16 rounding).
 //
 // A: activations [M tokens][K], W: weights [N][K] (nn.Linear layout), both
 // K-contiguous.  The weight tile is the MFMA "A" operand (rows = output
 // features) and the token tile the "B" operand (columns = tokens), so each
-// lane of a 32x32 accumulator ends up holding four consecutive output
-// features of one token and stores them with one 8-byte write.
+// lane of a 32x32 accumulator holds four consecutive output features of one
+// token and stores them with one 8-byte write.
 //
-// Block tile: 128 weight rows x 128 tokens x 64 K, four waves in a 2x2
-// arrangement, each wave 64 weight rows x 64 tokens = 2x2 MFMA 32x32x16
-// blocks.  Tiles are staged global -> registers -> LDS, double-buffered, one
-// barrier per K step.  LDS rows are 128 bytes; the eight 16-byte chunks of
-// row r are XOR-swizzled with (r >> 1) & 7 so that the 16 lanes of one
-// ds_read_b128 phase hit distinct banks.
+// One kernel template, several tile shapes (BW weight rows x BT tokens, K
+// steps of BK, waves in a WW x WT grid):
+//   - operands move global -> LDS with global_load_lds_dwordx4 (no VGPR
+//     staging) into a STAGES-deep ring.  Each step computes for only a few
+//     hundred cycles while a load takes thousands, so the large tiles use
+//     32-wide K steps and 4-8 stages to keep ~100 KB per CU in flight; each
+//     wave waits for its own loads with an explicit vmcnt and a barrier
+//     publishes the stage;
+//   - the 16-byte chunks of an LDS row are XOR-swizzled with the row's place
+//     in a 256-byte sweep of the 64 banks (measured: no bank conflicts),
+//     realised by choosing each lane's source address, since the DMA writes
+//     lanes contiguously;
+//   - every output element is one chain of v_mfma_f32_32x32x16_bf16 over its
+//     K range, in K order, whatever the tile shape or K step: results do not
+//     depend on the tile shape or on where a token sits in its tile.
 //
-// GeGLU epilogue (epilogue 1): the weight tile's first 64 rows are rows
-// n0..n0+63 of W (the GELU half) and the last 64 rows are rows N+n0..N+n0+63
-// (the gate half), so u and g of the same output feature sit in the same
-// lane and register: h = bf16(GELU(u) * g) with u, g unrounded float32.
+// Split-K (small M, where only a few weight tiles exist): the K range is cut
+// into S contiguous pieces (multiples of 64); each workgroup writes its
+// float32 partial tile, and the last of the S workgroups of a tile to finish
+// (atomic counter) adds the partials in piece order 0..S-1 and runs the
+// epilogue.  The sum order is fixed, so results are deterministic, and that
+// workgroup resets the counter, so a captured graph replays without clearing.
+//
+// GeGLU epilogue (epilogue 1): the first BW/2 rows of the weight tile are
+// rows n0.. of W (the GELU half), the last BW/2 rows are rows N+n0.. (the
+// gate half); each wave holds matching u and g fragments, so
+// h = bf16(GELU(u) * g) is formed from unrounded float32 u and g.
 #include "kernels.h"
 
 namespace laya {
 
 namespace {
 
-constexpr int BW = 128;  // weight rows per block tile
-constexpr int BT = 128;  // tokens per block tile
-constexpr int BK = 64;   // K per step
-constexpr int ROWB = BK * 2;  // bytes per LDS row
+constexpr int KMULT = 64;  // K and every split piece are multiples of 64
 
-__device__ __forceinline__ int swz(int row, int chunk) {
-    return row * BK + ((chunk ^ ((row >> 1) & 7)) << 3);
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
+
+// Last word of a buffer resource on CDNA: raw byte addressing (stride 0),
+// 32-bit data format, no swizzle.
+constexpr int kBufferWord3 = 0x00020000;
+
+// 16 bytes per lane from base + voff + soff into LDS (the wave's 1 KB block
+// at dst), through a buffer resource of `bytes` bytes: the hardware drops
+// accesses past its end.
+__device__ __forceinline__ void dma16(const void *base, uint32_t bytes, lds_ptr_t dst,
+                                      uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                          kBufferWord3),
+        dst, 16, voff, soff, 0, 0);
+}
+
+// s_waitcnt on vmcnt only (expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | (((N >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier for the load ring.  __syncthreads() also waits for every
+// outstanding global load (its release fence counts the in-flight DMA loads
+// of later stages), which would drain the whole ring at each step; here each
+// wave has already waited (vmcnt) for the loads of the stage it publishes,
+// and LDS reads are complete once their MFMAs have consumed them, so a bare
+// s_barrier suffices.  The empty asm statements keep the compiler from
+// moving LDS accesses across it.
+__device__ __forceinline__ void ring_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Physical 16-byte chunk of logical chunk `c` in stage row `r` (rows of BK
+// bf16): XOR with the row's index among the rows that share one 256-byte
+// sweep of the banks, so 16 consecutive rows at one logical chunk are spread
+// over all banks.  The map is an involution.
+template <int BK>
+__device__ __forceinline__ int pchunk(int r, int c) {
+    constexpr int CH = BK / 8;
+    constexpr int SH = BK == 64 ? 1 : 2;
+    return c ^ ((r >> SH) & (CH - 1));
+}
+template <int BK>
+__device__ __forceinline__ int swz(int r, int c) {
+    return r * BK + (pchunk<BK>(r, c) << 3);
 }
 
 // GELU(z) = z Phi(z) = 0.5 z erfc(-z / sqrt 2).  erfc keeps full relative
@@ -42,167 +104,459 @@ __device__ __forceinline__ float gelu_erf(float z) {
     return 0.5f * z * erfcf(-z * 0.70710678118654752f);
 }
 
-template <int EPI>
-__global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
-    const bf16_t *__restrict__ A, int32_t lda, const bf16_t *__restrict__ W, int32_t ldw,
-    bf16_t *__restrict__ C, int32_t ldc, const int32_t *M_dev, int32_t M_max, int32_t N,
-    int32_t K) {
-    const int32_t M = M_dev ? *M_dev : M_max;
-    const int32_t t0 = blockIdx.y * BT;
-    if (t0 >= M) return;
-    // output features covered by this block
-    constexpr int BN = EPI ? BW / 2 : BW;
-    const int32_t n0 = blockIdx.x * BN;
+// Which tile a workgroup computes; false for a workgroup with no live tile.
+// The grid is sized for the largest row count and only the first `live_by`
+// token tiles hold rows.  Workgroups are handed to the 8 XCDs in turn
+// (dispatch index i goes to XCD i % 8) and each XCD has its own L2, so the
+// live dispatch indices are first spread evenly over the XCDs as contiguous
+// ranges of tiles; each range is walked in groups of 4 token tiles (all
+// weight tiles of a group before the next group), so the tiles resident on
+// one XCD share a few activation panels and a few weight panels.
+__device__ __forceinline__ bool tile_order(int live_by, int &bx, int &by) {
+    const int nbx = gridDim.x;
+    const int live = nbx * live_by;
+    const int d = by * nbx + bx;  // dispatch index
+    if (d >= live) return false;
+    const int x = d & 7, j = d >> 3;
+    const int q = live >> 3, r = live & 7;
+    const int b = x * q + min(x, r) + j;  // position in XCD x's contiguous range
+    constexpr int GT = 4;
+    const int group = b / (GT * nbx);
+    const int first = group * GT;
+    const int gsize = min(live_by - first, GT);
+    const int idx = b - group * GT * nbx;
+    bx = idx / gsize;
+    by = first + idx % gsize;
+    return true;
+}
 
-    __shared__ __attribute__((aligned(16))) bf16_t sW[2][BW * BK];
-    __shared__ __attribute__((aligned(16))) bf16_t sA[2][BT * BK];
+template <int BW_, int BT_, int WW_, int WT_, int BK_, int STAGES_>
+struct Cfg {
+    static constexpr int BW = BW_, BT = BT_, WW = WW_, WT = WT_, BK = BK_, STAGES = STAGES_;
+    static constexpr int NWAVE = WW * WT, NTHR = NWAVE * 64;
+    static constexpr int RW = BW / WW, RT = BT / WT;  // rows / tokens per wave
+    static constexpr int FA = RW / 32, FB = RT / 32;  // 32x32 fragments per wave
+    static constexpr int STAGE_ELEMS = (BW + BT) * BK;
+    static constexpr int CH = BK / 8;                      // 16-byte chunks per row
+    static constexpr int RPL = 64 / CH;                    // rows per 1 KB DMA load
+    static constexpr int LOADS = (BW + BT) / RPL / NWAVE;  // DMA loads per wave per stage
+    static constexpr int WLOADS = BW / RPL / NWAVE;        // the first WLOADS are weight rows
+    static_assert(BK == 32 || BK == 64, "K step");
+    static_assert((BW / RPL) % NWAVE == 0 && (BT / RPL) % NWAVE == 0, "even split of loads");
+    static_assert(RW % 32 == 0 && RT % 32 == 0, "32x32 fragments");
+    static_assert(STAGES >= 2 && (STAGES - 1) * LOADS < 64, "vmcnt range");
+    static_assert(STAGES * STAGE_ELEMS * 2 <= 160 * 1024, "LDS");
+    static_assert(FA + FB <= 15, "lgkmcnt range");
+};
+
+struct GemmParams {
+    const bf16_t *A;
+    int32_t lda;
+    const bf16_t *W;
+    int32_t ldw;
+    bf16_t *C;
+    int32_t ldc;
+    const int32_t *M_dev;
+    int32_t M_max, N, K;
+    int32_t splits;
+    float *partial;     // [tiles][splits][BW*BT] (splits > 1)
+    uint32_t *counter;  // [tiles] (splits > 1), zero between launches
+};
+
+template <class G, int EPI, bool SPLITK>
+__global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
+    constexpr int BW = G::BW, BT = G::BT, FA = G::FA, FB = G::FB, STAGES = G::STAGES;
+    constexpr int BK = G::BK, CH = G::CH, RPL = G::RPL;
+    static_assert(EPI == 0 || FA % 2 == 0, "GeGLU needs matching u/g fragments");
+    const int32_t M = p.M_dev ? *p.M_dev : p.M_max;
+    int bx = blockIdx.x, by = blockIdx.y;
+    if (!SPLITK) {
+        if (!tile_order((M + BT - 1) / BT, bx, by)) return;
+    }
+    const int32_t t0 = by * BT;
+    if (t0 >= M) return;
+    constexpr int BN = EPI ? BW / 2 : BW;  // output features per tile
+    const int32_t n0 = bx * BN;
+    const int split = blockIdx.z;
+    const int N = p.N;
+
+    __shared__ __attribute__((aligned(16))) bf16_t smem[STAGES * G::STAGE_ELEMS];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
-    const int wr = wave >> 1;  // wave row (weight rows)
-    const int wc = wave & 1;   // wave column (tokens)
+    const int wr = wave / G::WT;  // wave row (weight rows)
+    const int wc = wave % G::WT;  // wave column (tokens)
 
-    // Global -> register staging: each thread moves 4 chunks of W and 4 of A.
-    // chunk id q = tid + 256*i: row = q >> 3, chunk = q & 7.
-    int w_src_row[4];
-    bool w_ok[4];
-    bool a_ok[4];
+    // K range of this split, in 64-wide pieces, then in BK steps
+    const int np_all = p.K / KMULT;
+    const int pb = (int)((int64_t)split * np_all / p.splits);
+    const int pe = (int)((int64_t)(split + 1) * np_all / p.splits);
+    const int kbase = pb * KMULT;
+    const int nk = (pe - pb) * (KMULT / BK);
+
+    // Per-lane DMA sources.  Load j of a wave covers LDS block
+    // jj = j * NWAVE + wave (1 KB: stage rows RPL*jj .. RPL*jj+RPL-1; weight
+    // rows come first, then tokens, and loads j < WLOADS are exactly the
+    // weight ones).  Lane L writes physical chunk L % CH of row RPL*jj + L/CH,
+    // so it fetches the logical chunk that the swizzle stores there.
+    // The loads are buffer loads into LDS: a per-lane 32-bit byte offset from
+    // the W or A base, the K step's byte offset in a scalar register, and a
+    // resource whose size is the operand's extent, so the hardware drops any
+    // access past it.  (Buffer rather than global loads: the waitcnt pass
+    // counts a global load into LDS as an LDS access too, which would force
+    // every wait on the fragment reads to lgkmcnt(0).)
+    const int rr = lane / CH, pc = lane % CH;
+    const uint32_t w_rows = EPI ? 2u * (uint32_t)N : (uint32_t)N;
+    const uint32_t w_bytes = ((w_rows - 1) * (uint32_t)p.ldw + (uint32_t)p.K) * 2u;
+    const uint32_t a_bytes = (((uint32_t)p.M_max - 1) * (uint32_t)p.lda + (uint32_t)p.K) * 2u;
+    uint32_t off[G::LOADS];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = (tid + 256 * i) >> 3;
-        int wrow;
-        if (EPI) {
-            wrow = (row < 64) ? (n0 + row) : (N + n0 + row - 64);
-            w_ok[i] = (n0 + (row & 63)) < N;
+    for (int j = 0; j < G::LOADS; ++j) {
+        const int jj = j * G::NWAVE + wave;
+        const int r = RPL * jj + rr;      // stage row
+        const int c = pchunk<BK>(r, pc);  // logical chunk stored at physical chunk pc
+        if (j < G::WLOADS) {
+            int grow;
+            if (EPI) {
+                const int half = BW / 2;
+                int f = n0 + (r % half);
+                if (f >= N) f = N - 1;  // clamp: rows past N are computed, never stored
+                grow = (r < half) ? f : N + f;
+            } else {
+                grow = n0 + r;
+                if (grow >= N) grow = N - 1;
+            }
+            off[j] = (uint32_t)(grow * p.ldw + kbase + c * 8) * 2u;
         } else {
-            wrow = n0 + row;
-            w_ok[i] = wrow < N;
+            int trow = t0 + (r - BW);
+            if (trow >= M) trow = M - 1;
+            off[j] = (uint32_t)(trow * p.lda + kbase + c * 8) * 2u;
         }
-        w_src_row[i] = wrow;
-        a_ok[i] = (t0 + row) < M;
     }
-    const int chunk_l = tid & 7;
-
-    u32x4_t rw[4], ra[4];
-    auto gload = [&](int k0) {
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    auto issue = [&](int kt, int stage) {
+        bf16_t *base = smem + stage * G::STAGE_ELEMS + wave_u * 512;
+        const int k0b = kt * BK * 2;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = (tid + 256 * i) >> 3;
-            rw[i] = w_ok[i] ? ld16(W + (size_t)w_src_row[i] * ldw + k0 + chunk_l * 8)
-                            : u32x4_t{0, 0, 0, 0};
-            ra[i] = a_ok[i] ? ld16(A + (size_t)(t0 + row) * lda + k0 + chunk_l * 8)
-                            : u32x4_t{0, 0, 0, 0};
-        }
-    };
-    auto sstore = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = (tid + 256 * i) >> 3;
-            *reinterpret_cast<u32x4_t *>(&sW[buf][swz(row, chunk_l)]) = rw[i];
-            *reinterpret_cast<u32x4_t *>(&sA[buf][swz(row, chunk_l)]) = ra[i];
+        for (int j = 0; j < G::LOADS; ++j) {
+            if (j < G::WLOADS)
+                dma16(p.W, w_bytes, (lds_ptr_t)(base + j * G::NWAVE * 512), off[j], k0b);
+            else
+                dma16(p.A, a_bytes, (lds_ptr_t)(base + j * G::NWAVE * 512), off[j], k0b);
         }
     };
 
-    f32x16_t acc[2][2];
+    f32x16_t acc[FA][FB];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < FA; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < FB; ++b)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
 
-    // Weight-row base of each of the wave's two A fragments within the tile.
-    int wbase[2];
-    if (EPI) {
-        wbase[0] = wr * 32;       // GELU half
-        wbase[1] = 64 + wr * 32;  // gate half
-    } else {
-        wbase[0] = wr * 64;
-        wbase[1] = wr * 64 + 32;
+    // stage-row base of each A (weight) fragment
+    int wrow[FA];
+#pragma unroll
+    for (int a = 0; a < FA; ++a) {
+        if (EPI)
+            wrow[a] = (a < FA / 2) ? (wr * (G::RW / 2) + 32 * a)
+                                   : (BW / 2 + wr * (G::RW / 2) + 32 * (a - FA / 2));
+        else
+            wrow[a] = wr * G::RW + 32 * a;
     }
-    const int tbase = wc * 64;
     const int l32 = lane & 31, lhi = lane >> 5;
 
-    const int nk = K / BK;
-    gload(0);
-    sstore(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) gload((kt + 1) * BK);
+    // Software pipeline.  Fragments are double-buffered in registers: the
+    // LDS reads of step s+1 are issued before the MFMAs of step s, so the
+    // matrix cores hide the LDS latency.  At the last step of a stage the
+    // wave waits for the next stage's loads, meets the others at the
+    // barrier, refills the stage it has finished reading, and issues the
+    // next stage's first reads before its last MFMAs of this stage.
+    constexpr int NS = BK / 16;  // MFMA steps per stage (2 or 4)
+    static_assert(NS % 2 == 0, "fragment buffers alternate per step");
+    bf16x8_t fw[2][FA], fa[2][FB];
+    auto read_frags = [&](int stage, int s, int buf) {
+        const bf16_t *sw = smem + stage * G::STAGE_ELEMS;
+        const bf16_t *sa = sw + BW * BK;
+        const int ch = 2 * s + lhi;
 #pragma unroll
-        for (int s = 0; s < BK / 16; ++s) {
-            const int ch = 2 * s + lhi;
-            bf16x8_t fw[2], fa[2];
+        for (int a = 0; a < FA; ++a)
+            fw[buf][a] = *reinterpret_cast<const bf16x8_t *>(&sw[swz<BK>(wrow[a] + l32, ch)]);
 #pragma unroll
-            for (int a = 0; a < 2; ++a)
-                fw[a] = *reinterpret_cast<const bf16x8_t *>(&sW[cur][swz(wbase[a] + l32, ch)]);
+        for (int b = 0; b < FB; ++b)
+            fa[buf][b] = *reinterpret_cast<const bf16x8_t *>(
+                &sa[swz<BK>(wc * G::RT + 32 * b + l32, ch)]);
+    };
+    auto mfmas = [&](int buf) {
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
-                fa[b] = *reinterpret_cast<const bf16x8_t *>(&sA[cur][swz(tbase + 32 * b + l32, ch)]);
+        for (int a = 0; a < FA; ++a)
 #pragma unroll
-            for (int a = 0; a < 2; ++a)
+            for (int b = 0; b < FB; ++b)
+                acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[buf][a], fa[buf][b],
+                                                                    acc[a][b], 0, 0, 0);
+    };
+
+    // prologue: every stage of the ring in flight, then stage 0 published
 #pragma unroll
-                for (int b = 0; b < 2; ++b)
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[a], fa[b], acc[a][b],
-                                                                        0, 0, 0);
+    for (int st = 0; st < STAGES; ++st)
+        if (st < nk) issue(st, st);
+    if (nk >= STAGES)
+        wait_vmcnt<(STAGES - 1) * G::LOADS>();
+    else
+        wait_vmcnt<0>();
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): no scalar loads left in flight, so
+                                         // the loop's LDS reads can be waited on in order
+    ring_barrier();
+    if (nk > 0) read_frags(0, 0, 0);
+
+    for (int i = 0; i < nk; ++i) {
+        const int stage = i % STAGES;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            if (s + 1 < NS) {
+                read_frags(stage, s + 1, (s + 1) & 1);
+            } else {
+                // outstanding loads after stage i+1: stages i+2 .. min(i+STAGES-1, nk-1)
+                if (i + STAGES <= nk)
+                    wait_vmcnt<(STAGES - 2) * G::LOADS>();
+                else
+                    wait_vmcnt<0>();
+                __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this stage fully read
+                ring_barrier();
+                if (i + STAGES < nk) issue(i + STAGES, stage);
+                // next stage's first fragments (after the last stage: an unused
+                // read of a valid stage, kept so the loop body has no branch
+                // around LDS reads and their waits stay exact)
+                read_frags((i + 1) % STAGES, 0, 0);
+            }
+            // the fragments of step s are complete once at most the reads of
+            // step s+1 remain in flight
+            __builtin_amdgcn_s_waitcnt(0xC07F | ((G::FA + G::FB) << 8));
+            __builtin_amdgcn_sched_barrier(0);
+            mfmas(s & 1);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        if (kt + 1 < nk) sstore(cur ^ 1);
+    }
+
+    if constexpr (SPLITK) {
+        // Publish this split's partial tile, then let the last split finish it.
+        const int tile = blockIdx.y * gridDim.x + blockIdx.x;
+        float *mine = p.partial + ((size_t)tile * p.splits + split) * (BW * BT);
+        // layout: [wave][a][b][e4][lane][4] -> each lane stores 16 contiguous bytes
+#pragma unroll
+        for (int a = 0; a < FA; ++a)
+#pragma unroll
+            for (int b = 0; b < FB; ++b)
+#pragma unroll
+                for (int e4 = 0; e4 < 4; ++e4) {
+                    const int blk = ((wave * FA + a) * FB + b) * 4 + e4;
+                    f32x4_t v = {acc[a][b][4 * e4], acc[a][b][4 * e4 + 1], acc[a][b][4 * e4 + 2],
+                                 acc[a][b][4 * e4 + 3]};
+                    *reinterpret_cast<f32x4_t *>(mine + (size_t)blk * 256 + lane * 4) = v;
+                }
+        __threadfence();
+        __shared__ uint32_t s_last;
         __syncthreads();
+        if (tid == 0) {
+            const uint32_t done = atomicAdd(&p.counter[tile], 1u);
+            s_last = (done == (uint32_t)(p.splits - 1)) ? 1u : 0u;
+        }
+        __syncthreads();
+        if (!s_last) return;
+        __threadfence();
+        // sum the partials in split order (own contribution from registers)
+        const float *base = p.partial + (size_t)tile * p.splits * (BW * BT);
+#pragma unroll
+        for (int a = 0; a < FA; ++a)
+#pragma unroll
+            for (int b = 0; b < FB; ++b)
+#pragma unroll
+                for (int e4 = 0; e4 < 4; ++e4) {
+                    const int blk = ((wave * FA + a) * FB + b) * 4 + e4;
+                    f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
+                    for (int s = 0; s < p.splits; ++s) {
+                        f32x4_t v;
+                        if (s == split)
+                            v = f32x4_t{acc[a][b][4 * e4], acc[a][b][4 * e4 + 1],
+                                        acc[a][b][4 * e4 + 2], acc[a][b][4 * e4 + 3]};
+                        else
+                            v = *reinterpret_cast<const f32x4_t *>(
+                                base + (size_t)s * (BW * BT) + (size_t)blk * 256 + lane * 4);
+                        if (s == 0)
+                            sum = v;
+                        else
+                            sum += v;
+                    }
+                    acc[a][b][4 * e4] = sum[0];
+                    acc[a][b][4 * e4 + 1] = sum[1];
+                    acc[a][b][4 * e4 + 2] = sum[2];
+                    acc[a][b][4 * e4 + 3] = sum[3];
+                }
+        if (tid == 0) p.counter[tile] = 0u;  // ready for the next launch
     }
 
     // Epilogue.  Accumulator element e of lane l in a 32x32 block holds
     // row (weight row) 8*(e/4) + 4*(l/32) + e%4 and column (token) l%32.
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-        const int32_t tok = t0 + tbase + 32 * b + l32;
+    for (int b = 0; b < FB; ++b) {
+        const int32_t tok = t0 + wc * G::RT + 32 * b + l32;
         if (tok >= M) continue;
-        bf16_t *crow = C + (size_t)tok * ldc;
+        bf16_t *crow = p.C + (size_t)tok * p.ldc;
         if (EPI) {
 #pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const int32_t f = n0 + wr * 32 + 8 * g4 + 4 * lhi;
-                if (f >= N) continue;
-                float h[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    h[e] = gelu_erf(acc[0][b][4 * g4 + e]) * acc[1][b][4 * g4 + e];
-                u32x2_t pk = {pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
-                *reinterpret_cast<u32x2_t *>(crow + f) = pk;
-            }
-        } else {
-#pragma unroll
-            for (int a = 0; a < 2; ++a) {
+            for (int a = 0; a < FA / 2; ++a)
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4) {
-                    const int32_t f = n0 + wbase[a] + 8 * g4 + 4 * lhi;
+                    const int32_t f = n0 + wr * (G::RW / 2) + 32 * a + 8 * g4 + 4 * lhi;
+                    if (f >= N) continue;
+                    float h[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        h[e] = gelu_erf(acc[a][b][4 * g4 + e]) * acc[a + FA / 2][b][4 * g4 + e];
+                    u32x2_t pk = {pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
+                    *reinterpret_cast<u32x2_t *>(crow + f) = pk;
+                }
+        } else {
+#pragma unroll
+            for (int a = 0; a < FA; ++a)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int32_t f = n0 + wrow[a] + 8 * g4 + 4 * lhi;
                     if (f >= N) continue;
                     const f32x16_t &v = acc[a][b];
                     u32x2_t pk = {pack_bf16x2(v[4 * g4], v[4 * g4 + 1]),
                                   pack_bf16x2(v[4 * g4 + 2], v[4 * g4 + 3])};
                     *reinterpret_cast<u32x2_t *>(crow + f) = pk;
                 }
-            }
         }
     }
 }
 
+// Tile configurations: weight rows x tokens, wave grid, K step, stages.
+using CfgXS = Cfg<32, 64, 1, 1, 64, 6>;    // small M, 1 wave (plain only)
+using CfgXSG = Cfg<64, 64, 1, 1, 64, 4>;   // small M, 1 wave (GeGLU-capable)
+using CfgS = Cfg<128, 64, 2, 2, 64, 4>;    // 4 waves of 64 rows x 32 tokens
+using CfgM = Cfg<128, 128, 2, 2, 32, 8>;   // 4 waves of 64 x 64
+using CfgL = Cfg<256, 128, 2, 4, 32, 6>;   // 8 waves of 128 x 32
+using CfgXL = Cfg<256, 256, 2, 4, 32, 4>;  // 8 waves of 128 x 64
+
+struct CfgInfo {
+    int bw, bt;
+};
+constexpr CfgInfo kCfgs[kGemmConfigs] = {{CfgXS::BW, CfgXS::BT}, {CfgXSG::BW, CfgXSG::BT},
+                                         {CfgS::BW, CfgS::BT},   {CfgM::BW, CfgM::BT},
+                                         {CfgL::BW, CfgL::BT},   {CfgXL::BW, CfgXL::BT}};
+
+template <class G, bool SPLITK>
+hipError_t launch_cfg(hipStream_t s, const GemmParams &p, int epilogue) {
+    const int bn = epilogue ? G::BW / 2 : G::BW;
+    const dim3 grid((p.N + bn - 1) / bn, (p.M_max + G::BT - 1) / G::BT, p.splits);
+    if (epilogue) {
+        if constexpr (G::FA % 2 == 0)
+            hipLaunchKernelGGL((gemm_kernel<G, 1, SPLITK>), grid, dim3(G::NTHR), 0, s, p);
+        else
+            return hipErrorInvalidValue;
+    } else {
+        hipLaunchKernelGGL((gemm_kernel<G, 0, SPLITK>), grid, dim3(G::NTHR), 0, s, p);
+    }
+    return hipGetLastError();
+}
+
+// Small tiles take split K; the large ones never do (K is always whole).
+template <class G>
+hipError_t launch_small(hipStream_t s, const GemmParams &p, int epilogue) {
+    return p.splits > 1 ? launch_cfg<G, true>(s, p, epilogue)
+                        : launch_cfg<G, false>(s, p, epilogue);
+}
+template <class G>
+hipError_t launch_large(hipStream_t s, const GemmParams &p, int epilogue) {
+    return p.splits > 1 ? hipErrorInvalidValue : launch_cfg<G, false>(s, p, epilogue);
+}
+
 }  // namespace
+
+int gemm_max_splits(int config) { return config <= 3 ? 8 : 1; }
+
+GemmPlan plan_gemm_tiles(int32_t M, int32_t N, int32_t K, int epilogue) {
+    // Tile shape with the least estimated time: whole waves of workgroups
+    // over the 256 compute units times the per-tile cost, with the relative
+    // per-CU throughput of each shape.
+    const int64_t nw = epilogue ? 2LL * N : N;
+    const int cand[4] = {2, 3, 4, 5};
+    const double eff[4] = {0.45, 0.70, 0.85, 1.0};
+    GemmPlan g{3, 1};
+    double best = 1e30;
+    for (int i = 0; i < 4; ++i) {
+        const CfgInfo &c = kCfgs[cand[i]];
+        const int64_t tiles = ((nw + c.bw - 1) / c.bw) * ((M + c.bt - 1) / c.bt);
+        const int64_t waves = (tiles + 255) / 256;
+        const double t = (double)waves * c.bw * c.bt / eff[i];
+        if (t < best) {
+            best = t;
+            g.config = cand[i];
+        }
+    }
+    (void)K;
+    return g;
+}
+
+GemmPlan plan_gemm(int32_t M_max, int32_t N, int32_t K, int epilogue) {
+    const int64_t nw = epilogue ? 2LL * N : N;  // weight rows read
+    const int np = K / KMULT;                   // 64-wide K pieces
+    GemmPlan g{};
+    if (M_max <= 64) {
+        // small M: stream the weights with many narrow tiles; split K until
+        // about 2 workgroups per CU
+        g.config = epilogue ? 1 : 0;
+        const int64_t tiles = (nw + kCfgs[g.config].bw - 1) / kCfgs[g.config].bw;
+        int s = 1;
+        while (s < 8 && tiles * s * 2 <= 512 && np / (s * 2) >= 2) s *= 2;
+        g.splits = s;
+    } else if (M_max <= 256) {
+        g.config = 2;
+        const int64_t tiles = ((nw + 127) / 128) * ((M_max + 63) / 64);
+        int s = 1;
+        while (s < 4 && tiles * s * 2 <= 512 && np / (s * 2) >= 4) s *= 2;
+        g.splits = s;
+    } else {
+        g = plan_gemm_tiles(M_max, N, K, epilogue);
+    }
+    return g;
+}
+
+size_t gemm_workspace_bytes(const GemmPlan &g, int32_t M_max, int32_t N, int epilogue) {
+    if (g.splits <= 1) return 0;
+    const CfgInfo &c = kCfgs[g.config];
+    const int bn = epilogue ? c.bw / 2 : c.bw;
+    const size_t tiles = (size_t)((N + bn - 1) / bn) * ((M_max + c.bt - 1) / c.bt);
+    return tiles * g.splits * c.bw * c.bt * 4;
+}
+
+size_t gemm_counter_count(const GemmPlan &g, int32_t M_max, int32_t N, int epilogue) {
+    if (g.splits <= 1) return 0;
+    const CfgInfo &c = kCfgs[g.config];
+    const int bn = epilogue ? c.bw / 2 : c.bw;
+    return (size_t)((N + bn - 1) / bn) * ((M_max + c.bt - 1) / c.bt);
+}
 
 hipError_t launch_gemm(hipStream_t s, const bf16_t *A, int32_t lda, const bf16_t *W,
                        int32_t ldw, bf16_t *C, int32_t ldc, const int32_t *M_dev,
-                       int32_t M_max, int32_t N, int32_t K, int epilogue) {
+                       int32_t M_max, int32_t N, int32_t K, int epilogue, const GemmPlan &plan,
+                       float *partial, uint32_t *counter) {
     if (M_max <= 0 || N <= 0) return hipSuccess;
-    if (K % BK != 0 || N % 64 != 0) return hipErrorInvalidValue;
-    const int bn = epilogue ? BW / 2 : BW;
-    const dim3 grid((N + bn - 1) / bn, (M_max + BT - 1) / BT);
-    if (epilogue)
-        hipLaunchKernelGGL(gemm_bf16_kernel<1>, grid, dim3(256), 0, s, A, lda, W, ldw, C, ldc,
-                           M_dev, M_max, N, K);
-    else
-        hipLaunchKernelGGL(gemm_bf16_kernel<0>, grid, dim3(256), 0, s, A, lda, W, ldw, C, ldc,
-                           M_dev, M_max, N, K);
-    return hipGetLastError();
+    if (K % KMULT != 0 || N % 64 != 0 || plan.config < 0 || plan.config >= kGemmConfigs ||
+        plan.splits < 1 || plan.splits > K / KMULT || plan.splits > gemm_max_splits(plan.config))
+        return hipErrorInvalidValue;
+    if (plan.splits > 1 && (!partial || !counter)) return hipErrorInvalidValue;
+    GemmParams p{A, lda, W, ldw, C, ldc, M_dev, M_max, N, K, plan.splits, partial, counter};
+    switch (plan.config) {
+        case 0: return launch_small<CfgXS>(s, p, epilogue);
+        case 1: return launch_small<CfgXSG>(s, p, epilogue);
+        case 2: return launch_small<CfgS>(s, p, epilogue);
+        case 3: return launch_small<CfgM>(s, p, epilogue);
+        case 4: return launch_large<CfgL>(s, p, epilogue);
+        default: return launch_large<CfgXL>(s, p, epilogue);
+    }
 }
 
 }  // namespace laya

@@ -41,10 +41,29 @@ hipError_t launch_layernorm(hipStream_t s, bf16_t *x, const bf16_t *r, bf16_t *n
                             const float *gamma, const int32_t *count_dev, int32_t count_max,
                             int32_t hidden, float eps);
 
-// C = bf16(A W^T), epilogue 0 plain, 1 GeGLU (W has 2N rows).
+// GEMM tile configuration and K split.  Every output element is one MFMA
+// chain per K range, the ranges summed in order, so a result depends only on
+// `splits` (never on the tile shape).
+constexpr int kGemmConfigs = 6;
+struct GemmPlan {
+    int config;  // 0 XS 32x64, 1 XSG 64x64, 2 S 128x64, 3 M 128x128, 4 L 256x128, 5 XL 256x256
+    int splits;  // K ranges (>= 1)
+};
+// plan for a GEMM launched with a grid for M_max rows (the K split depends
+// only on M_max); plan_gemm_tiles: the best whole-K tile shape for M rows.
+GemmPlan plan_gemm(int32_t M_max, int32_t N, int32_t K, int epilogue);
+GemmPlan plan_gemm_tiles(int32_t M, int32_t N, int32_t K, int epilogue);
+int gemm_max_splits(int config);
+// float32 partial-tile bytes and tile counters a plan needs (0 when splits == 1)
+size_t gemm_workspace_bytes(const GemmPlan &g, int32_t M_max, int32_t N, int epilogue);
+size_t gemm_counter_count(const GemmPlan &g, int32_t M_max, int32_t N, int epilogue);
+
+// C = bf16(A W^T), epilogue 0 plain, 1 GeGLU (W has 2N rows).  With
+// plan.splits > 1, `partial` and `counter` (zero-filled once) are required.
 hipError_t launch_gemm(hipStream_t s, const bf16_t *A, int32_t lda, const bf16_t *W,
                        int32_t ldw, bf16_t *C, int32_t ldc, const int32_t *M_dev,
-                       int32_t M_max, int32_t N, int32_t K, int epilogue);
+                       int32_t M_max, int32_t N, int32_t K, int epilogue, const GemmPlan &plan,
+                       float *partial, uint32_t *counter);
 
 hipError_t launch_rope(hipStream_t s, bf16_t *buf, int32_t ld, int32_t n_heads_rot,
                        const int32_t *count_dev, int32_t rows_max, const int32_t *pos,
