@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define LAYA_ABI_VERSION 1
+#define LAYA_ABI_VERSION 2
 
 #define LAYA_OK 0
 #define LAYA_E_INVALID -1     /* bad ids, lengths, markers, sizes, NULL pointers */
@@ -305,9 +305,37 @@ int laya_op_rope(void *stream, void *buf, int32_t ld, int32_t n_heads_rot, int32
                  const int32_t *pos, const void *cos_tab, const void *sin_tab,
                  int32_t max_pos);
 
+/* The QKV projection with its two consumers' layouts fused into the epilogue
+ * (the separate QKV, RoPE and attention steps of "[RFC]: Native Laya
+ * inference with Rust and CUDA #14", section Design; RoPE fused as the
+ * optimised variant of "[Performance]: Optimize native Rust/CUDA Laya
+ * inference #66", section Implementation priorities).  Computes
+ * z = bf16(A W^T) as laya_op_gemm epilogue 0 (same plan rules, same bits),
+ * then per output column f (heads of 64 columns):
+ *   f < rope_cols:           RoPE of the head exactly as laya_op_rope, at
+ *                            position pos[m] (device int32 [M]);
+ *   rope_cols <= f < vt_col0: stored plain in C;
+ *   f >= vt_col0:            stored transposed, vt[(f - vt_col0) * ldvt +
+ *                            vt_tok[m]] (vt device BF16, vt_tok device int32
+ *                            [M]); C is not written for these columns.
+ * rope_cols and vt_col0 are multiples of 64 with rope_cols <= vt_col0 <= N.
+ * cos_tab/sin_tab device BF16 [positions][32].  Not on tile shape 0. */
+int laya_op_gemm_qkv(void *stream, const void *A, int32_t lda, const void *W, int32_t ldw,
+                     void *C, int32_t ldc, int32_t M, int32_t N, int32_t K, const int32_t *pos,
+                     const void *cos_tab, const void *sin_tab, int32_t rope_cols, void *vt,
+                     int32_t ldvt, const int32_t *vt_tok, int32_t vt_col0, int32_t config,
+                     int32_t splits);
+
 /* Attention with a key-padding row and an optional sliding window, for a
- * packed batch.  Keys/values of row b are tokens row_off[b] .. row_off[b+1]-1
- * of k and v (device BF16, row stride ldkv, head h at columns 64h..64h+63).
+ * packed batch (flash attention over the native QKV buffer, "[RFC]: Native
+ * Laya inference with Rust and CUDA #14", section Design; single query rows
+ * honour the padding mask, "perf(model): exact Metal speed-ups of the
+ * forward pass").  Keys of row b are tokens row_off[b] .. row_off[b+1]-1 of
+ * k (device BF16, row stride ldk, head h at columns 64h..64h+63); its values
+ * are columns vt_col0[b] .. vt_col0[b] + len_b - 1 of vt (device BF16
+ * [n_heads*64][ldvt], row 64h + d = dimension d of head h), the layout that
+ * laya_op_gemm_qkv writes.  vt_col0 host int32 [B], each a multiple of 8 with
+ * vt_col0[b] + len_b <= ldvt.
  * Queries: if q_tok == NULL, every token t is a query, at q row t;
  * otherwise q row r is the query of token q_tok[r] (host int32 [n_q],
  * grouped so that queries of one row are consecutive).  Query of token t in
@@ -317,10 +345,10 @@ int laya_op_rope(void *stream, void *buf, int32_t ld, int32_t n_heads_rot, int32
  * row_off host int32 [B + 1].  Index metadata is built on the host and
  * uploaded into a buffer this call allocates and frees (diagnostic entry;
  * synchronises the stream). */
-int laya_op_attention(void *stream, const void *q, int32_t ldq, const void *k,
-                      const void *v, int32_t ldkv, void *o, int32_t ldo, int32_t n_heads,
-                      const int32_t *row_off, int32_t B, const int32_t *q_tok, int32_t n_q,
-                      int32_t half_window);
+int laya_op_attention(void *stream, const void *q, int32_t ldq, const void *k, int32_t ldk,
+                      const void *vt, int32_t ldvt, const int32_t *vt_col0, void *o, int32_t ldo,
+                      int32_t n_heads, const int32_t *row_off, int32_t B, const int32_t *q_tok,
+                      int32_t n_q, int32_t half_window);
 
 #ifdef __cplusplus
 }

@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol(lib):
     assert declared == set(b.EXPORTS)
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.laya_abi_version() == b.LAYA_ABI_VERSION == 1
+    assert lib.laya_abi_version() == b.LAYA_ABI_VERSION == 2
 
 
 def test_default_config_is_the_model(lib):
@@ -64,7 +64,7 @@ def test_invalid_configs(lib, change, code):
 
 def test_abi_mismatch(lib):
     c = b.Config.from_dict(MODEL)
-    c.abi_version = 2
+    c.abi_version = b.LAYA_ABI_VERSION + 1
     assert lib.laya_validate_config(ctypes.byref(c)) == b.LAYA_E_ABI
 
 

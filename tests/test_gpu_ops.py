@@ -187,6 +187,21 @@ def _attn_inputs(lengths, nh, seed):
     return T, row_off, q, kv
 
 
+def _vt_of(v, row_off, align=64, fill=float("nan")):
+    """V transposed into the layout the QKV epilogue writes: row b's keys at
+    columns vt_col0[b] .. (multiples of `align`); every other column holds
+    `fill`, which the kernel must never let into an output."""
+    import torch
+    lens = np.diff(row_off)
+    spans = (lens + align - 1) // align * align
+    vcol0 = np.concatenate([[0], np.cumsum(spans)])[:-1].astype(np.int32)
+    ld = int(vcol0[-1] + spans[-1])
+    vt = torch.full((v.shape[1], ld), fill, dtype=torch.bfloat16, device="cuda")
+    for b in range(len(lens)):
+        vt[:, vcol0[b]:vcol0[b] + lens[b]] = v[row_off[b]:row_off[b + 1]].t()
+    return vt, vcol0
+
+
 def _attn_oracle(q, kv, row_off, nh, hw, q_tok=None):
     H = nh * 64
     k, v = kv[:, :H], kv[:, H:]
@@ -209,13 +224,18 @@ def _attn_oracle(q, kv, row_off, nh, hw, q_tok=None):
 
 
 @pytest.mark.parametrize("hw", [-1, 64])
-def test_attention_against_oracle(B, hw):
+@pytest.mark.parametrize("align", [64, 8])
+def test_attention_against_oracle(B, hw, align):
+    """Every key length, global and local; V^T rows packed at 64- or 8-aligned
+    columns with NaN between them (a tile's tail then reads NaN or the next
+    row's values, which must not reach the output)."""
     import torch
     nh = 4
     T, row_off, q_h, kv_h = _attn_inputs(KEY_LENGTHS, nh, 20 + hw)
     q, kv = to_dev(q_h), to_dev(kv_h)
+    vt, vcol0 = _vt_of(kv[:, nh * 64:], row_off, align)
     o = torch.full((T, nh * 64), float("nan"), dtype=torch.bfloat16, device="cuda")
-    B.op_attention(q, kv[:, :nh * 64], kv[:, nh * 64:], o, nh, row_off, None, hw)
+    B.op_attention(q, kv[:, :nh * 64], vt, vcol0, o, nh, row_off, None, hw)
     _sync()
     got = from_dev(o)
     want = _attn_oracle(q_h, kv_h, row_off, nh, None if hw < 0 else hw)
@@ -226,7 +246,8 @@ def test_attention_against_oracle(B, hw):
         worst = max(worst, e)
         assert e < 4e-3, (KEY_LENGTHS[b], e)
     assert np.isfinite(got).all()
-    report("attention", {"half_window": hw, "lengths": KEY_LENGTHS, "worst_row_nrms": worst})
+    report("attention", {"half_window": hw, "align": align, "lengths": KEY_LENGTHS,
+                         "worst_row_nrms": worst})
 
 
 @pytest.mark.parametrize("hw", [-1, 64])
@@ -239,9 +260,10 @@ def test_attention_subset_rows_equal_full_rows(B, hw, n_rows):
     lens = [187, 37, 512, 64]
     T, row_off, q_h, kv_h = _attn_inputs(lens, nh, 40)
     q, kv = to_dev(q_h), to_dev(kv_h)
-    k, v = kv[:, :nh * 64], kv[:, nh * 64:]
+    k = kv[:, :nh * 64]
+    vt, vcol0 = _vt_of(kv[:, nh * 64:], row_off)
     full = torch.empty((T, nh * 64), dtype=torch.bfloat16, device="cuda")
-    B.op_attention(q, k, v, full, nh, row_off, None, hw)
+    B.op_attention(q, k, vt, vcol0, full, nh, row_off, None, hw)
     rng = np.random.default_rng(n_rows)
     per_row = []
     for b in range(len(lens)):
@@ -250,7 +272,7 @@ def test_attention_subset_rows_equal_full_rows(B, hw, n_rows):
     q_tok = np.concatenate(per_row)[:n_rows].astype(np.int32)
     qsub = q[torch.from_numpy(q_tok.astype(np.int64)).cuda()].contiguous()
     osub = torch.full((len(q_tok), nh * 64), float("nan"), dtype=torch.bfloat16, device="cuda")
-    B.op_attention(qsub, k, v, osub, nh, row_off, q_tok, hw)
+    B.op_attention(qsub, k, vt, vcol0, osub, nh, row_off, q_tok, hw)
     _sync()
     got = from_dev(osub)
     assert np.array_equal(bits_of(got), bits_of(from_dev(full)[q_tok]))
@@ -268,7 +290,8 @@ def test_attention_single_row_honours_padding(B):
     q, kv = to_dev(q_h), to_dev(kv_h)
     t = int(row_off[1] + 5)
     osub = torch.empty((1, nh * 64), dtype=torch.bfloat16, device="cuda")
-    B.op_attention(q[t:t + 1].contiguous(), kv[:, :nh * 64], kv[:, nh * 64:], osub, nh, row_off,
+    vt, vcol0 = _vt_of(kv[:, nh * 64:], row_off)
+    B.op_attention(q[t:t + 1].contiguous(), kv[:, :nh * 64], vt, vcol0, osub, nh, row_off,
                    np.array([t], np.int32), -1)
     _sync()
     want = _attn_oracle(q_h, kv_h, row_off, nh, None, [t])
@@ -284,11 +307,13 @@ def test_attention_keys_outside_window_do_not_matter(B):
     o1 = torch.empty((T, 64), dtype=torch.bfloat16, device="cuda")
     o2 = torch.empty((T, 64), dtype=torch.bfloat16, device="cuda")
     kv = to_dev(kv_h)
-    B.op_attention(q, kv[:, :64], kv[:, 64:], o1, nh, row_off, None, 64)
+    vt, vcol0 = _vt_of(kv[:, 64:], row_off)
+    B.op_attention(q, kv[:, :64], vt, vcol0, o1, nh, row_off, None, 64)
     kv2_h = kv_h.copy()
     kv2_h[300:] = 5.0  # keys/values at positions >= 300
     kv2 = to_dev(kv2_h)
-    B.op_attention(q, kv2[:, :64], kv2[:, 64:], o2, nh, row_off, None, 64)
+    vt2, _ = _vt_of(kv2[:, 64:], row_off)
+    B.op_attention(q, kv2[:, :64], vt2, vcol0, o2, nh, row_off, None, 64)
     _sync()
     a, b = from_dev(o1), from_dev(o2)
     assert np.array_equal(bits_of(a[:236]), bits_of(b[:236]))  # queries < 236 never see key 300
@@ -341,3 +366,61 @@ def test_gemm_split_k_repeats_bitwise(B):
         _sync()
         outs.append(bits_of(from_dev(c)))
     assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[1], outs[2])
+
+
+# ------------------------------------------------------- QKV epilogue (fused) --
+
+@pytest.mark.parametrize("M,H,cfgs,splits", [(48, 128, (1, 2, 3), (1, 2, 5)),
+                                             (300, 1024, (2, 3, 4, 5), (1,)),
+                                             (97, 256, (1, 2, 3), (1, 4))])
+def test_gemm_qkv_epilogue_equals_gemm_then_rope(B, M, H, cfgs, splits):
+    """The QKV epilogue gives bitwise the plain GEMM followed by the RoPE
+    kernel on the Q and K columns (which is bit-exact against the oracle), and
+    V transposed to per-token columns, for every tile shape and K split."""
+    import torch
+    K, N = 1024, 3 * H
+    a_h = oracle.bf16_round(random_normal((M, K), M + 5))
+    w_h = oracle.bf16_round(random_normal((N, K), N + 7, 0.03))
+    a, w = to_dev(a_h), to_dev(w_h)
+    cb, sb = B.rope_table(160000.0, 512, 64)
+    ct = torch.from_numpy(cb.view(np.int16)).cuda()
+    st = torch.from_numpy(sb.view(np.int16)).cuda()
+    rng = np.random.default_rng(M)
+    pos_h = rng.integers(0, 512, M).astype(np.int32)
+    pos = torch.from_numpy(pos_h).cuda()
+    # V^T columns: a permutation with gaps, as packed rows with aligned starts
+    vtok_h = (np.arange(M) + 3 * (np.arange(M) // 17)).astype(np.int32)
+    vtok = torch.from_numpy(vtok_h).cuda()
+    ldvt = int(vtok_h.max()) + 9
+    for sp in splits:
+        ref = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+        B.op_gemm(a, w, ref, M, N, K, 0, config=cfgs[0], splits=sp)
+        B.op_rope(ref, 2 * H // 64, pos, ct, st)
+        _sync()
+        ref_h = bits_of(from_dev(ref))
+        if sp == 1:
+            ref1 = ref_h
+        for cfg in cfgs:
+            c = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+            vt = torch.full((H, ldvt), float("nan"), dtype=torch.bfloat16, device="cuda")
+            B.op_gemm_qkv(a, w, c, M, N, K, pos, ct, st, 2 * H, vt, vtok, 2 * H, config=cfg,
+                          splits=sp)
+            _sync()
+            got = bits_of(from_dev(c))
+            assert np.array_equal(got[:, :2 * H], ref_h[:, :2 * H]), (cfg, sp)
+            vt_h = bits_of(from_dev(vt))
+            assert np.array_equal(vt_h[:, vtok_h].T, ref_h[:, 2 * H:]), (cfg, sp)
+            assert np.isnan(from_dev(c)[:, 2 * H:]).all()  # V block of C not written
+    # the rotated Q/K (split 1) against the oracle's RoPE of the plain GEMM's values
+    plain = _plain(B, a, w, M, N, K, cfgs[0])
+    want = oracle.rope_apply(plain[:, :2 * H].reshape(M, 2 * H // 64, 64), pos_h,
+                             *oracle.rope_tables(160000.0, 512, 64))
+    assert np.array_equal(bits_of(want.reshape(M, -1)), ref1[:, :2 * H])
+
+
+def _plain(B, a, w, M, N, K, cfg):
+    import torch
+    c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    B.op_gemm(a, w, c, M, N, K, 0, config=cfg, splits=1)
+    _sync()
+    return from_dev(c)

@@ -16,7 +16,7 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liblaya_encoder.so")
 
-LAYA_ABI_VERSION = 1
+LAYA_ABI_VERSION = 2
 LAYA_OK = 0
 LAYA_E_INVALID = -1
 LAYA_E_UNSUPPORTED = -2
@@ -41,7 +41,7 @@ EXPORTS = [
     "laya_encoder_last_error", "laya_last_error", "laya_encoder_layer_output",
     "laya_encoder_weight_digest", "laya_encoder_weight", "laya_encoder_stats",
     "laya_encoder_profile", "laya_rope_table", "laya_memcpy", "laya_op_gather", "laya_op_layernorm", "laya_op_gemm",
-    "laya_op_rope", "laya_op_attention",
+    "laya_op_gemm_qkv", "laya_op_rope", "laya_op_attention",
 ]
 
 
@@ -143,9 +143,15 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
                                         ctypes.c_int32]),
         "laya_op_rope": (ctypes.c_int, [_P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                         _P, _P, _P, ctypes.c_int32]),
-        "laya_op_attention": (ctypes.c_int, [_P, _P, ctypes.c_int32, _P, _P, ctypes.c_int32, _P,
-                                             ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int32,
-                                             _P, ctypes.c_int32, ctypes.c_int32]),
+        "laya_op_gemm_qkv": (ctypes.c_int, [_P, _P, ctypes.c_int32, _P, ctypes.c_int32, _P,
+                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                            ctypes.c_int32, _P, _P, _P, ctypes.c_int32, _P,
+                                            ctypes.c_int32, _P, ctypes.c_int32, ctypes.c_int32,
+                                            ctypes.c_int32]),
+        "laya_op_attention": (ctypes.c_int, [_P, _P, ctypes.c_int32, _P, ctypes.c_int32, _P,
+                                             ctypes.c_int32, _P, _P, ctypes.c_int32,
+                                             ctypes.c_int32, _P, ctypes.c_int32, _P,
+                                             ctypes.c_int32, ctypes.c_int32]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -364,14 +370,29 @@ def op_rope(buf, n_heads_rot: int, pos, cos_tab, sin_tab, rows: Optional[int] = 
                                _dp(sin_tab), cos_tab.shape[0]), "laya_op_rope")
 
 
-def op_attention(q, k, v, o, n_heads: int, row_off, q_tok=None, half_window: int = -1,
-                 stream: Optional[int] = None):
-    """q, k, v, o: device tensors (2-D, row-major; k/v may be column views of one
-    buffer).  row_off, q_tok: host int arrays."""
+def op_gemm_qkv(A, W, C, M: int, N: int, K: int, pos, cos_tab, sin_tab, rope_cols: int,
+                vt, vt_tok, vt_col0: int, config: int = -1, splits: int = 1,
+                stream: Optional[int] = None):
+    """QKV projection with RoPE on columns [0, rope_cols) and columns
+    [vt_col0, N) stored transposed into vt at columns vt_tok[m]."""
+    st = current_stream() if stream is None else stream
+    _check(load().laya_op_gemm_qkv(st, _dp(A), A.stride(0), _dp(W), W.stride(0), _dp(C),
+                                   C.stride(0), M, N, K, _dp(pos), _dp(cos_tab), _dp(sin_tab),
+                                   rope_cols, _dp(vt), 0 if vt is None else vt.stride(0),
+                                   _dp(vt_tok), vt_col0, config, splits), "laya_op_gemm_qkv")
+
+
+def op_attention(q, k, vt, vt_col0, o, n_heads: int, row_off, q_tok=None,
+                 half_window: int = -1, stream: Optional[int] = None):
+    """q, k, o: device tensors (2-D, row-major; k may be a column view of a
+    wider buffer); vt: device [n_heads*64][ldvt] transposed values with row b's
+    keys at columns vt_col0[b]...  row_off, vt_col0, q_tok: host int arrays."""
     st = current_stream() if stream is None else stream
     ro = _i32(row_off)
+    vc = _i32(vt_col0)
     qt = None if q_tok is None else _i32(q_tok)
-    _check(load().laya_op_attention(st, _dp(q), q.stride(0), _dp(k), _dp(v), k.stride(0),
-                                    _dp(o), o.stride(0), n_heads, _ptr(ro), len(ro) - 1,
-                                    _ptr(qt), 0 if qt is None else len(qt), half_window),
+    _check(load().laya_op_attention(st, _dp(q), q.stride(0), _dp(k), k.stride(0), _dp(vt),
+                                    vt.stride(0), _ptr(vc), _dp(o), o.stride(0), n_heads,
+                                    _ptr(ro), len(ro) - 1, _ptr(qt),
+                                    0 if qt is None else len(qt), half_window),
            "laya_op_attention")

@@ -54,3 +54,63 @@ LAYA_DEV u32x4_t ld16(const void *p) { return *reinterpret_cast<const u32x4_t *>
 LAYA_DEV void st16(void *p, u32x4_t v) { *reinterpret_cast<u32x4_t *>(p) = v; }
 
 LAYA_DEV bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// ---------------------------------------------------------------------------
+// Direct HBM -> LDS loads and the waits around them.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
+
+// Last word of a buffer resource on CDNA: raw byte addressing (stride 0),
+// 32-bit data format, no swizzle.
+constexpr int kBufferWord3 = 0x00020000;
+
+// 16 bytes per lane from base + voff + soff (bytes) into LDS: lane L writes
+// dst + 16 L (dst is the wave's 1 KB block).  The buffer resource covers
+// `bytes` bytes from base; the hardware drops accesses past its end.  These
+// are buffer loads rather than global ones because LLVM's wait-count pass
+// also counts a global load into LDS as an LDS access, which would force
+// every wait on an LDS read behind it to lgkmcnt(0).
+LAYA_DEV void dma16(const void *base, uint32_t bytes, lds_ptr_t dst, uint32_t voff,
+                    uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                          kBufferWord3),
+        dst, 16, voff, soff, 0, 0);
+}
+
+// s_waitcnt on vmcnt only (expcnt and lgkmcnt left at their maxima).
+template <int N>
+LAYA_DEV void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | (((N >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// s_waitcnt on lgkmcnt only.
+template <int N>
+LAYA_DEV void wait_lgkmcnt() {
+    static_assert(N >= 0 && N < 16, "lgkmcnt range");
+    __builtin_amdgcn_s_waitcnt(0xC07F | (N << 8));
+}
+
+// Workgroup barrier for load rings.  __syncthreads() also waits for every
+// outstanding global load (its release fence counts the in-flight DMA loads
+// of later stages), which would drain the ring; a wave reaching this barrier
+// has already waited (vmcnt) for the loads it publishes, and LDS reads are
+// complete once the instructions that use them have run, so a bare
+// s_barrier suffices.  The empty asm statements keep the compiler from
+// moving LDS accesses across it.
+LAYA_DEV void ring_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Dispatch index -> work index such that the live work items [0, live) are
+// spread evenly over the 8 XCDs as contiguous ranges (dispatch index d runs
+// on XCD d % 8, and each XCD has its own L2).  Returns -1 past `live`.
+LAYA_DEV int xcd_contiguous(int d, int live) {
+    if (d >= live) return -1;
+    const int x = d & 7, j = d >> 3;
+    const int q = live >> 3, r = live & 7;
+    return x * q + min(x, r) + j;
+}

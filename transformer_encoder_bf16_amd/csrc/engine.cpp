@@ -94,8 +94,8 @@ void build_rope_table(double theta, int max_pos, int head_dim, uint16_t *c, uint
 // ---------------------------------------------------------------------------
 int align_down(int k) { return k - k % 64; }
 
-void build_blocks_full(const int32_t *row_off, int B, int half_window, AttnBlock *out,
-                       int *n_out) {
+void build_blocks_full(const int32_t *row_off, const int32_t *vcol0, int B, int half_window,
+                       AttnBlock *out, int *n_out) {
     int n = 0;
     for (int b = 0; b < B; ++b) {
         const int kt0 = row_off[b], len = row_off[b + 1] - row_off[b];
@@ -104,6 +104,7 @@ void build_blocks_full(const int32_t *row_off, int B, int half_window, AttnBlock
             AttnBlock a{};
             a.kt0 = kt0;
             a.klen = len;
+            a.vcol0 = vcol0[b];
             if (half_window < 0) {
                 a.k_lo = 0;
                 a.k_hi = len;
@@ -120,8 +121,9 @@ void build_blocks_full(const int32_t *row_off, int B, int half_window, AttnBlock
 }
 
 // q_row[r] = row of query r, q_pos[r] = its position.
-void build_blocks_list(const int32_t *row_off, const int32_t *q_row, const int32_t *q_pos,
-                       int n_q, int half_window, AttnBlock *out, int *n_out) {
+void build_blocks_list(const int32_t *row_off, const int32_t *vcol0, const int32_t *q_row,
+                       const int32_t *q_pos, int n_q, int half_window, AttnBlock *out,
+                       int *n_out) {
     int n = 0;
     int r = 0;
     while (r < n_q) {
@@ -137,6 +139,7 @@ void build_blocks_list(const int32_t *row_off, const int32_t *q_row, const int32
         AttnBlock a{};
         a.kt0 = row_off[row];
         a.klen = len;
+        a.vcol0 = vcol0[row];
         if (half_window < 0) {
             a.k_lo = 0;
             a.k_hi = len;
@@ -270,7 +273,7 @@ struct GraphEntry {
 
 // Offsets (in int32) of the per-run index upload for shape key (B, S, R).
 struct MetaLayout {
-    int64_t hdr, row_off, blk_g, blk_l, blk_sub, mrk_tok, mrk_pos, pos, ids, total;
+    int64_t hdr, row_off, blk_g, blk_l, blk_sub, mrk_tok, mrk_pos, pos, vtok, ids, total;
     int nblk_full_max, nblk_sub_max;
     static int64_t up8(int64_t v) { return (v + 7) & ~int64_t(7); }
     MetaLayout(int B, int S, int R) {
@@ -292,6 +295,8 @@ struct MetaLayout {
         mrk_pos = o;
         o = up8(o + R);
         pos = o;
+        o = up8(o + (int64_t)B * S);
+        vtok = o;
         o = up8(o + (int64_t)B * S);
         ids = o;
         o = up8(o + (int64_t)B * S);
@@ -326,6 +331,8 @@ struct laya_encoder {
     bf16_t *xa = nullptr, *xb = nullptr, *nrm = nullptr, *qkv = nullptr, *att = nullptr,
            *proj = nullptr, *hid = nullptr, *out = nullptr;
     bf16_t *x_sub = nullptr, *n_sub = nullptr, *q_sub = nullptr;
+    bf16_t *vt = nullptr;  // transposed V [n_heads*64][ldvt], rows start 64-aligned
+    int32_t ldvt = 0;
     float *gemm_partial = nullptr;    // split-K partial tiles
     uint32_t *gemm_counter = nullptr;  // split-K tile counters (zero between launches)
     int32_t *meta_dev = nullptr;
@@ -435,15 +442,15 @@ laya::GemmPlan full_plan(int Tmax, int T, int N, int K, int epi) {
 PassPlans make_plans(const laya_config &c, int Tmax, int T, int R) {
     const int H = c.hidden, F = c.ffn;
     PassPlans p{};
-    p.qkv = full_plan(Tmax, T, 3 * H, H, 0);
+    p.qkv = full_plan(Tmax, T, 3 * H, H, 2);
     p.o = full_plan(Tmax, T, H, H, 0);
     p.up = full_plan(Tmax, T, F, H, 1);
     p.down = full_plan(Tmax, T, H, F, 0);
     if (R > 0) {
-        p.kv_sub = full_plan(Tmax, T, 2 * H, H, 0);
+        p.kv_sub = full_plan(Tmax, T, 2 * H, H, 2);
         p.kv_sub.splits = p.qkv.splits;
         if (p.kv_sub.splits > laya::gemm_max_splits(p.kv_sub.config)) p.kv_sub.config = 2;
-        p.q_sub = subset_plan(p.qkv, R, H, H, 0);
+        p.q_sub = subset_plan(p.qkv, R, H, H, 2);
         p.o_sub = subset_plan(p.o, R, H, H, 0);
         p.up_sub = subset_plan(p.up, R, F, H, 1);
         p.down_sub = subset_plan(p.down, R, H, F, 0);
@@ -464,7 +471,7 @@ void gemm_scratch_bound(const laya_config &c, size_t *bytes, size_t *counters) {
     int last_splits[4] = {-1, -1, -1, -1};
     for (int T = 1; T <= tcap; ++T) {
         const PassPlans p = make_plans(c, T, T, 0);
-        acc(p.qkv, T, 3 * H, 0);
+        acc(p.qkv, T, 3 * H, 2);
         acc(p.o, T, H, 0);
         acc(p.up, T, F, 1);
         acc(p.down, T, H, 0);
@@ -474,8 +481,8 @@ void gemm_scratch_bound(const laya_config &c, size_t *bytes, size_t *counters) {
         std::copy(sp, sp + 4, last_splits);
         for (int R = 1; R <= c.max_markers; ++R) {
             const PassPlans q = make_plans(c, T, T, R);
-            acc(q.kv_sub, T, 2 * H, 0);
-            acc(q.q_sub, R, H, 0);
+            acc(q.kv_sub, T, 2 * H, 2);
+            acc(q.q_sub, R, H, 2);
             acc(q.o_sub, R, H, 0);
             acc(q.up_sub, R, F, 1);
             acc(q.down_sub, R, H, 0);
@@ -497,6 +504,7 @@ int record(laya_encoder *enc, hipStream_t s, const RunShape &rs, Profiler *prof 
     const int32_t *T_dev = md + ml.hdr + H_T;
     const int32_t *ids = md + ml.ids;
     const int32_t *pos = md + ml.pos;
+    const int32_t *vtok = md + ml.vtok;
     const AttnBlock *blk_g = reinterpret_cast<const AttnBlock *>(md + ml.blk_g);
     const AttnBlock *blk_l = reinterpret_cast<const AttnBlock *>(md + ml.blk_l);
     const AttnBlock *blk_s = reinterpret_cast<const AttnBlock *>(md + ml.blk_sub);
@@ -555,6 +563,13 @@ int record(laya_encoder *enc, hipStream_t s, const RunShape &rs, Profiler *prof 
     const double ln_res_by = 4 * T * H * b2, ln_by = 2 * T * H * b2;
     const double attn_fl_per_pair = 4.0 * c.head_dim * nh;
 
+    // bytes the attention kernel may read from a K column block of row
+    // stride ld (the workspace holds tcap token rows), and from V^T
+    auto k_bytes = [&](int ld) {
+        return (uint32_t)(((size_t)(enc->tcap - 1) * ld + H) * 2);
+    };
+    const uint32_t vt_bytes = (uint32_t)((size_t)H * enc->ldvt * 2);
+
     bf16_t *xr = enc->xa, *xalt = enc->xb;
     L_OP(OP_GATHER, 0, 2 * T * H * b2 + 4 * T,
          laya::launch_gather(s, enc->emb, ids, T_dev, Tmax, H, xr));
@@ -585,16 +600,16 @@ int record(laya_encoder *enc, hipStream_t s, const RunShape &rs, Profiler *prof 
         }
         pending = false;
         if (!subset) {
+            // Q, K rotated in the epilogue; V stored transposed for attention
+            const laya::QkvEpilogue qe{pos, ctab, stab, 2 * H, 2 * H, enc->vt, enc->ldvt, vtok};
             L_OP(OP_QKV, gemm_fl(T, 3 * H, H), gemm_by(T, 3 * H, 3 * H, H),
                  laya::launch_gemm(s, enc->nrm, H, Wqkv, H, enc->qkv, 3 * H, T_dev, Tmax, 3 * H,
-                                   H, 0, plans.qkv, gp, gc));
-            L_OP(OP_ROPE, 0, 2 * T * 2 * H * b2,
-                 laya::launch_rope(s, enc->qkv, 3 * H, 2 * nh, T_dev, Tmax, pos, ctab, stab));
+                                   H, 2, plans.qkv, gp, gc, &qe));
+            const laya::AttnParams ap{enc->qkv, 3 * H, enc->qkv + H, 3 * H, k_bytes(3 * H),
+                                      enc->vt, enc->ldvt, vt_bytes, enc->att, H, blk, nblk,
+                                      ml.nblk_full_max, pos, nh, half};
             L_OP(OP_ATTENTION, attn_fl_per_pair * (glob ? rs.pairs_global : rs.pairs_local),
-                 4 * T * H * b2,
-                 laya::launch_attention(s, enc->qkv, 3 * H, enc->qkv + H, enc->qkv + 2 * H,
-                                        3 * H, enc->att, H, blk, nblk, ml.nblk_full_max, pos,
-                                        nh, half));
+                 4 * T * H * b2, laya::launch_attention(s, ap));
             L_OP(OP_OUT_PROJ, gemm_fl(T, H, H), gemm_by(T, H, H, H),
                  laya::launch_gemm(s, enc->att, H, Wo, H, enc->proj, H, T_dev, Tmax, H, H, 0,
                                    plans.o, gp, gc));
@@ -622,24 +637,23 @@ int record(laya_encoder *enc, hipStream_t s, const RunShape &rs, Profiler *prof 
         } else {
             // keys/values for every token, queries only for the marker rows
             const int Ri = rs.R;
+            const laya::QkvEpilogue qe_kv{pos, ctab, stab, H, H, enc->vt, enc->ldvt, vtok};
             L_OP(OP_KV, gemm_fl(T, 2 * H, H), gemm_by(T, 2 * H, 2 * H, H),
                  laya::launch_gemm(s, enc->nrm, H, Wqkv + (size_t)H * H, H, enc->qkv, 2 * H,
-                                   T_dev, Tmax, 2 * H, H, 0, plans.kv_sub, gp, gc));
+                                   T_dev, Tmax, 2 * H, H, 2, plans.kv_sub, gp, gc, &qe_kv));
             L_OP(OP_ROW_GATHER, 0, 2 * R * H * b2,
                  laya::launch_gather_rows(s, enc->nrm, H, mrk_tok, Ri, H, enc->n_sub, H));
             L_OP(OP_ROW_GATHER, 0, 2 * R * H * b2,
                  laya::launch_gather_rows(s, xr, H, mrk_tok, Ri, H, enc->x_sub, H));
+            const laya::QkvEpilogue qe_q{mrk_pos, ctab, stab, H, H, nullptr, 0, nullptr};
             L_OP(OP_Q, gemm_fl(R, H, H), gemm_by(R, H, H, H),
                  laya::launch_gemm(s, enc->n_sub, H, Wqkv, H, enc->q_sub, H, nullptr, Ri, H, H,
-                                   0, plans.q_sub, gp, gc));
-            L_OP(OP_ROPE, 0, 2 * T * H * b2,
-                 laya::launch_rope(s, enc->qkv, 2 * H, nh, T_dev, Tmax, pos, ctab, stab));
-            L_OP(OP_ROPE, 0, 2 * R * H * b2,
-                 laya::launch_rope(s, enc->q_sub, H, nh, nullptr, Ri, mrk_pos, ctab, stab));
+                                   2, plans.q_sub, gp, gc, &qe_q));
+            const laya::AttnParams ap{enc->q_sub, H, enc->qkv, 2 * H, k_bytes(2 * H),
+                                      enc->vt, enc->ldvt, vt_bytes, enc->att, H, blk_s, nblk_s,
+                                      ml.nblk_sub_max, mrk_pos, nh, half};
             L_OP(OP_ATTENTION, attn_fl_per_pair * rs.pairs_subset, (2 * R + 2 * T) * H * b2,
-                 laya::launch_attention(s, enc->q_sub, H, enc->qkv, enc->qkv + H, 2 * H,
-                                        enc->att, H, blk_s, nblk_s, ml.nblk_sub_max, mrk_pos,
-                                        nh, half));
+                 laya::launch_attention(s, ap));
             L_OP(OP_OUT_PROJ, gemm_fl(R, H, H), gemm_by(R, H, H, H),
                  laya::launch_gemm(s, enc->att, H, Wo, H, enc->proj, H, nullptr, Ri, H, H, 0,
                                    plans.o_sub, gp, gc));
@@ -839,6 +853,9 @@ int laya_encoder_create(const laya_config *cfg, uint64_t seed, int device, laya_
     const int64_t tcap = (int64_t)c.max_batch * c.max_seq;
     const int64_t rcap = std::max(1, c.max_markers);
     enc->tcap = tcap;
+    // every row's V^T columns start at a multiple of 64
+    const int32_t ldvt = (int32_t)(tcap + 64LL * c.max_batch);
+    enc->ldvt = ldvt;
     size_t wsz = 0;
     std::vector<std::pair<bf16_t **, size_t>> bufs = {
         {&enc->xa, (size_t)tcap * H},      {&enc->xb, (size_t)tcap * H},
@@ -846,7 +863,7 @@ int laya_encoder_create(const laya_config *cfg, uint64_t seed, int device, laya_
         {&enc->att, (size_t)tcap * H},     {&enc->proj, (size_t)tcap * H},
         {&enc->hid, (size_t)tcap * F},     {&enc->out, (size_t)tcap * H},
         {&enc->x_sub, (size_t)rcap * H},   {&enc->n_sub, (size_t)rcap * H},
-        {&enc->q_sub, (size_t)rcap * H}};
+        {&enc->q_sub, (size_t)rcap * H},   {&enc->vt, (size_t)H * ldvt}};
     for (auto &b : bufs) wsz += al(b.second * 2);
     const MetaLayout mlmax(c.max_batch, c.max_seq, c.max_markers);
     enc->meta_cap = mlmax.total;
@@ -953,17 +970,23 @@ int laya_encoder_run(laya_encoder *enc, void *stream, const int32_t *ids,
     int32_t *mh = enc->meta_host;
     T = 0;
     mh[ml.row_off] = 0;
+    std::vector<int32_t> vcol0(B);
+    int32_t vcol = 0;
     for (int b = 0; b < B; ++b) {
+        vcol0[b] = vcol;
         for (int p = 0; p < lengths[b]; ++p) {
             mh[ml.ids + T] = ids[(int64_t)b * S + p];
             mh[ml.pos + T] = p;
+            mh[ml.vtok + T] = vcol + p;
             ++T;
         }
         mh[ml.row_off + b + 1] = T;
+        vcol += (lengths[b] + 63) / 64 * 64;
     }
     int nbg = 0, nbl = 0, nbs = 0;
-    build_blocks_full(mh + ml.row_off, B, -1, reinterpret_cast<AttnBlock *>(mh + ml.blk_g), &nbg);
-    build_blocks_full(mh + ml.row_off, B, c.window / 2,
+    build_blocks_full(mh + ml.row_off, vcol0.data(), B, -1,
+                      reinterpret_cast<AttnBlock *>(mh + ml.blk_g), &nbg);
+    build_blocks_full(mh + ml.row_off, vcol0.data(), B, c.window / 2,
                       reinterpret_cast<AttnBlock *>(mh + ml.blk_l), &nbl);
     if (R > 0) {
         std::vector<int32_t> qrow(R);
@@ -976,7 +999,7 @@ int laya_encoder_run(laya_encoder *enc, void *stream, const int32_t *ids,
         // unless the model has no decision layers and its last encoder layer is local
         const int Llast = layer_count(c) - 1;
         const bool glob = Llast >= c.n_enc_layers || (Llast % c.global_every) == 0;
-        build_blocks_list(mh + ml.row_off, qrow.data(), mh + ml.mrk_pos, R,
+        build_blocks_list(mh + ml.row_off, vcol0.data(), qrow.data(), mh + ml.mrk_pos, R,
                           glob ? -1 : c.window / 2,
                           reinterpret_cast<AttnBlock *>(mh + ml.blk_sub), &nbs);
     }
@@ -1240,42 +1263,77 @@ int laya_op_layernorm(void *stream, void *x, const void *r, void *n, const float
     return LAYA_OK;
 }
 
-int laya_op_gemm(void *stream, const void *A, int32_t lda, const void *W, int32_t ldw, void *C,
-                 int32_t ldc, int32_t M, int32_t N, int32_t K, int32_t epilogue, int32_t config,
-                 int32_t splits) {
-    if (M < 0 || N <= 0 || K <= 0 || K % 64 || N % 64 || lda % 8 || ldw % 8 || ldc % 8 ||
-        lda < K || ldw < K || ldc < N || (epilogue != 0 && epilogue != 1) ||
-        (M > 0 && (!A || !W || !C)) || config < -1 || config >= laya::kGemmConfigs)
-        return set_global_error(LAYA_E_INVALID, "laya_op_gemm: bad arguments");
-    if (M == 0) return LAYA_OK;
+namespace {
+// One GEMM launch on caller buffers; split-K scratch is allocated for the
+// call and freed after it completes.
+int op_gemm_launch(const char *who, hipStream_t s, const void *A, int32_t lda, const void *W,
+                   int32_t ldw, void *C, int32_t ldc, int32_t M, int32_t N, int32_t K,
+                   int32_t epilogue, int32_t config, int32_t splits,
+                   const laya::QkvEpilogue *qe) {
     laya::GemmPlan plan = laya::plan_gemm(M, N, K, epilogue);
     if (config >= 0) plan = laya::GemmPlan{config, splits < 1 ? 1 : splits};
-    if (plan.splits > K / 64 || (plan.splits > 1 && plan.config > 3) ||
+    if (plan.splits > K / 64 || plan.splits > laya::gemm_max_splits(plan.config) ||
         (epilogue && plan.config == 0))
-        return set_global_error(LAYA_E_INVALID, "laya_op_gemm: unsupported config/splits");
-    hipStream_t s = static_cast<hipStream_t>(stream);
+        return set_global_error(LAYA_E_INVALID, std::string(who) + ": unsupported config/splits");
     const size_t pb = laya::gemm_workspace_bytes(plan, M, N, epilogue);
     const size_t pc = laya::gemm_counter_count(plan, M, N, epilogue);
     void *scratch = nullptr;
+    if (pb && hipMalloc(&scratch, pb + pc * 4) != hipSuccess)
+        return set_global_error(LAYA_E_NOMEM, std::string(who) + ": scratch hipMalloc failed");
+    hipError_t e = hipSuccess;
+    if (pb) e = hipMemsetAsync(static_cast<char *>(scratch) + pb, 0, pc * 4, s);
+    if (e == hipSuccess)
+        e = laya::launch_gemm(s, static_cast<const bf16_t *>(A), lda,
+                              static_cast<const bf16_t *>(W), ldw, static_cast<bf16_t *>(C), ldc,
+                              nullptr, M, N, K, epilogue, plan,
+                              pb ? static_cast<float *>(scratch) : nullptr,
+                              pb ? reinterpret_cast<uint32_t *>(static_cast<char *>(scratch) + pb)
+                                 : nullptr,
+                              qe);
     if (pb) {
-        OPCHK(hipMalloc(&scratch, pb + pc * 4));
-        hipError_t e = hipMemsetAsync(static_cast<char *>(scratch) + pb, 0, pc * 4, s);
-        if (e == hipSuccess)
-            e = laya::launch_gemm(s, static_cast<const bf16_t *>(A), lda,
-                                  static_cast<const bf16_t *>(W), ldw, static_cast<bf16_t *>(C),
-                                  ldc, nullptr, M, N, K, epilogue, plan,
-                                  static_cast<float *>(scratch),
-                                  reinterpret_cast<uint32_t *>(static_cast<char *>(scratch) + pb));
         if (e == hipSuccess) e = hipStreamSynchronize(s);
         hipFree(scratch);
-        if (e != hipSuccess)
-            return set_global_error(LAYA_E_DEVICE, std::string("laya_op_gemm: ") + hipGetErrorString(e));
-        return LAYA_OK;
     }
-    OPCHK(laya::launch_gemm(s, static_cast<const bf16_t *>(A), lda,
-                            static_cast<const bf16_t *>(W), ldw, static_cast<bf16_t *>(C), ldc,
-                            nullptr, M, N, K, epilogue, plan, nullptr, nullptr));
+    if (e != hipSuccess)
+        return set_global_error(LAYA_E_DEVICE, std::string(who) + ": " + hipGetErrorString(e));
     return LAYA_OK;
+}
+
+bool gemm_args_ok(const void *A, int32_t lda, const void *W, int32_t ldw, const void *C,
+                  int32_t ldc, int32_t M, int32_t N, int32_t K, int32_t config) {
+    return !(M < 0 || N <= 0 || K <= 0 || K % 64 || N % 64 || lda % 8 || ldw % 8 || ldc % 8 ||
+             lda < K || ldw < K || ldc < N || (M > 0 && (!A || !W || !C)) || config < -1 ||
+             config >= laya::kGemmConfigs);
+}
+}  // namespace
+
+int laya_op_gemm(void *stream, const void *A, int32_t lda, const void *W, int32_t ldw, void *C,
+                 int32_t ldc, int32_t M, int32_t N, int32_t K, int32_t epilogue, int32_t config,
+                 int32_t splits) {
+    if (!gemm_args_ok(A, lda, W, ldw, C, ldc, M, N, K, config) ||
+        (epilogue != 0 && epilogue != 1))
+        return set_global_error(LAYA_E_INVALID, "laya_op_gemm: bad arguments");
+    if (M == 0) return LAYA_OK;
+    return op_gemm_launch("laya_op_gemm", static_cast<hipStream_t>(stream), A, lda, W, ldw, C,
+                          ldc, M, N, K, epilogue, config, splits, nullptr);
+}
+
+int laya_op_gemm_qkv(void *stream, const void *A, int32_t lda, const void *W, int32_t ldw,
+                     void *C, int32_t ldc, int32_t M, int32_t N, int32_t K, const int32_t *pos,
+                     const void *cos_tab, const void *sin_tab, int32_t rope_cols, void *vt,
+                     int32_t ldvt, const int32_t *vt_tok, int32_t vt_col0, int32_t config,
+                     int32_t splits) {
+    if (!gemm_args_ok(A, lda, W, ldw, C, ldc, M, N, K, config) || rope_cols < 0 ||
+        rope_cols % 64 || vt_col0 % 64 || rope_cols > vt_col0 || vt_col0 > N ||
+        (M > 0 && rope_cols > 0 && (!pos || !cos_tab || !sin_tab)) ||
+        (M > 0 && vt_col0 < N && (!vt || !vt_tok || ldvt <= 0)))
+        return set_global_error(LAYA_E_INVALID, "laya_op_gemm_qkv: bad arguments");
+    if (M == 0) return LAYA_OK;
+    const laya::QkvEpilogue qe{pos, static_cast<const bf16_t *>(cos_tab),
+                               static_cast<const bf16_t *>(sin_tab), rope_cols, vt_col0,
+                               static_cast<bf16_t *>(vt), ldvt, vt_tok};
+    return op_gemm_launch("laya_op_gemm_qkv", static_cast<hipStream_t>(stream), A, lda, W, ldw,
+                          C, ldc, M, N, K, 2, config, splits, &qe);
 }
 
 int laya_op_rope(void *stream, void *buf, int32_t ld, int32_t n_heads_rot, int32_t rows,
@@ -1289,22 +1347,30 @@ int laya_op_rope(void *stream, void *buf, int32_t ld, int32_t n_heads_rot, int32
     return LAYA_OK;
 }
 
-int laya_op_attention(void *stream, const void *q, int32_t ldq, const void *k, const void *v,
-                      int32_t ldkv, void *o, int32_t ldo, int32_t n_heads,
-                      const int32_t *row_off, int32_t B, const int32_t *q_tok, int32_t n_q,
-                      int32_t half_window) {
-    if (B < 0 || n_heads <= 0 || ldq % 8 || ldkv % 8 || ldo % 8 || ldq < n_heads * 64 ||
-        ldkv < n_heads * 64 || ldo < n_heads * 64 || !row_off)
+int laya_op_attention(void *stream, const void *q, int32_t ldq, const void *k, int32_t ldk,
+                      const void *vt, int32_t ldvt, const int32_t *vt_col0, void *o, int32_t ldo,
+                      int32_t n_heads, const int32_t *row_off, int32_t B, const int32_t *q_tok,
+                      int32_t n_q, int32_t half_window) {
+    if (B < 0 || n_heads <= 0 || ldq % 8 || ldk % 8 || ldo % 8 || ldvt % 8 ||
+        ldq < n_heads * 64 || ldk < n_heads * 64 || ldo < n_heads * 64 || ldvt <= 0 || !row_off ||
+        (B > 0 && !vt_col0))
         return set_global_error(LAYA_E_INVALID, "laya_op_attention: bad arguments");
     if (row_off[0] != 0)
         return set_global_error(LAYA_E_INVALID, "laya_op_attention: row_off[0] != 0");
-    for (int b = 0; b < B; ++b)
+    for (int b = 0; b < B; ++b) {
         if (row_off[b + 1] <= row_off[b])
             return set_global_error(LAYA_E_INVALID, "laya_op_attention: empty or decreasing row");
+        if (vt_col0[b] < 0 || vt_col0[b] % 8 ||
+            (int64_t)vt_col0[b] + (row_off[b + 1] - row_off[b]) > ldvt)
+            return set_global_error(LAYA_E_INVALID, "laya_op_attention: bad vt_col0");
+    }
     const int T = B ? row_off[B] : 0;
     if (T == 0) return LAYA_OK;
-    if (!q || !k || !v || !o)
+    if (!q || !k || !vt || !o)
         return set_global_error(LAYA_E_INVALID, "laya_op_attention: NULL buffer");
+    if (((int64_t)(T - 1) * ldk + n_heads * 64) * 2 > INT32_MAX ||
+        (int64_t)n_heads * 64 * ldvt * 2 > INT32_MAX)
+        return set_global_error(LAYA_E_UNSUPPORTED, "laya_op_attention: buffers over 2 GiB");
     std::vector<int32_t> qpos;
     std::vector<AttnBlock> blocks;
     int nb = 0;
@@ -1313,7 +1379,7 @@ int laya_op_attention(void *stream, const void *q, int32_t ldq, const void *k, c
         for (int b = 0; b < B; ++b)
             for (int t = row_off[b]; t < row_off[b + 1]; ++t) qpos[t] = t - row_off[b];
         blocks.resize((size_t)B * (512 / laya::kAttnQueries + T / laya::kAttnQueries + 1));
-        build_blocks_full(row_off, B, half_window, blocks.data(), &nb);
+        build_blocks_full(row_off, vt_col0, B, half_window, blocks.data(), &nb);
     } else {
         if (n_q <= 0) return LAYA_OK;
         qpos.resize(n_q);
@@ -1327,7 +1393,8 @@ int laya_op_attention(void *stream, const void *q, int32_t ldq, const void *k, c
             qpos[r] = t - row_off[b];
         }
         blocks.resize(n_q);
-        build_blocks_list(row_off, qrow.data(), qpos.data(), n_q, half_window, blocks.data(), &nb);
+        build_blocks_list(row_off, vt_col0, qrow.data(), qpos.data(), n_q, half_window,
+                          blocks.data(), &nb);
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
     void *dmem = nullptr;
@@ -1337,13 +1404,16 @@ int laya_op_attention(void *stream, const void *q, int32_t ldq, const void *k, c
     if (e == hipSuccess)
         e = hipMemcpyAsync(static_cast<char *>(dmem) + bbytes, qpos.data(), qpos.size() * 4,
                            hipMemcpyHostToDevice, s);
-    if (e == hipSuccess)
-        e = laya::launch_attention(s, static_cast<const bf16_t *>(q), ldq,
-                                   static_cast<const bf16_t *>(k), static_cast<const bf16_t *>(v),
-                                   ldkv, static_cast<bf16_t *>(o), ldo,
-                                   static_cast<const AttnBlock *>(dmem), nullptr, nb,
-                                   reinterpret_cast<const int32_t *>(static_cast<char *>(dmem) + bbytes),
-                                   n_heads, half_window);
+    if (e == hipSuccess) {
+        const laya::AttnParams ap{
+            static_cast<const bf16_t *>(q), ldq, static_cast<const bf16_t *>(k), ldk,
+            (uint32_t)(((int64_t)(T - 1) * ldk + n_heads * 64) * 2),
+            static_cast<const bf16_t *>(vt), ldvt, (uint32_t)((int64_t)n_heads * 64 * ldvt * 2),
+            static_cast<bf16_t *>(o), ldo, static_cast<const AttnBlock *>(dmem), nullptr, nb,
+            reinterpret_cast<const int32_t *>(static_cast<char *>(dmem) + bbytes), n_heads,
+            half_window};
+        e = laya::launch_attention(s, ap);
+    }
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     hipFree(dmem);
     if (e != hipSuccess)

@@ -1,202 +1,236 @@
 // Masked bidirectional attention for packed rows on gfx950 matrix cores,
-// flash style: scores and the running softmax stay on chip, K/V tiles are
-// staged through LDS, and the output is written token-major ([token][head *
-// 64 + d]) so the output projection reads it with no transpose (the strided
-// attention output of "perf(model): exact Metal speed-ups of the forward
-// pass").  A work item (AttnBlock) is up to 64 queries of one batch row; the
-// key-padding mask is the row's length and, on local layers, a query at
-// position p sees key j iff |p - j| <= half_window.  The same kernel serves
-// the marker-row subset: its queries are an arbitrary list of rows of the
-// query buffer, each with its own position, while keys are the whole row
-// (a single query row applies the mask like any other, which the pages' Metal
-// single-query kernel did not).
+// flash style: scores and the running softmax stay on chip, K and V tiles
+// are staged through LDS, and the output is written token-major ([token][head
+// * 64 + d]) so the output projection reads it with no transpose (the
+// strided attention output of "perf(model): exact Metal speed-ups of the
+// forward pass").  A work item (AttnBlock) is up to 64 queries of one batch
+// row; the key-padding mask is the row's length and, on local layers, a query
+// at position p sees key j iff |p - j| <= half_window.  The same kernel
+// serves the marker-row subset: its queries are an arbitrary list of rows of
+// the query buffer, each with its own position, while keys are the whole row
+// (a single query row applies the mask like any other, which the pages'
+// Metal single-query kernel did not).
 //
-// Per workgroup: one block x one head, four waves of 16 queries.  For each
-// 64-key tile: S = Q K^T with MFMA 16x16x32 (queries as rows), scale,
-// mask, online softmax in float32 (max subtracted, exp2 domain), then
-// O += P V with MFMA 16x16x32 reading V from a transposed LDS copy.  The
-// matrix cores take BF16 operands, so the float32 P is split into a BF16 head
-// and a BF16 tail (p = hi + lo to about 16 significant bits) and both halves
-// are multiplied with V: rounding P to BF16 alone would perturb every output
-// by up to 2^-9 relative, a first-order departure from float32 softmax.
+// Layout of the work, per workgroup (one block x one head, 4 waves of 16
+// queries), per 64-key tile:
+//   - S^T = K Q^T with v_mfma_f32_16x16x32_bf16: keys are the MFMA rows and
+//     queries the columns, so each lane ends up with 16 scores of ONE query
+//     (lane l: query l%16, keys 8*(l/16)+0..7 of each 32-key half);
+//   - online softmax in float32, exp2 domain, the row maximum reduced over
+//     the 4 lanes of a query (two xor shuffles); the row sum is kept per lane
+//     and reduced once at the end;
+//   - O^T += V^T P^T: P^T is the MFMA B operand, whose lane layout (query
+//     l%16, 8 consecutive k slots per lane) is exactly the lane's own scores
+//     once the K rows of S^T are fed in the matching order, so P never leaves
+//     the registers.  V^T comes from the transposed V that the QKV GEMM
+//     writes (each row's keys start at a 64-aligned column).
+// The matrix cores take BF16 operands, so the float32 P is split into a BF16
+// head and a BF16 tail (p = hi + lo to about 16 significant bits) and both
+// halves are multiplied with V: rounding P to BF16 alone would perturb every
+// output by up to 2^-9 relative, a first-order departure from float32
+// softmax.
+//
+// K and V^T tiles go HBM -> LDS with buffer loads (no VGPR staging) into two
+// buffers: the next tile's loads are in flight while this tile is computed,
+// with one barrier per tile.
 #include "kernels.h"
 
 namespace laya {
 
 namespace {
 
-constexpr int KT = 64;          // keys per tile
-constexpr int LDK = 64;         // K tile row length (swizzled 16-byte chunks)
-constexpr int LDV = 64 + 8;     // transposed V row length (padded)
-constexpr int LDP = 64 + 8;     // P row length (padded)
+constexpr int KT = 64;                 // keys per tile
+constexpr int TILE_ELEMS = 64 * 64;    // one 64 x 64 BF16 tile
+constexpr int BUF_ELEMS = 2 * TILE_ELEMS;  // K tile, then V^T tile
 
-__device__ __forceinline__ int kswz(int key, int chunk) {
-    return key * LDK + ((chunk ^ ((key >> 1) & 7)) << 3);
+// Physical 16-byte chunk of logical chunk c in row r of a 128-byte-row tile.
+// Two rows share one 256-byte sweep of the 64 banks; the XOR spreads the 16
+// rows that one ds_read_b128 quarter-wave reads over all 16 chunk slots.
+// K tile rows are read 16 at a time as keys {0..3, 8..11, 16..19, 24..27}
+// (+ 4 e + 32 ks), V^T tile rows as 16 consecutive rows.
+__device__ __forceinline__ int kchunk(int r, int c) {
+    return c ^ (((r >> 1) & 1) | ((r >> 2) & 6));
 }
+__device__ __forceinline__ int vchunk(int r, int c) { return c ^ ((r >> 1) & 7); }
 
-__global__ __launch_bounds__(256) void attention_kernel(
-    const bf16_t *__restrict__ q, int32_t ldq, const bf16_t *__restrict__ k,
-    const bf16_t *__restrict__ v, int32_t ldkv, bf16_t *__restrict__ o, int32_t ldo,
-    const AttnBlock *__restrict__ blocks, const int32_t *nblk_dev, int32_t nblk_max,
-    const int32_t *__restrict__ qpos, int32_t half_window) {
-    const int32_t nblk = nblk_dev ? *nblk_dev : nblk_max;
-    const int32_t bi = blockIdx.x;
-    if (bi >= nblk) return;
-    const AttnBlock blk = blocks[bi];
-    const int h = blockIdx.y;
+__global__ __launch_bounds__(256) void attention_kernel(AttnParams p) {
+    const int32_t nblk = p.nblk_dev ? *p.nblk_dev : p.nblk_max;
+    // (block, head) work index: the blocks of one head are consecutive, and
+    // contiguous ranges go to one XCD, so a row's K/V tiles are fetched into
+    // one L2 for all of its blocks.
+    const int u = xcd_contiguous(blockIdx.y * gridDim.x + blockIdx.x, nblk * p.n_heads);
+    if (u < 0) return;
+    const int h = u / nblk;
+    const AttnBlock blk = p.blocks[u - h * nblk];
 
-    __shared__ __attribute__((aligned(16))) bf16_t sK[KT * LDK];
-    __shared__ __attribute__((aligned(16))) bf16_t sVt[64 * LDV];
-    __shared__ __attribute__((aligned(16))) bf16_t sP[4][2][16 * LDP];  // [wave][hi, lo]
+    __shared__ __attribute__((aligned(16))) bf16_t smem[2 * BUF_ELEMS];
 
     const int tid = threadIdx.x;
     const int w = tid >> 6, lane = tid & 63;
     const int g = lane >> 4, c16 = lane & 15;
 
-    // Q fragments: MFMA A rows are queries w*16 + c16 (clamped to a valid row).
-    const int qa = w * 16 + c16;
-    const int32_t qrow_a = blk.q_first + (qa < blk.q_count ? qa : 0);
-    const bf16_t *qp = q + (size_t)qrow_a * ldq + h * 64;
-    const bf16x8_t qf0 = as_bf16x8(ld16(qp + g * 8));
-    const bf16x8_t qf1 = as_bf16x8(ld16(qp + 32 + g * 8));
+    // This lane's query (MFMA column c16 of wave w), clamped to a valid row.
+    const int qi = w * 16 + c16;
+    const bool qvalid = qi < blk.q_count;
+    const int32_t qrow = blk.q_first + (qvalid ? qi : 0);
+    const bf16_t *qp = p.q + (size_t)qrow * p.ldq + h * 64;
+    const bf16x8_t qb0 = as_bf16x8(ld16(qp + 8 * g));       // dims 8g..8g+7
+    const bf16x8_t qb1 = as_bf16x8(ld16(qp + 32 + 8 * g));  // dims 32+8g..
+    const int32_t my_pos = p.qpos[qrow];
 
-    // Accumulator rows held by this lane: queries w*16 + g*4 + i.
-    int32_t qp_r[4];
-    bool qv_r[4];
+    // DMA sources.  Each wave loads 1 KB blocks jj = w and w + 4 of each tile
+    // (rows 8 jj .. 8 jj + 7); lane L fills physical chunk L % 8 of row
+    // 8 jj + L / 8 with the logical chunk the swizzle puts there.
+    const int dr = lane >> 3, dpc = lane & 7;
+    uint32_t koff[2], voff[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int qi = w * 16 + g * 4 + i;
-        qv_r[i] = qi < blk.q_count;
-        qp_r[i] = qpos[blk.q_first + (qv_r[i] ? qi : 0)];
+    for (int it = 0; it < 2; ++it) {
+        const int r = 8 * (w + 4 * it) + dr;
+        koff[it] = (uint32_t)(((blk.kt0 + r) * p.ldk + h * 64 + kchunk(r, dpc) * 8) * 2);
+        voff[it] = (uint32_t)(((h * 64 + r) * p.ldvt + blk.vcol0 + vchunk(r, dpc) * 8) * 2);
     }
+    const int w_u = __builtin_amdgcn_readfirstlane(w);
+    auto issue = [&](int32_t kb, int buf) {
+        bf16_t *base = smem + buf * BUF_ELEMS;
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+            const int jj = w_u + 4 * it;
+            // the tile offset goes into the per-lane offset, which is what the
+            // buffer's range check covers
+            dma16(p.k, p.k_bytes, (lds_ptr_t)(base + jj * 512),
+                  koff[it] + (uint32_t)(kb * p.ldk * 2), 0);
+            dma16(p.vt, p.vt_bytes, (lds_ptr_t)(base + TILE_ELEMS + jj * 512),
+                  voff[it] + (uint32_t)(kb * 2), 0);
+        }
+    };
 
     const float sl2 = 0.125f * 1.44269504088896341f;  // 1/sqrt(64) * log2(e)
-    float m[4], l[4];
+    float m = -INFINITY, lsum = 0.f;
     f32x4_t oacc[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        m[i] = -INFINITY;
-        l[i] = 0.f;
-    }
 #pragma unroll
     for (int d = 0; d < 4; ++d) oacc[d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    const bf16_t *kbase = k + (size_t)blk.kt0 * ldkv + h * 64;
-    const bf16_t *vbase = v + (size_t)blk.kt0 * ldkv + h * 64;
+    int buf = 0;
+    if (blk.k_lo < blk.k_hi) issue(blk.k_lo, 0);
+    for (int32_t kb = blk.k_lo; kb < blk.k_hi; kb += KT, buf ^= 1) {
+        wait_vmcnt<0>();  // this wave's loads of the tile (and the Q loads)
+        ring_barrier();   // every wave's loads landed; the other buffer is free
+        if (kb + KT < blk.k_hi) issue(kb + KT, buf ^ 1);
+        const bf16_t *sK = smem + buf * BUF_ELEMS;
+        const bf16_t *sV = sK + TILE_ELEMS;
 
-    for (int32_t kb = blk.k_lo; kb < blk.k_hi; kb += KT) {
-        __syncthreads();  // the previous tile's readers are done
-#pragma unroll
-        for (int it = 0; it < 2; ++it) {
-            const int idx = tid + 256 * it;
-            const int key = idx >> 3, ch = idx & 7;
-            const int32_t kj = kb + key;
-            u32x4_t kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
-            if (kj < blk.k_hi) {
-                kv = ld16(kbase + (size_t)kj * ldkv + ch * 8);
-                vv = ld16(vbase + (size_t)kj * ldkv + ch * 8);
-            }
-            *reinterpret_cast<u32x4_t *>(&sK[kswz(key, ch)]) = kv;
-#pragma unroll
-            for (int qd = 0; qd < 4; ++qd) {
-                sVt[(ch * 8 + 2 * qd) * LDV + key] = (bf16_t)(vv[qd] & 0xffffu);
-                sVt[(ch * 8 + 2 * qd + 1) * LDV + key] = (bf16_t)(vv[qd] >> 16);
-            }
-        }
-        __syncthreads();
-
-        // S = Q K^T: four 16-key blocks, each two MFMAs over d = 0..31, 32..63.
+        // S^T: block b = 2 ks + e covers keys 32 ks + 8 (m/4) + 4 e + m%4 for
+        // MFMA row m, so output row 4g + i of block b is key 32 ks + 8 g + 4 e + i.
         f32x4_t s[4];
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            const int key = b * 16 + c16;
-            const bf16x8_t k0 = *reinterpret_cast<const bf16x8_t *>(&sK[kswz(key, g)]);
-            const bf16x8_t k1 = *reinterpret_cast<const bf16x8_t *>(&sK[kswz(key, 4 + g)]);
+            const int r = 32 * (b >> 1) + 8 * (c16 >> 2) + 4 * (b & 1) + (c16 & 3);
+            const bf16x8_t k0 =
+                *reinterpret_cast<const bf16x8_t *>(&sK[r * 64 + kchunk(r, g) * 8]);
+            const bf16x8_t k1 =
+                *reinterpret_cast<const bf16x8_t *>(&sK[r * 64 + kchunk(r, 4 + g) * 8]);
             f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-            z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf0, k0, z, 0, 0, 0);
-            s[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf1, k1, z, 0, 0, 0);
+            z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qb0, z, 0, 0, 0);
+            s[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qb1, z, 0, 0, 0);
         }
 
-        // Mask + scale; lane holds S[query g*4+i][key b*16 + c16].
-        float mx[4];
+        // scale + mask; s[b][i] is key kb + 32 (b/2) + 8 g + 4 (b%2) + i
+        float mx = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            mx[i] = -INFINITY;
+        for (int b = 0; b < 4; ++b)
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const int32_t kj = kb + b * 16 + c16;
-                const int32_t dpos = qp_r[i] - kj;
+            for (int i = 0; i < 4; ++i) {
+                const int32_t kj = kb + 32 * (b >> 1) + 8 * g + 4 * (b & 1) + i;
+                const int32_t dpos = my_pos - kj;
                 const bool ok = (kj < blk.k_hi) &&
-                                (half_window < 0 || (dpos <= half_window && -dpos <= half_window));
+                                (p.half_window < 0 ||
+                                 (dpos <= p.half_window && -dpos <= p.half_window));
                 const float t = ok ? s[b][i] * sl2 : -INFINITY;
                 s[b][i] = t;
-                mx[i] = fmaxf(mx[i], t);
+                mx = fmaxf(mx, t);
             }
-            mx[i] = group16_max(mx[i]);
-        }
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float mnew = fmaxf(m, mx);
+        const float alpha = (mnew == -INFINITY) ? 1.f : exp2f(m - mnew);
+        m = mnew;
 
-        bf16_t *pw = sP[w][0];
-        bf16_t *pwl = sP[w][1];
+        // P = exp2(s - m), split into BF16 hi + lo, packed as the B operand
+        // of each 32-key half: slot 4 e + i <- block 2 ks + e, element i.
+        u32x4_t ph[2], pl[2];
+        float rs = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float mnew = fmaxf(m[i], mx[i]);
-            const float alpha = (mnew == -INFINITY) ? 1.f : exp2f(m[i] - mnew);
-            float rs = 0.f;
+        for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const float t = s[b][i];
-                const float p = (t == -INFINITY) ? 0.f : exp2f(t - mnew);
-                const uint32_t ph = f32_to_bf16(p);
-                const uint32_t pl = f32_to_bf16(p - bf16_to_f32(ph));  // p - hi is exact
-                rs += p;
-                pw[(g * 4 + i) * LDP + b * 16 + c16] = (bf16_t)ph;
-                pwl[(g * 4 + i) * LDP + b * 16 + c16] = (bf16_t)pl;
+            for (int qd = 0; qd < 4; ++qd) {
+                uint32_t hw[2], lw[2];
+#pragma unroll
+                for (int hl = 0; hl < 2; ++hl) {
+                    const int slot = 2 * qd + hl;
+                    const float t = s[2 * ks + (slot >> 2)][slot & 3];
+                    const float pv = (t == -INFINITY) ? 0.f : exp2f(t - mnew);
+                    rs += pv;
+                    hw[hl] = f32_to_bf16(pv);
+                    lw[hl] = f32_to_bf16(pv - bf16_to_f32(hw[hl]));  // pv - hi is exact
+                }
+                ph[ks][qd] = hw[0] | (hw[1] << 16);
+                pl[ks][qd] = lw[0] | (lw[1] << 16);
             }
-            l[i] = l[i] * alpha + group16_sum(rs);
-            m[i] = mnew;
+        lsum = lsum * alpha + rs;
 #pragma unroll
-            for (int d = 0; d < 4; ++d) oacc[d][i] *= alpha;
-        }
-        __syncthreads();  // P visible to the whole wave (and V tile still valid)
+        for (int d = 0; d < 4; ++d) oacc[d] *= alpha;
 
-        // O += (P_hi + P_lo) V: A = P [16 queries][keys], B = V [keys][d] from V^T.
+        // Keys past the row's end may hold anything (other rows, stale
+        // memory): their P is 0, and their V is zeroed so 0 * V stays 0.
+        u32x4_t vmask[2];
+        const bool tail = kb + KT > blk.k_hi;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const bf16x8_t pa =
-                *reinterpret_cast<const bf16x8_t *>(&pw[c16 * LDP + ks * 32 + g * 8]);
-            const bf16x8_t pal =
-                *reinterpret_cast<const bf16x8_t *>(&pwl[c16 * LDP + ks * 32 + g * 8]);
+        for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                const bf16x8_t vb = *reinterpret_cast<const bf16x8_t *>(
-                    &sVt[(d * 16 + c16) * LDV + ks * 32 + g * 8]);
-                oacc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, oacc[d], 0, 0, 0);
-                oacc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pal, vb, oacc[d], 0, 0, 0);
+            for (int qd = 0; qd < 4; ++qd) {
+                const int32_t k0 = kb + 32 * ks + 8 * g + 2 * qd;
+                vmask[ks][qd] = (!tail || k0 + 1 < blk.k_hi) ? 0xffffffffu
+                                : (k0 < blk.k_hi)             ? 0x0000ffffu
+                                                              : 0u;
             }
-        }
+
+        // O^T[d][q] += V^T[d][keys] P^T[keys][q]; V^T row 16 dblk + c16,
+        // keys 32 ks + 8 g .. + 7 (logical chunk 4 ks + g).
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int dblk = 0; dblk < 4; ++dblk) {
+                const int r = 16 * dblk + c16;
+                u32x4_t va = *reinterpret_cast<const u32x4_t *>(
+                    &sV[r * 64 + vchunk(r, 4 * ks + g) * 8]);
+                va &= vmask[ks];
+                const bf16x8_t vb = as_bf16x8(va);
+                oacc[dblk] =
+                    __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, as_bf16x8(ph[ks]), oacc[dblk], 0, 0, 0);
+                oacc[dblk] =
+                    __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, as_bf16x8(pl[ks]), oacc[dblk], 0, 0, 0);
+            }
     }
 
-    // O / l, stored as BF16 at [q row][h*64 + d]; lane holds O[query g*4+i][d*16 + c16].
+    // row sum over the query's 4 lanes; O / l stored as BF16 at
+    // [q row][h*64 + 16 dblk + 4 g + i]
+    lsum += __shfl_xor(lsum, 16, 64);
+    lsum += __shfl_xor(lsum, 32, 64);
+    if (!qvalid) return;
+    bf16_t *op = p.o + (size_t)qrow * p.ldo + h * 64 + 4 * g;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        if (!qv_r[i]) continue;
-        const int32_t orow = blk.q_first + w * 16 + g * 4 + i;
-        bf16_t *op = o + (size_t)orow * ldo + h * 64;
-#pragma unroll
-        for (int d = 0; d < 4; ++d) op[d * 16 + c16] = (bf16_t)f32_to_bf16(oacc[d][i] / l[i]);
+    for (int dblk = 0; dblk < 4; ++dblk) {
+        const f32x4_t v = oacc[dblk];
+        *reinterpret_cast<u32x2_t *>(op + 16 * dblk) =
+            u32x2_t{pack_bf16x2(v[0] / lsum, v[1] / lsum), pack_bf16x2(v[2] / lsum, v[3] / lsum)};
     }
 }
 
 }  // namespace
 
-hipError_t launch_attention(hipStream_t s, const bf16_t *q, int32_t ldq, const bf16_t *k,
-                            const bf16_t *v, int32_t ldkv, bf16_t *o, int32_t ldo,
-                            const AttnBlock *blocks, const int32_t *nblk_dev,
-                            int32_t nblk_max, const int32_t *qpos, int32_t n_heads,
-                            int32_t half_window) {
-    if (nblk_max <= 0) return hipSuccess;
-    hipLaunchKernelGGL(attention_kernel, dim3(nblk_max, n_heads), dim3(256), 0, s, q, ldq, k, v,
-                       ldkv, o, ldo, blocks, nblk_dev, nblk_max, qpos, half_window);
+hipError_t launch_attention(hipStream_t s, const AttnParams &p) {
+    if (p.nblk_max <= 0) return hipSuccess;
+    hipLaunchKernelGGL(attention_kernel, dim3(p.nblk_max, p.n_heads), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 

@@ -46,43 +46,6 @@ namespace {
 
 constexpr int KMULT = 64;  // K and every split piece are multiples of 64
 
-typedef __attribute__((address_space(3))) void *lds_ptr_t;
-
-// Last word of a buffer resource on CDNA: raw byte addressing (stride 0),
-// 32-bit data format, no swizzle.
-constexpr int kBufferWord3 = 0x00020000;
-
-// 16 bytes per lane from base + voff + soff into LDS (the wave's 1 KB block
-// at dst), through a buffer resource of `bytes` bytes: the hardware drops
-// accesses past its end.
-__device__ __forceinline__ void dma16(const void *base, uint32_t bytes, lds_ptr_t dst,
-                                      uint32_t voff, uint32_t soff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
-                                          kBufferWord3),
-        dst, 16, voff, soff, 0, 0);
-}
-
-// s_waitcnt on vmcnt only (expcnt and lgkmcnt left at their maxima).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | (((N >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-// Workgroup barrier for the load ring.  __syncthreads() also waits for every
-// outstanding global load (its release fence counts the in-flight DMA loads
-// of later stages), which would drain the whole ring at each step; here each
-// wave has already waited (vmcnt) for the loads of the stage it publishes,
-// and LDS reads are complete once their MFMAs have consumed them, so a bare
-// s_barrier suffices.  The empty asm statements keep the compiler from
-// moving LDS accesses across it.
-__device__ __forceinline__ void ring_barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
 // Physical 16-byte chunk of logical chunk `c` in stage row `r` (rows of BK
 // bf16): XOR with the row's index among the rows that share one 256-byte
 // sweep of the banks, so 16 consecutive rows at one logical chunk are spread
@@ -114,12 +77,8 @@ __device__ __forceinline__ float gelu_erf(float z) {
 // one XCD share a few activation panels and a few weight panels.
 __device__ __forceinline__ bool tile_order(int live_by, int &bx, int &by) {
     const int nbx = gridDim.x;
-    const int live = nbx * live_by;
-    const int d = by * nbx + bx;  // dispatch index
-    if (d >= live) return false;
-    const int x = d & 7, j = d >> 3;
-    const int q = live >> 3, r = live & 7;
-    const int b = x * q + min(x, r) + j;  // position in XCD x's contiguous range
+    const int b = xcd_contiguous(by * nbx + bx, nbx * live_by);
+    if (b < 0) return false;
     constexpr int GT = 4;
     const int group = b / (GT * nbx);
     const int first = group * GT;
@@ -161,13 +120,15 @@ struct GemmParams {
     int32_t splits;
     float *partial;     // [tiles][splits][BW*BT] (splits > 1)
     uint32_t *counter;  // [tiles] (splits > 1), zero between launches
+    QkvEpilogue qe;     // epilogue 2 only
 };
 
 template <class G, int EPI, bool SPLITK>
 __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
     constexpr int BW = G::BW, BT = G::BT, FA = G::FA, FB = G::FB, STAGES = G::STAGES;
     constexpr int BK = G::BK, CH = G::CH, RPL = G::RPL;
-    static_assert(EPI == 0 || FA % 2 == 0, "GeGLU needs matching u/g fragments");
+    static_assert(EPI == 0 || FA % 2 == 0, "GeGLU / QKV need paired fragments");
+    static_assert(EPI != 2 || G::RW % 64 == 0, "QKV epilogue: a wave's rows are whole heads");
     const int32_t M = p.M_dev ? *p.M_dev : p.M_max;
     int bx = blockIdx.x, by = blockIdx.y;
     if (!SPLITK) {
@@ -175,7 +136,7 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
     }
     const int32_t t0 = by * BT;
     if (t0 >= M) return;
-    constexpr int BN = EPI ? BW / 2 : BW;  // output features per tile
+    constexpr int BN = EPI == 1 ? BW / 2 : BW;  // output features per tile
     const int32_t n0 = bx * BN;
     const int split = blockIdx.z;
     const int N = p.N;
@@ -206,7 +167,7 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
     // counts a global load into LDS as an LDS access too, which would force
     // every wait on the fragment reads to lgkmcnt(0).)
     const int rr = lane / CH, pc = lane % CH;
-    const uint32_t w_rows = EPI ? 2u * (uint32_t)N : (uint32_t)N;
+    const uint32_t w_rows = EPI == 1 ? 2u * (uint32_t)N : (uint32_t)N;
     const uint32_t w_bytes = ((w_rows - 1) * (uint32_t)p.ldw + (uint32_t)p.K) * 2u;
     const uint32_t a_bytes = (((uint32_t)p.M_max - 1) * (uint32_t)p.lda + (uint32_t)p.K) * 2u;
     uint32_t off[G::LOADS];
@@ -217,7 +178,7 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
         const int c = pchunk<BK>(r, pc);  // logical chunk stored at physical chunk pc
         if (j < G::WLOADS) {
             int grow;
-            if (EPI) {
+            if (EPI == 1) {
                 const int half = BW / 2;
                 int f = n0 + (r % half);
                 if (f >= N) f = N - 1;  // clamp: rows past N are computed, never stored
@@ -258,7 +219,7 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
     int wrow[FA];
 #pragma unroll
     for (int a = 0; a < FA; ++a) {
-        if (EPI)
+        if (EPI == 1)
             wrow[a] = (a < FA / 2) ? (wr * (G::RW / 2) + 32 * a)
                                    : (BW / 2 + wr * (G::RW / 2) + 32 * (a - FA / 2));
         else
@@ -304,7 +265,7 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
         wait_vmcnt<(STAGES - 1) * G::LOADS>();
     else
         wait_vmcnt<0>();
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): no scalar loads left in flight, so
+    wait_lgkmcnt<0>();  // no scalar loads left in flight, so
                                          // the loop's LDS reads can be waited on in order
     ring_barrier();
     if (nk > 0) read_frags(0, 0, 0);
@@ -321,7 +282,7 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
                     wait_vmcnt<(STAGES - 2) * G::LOADS>();
                 else
                     wait_vmcnt<0>();
-                __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this stage fully read
+                wait_lgkmcnt<0>();  // this stage fully read
                 ring_barrier();
                 if (i + STAGES < nk) issue(i + STAGES, stage);
                 // next stage's first fragments (after the last stage: an unused
@@ -331,7 +292,7 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
             }
             // the fragments of step s are complete once at most the reads of
             // step s+1 remain in flight
-            __builtin_amdgcn_s_waitcnt(0xC07F | ((G::FA + G::FB) << 8));
+            wait_lgkmcnt<G::FA + G::FB>();
             __builtin_amdgcn_sched_barrier(0);
             mfmas(s & 1);
             __builtin_amdgcn_sched_barrier(0);
@@ -397,12 +358,13 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
 
     // Epilogue.  Accumulator element e of lane l in a 32x32 block holds
     // row (weight row) 8*(e/4) + 4*(l/32) + e%4 and column (token) l%32.
+    auto bf16r = [](float v) { return bf16_to_f32(f32_to_bf16(v)); };
 #pragma unroll
     for (int b = 0; b < FB; ++b) {
         const int32_t tok = t0 + wc * G::RT + 32 * b + l32;
         if (tok >= M) continue;
         bf16_t *crow = p.C + (size_t)tok * p.ldc;
-        if (EPI) {
+        if constexpr (EPI == 1) {
 #pragma unroll
             for (int a = 0; a < FA / 2; ++a)
 #pragma unroll
@@ -416,6 +378,61 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
                     u32x2_t pk = {pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
                     *reinterpret_cast<u32x2_t *>(crow + f) = pk;
                 }
+        } else if constexpr (EPI == 2) {
+            // Fragments a (dims 0..31 of a head) and a+1 (dims 32..63) sit in
+            // the same lanes, so the rotation pairs (i, i+32) are in registers.
+            const QkvEpilogue &q = p.qe;
+#pragma unroll
+            for (int a = 0; a < FA; a += 2) {
+                const int32_t f0 = n0 + wrow[a];  // first column of the head
+                if (f0 >= N) continue;
+                if (f0 < q.rope_cols) {
+                    const uint32_t ps = (uint32_t)q.pos[tok] * 32u;
+#pragma unroll
+                    for (int g4 = 0; g4 < 4; ++g4) {
+                        const int j = 8 * g4 + 4 * lhi;  // pair index of element 4*g4
+                        const u32x2_t cv = *reinterpret_cast<const u32x2_t *>(q.cos_tab + ps + j);
+                        const u32x2_t sv = *reinterpret_cast<const u32x2_t *>(q.sin_tab + ps + j);
+                        float xo[4], yo[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float x = bf16r(acc[a][b][4 * g4 + e]);
+                            const float y = bf16r(acc[a + 1][b][4 * g4 + e]);
+                            const float c = (e & 1) ? bf16hi(cv[e >> 1]) : bf16lo(cv[e >> 1]);
+                            const float sn = (e & 1) ? bf16hi(sv[e >> 1]) : bf16lo(sv[e >> 1]);
+                            // both products of BF16 values are exact in float32
+                            xo[e] = fmaf(x, c, -(y * sn));
+                            yo[e] = fmaf(y, c, x * sn);
+                        }
+                        *reinterpret_cast<u32x2_t *>(crow + f0 + j) =
+                            u32x2_t{pack_bf16x2(xo[0], xo[1]), pack_bf16x2(xo[2], xo[3])};
+                        *reinterpret_cast<u32x2_t *>(crow + f0 + 32 + j) =
+                            u32x2_t{pack_bf16x2(yo[0], yo[1]), pack_bf16x2(yo[2], yo[3])};
+                    }
+                } else if (f0 >= q.vt_col0) {
+                    // transposed: column f - vt_col0 of vt holds this token at vt_tok[tok]
+                    bf16_t *vcol = q.vt + q.vt_tok[tok];
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) {
+                            const int32_t f = f0 + 32 * h2 + 8 * (e / 4) + 4 * lhi + e % 4;
+                            vcol[(size_t)(f - q.vt_col0) * q.ldvt] =
+                                (bf16_t)f32_to_bf16(acc[a + h2][b][e]);
+                        }
+                } else {
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                        for (int g4 = 0; g4 < 4; ++g4) {
+                            const int32_t f = f0 + 32 * h2 + 8 * g4 + 4 * lhi;
+                            const f32x16_t &v = acc[a + h2][b];
+                            *reinterpret_cast<u32x2_t *>(crow + f) =
+                                u32x2_t{pack_bf16x2(v[4 * g4], v[4 * g4 + 1]),
+                                        pack_bf16x2(v[4 * g4 + 2], v[4 * g4 + 3])};
+                        }
+                }
+            }
         } else {
 #pragma unroll
             for (int a = 0; a < FA; ++a)
@@ -449,15 +466,17 @@ constexpr CfgInfo kCfgs[kGemmConfigs] = {{CfgXS::BW, CfgXS::BT}, {CfgXSG::BW, Cf
 
 template <class G, bool SPLITK>
 hipError_t launch_cfg(hipStream_t s, const GemmParams &p, int epilogue) {
-    const int bn = epilogue ? G::BW / 2 : G::BW;
+    const int bn = epilogue == 1 ? G::BW / 2 : G::BW;
     const dim3 grid((p.N + bn - 1) / bn, (p.M_max + G::BT - 1) / G::BT, p.splits);
-    if (epilogue) {
-        if constexpr (G::FA % 2 == 0)
+    if (epilogue == 0) {
+        hipLaunchKernelGGL((gemm_kernel<G, 0, SPLITK>), grid, dim3(G::NTHR), 0, s, p);
+    } else if constexpr (G::FA % 2 == 0 && G::RW % 64 == 0) {
+        if (epilogue == 1)
             hipLaunchKernelGGL((gemm_kernel<G, 1, SPLITK>), grid, dim3(G::NTHR), 0, s, p);
         else
-            return hipErrorInvalidValue;
+            hipLaunchKernelGGL((gemm_kernel<G, 2, SPLITK>), grid, dim3(G::NTHR), 0, s, p);
     } else {
-        hipLaunchKernelGGL((gemm_kernel<G, 0, SPLITK>), grid, dim3(G::NTHR), 0, s, p);
+        return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
@@ -481,7 +500,7 @@ GemmPlan plan_gemm_tiles(int32_t M, int32_t N, int32_t K, int epilogue) {
     // Tile shape with the least estimated time: whole waves of workgroups
     // over the 256 compute units times the per-tile cost, with the relative
     // per-CU throughput of each shape.
-    const int64_t nw = epilogue ? 2LL * N : N;
+    const int64_t nw = epilogue == 1 ? 2LL * N : N;
     const int cand[4] = {2, 3, 4, 5};
     const double eff[4] = {0.45, 0.70, 0.85, 1.0};
     GemmPlan g{3, 1};
@@ -501,7 +520,7 @@ GemmPlan plan_gemm_tiles(int32_t M, int32_t N, int32_t K, int epilogue) {
 }
 
 GemmPlan plan_gemm(int32_t M_max, int32_t N, int32_t K, int epilogue) {
-    const int64_t nw = epilogue ? 2LL * N : N;  // weight rows read
+    const int64_t nw = epilogue == 1 ? 2LL * N : N;  // weight rows read
     const int np = K / KMULT;                   // 64-wide K pieces
     GemmPlan g{};
     if (M_max <= 64) {
@@ -527,7 +546,7 @@ GemmPlan plan_gemm(int32_t M_max, int32_t N, int32_t K, int epilogue) {
 size_t gemm_workspace_bytes(const GemmPlan &g, int32_t M_max, int32_t N, int epilogue) {
     if (g.splits <= 1) return 0;
     const CfgInfo &c = kCfgs[g.config];
-    const int bn = epilogue ? c.bw / 2 : c.bw;
+    const int bn = epilogue == 1 ? c.bw / 2 : c.bw;
     const size_t tiles = (size_t)((N + bn - 1) / bn) * ((M_max + c.bt - 1) / c.bt);
     return tiles * g.splits * c.bw * c.bt * 4;
 }
@@ -535,20 +554,25 @@ size_t gemm_workspace_bytes(const GemmPlan &g, int32_t M_max, int32_t N, int epi
 size_t gemm_counter_count(const GemmPlan &g, int32_t M_max, int32_t N, int epilogue) {
     if (g.splits <= 1) return 0;
     const CfgInfo &c = kCfgs[g.config];
-    const int bn = epilogue ? c.bw / 2 : c.bw;
+    const int bn = epilogue == 1 ? c.bw / 2 : c.bw;
     return (size_t)((N + bn - 1) / bn) * ((M_max + c.bt - 1) / c.bt);
 }
 
 hipError_t launch_gemm(hipStream_t s, const bf16_t *A, int32_t lda, const bf16_t *W,
                        int32_t ldw, bf16_t *C, int32_t ldc, const int32_t *M_dev,
                        int32_t M_max, int32_t N, int32_t K, int epilogue, const GemmPlan &plan,
-                       float *partial, uint32_t *counter) {
+                       float *partial, uint32_t *counter, const QkvEpilogue *qe) {
     if (M_max <= 0 || N <= 0) return hipSuccess;
+    if (epilogue == 2 && (!qe || qe->rope_cols % 64 || qe->vt_col0 % 64 ||
+                          qe->rope_cols > qe->vt_col0 || (qe->rope_cols > 0 && !qe->pos) ||
+                          (qe->vt_col0 < N && (!qe->vt || !qe->vt_tok))))
+        return hipErrorInvalidValue;
     if (K % KMULT != 0 || N % 64 != 0 || plan.config < 0 || plan.config >= kGemmConfigs ||
         plan.splits < 1 || plan.splits > K / KMULT || plan.splits > gemm_max_splits(plan.config))
         return hipErrorInvalidValue;
     if (plan.splits > 1 && (!partial || !counter)) return hipErrorInvalidValue;
-    GemmParams p{A, lda, W, ldw, C, ldc, M_dev, M_max, N, K, plan.splits, partial, counter};
+    GemmParams p{A, lda, W, ldw, C, ldc, M_dev, M_max, N, K, plan.splits, partial, counter,
+                 epilogue == 2 ? *qe : QkvEpilogue{}};
     switch (plan.config) {
         case 0: return launch_small<CfgXS>(s, p, epilogue);
         case 1: return launch_small<CfgXSG>(s, p, epilogue);

@@ -13,11 +13,12 @@ namespace laya {
 
 // Attention work item: up to 64 queries of one batch row, one head per
 // workgroup.  Keys of the row are tokens kt0 .. kt0+klen-1 (positions
-// 0..klen-1); the block only visits key positions [k_lo, k_hi).  Queries are
-// rows q_first .. q_first+q_count-1 of the query/output buffers, with
-// positions qpos[q_first + i].
+// 0..klen-1) of the K buffer and columns vcol0 .. vcol0+klen-1 of the
+// transposed V; the block only visits key positions [k_lo, k_hi), k_lo a
+// multiple of 64.  Queries are rows q_first .. q_first+q_count-1 of the
+// query/output buffers, with positions qpos[q_first + i].
 struct AttnBlock {
-    int32_t kt0, klen, k_lo, k_hi, q_first, q_count, pad0, pad1;
+    int32_t kt0, klen, k_lo, k_hi, q_first, q_count, vcol0, pad;
 };
 static_assert(sizeof(AttnBlock) == 32, "AttnBlock is 8 int32");
 
@@ -58,21 +59,55 @@ int gemm_max_splits(int config);
 size_t gemm_workspace_bytes(const GemmPlan &g, int32_t M_max, int32_t N, int epilogue);
 size_t gemm_counter_count(const GemmPlan &g, int32_t M_max, int32_t N, int epilogue);
 
-// C = bf16(A W^T), epilogue 0 plain, 1 GeGLU (W has 2N rows).  With
-// plan.splits > 1, `partial` and `counter` (zero-filled once) are required.
+// Epilogue 2 (QKV projection): output columns [0, rope_cols) are heads of
+// 64 that are rotated (RoPE, rotate-half pairs (i, i+32), c/s = tab[pos][i])
+// after rounding to BF16, exactly as the standalone RoPE kernel does;
+// columns [vt_col0, N) are stored transposed, column f of token t at
+// vt[(f - vt_col0) * ldvt + vt_tok[t]]; columns in between are stored plain.
+// rope_cols and vt_col0 are multiples of 64.
+struct QkvEpilogue {
+    const int32_t *pos;               // position of each output row (token)
+    const bf16_t *cos_tab, *sin_tab;  // [positions][32]
+    int32_t rope_cols;
+    int32_t vt_col0;
+    bf16_t *vt;
+    int32_t ldvt;
+    const int32_t *vt_tok;  // vt column of each output row
+};
+
+// C = bf16(A W^T), epilogue 0 plain, 1 GeGLU (W has 2N rows), 2 QKV (`qe`).
+// With plan.splits > 1, `partial` and `counter` (zero-filled once) are required.
 hipError_t launch_gemm(hipStream_t s, const bf16_t *A, int32_t lda, const bf16_t *W,
                        int32_t ldw, bf16_t *C, int32_t ldc, const int32_t *M_dev,
                        int32_t M_max, int32_t N, int32_t K, int epilogue, const GemmPlan &plan,
-                       float *partial, uint32_t *counter);
+                       float *partial, uint32_t *counter, const QkvEpilogue *qe = nullptr);
 
 hipError_t launch_rope(hipStream_t s, bf16_t *buf, int32_t ld, int32_t n_heads_rot,
                        const int32_t *count_dev, int32_t rows_max, const int32_t *pos,
                        const bf16_t *cos_tab, const bf16_t *sin_tab);
 
-hipError_t launch_attention(hipStream_t s, const bf16_t *q, int32_t ldq, const bf16_t *k,
-                            const bf16_t *v, int32_t ldkv, bf16_t *o, int32_t ldo,
-                            const AttnBlock *blocks, const int32_t *nblk_dev,
-                            int32_t nblk_max, const int32_t *qpos, int32_t n_heads,
-                            int32_t half_window);
+// Attention over packed rows.  q [rows][ldq] (head h at columns h*64..),
+// k [rows][ldk] likewise, vt [n_heads*64][ldvt] (row h*64+d holds dimension
+// d of head h for every key column), o [rows][ldo].  k_bytes / vt_bytes
+// bound what the kernel may read from k / vt (reads past them give zero).
+struct AttnParams {
+    const bf16_t *q;
+    int32_t ldq;
+    const bf16_t *k;
+    int32_t ldk;
+    uint32_t k_bytes;
+    const bf16_t *vt;
+    int32_t ldvt;
+    uint32_t vt_bytes;
+    bf16_t *o;
+    int32_t ldo;
+    const AttnBlock *blocks;
+    const int32_t *nblk_dev;
+    int32_t nblk_max;
+    const int32_t *qpos;
+    int32_t n_heads;
+    int32_t half_window;  // -1: global
+};
+hipError_t launch_attention(hipStream_t s, const AttnParams &p);
 
 }  // namespace laya
