@@ -340,8 +340,10 @@ int laya_op_gemm_qkv(void *stream, const void *A, int32_t lda, const void *W, in
  * otherwise q row r is the query of token q_tok[r] (host int32 [n_q],
  * grouped so that queries of one row are consecutive).  Query of token t in
  * row b at position p sees key j of the same row iff half_window < 0 or
- * |p - j| <= half_window; scores (q . k) / 8 in float32, softmax in float32,
- * o = sum p v stored as BF16 at o row r (device BF16, row stride ldo).
+ * |p - j| <= half_window; scores (q . k) / 8 in float32, softmax in float32
+ * (the weights enter the products with v as a BF16 head plus a BF16 tail,
+ * numerator and denominator alike), o = sum p v / sum p stored as BF16 at
+ * o row r (device BF16, row stride ldo).
  * row_off host int32 [B + 1].  Index metadata is built on the host and
  * uploaded into a buffer this call allocates and frees (diagnostic entry;
  * synchronises the stream). */

@@ -26,6 +26,14 @@ LAYA_DEV uint32_t f32_to_bf16(float f) {
     return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Two float32 -> packed BF16 with the hardware conversion (round to nearest
+// even; v_cvt_pk_bf16_f32 on gfx950).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+LAYA_DEV uint32_t cvt_pk_bf16(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+}
+
 LAYA_DEV uint32_t pack_bf16x2(float lo, float hi) {
     return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
 }

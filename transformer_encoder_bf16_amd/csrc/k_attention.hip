@@ -17,18 +17,20 @@
 //     queries the columns, so each lane ends up with 16 scores of ONE query
 //     (lane l: query l%16, keys 8*(l/16)+0..7 of each 32-key half);
 //   - online softmax in float32, exp2 domain, the row maximum reduced over
-//     the 4 lanes of a query (two xor shuffles); the row sum is kept per lane
-//     and reduced once at the end;
+//     the 4 lanes of a query (two xor shuffles); tiles inside every window
+//     of the wave skip the mask;
 //   - O^T += V^T P^T: P^T is the MFMA B operand, whose lane layout (query
 //     l%16, 8 consecutive k slots per lane) is exactly the lane's own scores
 //     once the K rows of S^T are fed in the matching order, so P never leaves
 //     the registers.  V^T comes from the transposed V that the QKV GEMM
-//     writes (each row's keys start at a 64-aligned column).
+//     writes (each row's keys start at a 64-aligned column).  The row sum is
+//     the same product with an all-ones A operand.
 // The matrix cores take BF16 operands, so the float32 P is split into a BF16
 // head and a BF16 tail (p = hi + lo to about 16 significant bits) and both
 // halves are multiplied with V: rounding P to BF16 alone would perturb every
 // output by up to 2^-9 relative, a first-order departure from float32
-// softmax.
+// softmax (measured ~2e-3 nRMS; fp16 P, 2^-12, still ~8e-4 and 1.6x the
+// first layer's error against the oracle).
 //
 // K and V^T tiles go HBM -> LDS with buffer loads (no VGPR staging) into two
 // buffers: the next tile's loads are in flight while this tile is computed,
@@ -53,7 +55,8 @@ __device__ __forceinline__ int kchunk(int r, int c) {
 }
 __device__ __forceinline__ int vchunk(int r, int c) { return c ^ ((r >> 1) & 7); }
 
-__global__ __launch_bounds__(256) void attention_kernel(AttnParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void attention_kernel(
+    AttnParams p) {
     const int32_t nblk = p.nblk_dev ? *p.nblk_dev : p.nblk_max;
     // (block, head) work index: the blocks of one head are consecutive, and
     // contiguous ranges go to one XCD, so a row's K/V tiles are fetched into
@@ -104,17 +107,56 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnParams p) {
         }
     };
 
+    // Keys this lane's query may see: [q_lo, q_hi) (row end and window), and
+    // the keys every query of the wave sees, [w_lo, w_hi): tiles inside that
+    // range need no mask.
+    const int32_t q_lo = p.half_window < 0 ? 0 : max(0, my_pos - p.half_window);
+    const int32_t q_hi =
+        p.half_window < 0 ? blk.k_hi : min(blk.k_hi, my_pos + p.half_window + 1);
+    const uint32_t q_span = (uint32_t)(q_hi - q_lo);
+    int32_t w_lo = q_lo, w_hi = q_hi;
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+        w_lo = max(w_lo, __shfl_xor(w_lo, off, 64));
+        w_hi = min(w_hi, __shfl_xor(w_hi, off, 64));
+    }
+    w_lo = __builtin_amdgcn_readfirstlane(w_lo);
+    w_hi = __builtin_amdgcn_readfirstlane(w_hi);
+
     const float sl2 = 0.125f * 1.44269504088896341f;  // 1/sqrt(64) * log2(e)
-    float m = -INFINITY, lsum = 0.f;
-    f32x4_t oacc[4];
+    float m = -INFINITY;  // running maximum, raw score units
+    f32x4_t oacc[4];       // O^T rows 16 dblk + 4 g + i, column c16
 #pragma unroll
     for (int d = 0; d < 4; ++d) oacc[d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    f32x4_t lacc = {0.f, 0.f, 0.f, 0.f};  // running row sum (all 4 elements)
+    const bf16x8_t ones = as_bf16x8(u32x4_t{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
 
     int buf = 0;
     if (blk.k_lo < blk.k_hi) issue(blk.k_lo, 0);
     for (int32_t kb = blk.k_lo; kb < blk.k_hi; kb += KT, buf ^= 1) {
         wait_vmcnt<0>();  // this wave's loads of the tile (and the Q loads)
-        ring_barrier();   // every wave's loads landed; the other buffer is free
+        if (kb + KT > blk.k_hi) {
+            // Keys past the row's end may hold anything (other rows, stale
+            // memory): their P is 0, and their V is zeroed here, in the rows
+            // this wave loaded, so that 0 * V stays 0.
+            bf16_t *sVw = smem + buf * BUF_ELEMS + TILE_ELEMS;
+#pragma unroll
+            for (int it = 0; it < 2; ++it) {
+                const int r = 8 * (w + 4 * it) + dr;
+                const int left = blk.k_hi - kb - 8 * vchunk(r, dpc);  // valid keys in the chunk
+                if (left < 8) {
+                    u32x4_t *cp = reinterpret_cast<u32x4_t *>(&sVw[r * 64 + dpc * 8]);
+                    u32x4_t v = *cp;
+#pragma unroll
+                    for (int qd = 0; qd < 4; ++qd)
+                        v[qd] &= (2 * qd < left ? 0x0000ffffu : 0u) |
+                                 (2 * qd + 1 < left ? 0xffff0000u : 0u);
+                    *cp = v;
+                }
+            }
+            wait_lgkmcnt<0>();
+        }
+        ring_barrier();  // every wave's loads landed; the other buffer is free
         if (kb + KT < blk.k_hi) issue(kb + KT, buf ^ 1);
         const bf16_t *sK = smem + buf * BUF_ELEMS;
         const bf16_t *sV = sK + TILE_ELEMS;
@@ -134,88 +176,79 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnParams p) {
             s[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qb1, z, 0, 0, 0);
         }
 
-        // scale + mask; s[b][i] is key kb + 32 (b/2) + 8 g + 4 (b%2) + i
-        float mx = -INFINITY;
+        // mask, only on tiles that are not inside every window of the wave;
+        // s[b][i] is key kb + 32 (b/2) + 8 g + 4 (b%2) + i
+        if (!(kb >= w_lo && kb + KT <= w_hi)) {
+            const int32_t base = kb + 8 * g - q_lo;
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+            for (int b = 0; b < 4; ++b)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int32_t kj = kb + 32 * (b >> 1) + 8 * g + 4 * (b & 1) + i;
-                const int32_t dpos = my_pos - kj;
-                const bool ok = (kj < blk.k_hi) &&
-                                (p.half_window < 0 ||
-                                 (dpos <= p.half_window && -dpos <= p.half_window));
-                const float t = ok ? s[b][i] * sl2 : -INFINITY;
-                s[b][i] = t;
-                mx = fmaxf(mx, t);
-            }
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t rel = (uint32_t)(base + 32 * (b >> 1) + 4 * (b & 1) + i);
+                    s[b][i] = rel < q_span ? s[b][i] : -INFINITY;
+                }
+        }
+        // running maximum in raw score units (the scale is positive)
+        float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                         fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+        mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(s[2][0], s[2][1]), fmaxf(s[2][2], s[2][3])),
+                             fmaxf(fmaxf(s[3][0], s[3][1]), fmaxf(s[3][2], s[3][3]))));
         mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
         const float mnew = fmaxf(m, mx);
-        const float alpha = (mnew == -INFINITY) ? 1.f : exp2f(m - mnew);
+        const bool none = mnew == -INFINITY;  // every key so far masked
+        const float alpha = none ? 1.f : __builtin_amdgcn_exp2f((m - mnew) * sl2);
+        const float neg = none ? 0.f : -mnew * sl2;
         m = mnew;
-
-        // P = exp2(s - m), split into BF16 hi + lo, packed as the B operand
-        // of each 32-key half: slot 4 e + i <- block 2 ks + e, element i.
+        // P = 2^(s * scale - m * scale), split into BF16 hi + lo and packed
+        // as the B operand of each 32-key half: slot 4 e + i <- block 2 ks + e,
+        // element i (masked keys: 2^-inf = 0).
         u32x4_t ph[2], pl[2];
-        float rs = 0.f;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
             for (int qd = 0; qd < 4; ++qd) {
-                uint32_t hw[2], lw[2];
-#pragma unroll
-                for (int hl = 0; hl < 2; ++hl) {
-                    const int slot = 2 * qd + hl;
-                    const float t = s[2 * ks + (slot >> 2)][slot & 3];
-                    const float pv = (t == -INFINITY) ? 0.f : exp2f(t - mnew);
-                    rs += pv;
-                    hw[hl] = f32_to_bf16(pv);
-                    lw[hl] = f32_to_bf16(pv - bf16_to_f32(hw[hl]));  // pv - hi is exact
-                }
-                ph[ks][qd] = hw[0] | (hw[1] << 16);
-                pl[ks][qd] = lw[0] | (lw[1] << 16);
+                const int b0 = 2 * ks + (qd >> 1), i0 = 2 * (qd & 1);
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(s[b0][i0], sl2, neg));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(s[b0][i0 + 1], sl2, neg));
+                const uint32_t hi = cvt_pk_bf16(p0, p1);
+                ph[ks][qd] = hi;
+                pl[ks][qd] = cvt_pk_bf16(p0 - bf16lo(hi), p1 - bf16hi(hi));  // exact tails
             }
-        lsum = lsum * alpha + rs;
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {  // the maximum moved for some query
 #pragma unroll
-        for (int d = 0; d < 4; ++d) oacc[d] *= alpha;
+            for (int d = 0; d < 4; ++d) oacc[d] *= alpha;
+            lacc *= alpha;
+        }
 
-        // Keys past the row's end may hold anything (other rows, stale
-        // memory): their P is 0, and their V is zeroed so 0 * V stays 0.
-        u32x4_t vmask[2];
-        const bool tail = kb + KT > blk.k_hi;
+        // O^T[d][q] += V^T[d][keys] (P_hi + P_lo)^T[keys][q]; V^T row
+        // 16 dblk + c16, keys 32 ks + 8 g .. + 7 (logical chunk 4 ks + g).  The
+        // row sum is the same product with an all-ones A operand, so every
+        // lane gets its query's sum of exactly the weights that multiply V.
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int qd = 0; qd < 4; ++qd) {
-                const int32_t k0 = kb + 32 * ks + 8 * g + 2 * qd;
-                vmask[ks][qd] = (!tail || k0 + 1 < blk.k_hi) ? 0xffffffffu
-                                : (k0 < blk.k_hi)             ? 0x0000ffffu
-                                                              : 0u;
-            }
-
-        // O^T[d][q] += V^T[d][keys] P^T[keys][q]; V^T row 16 dblk + c16,
-        // keys 32 ks + 8 g .. + 7 (logical chunk 4 ks + g).
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
+        for (int ks = 0; ks < 2; ++ks) {
+            const bf16x8_t phb = as_bf16x8(ph[ks]), plb = as_bf16x8(pl[ks]);
+            bf16x8_t vb[4];
 #pragma unroll
             for (int dblk = 0; dblk < 4; ++dblk) {
                 const int r = 16 * dblk + c16;
-                u32x4_t va = *reinterpret_cast<const u32x4_t *>(
+                vb[dblk] = *reinterpret_cast<const bf16x8_t *>(
                     &sV[r * 64 + vchunk(r, 4 * ks + g) * 8]);
-                va &= vmask[ks];
-                const bf16x8_t vb = as_bf16x8(va);
-                oacc[dblk] =
-                    __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, as_bf16x8(ph[ks]), oacc[dblk], 0, 0, 0);
-                oacc[dblk] =
-                    __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, as_bf16x8(pl[ks]), oacc[dblk], 0, 0, 0);
             }
+            // independent accumulators between dependent MFMAs
+#pragma unroll
+            for (int dblk = 0; dblk < 4; ++dblk)
+                oacc[dblk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb[dblk], phb, oacc[dblk], 0, 0, 0);
+            lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, phb, lacc, 0, 0, 0);
+#pragma unroll
+            for (int dblk = 0; dblk < 4; ++dblk)
+                oacc[dblk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb[dblk], plb, oacc[dblk], 0, 0, 0);
+            lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, plb, lacc, 0, 0, 0);
+        }
     }
 
-    // row sum over the query's 4 lanes; O / l stored as BF16 at
-    // [q row][h*64 + 16 dblk + 4 g + i]
-    lsum += __shfl_xor(lsum, 16, 64);
-    lsum += __shfl_xor(lsum, 32, 64);
+    // O / l stored as BF16 at [q row][h*64 + 16 dblk + 4 g + i]
+    const float lsum = lacc[0];
     if (!qvalid) return;
     bf16_t *op = p.o + (size_t)qrow * p.ldo + h * 64 + 4 * g;
 #pragma unroll

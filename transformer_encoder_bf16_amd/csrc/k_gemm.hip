@@ -410,7 +410,8 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
                             u32x2_t{pack_bf16x2(yo[0], yo[1]), pack_bf16x2(yo[2], yo[3])};
                     }
                 } else if (f0 >= q.vt_col0) {
-                    // transposed: column f - vt_col0 of vt holds this token at vt_tok[tok]
+                    // transposed: row f - vt_col0 of vt holds this token at column
+                    // vt_tok[tok]
                     bf16_t *vcol = q.vt + q.vt_tok[tok];
 #pragma unroll
                     for (int h2 = 0; h2 < 2; ++h2)

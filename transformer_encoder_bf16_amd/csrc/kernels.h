@@ -87,8 +87,8 @@ hipError_t launch_rope(hipStream_t s, bf16_t *buf, int32_t ld, int32_t n_heads_r
                        const bf16_t *cos_tab, const bf16_t *sin_tab);
 
 // Attention over packed rows.  q [rows][ldq] (head h at columns h*64..),
-// k [rows][ldk] likewise, vt [n_heads*64][ldvt] (row h*64+d holds dimension
-// d of head h for every key column), o [rows][ldo].  k_bytes / vt_bytes
+// k [rows][ldk] likewise, vt [n_heads*64][ldvt] (row h*64+d holds
+// dimension d of head h for every key column), o [rows][ldo]; all BF16.  k_bytes / vt_bytes
 // bound what the kernel may read from k / vt (reads past them give zero).
 struct AttnParams {
     const bf16_t *q;
