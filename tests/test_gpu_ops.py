@@ -127,6 +127,35 @@ def test_gemm_geglu(B, M, F, K):
     assert e < 1e-4
 
 
+def test_gelu_epilogue_across_its_range(B):
+    """The GeGLU epilogue's GELU on BF16 values across [-12, 12] (u = one
+    weight times 1, gate 1): within one BF16 ulp of bf16(GELU) evaluated in
+    float64, and exact for nearly all, including the negative tail where
+    GELU falls to ~1e-32 (the range where its value is a normal float32)."""
+    import torch
+    u = oracle.bf16_round(np.linspace(-12.0, 12.0, 8192).astype(np.float32))
+    u = np.unique(u)
+    F = (len(u) + 63) // 64 * 64
+    u = np.concatenate([u, np.zeros(F - len(u), np.float32)])
+    K, M = 64, 64
+    a_h = np.zeros((M, K), np.float32)
+    a_h[:, 0] = 1.0
+    w_h = np.zeros((2 * F, K), np.float32)
+    w_h[:F, 0] = u
+    w_h[F:, 0] = 1.0
+    c = torch.full((M, F), float("nan"), dtype=torch.bfloat16, device="cuda")
+    B.op_gemm(to_dev(a_h), to_dev(w_h), c, M, F, K, 1)
+    _sync()
+    got = from_dev(c)[0]
+    want = oracle.bf16_round(oracle.gelu(u))
+    d = ulp_diff(got, want)
+    report("gelu_range", {"values": int(len(u)), "max_ulp": int(d.max()),
+                          "frac_exact": float((d == 0).mean())})
+    assert d.max() <= 1
+    assert (d == 0).mean() > 0.99
+    assert np.array_equal(from_dev(c)[1:], np.broadcast_to(got, (M - 1, F)))
+
+
 def test_gemm_rejects_bad_shapes(B):
     import torch
     a = torch.zeros((4, 96), dtype=torch.bfloat16, device="cuda")

@@ -26,17 +26,18 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
     # packed float32 instructions stay off: plain float code only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # MFMA accumulators in ordinary VGPRs (gfx950 allows it): no copies
-    # between accumulation and arithmetic registers, and fewer registers in all
-    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", INCLUDE, "-I", CSRC,
 ]
 
 
-# Per-file additions.  The attention kernel never lets a NaN into its float
-# arithmetic (masked scores are replaced by -inf with a select, values past a
-# row's end are zeroed as bits), so its maxima need no NaN quieting.
-FILE_FLAGS = {"k_attention.hip": ["-fno-honor-nans"]}
+# Per-file additions.  Attention: MFMA accumulators in ordinary VGPRs
+# (gfx950 allows it), so the softmax works on them with no copies between
+# accumulation and arithmetic registers; and since the kernel never lets a
+# NaN into its float arithmetic (masked scores are replaced by -inf with a
+# select, values past a row's end are zeroed as bits), its maxima need no NaN
+# quieting.  The GEMMs keep their accumulators in AGPRs: the large tiles need
+# more than the 256 ordinary VGPRs.
+FILE_FLAGS = {"k_attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"]}
 
 
 def _compile(src: str) -> str:

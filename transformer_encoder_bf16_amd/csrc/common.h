@@ -19,24 +19,17 @@ LAYA_DEV float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 LAYA_DEV float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 LAYA_DEV float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// float32 -> BF16 bits, round to nearest even; NaN stays a quiet NaN.
-LAYA_DEV uint32_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
-
-// Two float32 -> packed BF16 with the hardware conversion (round to nearest
-// even; v_cvt_pk_bf16_f32 on gfx950).
+// float32 -> BF16, round to nearest even (NaN stays NaN), with the gfx950
+// conversion instruction v_cvt_pk_bf16_f32.
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 LAYA_DEV uint32_t cvt_pk_bf16(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
-
-LAYA_DEV uint32_t pack_bf16x2(float lo, float hi) {
-    return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+LAYA_DEV uint32_t f32_to_bf16(float f) {
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
+LAYA_DEV uint32_t pack_bf16x2(float lo, float hi) { return cvt_pk_bf16(lo, hi); }
 
 // Wave-wide (64 lanes) butterfly sums / maxima.
 LAYA_DEV float wave_sum(float v) {

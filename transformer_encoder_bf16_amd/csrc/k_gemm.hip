@@ -61,10 +61,35 @@ __device__ __forceinline__ int swz(int r, int c) {
     return r * BK + (pchunk<BK>(r, c) << 3);
 }
 
+// erfc(x) by the Chebyshev fit of Numerical Recipes in C (2nd ed., section
+// 6.2, routine erfcc): for z = |x| and t = 1 / (1 + z/2),
+// erfc(z) = t exp(-z^2 + P(t)) with a degree-9 polynomial P, fractional error
+// below 1.2e-7 everywhere; erfc(-z) = 2 - erfc(z).  About 15 instructions,
+// against several times that for the multi-range library erfcf, which
+// dominated the GeGLU epilogue.  In float32 the exponent's rounding adds a
+// relative error of about 1e-7 * z^2, still far below the BF16 rounding of
+// the output.
+__device__ __forceinline__ float erfc_cheb(float x) {
+    const float z = fabsf(x);
+    const float t = __builtin_amdgcn_rcpf(fmaf(0.5f, z, 1.0f));
+    float q = 0.17087277f;
+    q = fmaf(q, t, -0.82215223f);
+    q = fmaf(q, t, 1.48851587f);
+    q = fmaf(q, t, -1.13520398f);
+    q = fmaf(q, t, 0.27886807f);
+    q = fmaf(q, t, -0.18628806f);
+    q = fmaf(q, t, 0.09678418f);
+    q = fmaf(q, t, 0.37409196f);
+    q = fmaf(q, t, 1.00002368f);
+    q = fmaf(q, t, -1.26551223f);
+    const float r = t * __expf(fmaf(-z, z, q));
+    return x >= 0.f ? r : 2.f - r;
+}
+
 // GELU(z) = z Phi(z) = 0.5 z erfc(-z / sqrt 2).  erfc keeps full relative
 // accuracy in the negative tail, where 1 + erf(z / sqrt 2) would cancel.
 __device__ __forceinline__ float gelu_erf(float z) {
-    return 0.5f * z * erfcf(-z * 0.70710678118654752f);
+    return 0.5f * z * erfc_cheb(-z * 0.70710678118654752f);
 }
 
 // Which tile a workgroup computes; false for a workgroup with no live tile.
@@ -357,26 +382,37 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
     }
 
     // Epilogue.  Accumulator element e of lane l in a 32x32 block holds
-    // row (weight row) 8*(e/4) + 4*(l/32) + e%4 and column (token) l%32.
+    // row (weight row) 8*(e/4) + 4*(l/32) + e%4 and column (token) l%32, so a
+    // lane has 4 consecutive output features of one token.  The BF16 output
+    // tile is first assembled in LDS ([token][feature], 16-byte chunks
+    // XOR-swizzled by token), then written with 16-byte stores along whole
+    // row segments: direct stores would touch 32 token rows per instruction.
+    // Columns bound for the transposed V (epilogue 2) are stored directly.
+    constexpr int NCH = BN / 8;  // 16-byte chunks per tile row
+    static_assert(BT * BN * 2 <= STAGES * G::STAGE_ELEMS * 2, "output tile fits the ring");
+    __syncthreads();  // every wave is done with the ring
+    bf16_t *sC = smem;
+    auto put4 = [&](int tl, int fl, uint32_t lo, uint32_t hi) {
+        const int c = fl >> 3;
+        *reinterpret_cast<u32x2_t *>(
+            &sC[tl * BN + ((c ^ (tl & (NCH - 1))) << 3) + (fl & 4)]) = u32x2_t{lo, hi};
+    };
     auto bf16r = [](float v) { return bf16_to_f32(f32_to_bf16(v)); };
 #pragma unroll
     for (int b = 0; b < FB; ++b) {
-        const int32_t tok = t0 + wc * G::RT + 32 * b + l32;
-        if (tok >= M) continue;
-        bf16_t *crow = p.C + (size_t)tok * p.ldc;
+        const int tl = wc * G::RT + 32 * b + l32;  // token within the tile
+        const int32_t tok = t0 + tl;
         if constexpr (EPI == 1) {
 #pragma unroll
             for (int a = 0; a < FA / 2; ++a)
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4) {
-                    const int32_t f = n0 + wr * (G::RW / 2) + 32 * a + 8 * g4 + 4 * lhi;
-                    if (f >= N) continue;
+                    const int fl = wr * (G::RW / 2) + 32 * a + 8 * g4 + 4 * lhi;
                     float h[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         h[e] = gelu_erf(acc[a][b][4 * g4 + e]) * acc[a + FA / 2][b][4 * g4 + e];
-                    u32x2_t pk = {pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
-                    *reinterpret_cast<u32x2_t *>(crow + f) = pk;
+                    put4(tl, fl, pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
                 }
         } else if constexpr (EPI == 2) {
             // Fragments a (dims 0..31 of a head) and a+1 (dims 32..63) sit in
@@ -387,7 +423,7 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
                 const int32_t f0 = n0 + wrow[a];  // first column of the head
                 if (f0 >= N) continue;
                 if (f0 < q.rope_cols) {
-                    const uint32_t ps = (uint32_t)q.pos[tok] * 32u;
+                    const uint32_t ps = (uint32_t)q.pos[tok < M ? tok : M - 1] * 32u;
 #pragma unroll
                     for (int g4 = 0; g4 < 4; ++g4) {
                         const int j = 8 * g4 + 4 * lhi;  // pair index of element 4*g4
@@ -404,33 +440,33 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
                             xo[e] = fmaf(x, c, -(y * sn));
                             yo[e] = fmaf(y, c, x * sn);
                         }
-                        *reinterpret_cast<u32x2_t *>(crow + f0 + j) =
-                            u32x2_t{pack_bf16x2(xo[0], xo[1]), pack_bf16x2(xo[2], xo[3])};
-                        *reinterpret_cast<u32x2_t *>(crow + f0 + 32 + j) =
-                            u32x2_t{pack_bf16x2(yo[0], yo[1]), pack_bf16x2(yo[2], yo[3])};
+                        put4(tl, wrow[a] + j, pack_bf16x2(xo[0], xo[1]), pack_bf16x2(xo[2], xo[3]));
+                        put4(tl, wrow[a] + 32 + j, pack_bf16x2(yo[0], yo[1]),
+                             pack_bf16x2(yo[2], yo[3]));
                     }
                 } else if (f0 >= q.vt_col0) {
                     // transposed: row f - vt_col0 of vt holds this token at column
-                    // vt_tok[tok]
-                    bf16_t *vcol = q.vt + q.vt_tok[tok];
+                    // vt_tok[tok] (32 lanes write 32 consecutive tokens)
+                    if (tok < M) {
+                        bf16_t *vcol = q.vt + q.vt_tok[tok];
 #pragma unroll
-                    for (int h2 = 0; h2 < 2; ++h2)
+                        for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-                        for (int e = 0; e < 16; ++e) {
-                            const int32_t f = f0 + 32 * h2 + 8 * (e / 4) + 4 * lhi + e % 4;
-                            vcol[(size_t)(f - q.vt_col0) * q.ldvt] =
-                                (bf16_t)f32_to_bf16(acc[a + h2][b][e]);
-                        }
+                            for (int e = 0; e < 16; ++e) {
+                                const int32_t f = f0 + 32 * h2 + 8 * (e / 4) + 4 * lhi + e % 4;
+                                vcol[(size_t)(f - q.vt_col0) * q.ldvt] =
+                                    (bf16_t)f32_to_bf16(acc[a + h2][b][e]);
+                            }
+                    }
                 } else {
 #pragma unroll
                     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
                         for (int g4 = 0; g4 < 4; ++g4) {
-                            const int32_t f = f0 + 32 * h2 + 8 * g4 + 4 * lhi;
                             const f32x16_t &v = acc[a + h2][b];
-                            *reinterpret_cast<u32x2_t *>(crow + f) =
-                                u32x2_t{pack_bf16x2(v[4 * g4], v[4 * g4 + 1]),
-                                        pack_bf16x2(v[4 * g4 + 2], v[4 * g4 + 3])};
+                            put4(tl, wrow[a] + 32 * h2 + 8 * g4 + 4 * lhi,
+                                 pack_bf16x2(v[4 * g4], v[4 * g4 + 1]),
+                                 pack_bf16x2(v[4 * g4 + 2], v[4 * g4 + 3]));
                         }
                 }
             }
@@ -439,14 +475,23 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
             for (int a = 0; a < FA; ++a)
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4) {
-                    const int32_t f = n0 + wrow[a] + 8 * g4 + 4 * lhi;
-                    if (f >= N) continue;
                     const f32x16_t &v = acc[a][b];
-                    u32x2_t pk = {pack_bf16x2(v[4 * g4], v[4 * g4 + 1]),
-                                  pack_bf16x2(v[4 * g4 + 2], v[4 * g4 + 3])};
-                    *reinterpret_cast<u32x2_t *>(crow + f) = pk;
+                    put4(tl, wrow[a] + 8 * g4 + 4 * lhi, pack_bf16x2(v[4 * g4], v[4 * g4 + 1]),
+                         pack_bf16x2(v[4 * g4 + 2], v[4 * g4 + 3]));
                 }
         }
+    }
+    __syncthreads();
+    // columns this tile writes to C: [n0, min(N, n0 + BN), and below vt_col0)
+    int32_t n_end = min(N, n0 + BN);
+    if constexpr (EPI == 2) n_end = min(n_end, max(p.qe.vt_col0, n0));
+#pragma unroll 4
+    for (int idx = tid; idx < BT * NCH; idx += G::NTHR) {
+        const int tl = idx / NCH, c = idx % NCH;
+        const int32_t tok = t0 + tl, f = n0 + 8 * c;
+        if (tok < M && f < n_end)
+            st16(p.C + (size_t)tok * p.ldc + f,
+                 *reinterpret_cast<const u32x4_t *>(&sC[tl * BN + ((c ^ (tl & (NCH - 1))) << 3)]));
     }
 }
 
@@ -454,16 +499,18 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
 using CfgXS = Cfg<32, 64, 1, 1, 64, 6>;    // small M, 1 wave (plain only)
 using CfgXSG = Cfg<64, 64, 1, 1, 64, 4>;   // small M, 1 wave (GeGLU-capable)
 using CfgS = Cfg<128, 64, 2, 2, 64, 4>;    // 4 waves of 64 rows x 32 tokens
-using CfgM = Cfg<128, 128, 2, 2, 32, 8>;   // 4 waves of 64 x 64
-using CfgL = Cfg<256, 128, 2, 4, 32, 6>;   // 8 waves of 128 x 32
-using CfgXL = Cfg<256, 256, 2, 4, 32, 4>;  // 8 waves of 128 x 64
+using CfgM = Cfg<128, 128, 2, 2, 64, 4>;   // 4 waves of 64 x 64
+using CfgL = Cfg<256, 128, 2, 4, 64, 3>;   // 8 waves of 128 x 32
+using CfgXL = Cfg<256, 256, 2, 4, 64, 2>;  // 8 waves of 128 x 64
+using CfgXL4 = Cfg<256, 256, 2, 2, 64, 2>;  // 4 waves of 128 x 128
 
 struct CfgInfo {
     int bw, bt;
 };
 constexpr CfgInfo kCfgs[kGemmConfigs] = {{CfgXS::BW, CfgXS::BT}, {CfgXSG::BW, CfgXSG::BT},
                                          {CfgS::BW, CfgS::BT},   {CfgM::BW, CfgM::BT},
-                                         {CfgL::BW, CfgL::BT},   {CfgXL::BW, CfgXL::BT}};
+                                         {CfgL::BW, CfgL::BT},   {CfgXL::BW, CfgXL::BT},
+                                         {CfgXL4::BW, CfgXL4::BT}};
 
 template <class G, bool SPLITK>
 hipError_t launch_cfg(hipStream_t s, const GemmParams &p, int epilogue) {
@@ -580,7 +627,8 @@ hipError_t launch_gemm(hipStream_t s, const bf16_t *A, int32_t lda, const bf16_t
         case 2: return launch_small<CfgS>(s, p, epilogue);
         case 3: return launch_small<CfgM>(s, p, epilogue);
         case 4: return launch_large<CfgL>(s, p, epilogue);
-        default: return launch_large<CfgXL>(s, p, epilogue);
+        case 5: return launch_large<CfgXL>(s, p, epilogue);
+        default: return launch_large<CfgXL4>(s, p, epilogue);
     }
 }
 

@@ -45,9 +45,10 @@ hipError_t launch_layernorm(hipStream_t s, bf16_t *x, const bf16_t *r, bf16_t *n
 // GEMM tile configuration and K split.  Every output element is one MFMA
 // chain per K range, the ranges summed in order, so a result depends only on
 // `splits` (never on the tile shape).
-constexpr int kGemmConfigs = 6;
+constexpr int kGemmConfigs = 7;
 struct GemmPlan {
-    int config;  // 0 XS 32x64, 1 XSG 64x64, 2 S 128x64, 3 M 128x128, 4 L 256x128, 5 XL 256x256
+    int config;  // 0 XS 32x64, 1 XSG 64x64, 2 S 128x64, 3 M 128x128, 4 L 256x128, 5 XL 256x256,
+                 // 6 XL4 256x256 (4 waves)
     int splits;  // K ranges (>= 1)
 };
 // plan for a GEMM launched with a grid for M_max rows (the K split depends
