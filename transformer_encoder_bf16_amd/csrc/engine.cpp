@@ -334,7 +334,6 @@ struct laya_encoder {
     bf16_t *vt = nullptr;  // transposed V [n_heads*64][ldvt], rows start 64-aligned
     int32_t ldvt = 0;
     float *gemm_partial = nullptr;    // split-K partial tiles
-    uint32_t *gemm_counter = nullptr;  // split-K tile counters (zero between launches)
     int32_t *meta_dev = nullptr;
     int32_t *meta_host = nullptr;
     int64_t meta_cap = 0;
@@ -458,15 +457,13 @@ PassPlans make_plans(const laya_config &c, int Tmax, int T, int R) {
     return p;
 }
 
-// Largest split-K partial buffer (bytes) and counter count over every shape
-// the handle accepts.
-void gemm_scratch_bound(const laya_config &c, size_t *bytes, size_t *counters) {
+// Largest split-K partial buffer (bytes) over every shape the handle accepts.
+void gemm_scratch_bound(const laya_config &c, size_t *bytes) {
     const int H = c.hidden, F = c.ffn;
     const int tcap = c.max_batch * c.max_seq;
-    size_t b = 0, n = 0;
+    size_t b = 0;
     auto acc = [&](const laya::GemmPlan &g, int M, int N, int epi) {
         b = std::max(b, laya::gemm_workspace_bytes(g, M, N, epi));
-        n = std::max(n, laya::gemm_counter_count(g, M, N, epi));
     };
     int last_splits[4] = {-1, -1, -1, -1};
     for (int T = 1; T <= tcap; ++T) {
@@ -489,7 +486,6 @@ void gemm_scratch_bound(const laya_config &c, size_t *bytes, size_t *counters) {
         }
     }
     *bytes = b;
-    *counters = n;
 }
 
 // Queue the whole pass on stream s.  Reads T, the row layout and the
@@ -516,7 +512,6 @@ int record(laya_encoder *enc, hipStream_t s, const RunShape &rs, Profiler *prof 
     const int hw = c.window / 2;
     const PassPlans plans = make_plans(c, Tmax, rs.T, rs.R);
     float *gp = enc->gemm_partial;
-    uint32_t *gc = enc->gemm_counter;
     enc->launches = 0;
 
     size_t ci = 0;
@@ -604,7 +599,7 @@ int record(laya_encoder *enc, hipStream_t s, const RunShape &rs, Profiler *prof 
             const laya::QkvEpilogue qe{pos, ctab, stab, 2 * H, 2 * H, enc->vt, enc->ldvt, vtok};
             L_OP(OP_QKV, gemm_fl(T, 3 * H, H), gemm_by(T, 3 * H, 3 * H, H),
                  laya::launch_gemm(s, enc->nrm, H, Wqkv, H, enc->qkv, 3 * H, T_dev, Tmax, 3 * H,
-                                   H, 2, plans.qkv, gp, gc, &qe));
+                                   H, 2, plans.qkv, gp, &qe));
             const laya::AttnParams ap{enc->qkv, 3 * H, enc->qkv + H, 3 * H, k_bytes(3 * H),
                                       enc->vt, enc->ldvt, vt_bytes, enc->att, H, blk, nblk,
                                       ml.nblk_full_max, pos, nh, half};
@@ -612,16 +607,16 @@ int record(laya_encoder *enc, hipStream_t s, const RunShape &rs, Profiler *prof 
                  4 * T * H * b2, laya::launch_attention(s, ap));
             L_OP(OP_OUT_PROJ, gemm_fl(T, H, H), gemm_by(T, H, H, H),
                  laya::launch_gemm(s, enc->att, H, Wo, H, enc->proj, H, T_dev, Tmax, H, H, 0,
-                                   plans.o, gp, gc));
+                                   plans.o, gp));
             L_OP(OP_LAYERNORM, 0, ln_res_by,
                  laya::launch_layernorm(s, xr, enc->proj, enc->nrm, g1, T_dev, Tmax, H,
                                         c.ln_eps));
             L_OP(OP_UP_GEGLU, gemm_fl(T, 2 * F, H), gemm_by(T, 2 * F, F, H),
                  laya::launch_gemm(s, enc->nrm, H, Wi, H, enc->hid, F, T_dev, Tmax, F, H, 1,
-                                   plans.up, gp, gc));
+                                   plans.up, gp));
             L_OP(OP_DOWN, gemm_fl(T, H, F), gemm_by(T, H, H, F),
                  laya::launch_gemm(s, enc->hid, F, Wo2, F, enc->proj, H, T_dev, Tmax, H, F, 0,
-                                   plans.down, gp, gc));
+                                   plans.down, gp));
             pending = true;
             if (L == c.n_enc_layers - 1) {
                 // x += f; the encoder's final LayerNorm output becomes the decision stream
@@ -640,7 +635,7 @@ int record(laya_encoder *enc, hipStream_t s, const RunShape &rs, Profiler *prof 
             const laya::QkvEpilogue qe_kv{pos, ctab, stab, H, H, enc->vt, enc->ldvt, vtok};
             L_OP(OP_KV, gemm_fl(T, 2 * H, H), gemm_by(T, 2 * H, 2 * H, H),
                  laya::launch_gemm(s, enc->nrm, H, Wqkv + (size_t)H * H, H, enc->qkv, 2 * H,
-                                   T_dev, Tmax, 2 * H, H, 2, plans.kv_sub, gp, gc, &qe_kv));
+                                   T_dev, Tmax, 2 * H, H, 2, plans.kv_sub, gp, &qe_kv));
             L_OP(OP_ROW_GATHER, 0, 2 * R * H * b2,
                  laya::launch_gather_rows(s, enc->nrm, H, mrk_tok, Ri, H, enc->n_sub, H));
             L_OP(OP_ROW_GATHER, 0, 2 * R * H * b2,
@@ -648,7 +643,7 @@ int record(laya_encoder *enc, hipStream_t s, const RunShape &rs, Profiler *prof 
             const laya::QkvEpilogue qe_q{mrk_pos, ctab, stab, H, H, nullptr, 0, nullptr};
             L_OP(OP_Q, gemm_fl(R, H, H), gemm_by(R, H, H, H),
                  laya::launch_gemm(s, enc->n_sub, H, Wqkv, H, enc->q_sub, H, nullptr, Ri, H, H,
-                                   2, plans.q_sub, gp, gc, &qe_q));
+                                   2, plans.q_sub, gp, &qe_q));
             const laya::AttnParams ap{enc->q_sub, H, enc->qkv, 2 * H, k_bytes(2 * H),
                                       enc->vt, enc->ldvt, vt_bytes, enc->att, H, blk_s, nblk_s,
                                       ml.nblk_sub_max, mrk_pos, nh, half};
@@ -656,16 +651,16 @@ int record(laya_encoder *enc, hipStream_t s, const RunShape &rs, Profiler *prof 
                  laya::launch_attention(s, ap));
             L_OP(OP_OUT_PROJ, gemm_fl(R, H, H), gemm_by(R, H, H, H),
                  laya::launch_gemm(s, enc->att, H, Wo, H, enc->proj, H, nullptr, Ri, H, H, 0,
-                                   plans.o_sub, gp, gc));
+                                   plans.o_sub, gp));
             L_OP(OP_LAYERNORM, 0, 4 * R * H * b2,
                  laya::launch_layernorm(s, enc->x_sub, enc->proj, enc->n_sub, g1, nullptr, Ri,
                                         H, c.ln_eps));
             L_OP(OP_UP_GEGLU, gemm_fl(R, 2 * F, H), gemm_by(R, 2 * F, F, H),
                  laya::launch_gemm(s, enc->n_sub, H, Wi, H, enc->hid, F, nullptr, Ri, F, H, 1,
-                                   plans.up_sub, gp, gc));
+                                   plans.up_sub, gp));
             L_OP(OP_DOWN, gemm_fl(R, H, F), gemm_by(R, H, H, F),
                  laya::launch_gemm(s, enc->hid, F, Wo2, F, enc->proj, H, nullptr, Ri, H, F, 0,
-                                   plans.down_sub, gp, gc));
+                                   plans.down_sub, gp));
             L_OP(OP_LAYERNORM, 0, 4 * R * H * b2,
                  laya::launch_layernorm(s, enc->x_sub, enc->proj, enc->out, g1, nullptr, Ri, H,
                                         c.ln_eps));
@@ -869,12 +864,10 @@ int laya_encoder_create(const laya_config *cfg, uint64_t seed, int device, laya_
     enc->meta_cap = mlmax.total;
     const size_t meta_off = wsz;
     wsz += al((size_t)enc->meta_cap * 4);
-    size_t gp_bytes = 0, gc_count = 0;
-    gemm_scratch_bound(c, &gp_bytes, &gc_count);
+    size_t gp_bytes = 0;
+    gemm_scratch_bound(c, &gp_bytes);
     const size_t gp_off = wsz;
     wsz += al(gp_bytes);
-    const size_t gc_off = wsz;
-    wsz += al(gc_count * 4);
     enc->ws_bytes = wsz;
     if (hipMalloc(&enc->ws, wsz) != hipSuccess)
         return bail(set_global_error(LAYA_E_NOMEM, "workspace: hipMalloc failed"));
@@ -889,7 +882,6 @@ int laya_encoder_create(const laya_config *cfg, uint64_t seed, int device, laya_
         }
         enc->meta_dev = reinterpret_cast<int32_t *>(p + meta_off);
         enc->gemm_partial = gp_bytes ? reinterpret_cast<float *>(p + gp_off) : nullptr;
-        enc->gemm_counter = gc_count ? reinterpret_cast<uint32_t *>(p + gc_off) : nullptr;
     }
     if (hipHostMalloc((void **)&enc->meta_host, (size_t)enc->meta_cap * 4, hipHostMallocDefault) !=
         hipSuccess)
@@ -1276,20 +1268,13 @@ int op_gemm_launch(const char *who, hipStream_t s, const void *A, int32_t lda, c
         (epilogue && plan.config == 0))
         return set_global_error(LAYA_E_INVALID, std::string(who) + ": unsupported config/splits");
     const size_t pb = laya::gemm_workspace_bytes(plan, M, N, epilogue);
-    const size_t pc = laya::gemm_counter_count(plan, M, N, epilogue);
     void *scratch = nullptr;
-    if (pb && hipMalloc(&scratch, pb + pc * 4) != hipSuccess)
+    if (pb && hipMalloc(&scratch, pb) != hipSuccess)
         return set_global_error(LAYA_E_NOMEM, std::string(who) + ": scratch hipMalloc failed");
-    hipError_t e = hipSuccess;
-    if (pb) e = hipMemsetAsync(static_cast<char *>(scratch) + pb, 0, pc * 4, s);
-    if (e == hipSuccess)
-        e = laya::launch_gemm(s, static_cast<const bf16_t *>(A), lda,
-                              static_cast<const bf16_t *>(W), ldw, static_cast<bf16_t *>(C), ldc,
-                              nullptr, M, N, K, epilogue, plan,
-                              pb ? static_cast<float *>(scratch) : nullptr,
-                              pb ? reinterpret_cast<uint32_t *>(static_cast<char *>(scratch) + pb)
-                                 : nullptr,
-                              qe);
+    hipError_t e = laya::launch_gemm(s, static_cast<const bf16_t *>(A), lda,
+                                     static_cast<const bf16_t *>(W), ldw,
+                                     static_cast<bf16_t *>(C), ldc, nullptr, M, N, K, epilogue,
+                                     plan, static_cast<float *>(scratch), qe);
     if (pb) {
         if (e == hipSuccess) e = hipStreamSynchronize(s);
         hipFree(scratch);

@@ -28,11 +28,12 @@
 //     depend on the tile shape or on where a token sits in its tile.
 //
 // Split-K (small M, where only a few weight tiles exist): the K range is cut
-// into S contiguous pieces (multiples of 64); each workgroup writes its
-// float32 partial tile, and the last of the S workgroups of a tile to finish
-// (atomic counter) adds the partials in piece order 0..S-1 and runs the
-// epilogue.  The sum order is fixed, so results are deterministic, and that
-// workgroup resets the counter, so a captured graph replays without clearing.
+// into S contiguous pieces (multiples of 64); one launch writes each piece's
+// float32 partial tile, a second launch adds the partials in piece order
+// 0..S-1 and runs the epilogue.  The sum order is fixed, so results are
+// deterministic.  Two launches rather than a last-arriving workgroup: on a
+// multi-XCD part a device-scope fence writes back the XCD's whole L2, which
+// cost tens of microseconds when every workgroup issued one.
 //
 // GeGLU epilogue (epilogue 1): the first BW/2 rows of the weight tile are
 // rows n0.. of W (the GELU half), the last BW/2 rows are rows N+n0.. (the
@@ -143,12 +144,17 @@ struct GemmParams {
     const int32_t *M_dev;
     int32_t M_max, N, K;
     int32_t splits;
-    float *partial;     // [tiles][splits][BW*BT] (splits > 1)
-    uint32_t *counter;  // [tiles] (splits > 1), zero between launches
-    QkvEpilogue qe;     // epilogue 2 only
+    float *partial;  // [tiles][splits][BW*BT] (splits > 1)
+    QkvEpilogue qe;  // epilogue 2 only
 };
 
-template <class G, int EPI, bool SPLITK>
+// MODE 0: whole K, C written.  MODE 1: one K range per blockIdx.z, its
+// float32 partial tile written to p.partial.  MODE 2: the partials of each
+// tile summed in range order, then the epilogue (a second launch, so the
+// partials are visible without any cross-XCD fence).
+enum { kWholeK = 0, kPartial = 1, kReduce = 2 };
+
+template <class G, int EPI, int MODE>
 __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
     constexpr int BW = G::BW, BT = G::BT, FA = G::FA, FB = G::FB, STAGES = G::STAGES;
     constexpr int BK = G::BK, CH = G::CH, RPL = G::RPL;
@@ -156,7 +162,7 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
     static_assert(EPI != 2 || G::RW % 64 == 0, "QKV epilogue: a wave's rows are whole heads");
     const int32_t M = p.M_dev ? *p.M_dev : p.M_max;
     int bx = blockIdx.x, by = blockIdx.y;
-    if (!SPLITK) {
+    if (MODE == kWholeK) {
         if (!tile_order((M + BT - 1) / BT, bx, by)) return;
     }
     const int32_t t0 = by * BT;
@@ -282,53 +288,55 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
                                                                     acc[a][b], 0, 0, 0);
     };
 
+    if constexpr (MODE != kReduce) {
     // prologue: every stage of the ring in flight, then stage 0 published
-#pragma unroll
-    for (int st = 0; st < STAGES; ++st)
-        if (st < nk) issue(st, st);
-    if (nk >= STAGES)
-        wait_vmcnt<(STAGES - 1) * G::LOADS>();
-    else
-        wait_vmcnt<0>();
-    wait_lgkmcnt<0>();  // no scalar loads left in flight, so
-                                         // the loop's LDS reads can be waited on in order
-    ring_barrier();
-    if (nk > 0) read_frags(0, 0, 0);
-
-    for (int i = 0; i < nk; ++i) {
-        const int stage = i % STAGES;
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            if (s + 1 < NS) {
-                read_frags(stage, s + 1, (s + 1) & 1);
-            } else {
-                // outstanding loads after stage i+1: stages i+2 .. min(i+STAGES-1, nk-1)
-                if (i + STAGES <= nk)
-                    wait_vmcnt<(STAGES - 2) * G::LOADS>();
-                else
-                    wait_vmcnt<0>();
-                wait_lgkmcnt<0>();  // this stage fully read
-                ring_barrier();
-                if (i + STAGES < nk) issue(i + STAGES, stage);
-                // next stage's first fragments (after the last stage: an unused
-                // read of a valid stage, kept so the loop body has no branch
-                // around LDS reads and their waits stay exact)
-                read_frags((i + 1) % STAGES, 0, 0);
-            }
-            // the fragments of step s are complete once at most the reads of
-            // step s+1 remain in flight
-            wait_lgkmcnt<G::FA + G::FB>();
-            __builtin_amdgcn_sched_barrier(0);
-            mfmas(s & 1);
-            __builtin_amdgcn_sched_barrier(0);
-        }
+  #pragma unroll
+      for (int st = 0; st < STAGES; ++st)
+          if (st < nk) issue(st, st);
+      if (nk >= STAGES)
+          wait_vmcnt<(STAGES - 1) * G::LOADS>();
+      else
+          wait_vmcnt<0>();
+      wait_lgkmcnt<0>();  // no scalar loads left in flight, so
+                                           // the loop's LDS reads can be waited on in order
+      ring_barrier();
+      if (nk > 0) read_frags(0, 0, 0);
+  
+      for (int i = 0; i < nk; ++i) {
+          const int stage = i % STAGES;
+  #pragma unroll
+          for (int s = 0; s < NS; ++s) {
+              if (s + 1 < NS) {
+                  read_frags(stage, s + 1, (s + 1) & 1);
+              } else {
+                  // outstanding loads after stage i+1: stages i+2 .. min(i+STAGES-1, nk-1)
+                  if (i + STAGES <= nk)
+                      wait_vmcnt<(STAGES - 2) * G::LOADS>();
+                  else
+                      wait_vmcnt<0>();
+                  wait_lgkmcnt<0>();  // this stage fully read
+                  ring_barrier();
+                  if (i + STAGES < nk) issue(i + STAGES, stage);
+                  // next stage's first fragments (after the last stage: an unused
+                  // read of a valid stage, kept so the loop body has no branch
+                  // around LDS reads and their waits stay exact)
+                  read_frags((i + 1) % STAGES, 0, 0);
+              }
+              // the fragments of step s are complete once at most the reads of
+              // step s+1 remain in flight
+              wait_lgkmcnt<G::FA + G::FB>();
+              __builtin_amdgcn_sched_barrier(0);
+              mfmas(s & 1);
+              __builtin_amdgcn_sched_barrier(0);
+          }
+      }
     }
 
-    if constexpr (SPLITK) {
-        // Publish this split's partial tile, then let the last split finish it.
-        const int tile = blockIdx.y * gridDim.x + blockIdx.x;
+    // Partial tiles: [tile][split][wave][a][b][e4][lane][4] float32, so each
+    // lane moves 16 contiguous bytes.
+    const int tile = blockIdx.y * gridDim.x + blockIdx.x;
+    if constexpr (MODE == kPartial) {
         float *mine = p.partial + ((size_t)tile * p.splits + split) * (BW * BT);
-        // layout: [wave][a][b][e4][lane][4] -> each lane stores 16 contiguous bytes
 #pragma unroll
         for (int a = 0; a < FA; ++a)
 #pragma unroll
@@ -336,49 +344,50 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
 #pragma unroll
                 for (int e4 = 0; e4 < 4; ++e4) {
                     const int blk = ((wave * FA + a) * FB + b) * 4 + e4;
-                    f32x4_t v = {acc[a][b][4 * e4], acc[a][b][4 * e4 + 1], acc[a][b][4 * e4 + 2],
-                                 acc[a][b][4 * e4 + 3]};
+                    const f32x4_t v = {acc[a][b][4 * e4], acc[a][b][4 * e4 + 1],
+                                       acc[a][b][4 * e4 + 2], acc[a][b][4 * e4 + 3]};
                     *reinterpret_cast<f32x4_t *>(mine + (size_t)blk * 256 + lane * 4) = v;
                 }
-        __threadfence();
-        __shared__ uint32_t s_last;
-        __syncthreads();
-        if (tid == 0) {
-            const uint32_t done = atomicAdd(&p.counter[tile], 1u);
-            s_last = (done == (uint32_t)(p.splits - 1)) ? 1u : 0u;
-        }
-        __syncthreads();
-        if (!s_last) return;
-        __threadfence();
-        // sum the partials in split order (own contribution from registers)
-        const float *base = p.partial + (size_t)tile * p.splits * (BW * BT);
+        return;
+    }
+    if constexpr (MODE == kReduce) {
+        // sum of the K ranges' partials, in range order; each range's whole
+        // share of the tile is loaded before it is added, so a wave has all
+        // of its loads for one range in flight at once
+        const float *base = p.partial + (size_t)tile * p.splits * (BW * BT) + lane * 4;
+        auto part = [&](int sp, int a, int b, int e4) {
+            const int blk = ((wave * FA + a) * FB + b) * 4 + e4;
+            return *reinterpret_cast<const f32x4_t *>(base + (size_t)sp * (BW * BT) +
+                                                     (size_t)blk * 256);
+        };
+        f32x4_t sum[FA][FB][4];
 #pragma unroll
         for (int a = 0; a < FA; ++a)
 #pragma unroll
             for (int b = 0; b < FB; ++b)
 #pragma unroll
-                for (int e4 = 0; e4 < 4; ++e4) {
-                    const int blk = ((wave * FA + a) * FB + b) * 4 + e4;
-                    f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
-                    for (int s = 0; s < p.splits; ++s) {
-                        f32x4_t v;
-                        if (s == split)
-                            v = f32x4_t{acc[a][b][4 * e4], acc[a][b][4 * e4 + 1],
-                                        acc[a][b][4 * e4 + 2], acc[a][b][4 * e4 + 3]};
-                        else
-                            v = *reinterpret_cast<const f32x4_t *>(
-                                base + (size_t)s * (BW * BT) + (size_t)blk * 256 + lane * 4);
-                        if (s == 0)
-                            sum = v;
-                        else
-                            sum += v;
-                    }
-                    acc[a][b][4 * e4] = sum[0];
-                    acc[a][b][4 * e4 + 1] = sum[1];
-                    acc[a][b][4 * e4 + 2] = sum[2];
-                    acc[a][b][4 * e4 + 3] = sum[3];
-                }
-        if (tid == 0) p.counter[tile] = 0u;  // ready for the next launch
+                for (int e4 = 0; e4 < 4; ++e4) sum[a][b][e4] = part(0, a, b, e4);
+        for (int sp = 1; sp < p.splits; ++sp) {
+            f32x4_t t[FA][FB][4];
+#pragma unroll
+            for (int a = 0; a < FA; ++a)
+#pragma unroll
+                for (int b = 0; b < FB; ++b)
+#pragma unroll
+                    for (int e4 = 0; e4 < 4; ++e4) t[a][b][e4] = part(sp, a, b, e4);
+#pragma unroll
+            for (int a = 0; a < FA; ++a)
+#pragma unroll
+                for (int b = 0; b < FB; ++b)
+#pragma unroll
+                    for (int e4 = 0; e4 < 4; ++e4) sum[a][b][e4] += t[a][b][e4];
+        }
+#pragma unroll
+        for (int a = 0; a < FA; ++a)
+#pragma unroll
+            for (int b = 0; b < FB; ++b)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[a][b][e] = sum[a][b][e / 4][e % 4];
     }
 
     // Epilogue.  Accumulator element e of lane l in a 32x32 block holds
@@ -512,32 +521,35 @@ constexpr CfgInfo kCfgs[kGemmConfigs] = {{CfgXS::BW, CfgXS::BT}, {CfgXSG::BW, Cf
                                          {CfgL::BW, CfgL::BT},   {CfgXL::BW, CfgXL::BT},
                                          {CfgXL4::BW, CfgXL4::BT}};
 
-template <class G, bool SPLITK>
-hipError_t launch_cfg(hipStream_t s, const GemmParams &p, int epilogue) {
+template <class G, int MODE>
+hipError_t launch_mode(hipStream_t s, const GemmParams &p, int epilogue) {
     const int bn = epilogue == 1 ? G::BW / 2 : G::BW;
-    const dim3 grid((p.N + bn - 1) / bn, (p.M_max + G::BT - 1) / G::BT, p.splits);
+    const dim3 grid((p.N + bn - 1) / bn, (p.M_max + G::BT - 1) / G::BT,
+                    MODE == kPartial ? p.splits : 1);
     if (epilogue == 0) {
-        hipLaunchKernelGGL((gemm_kernel<G, 0, SPLITK>), grid, dim3(G::NTHR), 0, s, p);
+        hipLaunchKernelGGL((gemm_kernel<G, 0, MODE>), grid, dim3(G::NTHR), 0, s, p);
     } else if constexpr (G::FA % 2 == 0 && G::RW % 64 == 0) {
         if (epilogue == 1)
-            hipLaunchKernelGGL((gemm_kernel<G, 1, SPLITK>), grid, dim3(G::NTHR), 0, s, p);
+            hipLaunchKernelGGL((gemm_kernel<G, 1, MODE>), grid, dim3(G::NTHR), 0, s, p);
         else
-            hipLaunchKernelGGL((gemm_kernel<G, 2, SPLITK>), grid, dim3(G::NTHR), 0, s, p);
+            hipLaunchKernelGGL((gemm_kernel<G, 2, MODE>), grid, dim3(G::NTHR), 0, s, p);
     } else {
         return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
-// Small tiles take split K; the large ones never do (K is always whole).
+// Small tiles take split K (partials, then a reduce launch); the large ones
+// never do (K is always whole).
 template <class G>
 hipError_t launch_small(hipStream_t s, const GemmParams &p, int epilogue) {
-    return p.splits > 1 ? launch_cfg<G, true>(s, p, epilogue)
-                        : launch_cfg<G, false>(s, p, epilogue);
+    if (p.splits == 1) return launch_mode<G, kWholeK>(s, p, epilogue);
+    const hipError_t e = launch_mode<G, kPartial>(s, p, epilogue);
+    return e != hipSuccess ? e : launch_mode<G, kReduce>(s, p, epilogue);
 }
 template <class G>
 hipError_t launch_large(hipStream_t s, const GemmParams &p, int epilogue) {
-    return p.splits > 1 ? hipErrorInvalidValue : launch_cfg<G, false>(s, p, epilogue);
+    return p.splits > 1 ? hipErrorInvalidValue : launch_mode<G, kWholeK>(s, p, epilogue);
 }
 
 }  // namespace
@@ -599,17 +611,10 @@ size_t gemm_workspace_bytes(const GemmPlan &g, int32_t M_max, int32_t N, int epi
     return tiles * g.splits * c.bw * c.bt * 4;
 }
 
-size_t gemm_counter_count(const GemmPlan &g, int32_t M_max, int32_t N, int epilogue) {
-    if (g.splits <= 1) return 0;
-    const CfgInfo &c = kCfgs[g.config];
-    const int bn = epilogue == 1 ? c.bw / 2 : c.bw;
-    return (size_t)((N + bn - 1) / bn) * ((M_max + c.bt - 1) / c.bt);
-}
-
 hipError_t launch_gemm(hipStream_t s, const bf16_t *A, int32_t lda, const bf16_t *W,
                        int32_t ldw, bf16_t *C, int32_t ldc, const int32_t *M_dev,
                        int32_t M_max, int32_t N, int32_t K, int epilogue, const GemmPlan &plan,
-                       float *partial, uint32_t *counter, const QkvEpilogue *qe) {
+                       float *partial, const QkvEpilogue *qe) {
     if (M_max <= 0 || N <= 0) return hipSuccess;
     if (epilogue == 2 && (!qe || qe->rope_cols % 64 || qe->vt_col0 % 64 ||
                           qe->rope_cols > qe->vt_col0 || (qe->rope_cols > 0 && !qe->pos) ||
@@ -618,8 +623,8 @@ hipError_t launch_gemm(hipStream_t s, const bf16_t *A, int32_t lda, const bf16_t
     if (K % KMULT != 0 || N % 64 != 0 || plan.config < 0 || plan.config >= kGemmConfigs ||
         plan.splits < 1 || plan.splits > K / KMULT || plan.splits > gemm_max_splits(plan.config))
         return hipErrorInvalidValue;
-    if (plan.splits > 1 && (!partial || !counter)) return hipErrorInvalidValue;
-    GemmParams p{A, lda, W, ldw, C, ldc, M_dev, M_max, N, K, plan.splits, partial, counter,
+    if (plan.splits > 1 && !partial) return hipErrorInvalidValue;
+    GemmParams p{A, lda, W, ldw, C, ldc, M_dev, M_max, N, K, plan.splits, partial,
                  epilogue == 2 ? *qe : QkvEpilogue{}};
     switch (plan.config) {
         case 0: return launch_small<CfgXS>(s, p, epilogue);

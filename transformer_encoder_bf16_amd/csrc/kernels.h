@@ -56,9 +56,8 @@ struct GemmPlan {
 GemmPlan plan_gemm(int32_t M_max, int32_t N, int32_t K, int epilogue);
 GemmPlan plan_gemm_tiles(int32_t M, int32_t N, int32_t K, int epilogue);
 int gemm_max_splits(int config);
-// float32 partial-tile bytes and tile counters a plan needs (0 when splits == 1)
+// float32 partial-tile bytes a plan needs (0 when splits == 1)
 size_t gemm_workspace_bytes(const GemmPlan &g, int32_t M_max, int32_t N, int epilogue);
-size_t gemm_counter_count(const GemmPlan &g, int32_t M_max, int32_t N, int epilogue);
 
 // Epilogue 2 (QKV projection): output columns [0, rope_cols) are heads of
 // 64 that are rotated (RoPE, rotate-half pairs (i, i+32), c/s = tab[pos][i])
@@ -77,11 +76,11 @@ struct QkvEpilogue {
 };
 
 // C = bf16(A W^T), epilogue 0 plain, 1 GeGLU (W has 2N rows), 2 QKV (`qe`).
-// With plan.splits > 1, `partial` and `counter` (zero-filled once) are required.
+// With plan.splits > 1, `partial` is required and two kernels are queued.
 hipError_t launch_gemm(hipStream_t s, const bf16_t *A, int32_t lda, const bf16_t *W,
                        int32_t ldw, bf16_t *C, int32_t ldc, const int32_t *M_dev,
                        int32_t M_max, int32_t N, int32_t K, int epilogue, const GemmPlan &plan,
-                       float *partial, uint32_t *counter, const QkvEpilogue *qe = nullptr);
+                       float *partial, const QkvEpilogue *qe = nullptr);
 
 hipError_t launch_rope(hipStream_t s, bf16_t *buf, int32_t ld, int32_t n_heads_rot,
                        const int32_t *count_dev, int32_t rows_max, const int32_t *pos,
