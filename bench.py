@@ -40,6 +40,19 @@ DOMINANT_KERNEL_SYMBOL = {
     "layernorm": "layernorm_kernel", "rope": "rope_kernel",
 }
 
+# HBM traffic of the dominant kernel, measured: per-launch FETCH_SIZE and
+# WRITE_SIZE (KiB) of the GeGLU up projection at mixed_16 from two
+# rocprofv3 --pmc runs of this script, each divided by what the same counter
+# reads per byte moved by a plain 1 GiB device copy (this script's
+# --copy-calibration-mib mode).  Commands and figures:
+# profiles/up_geglu_gemm_mixed_16_traffic.md.  The figure holds only for the
+# GEMM sources it was taken with (SHA-256 over k_gemm.hip, common.h,
+# kernels.h); after any change to them the traffic is reported as null.
+TRAFFIC = {"op": "up_geglu_gemm", "workload": "mixed_16", "fetch_kib": 53424.2,
+           "write_kib": 20756.2, "fetch_per_byte": 0.5000, "write_per_byte": 1.0000,
+           "sources_sha256": "f923591729c2a3adb748d583538057ac2cf1a079a84aae31610d92f3c1449211"}
+TRAFFIC_SOURCES = ("k_gemm.hip", "common.h", "kernels.h")
+
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense BF16 MFMA
 PEAK_HBM_GBS = 8000.0
 
@@ -54,7 +67,23 @@ def parse():
     p.add_argument("--profile-passes", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-rows", type=int, default=4)
+    p.add_argument("--copy-calibration-mib", type=int, default=0,
+                   help="only run a plain device-to-device copy of this many MiB three times "
+                        "(the reference for scaling HBM byte counters), then exit")
     return p.parse_args()
+
+
+def copy_calibration(mib):
+    """A plain copy of known size: reads and writes mib MiB per launch."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": n, "launches": 3}), flush=True)
 
 
 def op_table(enc, batch, mk, repeats):
@@ -84,6 +113,21 @@ def op_table(enc, batch, mk, repeats):
                                                                     v["calls"], sec)
         table[k] = row
     return table, tot / repeats
+
+
+def measured_traffic(op, workload):
+    """HBM bytes per launch of `op` from the recorded counters, or None."""
+    import hashlib
+    if op != TRAFFIC["op"] or workload != TRAFFIC["workload"]:
+        return None
+    h = hashlib.sha256()
+    for name in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, "transformer_encoder_bf16_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest() != TRAFFIC["sources_sha256"]:
+        return None
+    return round(TRAFFIC["fetch_kib"] * 1024 / TRAFFIC["fetch_per_byte"] +
+                 TRAFFIC["write_kib"] * 1024 / TRAFFIC["write_per_byte"])
 
 
 def cpu_baseline(cfg, batch, rows):
@@ -116,6 +160,10 @@ def main():
               f"sharded across GPUs in this build", file=sys.stderr)
         sys.exit(2)
     import torch
+    if args.copy_calibration_mib:
+        torch.cuda.set_device(0)
+        copy_calibration(args.copy_calibration_mib)
+        return
     from transformer_encoder_bf16_amd import binding
     from transformer_encoder_bf16_amd.inputs import MODEL, WEIGHT_SEED, WORKLOADS, make_batch
 
@@ -183,7 +231,7 @@ def main():
         roof = {"bound": "hbm", "achieved": round(d["_bytes"] / d["_sec"] / 1e9, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(dom, args.workload)
     roof["op"] = dom
     roof["kernel"] = DOMINANT_KERNEL_SYMBOL.get(dom, dom)
     roof["avg_launch_us"] = d["avg_launch_us"]

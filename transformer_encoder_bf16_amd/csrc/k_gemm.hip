@@ -9,23 +9,24 @@
 // K-contiguous.  The weight tile is the MFMA "A" operand (rows = output
 // features) and the token tile the "B" operand (columns = tokens), so each
 // lane of a 32x32 accumulator holds four consecutive output features of one
-// token and stores them with one 8-byte write.
+// token.
 //
 // One kernel template, several tile shapes (BW weight rows x BT tokens, K
 // steps of BK, waves in a WW x WT grid):
-//   - operands move global -> LDS with global_load_lds_dwordx4 (no VGPR
-//     staging) into a STAGES-deep ring.  Each step computes for only a few
-//     hundred cycles while a load takes thousands, so the large tiles use
-//     32-wide K steps and 4-8 stages to keep ~100 KB per CU in flight; each
-//     wave waits for its own loads with an explicit vmcnt and a barrier
-//     publishes the stage;
+//   - operands move HBM -> LDS with buffer_load_dwordx4 ... lds (no VGPR
+//     staging) into a STAGES-deep ring; each wave waits for its own loads
+//     with an explicit vmcnt and a bare barrier publishes the stage;
 //   - the 16-byte chunks of an LDS row are XOR-swizzled with the row's place
 //     in a 256-byte sweep of the 64 banks (measured: no bank conflicts),
 //     realised by choosing each lane's source address, since the DMA writes
 //     lanes contiguously;
+//   - fragment reads for the next 16-wide K step are issued before the
+//     MFMAs of the current one (two register buffers);
 //   - every output element is one chain of v_mfma_f32_32x32x16_bf16 over its
 //     K range, in K order, whatever the tile shape or K step: results do not
-//     depend on the tile shape or on where a token sits in its tile.
+//     depend on the tile shape or on where a token sits in its tile;
+//   - the output tile is assembled in LDS and written with 16-byte stores
+//     along whole row segments.
 //
 // Split-K (small M, where only a few weight tiles exist): the K range is cut
 // into S contiguous pieces (multiples of 64); one launch writes each piece's
@@ -39,6 +40,9 @@
 // rows n0.. of W (the GELU half), the last BW/2 rows are rows N+n0.. (the
 // gate half); each wave holds matching u and g fragments, so
 // h = bf16(GELU(u) * g) is formed from unrounded float32 u and g.
+//
+// QKV epilogue (epilogue 2): RoPE on the Q and K heads in registers and the
+// V columns stored transposed for attention (see QkvEpilogue).
 #include "kernels.h"
 
 namespace laya {
