@@ -67,6 +67,16 @@ def parse():
     p.add_argument("--profile-passes", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-rows", type=int, default=4)
+    p.add_argument("--protocol", action="store_true",
+                   help="the full measurement protocol over every workload (ABBA rounds of "
+                        "eager and graph calls, device timer, capture cost, per-op shares, "
+                        "roofline time, RoPE variant A/B, oracle timing); writes a results "
+                        "JSON to --protocol-out and prints a summary")
+    p.add_argument("--protocol-out", default="protocol_results.json")
+    p.add_argument("--protocol-warmup", type=int, default=20)
+    p.add_argument("--protocol-calls", type=int, default=100)
+    p.add_argument("--protocol-oracle-calls", type=int, default=3,
+                   help="oracle calls per workload in --protocol (0: skip the oracle)")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="only run a plain device-to-device copy of this many MiB three times "
                         "(the reference for scaling HBM byte counters), then exit")
@@ -153,6 +163,175 @@ def cpu_baseline(cfg, batch, rows):
                       f"by the token fraction"}
 
 
+def _host_calls(enc, batch, flags, n, sync):
+    out = []
+    for _ in range(n):
+        t = time.perf_counter()
+        enc.run(batch.ids, batch.lengths, markers=batch.markers, flags=flags)
+        sync()
+        out.append((time.perf_counter() - t) * 1e3)
+    return out
+
+
+def _summ(samples):
+    a = np.asarray(samples)
+    return {"p50_ms": round(float(np.percentile(a, 50)), 4),
+            "p95_ms": round(float(np.percentile(a, 95)), 4),
+            "calls_per_s": round(len(a) / (a.sum() / 1e3), 3)}
+
+
+def _metadata(enc, cfg):
+    import hashlib
+    import subprocess
+    import torch
+    from transformer_encoder_bf16_amd import binding
+    with open(binding.LIB_PATH, "rb") as f:
+        lib_sha = hashlib.sha256(f.read()).hexdigest()
+    try:
+        sha = subprocess.run(["git", "rev-parse", "HEAD"], cwd=ROOT, capture_output=True,
+                             text=True, timeout=10).stdout.strip() or None
+    except Exception:
+        sha = None
+    cpu = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), None)
+    except OSError:
+        pass
+    smt = None
+    try:
+        with open("/sys/devices/system/cpu/smt/active") as f:
+            smt = f.read().strip() == "1"
+    except OSError:
+        pass
+    n_tensors = 1 + 4 * (cfg["n_enc_layers"] + cfg["n_dec_layers"])
+    digests = [format(enc.weight_digest(t), "016x") for t in range(n_tensors)]
+    props = torch.cuda.get_device_properties(0)
+    return {"git_sha": sha, "library_sha256": lib_sha, "gpu": props.name,
+            "gpu_arch": getattr(props, "gcnArchName", None), "host_cpu": cpu,
+            "host_cores": os.cpu_count(), "smt": smt, "weight_fnv1a64": digests}
+
+
+def protocol(args):
+    """The measurement protocol over every workload.  Per workload: one
+    feasibility call (excluded, also the first graph capture), then rounds in
+    ABBA order (eager, graph, graph, eager), each with warmups and measured
+    calls timed on the host from the call to the completion sync (packing,
+    upload and sync included); a device timer (HIP events around resident
+    graph replays on the stream); the per-op table of one event-profiled
+    eager pass and the roofline time sum over op classes of max(FLOP/peak,
+    bytes/peak); the RoPE variants (fused into the QKV epilogue against the
+    standalone kernel) in ABBA order; and the CPU oracle."""
+    import torch
+    from transformer_encoder_bf16_amd import binding
+    from transformer_encoder_bf16_amd.inputs import ALL_WORKLOADS, MODEL, WEIGHT_SEED, make_batch
+
+    if not os.path.exists(binding.LIB_PATH):
+        from transformer_encoder_bf16_amd import build_lib
+        build_lib.build()
+    torch.cuda.set_device(0)
+    sync = torch.cuda.synchronize
+    enc = binding.Encoder(MODEL, seed=WEIGHT_SEED, device=0)
+    meta = _metadata(enc, MODEL)
+    meta["create_ms"] = round(enc.stats()["create_ms"], 1)
+    results = {"metric": METRIC, "protocol": {"warmup": args.protocol_warmup,
+                                              "calls": args.protocol_calls,
+                                              "order": ["eager", "graph", "graph", "eager"]},
+               "meta": meta, "workloads": {}}
+    stream = torch.cuda.current_stream()
+    for name, wl in ALL_WORKLOADS.items():
+        batch = make_batch(MODEL, wl)
+        res = {"B": batch.B, "S": batch.S, "T": batch.T,
+               "R": 0 if batch.markers is None else int(len(batch.markers)), "seed": wl.seed}
+        t = time.perf_counter()
+        enc.run(batch.ids, batch.lengths, markers=batch.markers)  # feasibility + capture
+        sync()
+        res["first_graph_call_ms"] = round((time.perf_counter() - t) * 1e3, 3)
+        res["capture_ms"] = round(enc.stats()["last_capture_ms"], 3)
+        rounds = []
+        for mode in ("eager", "graph", "graph", "eager"):
+            flags = binding.RUN_EAGER if mode == "eager" else 0
+            _host_calls(enc, batch, flags, args.protocol_warmup, sync)
+            samples = _host_calls(enc, batch, flags, args.protocol_calls, sync)
+            rounds.append({"mode": mode, **_summ(samples),
+                           "samples_ms": [round(x, 4) for x in samples]})
+        res["rounds"] = rounds
+        for mode in ("eager", "graph"):
+            all_s = [x for r in rounds if r["mode"] == mode for x in r["samples_ms"]]
+            res[f"{mode}_host"] = _summ(all_s)
+        # device timer: HIP events on the stream around resident graph replays
+        enc.run(batch.ids, batch.lengths, markers=batch.markers)
+        dev = []
+        for _ in range(args.protocol_calls):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            enc.run(batch.ids, batch.lengths, markers=batch.markers, flags=binding.RUN_RESIDENT)
+            e1.record(stream)
+            e1.synchronize()
+            dev.append(e0.elapsed_time(e1))
+        res["device_graph"] = {"p50_ms": round(float(np.percentile(dev, 50)), 4),
+                               "p95_ms": round(float(np.percentile(dev, 95)), 4)}
+        # per-op shares and the roofline time
+        table, pass_ms = op_table(enc, batch, batch.markers, 1)
+        t_roof = sum(max(v["_flops"] / (PEAK_BF16_TFLOPS * 1e12), v["_bytes"] / (PEAK_HBM_GBS * 1e9))
+                     for v in table.values())
+        res["profiled_eager_pass_ms"] = round(pass_ms, 4)
+        res["roofline_time_ms"] = round(t_roof * 1e3, 4)
+        res["graph_p50_over_roofline"] = round(res["graph_host"]["p50_ms"] / (t_roof * 1e3), 2)
+        res["ops"] = {k: {f: v for f, v in row.items() if not f.startswith("_")}
+                      for k, row in table.items()}
+        # RoPE variants, ABBA: fused, standalone, standalone, fused (graph replays)
+        ab = []
+        for variant in ("fused", "standalone", "standalone", "fused"):
+            flags = binding.RUN_ROPE_STANDALONE if variant == "standalone" else 0
+            enc.run(batch.ids, batch.lengths, markers=batch.markers, flags=flags)
+            sync()
+            _host_calls(enc, batch, flags | binding.RUN_RESIDENT, args.protocol_warmup, sync)
+            samples = _host_calls(enc, batch, flags | binding.RUN_RESIDENT,
+                                  args.protocol_calls, sync)
+            ab.append({"variant": variant, **_summ(samples)})
+        bits = {}
+        for variant, flags in (("fused", binding.RUN_EAGER),
+                               ("standalone", binding.RUN_EAGER | binding.RUN_ROPE_STANDALONE)):
+            out = enc.run(batch.ids, batch.lengths, markers=batch.markers, flags=flags)
+            sync()
+            bits[variant] = enc.hidden_bits(out)
+        res["rope_ab"] = {"rounds": ab,
+                          "bitwise_equal": bool(np.array_equal(bits["fused"], bits["standalone"]))}
+        if args.protocol_oracle_calls > 0:
+            res["oracle"] = oracle_timing(MODEL, batch, args.protocol_oracle_calls)
+        results["workloads"][name] = res
+        print(f"{name:14s} T={res['T']:5d} graph p50 {res['graph_host']['p50_ms']:8.3f} ms "
+              f"({res['graph_host']['calls_per_s']:8.1f} calls/s)  eager p50 "
+              f"{res['eager_host']['p50_ms']:8.3f}  device p50 {res['device_graph']['p50_ms']:8.3f}  "
+              f"roofline {res['roofline_time_ms']:7.3f} ms  capture {res['capture_ms']:7.1f} ms  "
+              f"rope fused/standalone p50 {ab[0]['p50_ms']:.3f}/{ab[1]['p50_ms']:.3f}", flush=True)
+    enc.close()
+    with open(args.protocol_out, "w") as f:
+        json.dump(results, f)
+    print(json.dumps({"protocol_out": args.protocol_out,
+                      "workloads": {k: {"graph_p50_ms": v["graph_host"]["p50_ms"],
+                                        "calls_per_s": v["graph_host"]["calls_per_s"],
+                                        "roofline_ms": v["roofline_time_ms"]}
+                                    for k, v in results["workloads"].items()}}), flush=True)
+
+
+def oracle_timing(cfg, batch, calls):
+    """The CPU oracle on the whole batch: one warm call, then `calls` timed."""
+    import oracle
+    w = oracle.Weights(cfg, 1)
+    o = oracle.Oracle(cfg, w)
+    o.forward(batch.ids[:1, :4], np.array([4], np.int32))  # widen weights (untimed)
+    o.forward(batch.ids, batch.lengths, markers=batch.markers)
+    ts = []
+    for _ in range(calls):
+        t = time.perf_counter()
+        o.forward(batch.ids, batch.lengths, markers=batch.markers)
+        ts.append((time.perf_counter() - t) * 1e3)
+    return {"calls": calls, "p50_ms": round(float(np.percentile(ts, 50)), 1),
+            "calls_per_s": round(calls / (sum(ts) / 1e3), 4), "cores": os.cpu_count()}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -163,6 +342,9 @@ def main():
     if args.copy_calibration_mib:
         torch.cuda.set_device(0)
         copy_calibration(args.copy_calibration_mib)
+        return
+    if args.protocol:
+        protocol(args)
         return
     from transformer_encoder_bf16_amd import binding
     from transformer_encoder_bf16_amd.inputs import MODEL, WEIGHT_SEED, WORKLOADS, make_batch

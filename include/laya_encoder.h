@@ -58,6 +58,10 @@ extern "C" {
 #define LAYA_RUN_RESIDENT 4u       /* rerun on the indices already uploaded by the previous
                                       run of the same (B, S, R): no packing, no upload;
                                       token_ids/lengths/markers are not read */
+#define LAYA_RUN_ROPE_STANDALONE 8u /* RoPE by its own kernel after the QKV projection
+                                      instead of in the projection's epilogue (the
+                                      pages' original step order; the two variants give
+                                      bitwise equal outputs and have separate graphs) */
 
 /* Model and limit configuration.  laya_config_init() fills the 421M-parameter
  * shape: vocab 50368, hidden 1024, 16 heads of 64, GeGLU inner width 2624,
@@ -173,7 +177,8 @@ int laya_encoder_create(const laya_config *cfg, uint64_t weight_seed, int device
  * queries, attention, output projection and FFN only for the R marker rows;
  * out->hidden is [R][hidden] in marker-list order (duplicates allowed).
  *
- * Without LAYA_RUN_EAGER the launch sequence for the shape key (B, S, R) is
+ * Without LAYA_RUN_EAGER the launch sequence for the shape key (B, S, R and
+ * the LAYA_RUN_ROPE_STANDALONE choice) is
  * captured once into a hipGraph (two eager warmups, then capture; the cost is
  * reported by laya_encoder_stats) and replayed on `stream` afterwards; the
  * kernels read T and the row layout from device memory, so one graph serves
@@ -225,6 +230,16 @@ int laya_encoder_weight(laya_encoder *enc, int32_t tensor_id, const void **dev,
                         int32_t *rows, int32_t *cols);
 
 int laya_encoder_stats(const laya_encoder *enc, laya_stats *stats);
+
+/* Diagnostic: fill every byte of the handle's workspace (activations,
+ * transposed V, split-K partials, index upload) with `byte` (0xFF makes every
+ * BF16 and float32 value a NaN), on `stream`, then synchronise.  A run after
+ * it must give bitwise the same output as before: no kernel may depend on
+ * stale workspace contents (the key-padding rows of a batch, the tiles past a
+ * row's end, the partial tiles of a previous call).  Captured graphs stay
+ * valid; the next non-resident run uploads its indices again.  Returns
+ * LAYA_E_INVALID for a NULL handle and LAYA_E_DEVICE on a HIP failure. */
+int laya_encoder_fill_workspace(laya_encoder *enc, void *stream, uint8_t byte);
 
 /* Per-op time of one eager pass (the pages' per-op share table of the
  * "profile_forward" tool, page "perf(model): exact Metal speed-ups of the

@@ -24,7 +24,7 @@ import pytest
 
 import oracle
 from tests.gpu_helpers import bits_of, ensure_built, report
-from transformer_encoder_bf16_amd.inputs import (MODEL, TINY, WEIGHT_SEED, WORKLOADS, make_batch,
+from transformer_encoder_bf16_amd.inputs import (ALL_WORKLOADS, MODEL, TINY, WEIGHT_SEED, WORKLOADS, make_batch,
                                                  random_batch)
 
 pytestmark = pytest.mark.gpu
@@ -114,9 +114,9 @@ def _run_bits(binding, enc, batch, flags=0, markers=None):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("name", list(WORKLOADS))
+@pytest.mark.parametrize("name", list(ALL_WORKLOADS))
 def test_workload_matches_oracle(binding, enc, orc, orc64, name):
-    wl = WORKLOADS[name]
+    wl = ALL_WORKLOADS[name]
     batch = make_batch(MODEL, wl)
     markers = batch.markers
     print(f"[{name}] B={batch.B} S={batch.S} T={batch.T} R={0 if markers is None else len(markers)}",
@@ -235,3 +235,51 @@ def test_empty_batch_and_invalid_args(binding, enc):
     a, _ = _run_bits(binding, enc, batch, binding.RUN_EAGER)
     b_, _ = _run_bits(binding, enc, batch, binding.RUN_EAGER)
     assert np.array_equal(a, b_)
+
+
+def test_configs_in_reverse_order_are_bitwise_equal(binding, enc):
+    """The five configs run in order, then in reverse order on the same handle
+    (reused workspace and graphs): every output is bitwise the same."""
+    batches = {n: make_batch(MODEL, WORKLOADS[n]) for n in WORKLOADS}
+    first = {n: _run_bits(binding, enc, b, 0, b.markers)[0] for n, b in batches.items()}
+    for n in reversed(list(batches)):
+        b = batches[n]
+        again, _ = _run_bits(binding, enc, b, 0, b.markers)
+        assert np.array_equal(again, first[n]), n
+
+
+@pytest.mark.parametrize("name", ["short_1", "short_3", "long_3", "marker_subset"])
+def test_nan_poisoned_workspace_changes_nothing(binding, enc, name):
+    """Every workspace byte set to 0xFF (NaN in every BF16 and float32 slot)
+    before an eager run and before a graph replay: the outputs are bitwise
+    those of a clean run, so no kernel reads stale workspace contents."""
+    batch = make_batch(MODEL, WORKLOADS[name])
+    clean, _ = _run_bits(binding, enc, batch, binding.RUN_EAGER, batch.markers)
+    enc.fill_workspace(0xFF)
+    eager, _ = _run_bits(binding, enc, batch, binding.RUN_EAGER, batch.markers)
+    assert np.array_equal(eager, clean)
+    graph_clean, _ = _run_bits(binding, enc, batch, 0, batch.markers)
+    enc.fill_workspace(0xFF)
+    graph, _ = _run_bits(binding, enc, batch, 0, batch.markers)
+    assert np.array_equal(graph, graph_clean) and np.array_equal(graph, clean)
+
+
+@pytest.mark.parametrize("name", ["short_1", "long_3", "marker_subset"])
+def test_rope_variants_are_bitwise_equal(binding, enc, name):
+    """RoPE in the QKV projection's epilogue (the default) and RoPE by its own
+    kernel after the projection give bitwise equal outputs, eager and graph."""
+    batch = make_batch(MODEL, WORKLOADS[name])
+    fused, _ = _run_bits(binding, enc, batch, binding.RUN_EAGER, batch.markers)
+    alone, _ = _run_bits(binding, enc, batch, binding.RUN_EAGER | binding.RUN_ROPE_STANDALONE,
+                         batch.markers)
+    alone_g, _ = _run_bits(binding, enc, batch, binding.RUN_ROPE_STANDALONE, batch.markers)
+    fused_g, _ = _run_bits(binding, enc, batch, 0, batch.markers)
+    assert np.array_equal(fused, alone)
+    assert np.array_equal(alone_g, alone) and np.array_equal(fused_g, fused)
+
+
+def test_unknown_run_flags_are_rejected(binding, enc):
+    batch = make_batch(MODEL, WORKLOADS["short_1"])
+    with pytest.raises(binding.LayaError) as ei:
+        enc.run(batch.ids, batch.lengths, flags=64)
+    assert ei.value.code == binding.LAYA_E_INVALID

@@ -27,6 +27,7 @@ LAYA_E_ABI = -6
 RUN_EAGER = 1
 RUN_CAPTURE_LAYERS = 2
 RUN_RESIDENT = 4
+RUN_ROPE_STANDALONE = 8
 
 ERROR_NAMES = {
     LAYA_E_INVALID: "LAYA_E_INVALID", LAYA_E_UNSUPPORTED: "LAYA_E_UNSUPPORTED",
@@ -40,7 +41,7 @@ EXPORTS = [
     "laya_encoder_create", "laya_encoder_run", "laya_encoder_destroy",
     "laya_encoder_last_error", "laya_last_error", "laya_encoder_layer_output",
     "laya_encoder_weight_digest", "laya_encoder_weight", "laya_encoder_stats",
-    "laya_encoder_profile", "laya_rope_table", "laya_memcpy", "laya_op_gather", "laya_op_layernorm", "laya_op_gemm",
+    "laya_encoder_profile", "laya_encoder_fill_workspace", "laya_rope_table", "laya_memcpy", "laya_op_gather", "laya_op_layernorm", "laya_op_gemm",
     "laya_op_gemm_qkv", "laya_op_rope", "laya_op_attention",
 ]
 
@@ -126,6 +127,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         "laya_encoder_weight": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.POINTER(_P), _I32P,
                                                _I32P]),
         "laya_encoder_stats": (ctypes.c_int, [_P, ctypes.POINTER(Stats)]),
+        "laya_encoder_fill_workspace": (ctypes.c_int, [_P, _P, ctypes.c_uint8]),
         "laya_encoder_profile": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32,
                                                 _P, ctypes.c_int32, ctypes.POINTER(OpTime),
                                                 ctypes.c_int32, _I32P,
@@ -331,6 +333,12 @@ class Encoder:
             res[a.name.decode()] = {"calls": a.calls, "ms": a.total_ms, "flops": a.flops,
                                     "bytes": a.bytes}
         return res, tot.value
+
+    def fill_workspace(self, byte: int, stream: Optional[int] = None):
+        """Diagnostic: every workspace byte set to `byte` (0xFF: NaN everywhere)."""
+        st = current_stream() if stream is None else stream
+        _check(self.lib.laya_encoder_fill_workspace(self.handle, st, byte),
+               "laya_encoder_fill_workspace", self.handle)
 
     def stats(self) -> dict:
         s = Stats()

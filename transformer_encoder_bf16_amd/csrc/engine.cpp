@@ -341,7 +341,7 @@ struct laya_encoder {
     bool upload_pending = false;
     hipStream_t cap_stream = nullptr;
 
-    std::map<std::tuple<int, int, int>, GraphEntry> graphs;
+    std::map<std::tuple<int, int, int, int>, GraphEntry> graphs;  // (B, S, R, variant)
 
     // per-layer captures
     void *cap_mem = nullptr;
@@ -382,6 +382,7 @@ struct RunShape {
     int B, S, R;
     int T;  // actual tokens (host value; used only for captures in eager mode)
     bool capture_layers;
+    bool rope_standalone = false;  // RoPE by its own kernel instead of the QKV epilogue
     // host-side algorithmic counts, used only when profiling
     double pairs_global = 0, pairs_local = 0, pairs_subset = 0;
 };
@@ -595,11 +596,16 @@ int record(laya_encoder *enc, hipStream_t s, const RunShape &rs, Profiler *prof 
         }
         pending = false;
         if (!subset) {
-            // Q, K rotated in the epilogue; V stored transposed for attention
-            const laya::QkvEpilogue qe{pos, ctab, stab, 2 * H, 2 * H, enc->vt, enc->ldvt, vtok};
+            // Q, K rotated in the epilogue (or by the RoPE kernel after it); V
+            // stored transposed for attention
+            const int rope_cols = rs.rope_standalone ? 0 : 2 * H;
+            const laya::QkvEpilogue qe{pos, ctab, stab, rope_cols, 2 * H, enc->vt, enc->ldvt, vtok};
             L_OP(OP_QKV, gemm_fl(T, 3 * H, H), gemm_by(T, 3 * H, 3 * H, H),
                  laya::launch_gemm(s, enc->nrm, H, Wqkv, H, enc->qkv, 3 * H, T_dev, Tmax, 3 * H,
                                    H, 2, plans.qkv, gp, &qe));
+            if (rs.rope_standalone)
+                L_OP(OP_ROPE, 0, 2 * T * 2 * H * b2,
+                     laya::launch_rope(s, enc->qkv, 3 * H, 2 * nh, T_dev, Tmax, pos, ctab, stab));
             const laya::AttnParams ap{enc->qkv, 3 * H, enc->qkv + H, 3 * H, k_bytes(3 * H),
                                       enc->vt, enc->ldvt, vt_bytes, enc->att, H, blk, nblk,
                                       ml.nblk_full_max, pos, nh, half};
@@ -632,18 +638,27 @@ int record(laya_encoder *enc, hipStream_t s, const RunShape &rs, Profiler *prof 
         } else {
             // keys/values for every token, queries only for the marker rows
             const int Ri = rs.R;
-            const laya::QkvEpilogue qe_kv{pos, ctab, stab, H, H, enc->vt, enc->ldvt, vtok};
+            const laya::QkvEpilogue qe_kv{pos,      ctab,          stab,
+                                          rs.rope_standalone ? 0 : H, H, enc->vt,
+                                          enc->ldvt, vtok};
             L_OP(OP_KV, gemm_fl(T, 2 * H, H), gemm_by(T, 2 * H, 2 * H, H),
                  laya::launch_gemm(s, enc->nrm, H, Wqkv + (size_t)H * H, H, enc->qkv, 2 * H,
                                    T_dev, Tmax, 2 * H, H, 2, plans.kv_sub, gp, &qe_kv));
+            if (rs.rope_standalone)
+                L_OP(OP_ROPE, 0, 2 * T * H * b2,
+                     laya::launch_rope(s, enc->qkv, 2 * H, nh, T_dev, Tmax, pos, ctab, stab));
             L_OP(OP_ROW_GATHER, 0, 2 * R * H * b2,
                  laya::launch_gather_rows(s, enc->nrm, H, mrk_tok, Ri, H, enc->n_sub, H));
             L_OP(OP_ROW_GATHER, 0, 2 * R * H * b2,
                  laya::launch_gather_rows(s, xr, H, mrk_tok, Ri, H, enc->x_sub, H));
-            const laya::QkvEpilogue qe_q{mrk_pos, ctab, stab, H, H, nullptr, 0, nullptr};
+            const laya::QkvEpilogue qe_q{mrk_pos, ctab, stab, rs.rope_standalone ? 0 : H, H,
+                                         nullptr, 0, nullptr};
             L_OP(OP_Q, gemm_fl(R, H, H), gemm_by(R, H, H, H),
                  laya::launch_gemm(s, enc->n_sub, H, Wqkv, H, enc->q_sub, H, nullptr, Ri, H, H,
                                    2, plans.q_sub, gp, &qe_q));
+            if (rs.rope_standalone)
+                L_OP(OP_ROPE, 0, 2 * R * H * b2,
+                     laya::launch_rope(s, enc->q_sub, H, nh, nullptr, Ri, mrk_pos, ctab, stab));
             const laya::AttnParams ap{enc->q_sub, H, enc->qkv, 2 * H, k_bytes(2 * H),
                                       enc->vt, enc->ldvt, vt_bytes, enc->att, H, blk_s, nblk_s,
                                       ml.nblk_sub_max, mrk_pos, nh, half};
@@ -929,6 +944,9 @@ int laya_encoder_run(laya_encoder *enc, void *stream, const int32_t *ids,
     if (!enc) return set_global_error(LAYA_E_INVALID, "handle is NULL");
     if (enc->poisoned) return fail(enc, LAYA_E_POISONED, "handle poisoned by an earlier device failure");
     if (!out) return fail(enc, LAYA_E_INVALID, "out is NULL");
+    if (flags & ~(LAYA_RUN_EAGER | LAYA_RUN_CAPTURE_LAYERS | LAYA_RUN_RESIDENT |
+                  LAYA_RUN_ROPE_STANDALONE))
+        return fail(enc, LAYA_E_INVALID, "unknown run flags");
     const bool resident = (flags & LAYA_RUN_RESIDENT) != 0;
     std::string why;
     int rc = LAYA_OK;
@@ -1014,7 +1032,9 @@ int laya_encoder_run(laya_encoder *enc, void *stream, const int32_t *ids,
 
     const bool capture = (flags & LAYA_RUN_CAPTURE_LAYERS) != 0;
     const bool eager = capture || (flags & LAYA_RUN_EAGER) != 0;
+    const bool rope_sa = (flags & LAYA_RUN_ROPE_STANDALONE) != 0;
     RunShape rs{B, S, R, T, capture};
+    rs.rope_standalone = rope_sa;
     if (capture) {
         int r2 = ensure_captures(enc);
         if (r2 != LAYA_OK) return r2;
@@ -1026,11 +1046,12 @@ int laya_encoder_run(laya_encoder *enc, void *stream, const int32_t *ids,
         enc->stats.launches_last_run = enc->launches;
         enc->have_caps = capture;
     } else {
-        auto key = std::make_tuple((int)B, (int)S, (int)R);
+        auto key = std::make_tuple((int)B, (int)S, (int)R, rope_sa ? 1 : 0);
         auto it = enc->graphs.find(key);
         if (it == enc->graphs.end()) {
             auto t0 = std::chrono::steady_clock::now();
             RunShape warm{B, S, R, T, false};
+            warm.rope_standalone = rope_sa;
             for (int w = 0; w < 2; ++w) {
                 int r2 = record(enc, s, warm);
                 if (r2 != LAYA_OK) return r2;
@@ -1133,6 +1154,21 @@ int laya_encoder_weight_digest(laya_encoder *enc, int32_t tid, uint64_t *fnv) {
 int laya_encoder_stats(const laya_encoder *enc, laya_stats *st) {
     if (!enc || !st) return set_global_error(LAYA_E_INVALID, "NULL argument");
     *st = enc->stats;
+    return LAYA_OK;
+}
+
+int laya_encoder_fill_workspace(laya_encoder *enc, void *stream, uint8_t byte) {
+    if (!enc) return set_global_error(LAYA_E_INVALID, "handle is NULL");
+    if (enc->poisoned) return fail(enc, LAYA_E_POISONED, "handle poisoned by an earlier device failure");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    HIPCHK(hipSetDevice(enc->device));
+    if (enc->upload_pending) {
+        HIPCHK(hipEventSynchronize(enc->upload_done));
+        enc->upload_pending = false;
+    }
+    HIPCHK(hipMemsetAsync(enc->ws, byte, enc->ws_bytes, s));
+    HIPCHK(hipStreamSynchronize(s));
+    enc->have_upload = false;  // the index upload is gone with the rest
     return LAYA_OK;
 }
 

@@ -87,6 +87,23 @@ WORKLOADS = {
     "marker_subset": Workload("marker_subset", 8, 187, 187, 187, 41, 12),
 }
 
+# Further shapes the pages time: long_1 (one 464-token request, the H800
+# comparison table of "Run Laya encoder and decision layers on CUDA") and a
+# set of five single-request inputs (the recipe benchmark of the same page,
+# section CUDA-event timings and reproduction, which does not list their
+# lengths: here one request at each single-row length the pages use, 48, 64,
+# 187, 464 and 512 tokens).
+EXTRA_WORKLOADS = {
+    "long_1": Workload("long_1", 1, 464, 464, 464, 17),
+    "b1_48": Workload("b1_48", 1, 48, 48, 48, 51),
+    "b1_64": Workload("b1_64", 1, 64, 64, 64, 52),
+    "b1_187": Workload("b1_187", 1, 187, 187, 187, 53),
+    "b1_464": Workload("b1_464", 1, 464, 464, 464, 54),
+    "b1_512": Workload("b1_512", 1, 512, 512, 512, 55),
+}
+B1_SET = ("b1_48", "b1_64", "b1_187", "b1_464", "b1_512")
+ALL_WORKLOADS = {**WORKLOADS, **EXTRA_WORKLOADS}
+
 
 @dataclass
 class Batch:
