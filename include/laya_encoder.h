@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define LAYA_ABI_VERSION 2
+#define LAYA_ABI_VERSION 3
 
 #define LAYA_OK 0
 #define LAYA_E_INVALID -1     /* bad ids, lengths, markers, sizes, NULL pointers */
@@ -51,6 +51,9 @@ extern "C" {
 #define LAYA_E_DEVICE -4      /* a HIP call failed; the handle is poisoned */
 #define LAYA_E_POISONED -5    /* the handle saw a device failure earlier */
 #define LAYA_E_ABI -6         /* laya_config.abi_version != LAYA_ABI_VERSION */
+#define LAYA_E_BUSY -7        /* request queue full */
+#define LAYA_E_TIMEOUT -8     /* request deadline passed before it could run */
+#define LAYA_E_CANCELLED -9   /* request dropped because its queue was destroyed */
 
 /* laya_encoder_run flags */
 #define LAYA_RUN_EAGER 1u          /* launch kernels directly instead of replaying a graph */
@@ -85,6 +88,9 @@ typedef struct laya_config {
     int32_t max_batch;     /* <= 16 */
     int32_t max_seq;       /* <= 512; also the number of rotary-table positions */
     int32_t max_markers;   /* <= 2048 */
+    int32_t max_graphs;    /* captured graphs kept (LRU over shape keys), >= 1; 4 by default */
+    int32_t workspace_budget_mib; /* create fails with LAYA_E_NOMEM if the workspace needs more;
+                                     512 by default */
 } laya_config;
 
 /* Device-resident result of a run.  Owned by the handle; valid until the next
@@ -100,7 +106,8 @@ typedef struct laya_output {
 typedef struct laya_stats {
     double create_ms;        /* weights generated, tables built, workspace allocated */
     double last_capture_ms;  /* last graph miss: 2 eager warmups + capture + instantiate */
-    int32_t graphs_cached;   /* instantiated graphs held by the handle */
+    int32_t graphs_cached;   /* instantiated graphs held by the handle (<= max_graphs) */
+    int32_t graph_evictions; /* graphs destroyed to make room for a new shape */
     int32_t launches_last_run; /* kernel launches of the last eager run (or captured graph) */
     int64_t weight_bytes;    /* device bytes of resident weights */
     int64_t workspace_bytes; /* device bytes of the activation workspace */
@@ -240,6 +247,63 @@ int laya_encoder_stats(const laya_encoder *enc, laya_stats *stats);
  * valid; the next non-resident run uploads its indices again.  Returns
  * LAYA_E_INVALID for a NULL handle and LAYA_E_DEVICE on a HIP failure. */
 int laya_encoder_fill_workspace(laya_encoder *enc, void *stream, uint8_t byte);
+
+/* The handle's configuration (as given to laya_encoder_create).  Host only. */
+int laya_encoder_config(const laya_encoder *enc, laya_config *out);
+
+/* LAYA_OK while the handle can run, LAYA_E_POISONED after a device failure
+ * (the docs page's health check: a native failure stops this executor,
+ * "Laya native CUDA worker", section Start and check).  Host only. */
+int laya_encoder_health(const laya_encoder *enc);
+
+/* Diagnostic for testing failure handling: marks the handle as if a device
+ * call had failed (every later call returns LAYA_E_POISONED, health reports
+ * it); nothing runs on the device. */
+int laya_encoder_inject_failure(laya_encoder *enc);
+
+/* ---------------------------------------------------------------------------
+ * Serial request queue (the docs page's serving model, "Laya native CUDA
+ * worker", section Architecture: one GPU worker runs complete requests one
+ * at a time, in order; the queue holds a bounded number of requests and
+ * refuses more; a deadline counts queueing and upload; no cross-request
+ * batching).  The queue owns a worker thread with its own HIP stream; while
+ * a queue exists, the caller must not run the handle directly.
+ * ------------------------------------------------------------------------- */
+typedef struct laya_queue laya_queue;
+
+/* capacity: requests waiting (not counting the one running), >= 1 (the
+ * pages use 32); deadline_ms > 0: a request that has not started within
+ * deadline_ms of its submission fails with LAYA_E_TIMEOUT (the pages use
+ * 30000).  LAYA_E_INVALID for bad arguments, LAYA_E_POISONED if the handle
+ * already failed, LAYA_E_DEVICE if the worker's stream cannot be made. */
+int laya_queue_create(laya_encoder *enc, int32_t capacity, double deadline_ms,
+                      laya_queue **out);
+
+/* Validates and copies the request (host arrays as for laya_encoder_run; the
+ * caller may free them on return) and queues it.  out_host: caller-owned host
+ * memory of out_cap bytes that receives the BF16 hidden states ([T or R]
+ * [hidden]); it must stay valid until laya_queue_wait returns for the ticket.
+ * Returns LAYA_E_INVALID (bad request or out_cap too small), LAYA_E_BUSY
+ * (capacity requests already waiting), LAYA_E_POISONED (the executor has
+ * stopped); *ticket identifies the request otherwise. */
+int laya_queue_submit(laya_queue *q, const int32_t *token_ids, const int32_t *lengths,
+                      int32_t B, int32_t S, const int32_t *markers, int32_t R, void *out_host,
+                      size_t out_cap, uint64_t *ticket);
+
+/* Blocks until the request is done and returns its status: LAYA_OK (out_host
+ * filled, *rows set), LAYA_E_TIMEOUT, LAYA_E_POISONED (the executor stopped
+ * before or while it ran), LAYA_E_DEVICE (it failed on the device; the
+ * executor stops), LAYA_E_CANCELLED.  *latency_ms (optional): submission to
+ * completion.  A ticket can be waited for once; LAYA_E_INVALID otherwise. */
+int laya_queue_wait(laya_queue *q, uint64_t ticket, int32_t *rows, double *latency_ms);
+
+/* LAYA_OK while the worker can serve, LAYA_E_POISONED once it has stopped. */
+int laya_queue_health(const laya_queue *q);
+
+/* Stops the worker after the running request; requests still waiting fail
+ * with LAYA_E_CANCELLED.  Waits on the worker thread.  No laya_queue_wait may
+ * be in progress on another thread when it is called. */
+int laya_queue_destroy(laya_queue *q);
 
 /* Per-op time of one eager pass (the pages' per-op share table of the
  * "profile_forward" tool, page "perf(model): exact Metal speed-ups of the

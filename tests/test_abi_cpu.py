@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol(lib):
     assert declared == set(b.EXPORTS)
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.laya_abi_version() == b.LAYA_ABI_VERSION == 2
+    assert lib.laya_abi_version() == b.LAYA_ABI_VERSION == 3
 
 
 def test_default_config_is_the_model(lib):
@@ -55,6 +55,8 @@ def test_valid_configs(lib, cfg):
     (dict(window=127), b.LAYA_E_UNSUPPORTED),
     (dict(vocab=0), b.LAYA_E_INVALID),
     (dict(ln_eps=0.0), b.LAYA_E_INVALID),
+    (dict(max_graphs=0), b.LAYA_E_INVALID),
+    (dict(workspace_budget_mib=0), b.LAYA_E_INVALID),
 ])
 def test_invalid_configs(lib, change, code):
     cfg = dict(MODEL)
@@ -126,3 +128,13 @@ def test_create_without_gpu_fails_cleanly(lib):
     assert rc == b.LAYA_E_DEVICE
     assert not h.value
     assert lib.laya_encoder_destroy(None) == b.LAYA_OK
+
+
+def test_queue_and_health_reject_null_handles(lib):
+    q = ctypes.c_void_p()
+    assert lib.laya_queue_create(None, 32, 30000.0, ctypes.byref(q)) == b.LAYA_E_INVALID
+    assert lib.laya_queue_health(None) == b.LAYA_E_INVALID
+    assert lib.laya_queue_wait(None, 1, None, None) == b.LAYA_E_INVALID
+    assert lib.laya_queue_destroy(None) == b.LAYA_OK
+    assert lib.laya_encoder_health(None) == b.LAYA_E_INVALID
+    assert lib.laya_encoder_inject_failure(None) == b.LAYA_E_INVALID

@@ -16,7 +16,7 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liblaya_encoder.so")
 
-LAYA_ABI_VERSION = 2
+LAYA_ABI_VERSION = 3
 LAYA_OK = 0
 LAYA_E_INVALID = -1
 LAYA_E_UNSUPPORTED = -2
@@ -24,6 +24,9 @@ LAYA_E_NOMEM = -3
 LAYA_E_DEVICE = -4
 LAYA_E_POISONED = -5
 LAYA_E_ABI = -6
+LAYA_E_BUSY = -7
+LAYA_E_TIMEOUT = -8
+LAYA_E_CANCELLED = -9
 RUN_EAGER = 1
 RUN_CAPTURE_LAYERS = 2
 RUN_RESIDENT = 4
@@ -32,7 +35,8 @@ RUN_ROPE_STANDALONE = 8
 ERROR_NAMES = {
     LAYA_E_INVALID: "LAYA_E_INVALID", LAYA_E_UNSUPPORTED: "LAYA_E_UNSUPPORTED",
     LAYA_E_NOMEM: "LAYA_E_NOMEM", LAYA_E_DEVICE: "LAYA_E_DEVICE",
-    LAYA_E_POISONED: "LAYA_E_POISONED", LAYA_E_ABI: "LAYA_E_ABI",
+    LAYA_E_POISONED: "LAYA_E_POISONED", LAYA_E_ABI: "LAYA_E_ABI", LAYA_E_BUSY: "LAYA_E_BUSY",
+    LAYA_E_TIMEOUT: "LAYA_E_TIMEOUT", LAYA_E_CANCELLED: "LAYA_E_CANCELLED",
 }
 
 # Every symbol the header declares (checked by the CPU tests).
@@ -41,7 +45,9 @@ EXPORTS = [
     "laya_encoder_create", "laya_encoder_run", "laya_encoder_destroy",
     "laya_encoder_last_error", "laya_last_error", "laya_encoder_layer_output",
     "laya_encoder_weight_digest", "laya_encoder_weight", "laya_encoder_stats",
-    "laya_encoder_profile", "laya_encoder_fill_workspace", "laya_rope_table", "laya_memcpy", "laya_op_gather", "laya_op_layernorm", "laya_op_gemm",
+    "laya_encoder_profile", "laya_encoder_fill_workspace", "laya_encoder_config",
+    "laya_encoder_health", "laya_encoder_inject_failure", "laya_queue_create", "laya_queue_submit",
+    "laya_queue_wait", "laya_queue_health", "laya_queue_destroy", "laya_rope_table", "laya_memcpy", "laya_op_gather", "laya_op_layernorm", "laya_op_gemm",
     "laya_op_gemm_qkv", "laya_op_rope", "laya_op_attention",
 ]
 
@@ -62,6 +68,7 @@ class Config(ctypes.Structure):
         ("theta_global", ctypes.c_float), ("theta_local", ctypes.c_float),
         ("ln_eps", ctypes.c_float), ("max_batch", ctypes.c_int32),
         ("max_seq", ctypes.c_int32), ("max_markers", ctypes.c_int32),
+        ("max_graphs", ctypes.c_int32), ("workspace_budget_mib", ctypes.c_int32),
     ]
 
     @classmethod
@@ -87,7 +94,8 @@ class OpTime(ctypes.Structure):
 
 class Stats(ctypes.Structure):
     _fields_ = [("create_ms", ctypes.c_double), ("last_capture_ms", ctypes.c_double),
-                ("graphs_cached", ctypes.c_int32), ("launches_last_run", ctypes.c_int32),
+                ("graphs_cached", ctypes.c_int32), ("graph_evictions", ctypes.c_int32),
+                ("launches_last_run", ctypes.c_int32),
                 ("weight_bytes", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64)]
 
 
@@ -128,6 +136,18 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
                                                _I32P]),
         "laya_encoder_stats": (ctypes.c_int, [_P, ctypes.POINTER(Stats)]),
         "laya_encoder_fill_workspace": (ctypes.c_int, [_P, _P, ctypes.c_uint8]),
+        "laya_encoder_config": (ctypes.c_int, [_P, ctypes.POINTER(Config)]),
+        "laya_encoder_health": (ctypes.c_int, [_P]),
+        "laya_encoder_inject_failure": (ctypes.c_int, [_P]),
+        "laya_queue_create": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.c_double,
+                                             ctypes.POINTER(_P)]),
+        "laya_queue_submit": (ctypes.c_int, [_P, _P, _P, ctypes.c_int32, ctypes.c_int32, _P,
+                                             ctypes.c_int32, _P, ctypes.c_size_t,
+                                             ctypes.POINTER(ctypes.c_uint64)]),
+        "laya_queue_wait": (ctypes.c_int, [_P, ctypes.c_uint64, _I32P,
+                                           ctypes.POINTER(ctypes.c_double)]),
+        "laya_queue_health": (ctypes.c_int, [_P]),
+        "laya_queue_destroy": (ctypes.c_int, [_P]),
         "laya_encoder_profile": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32,
                                                 _P, ctypes.c_int32, ctypes.POINTER(OpTime),
                                                 ctypes.c_int32, _I32P,
@@ -340,6 +360,15 @@ class Encoder:
         _check(self.lib.laya_encoder_fill_workspace(self.handle, st, byte),
                "laya_encoder_fill_workspace", self.handle)
 
+    def health(self) -> int:
+        """LAYA_OK, or LAYA_E_POISONED once a device failure stopped the handle."""
+        return self.lib.laya_encoder_health(self.handle)
+
+    def inject_failure(self):
+        """Diagnostic: mark the handle failed (no device work)."""
+        _check(self.lib.laya_encoder_inject_failure(self.handle), "laya_encoder_inject_failure",
+               self.handle)
+
     def stats(self) -> dict:
         s = Stats()
         _check(self.lib.laya_encoder_stats(self.handle, ctypes.byref(s)), "laya_encoder_stats")
@@ -404,3 +433,59 @@ def op_attention(q, k, vt, vt_col0, o, n_heads: int, row_off, q_tok=None,
                                     _ptr(ro), len(ro) - 1, _ptr(qt),
                                     0 if qt is None else len(qt), half_window),
            "laya_op_attention")
+
+
+class Queue:
+    """The serial request queue over an Encoder (laya_queue_*): one worker
+    runs whole requests in order; submit() copies a request and returns a
+    ticket, wait() returns (status, hidden BF16 bits [rows, hidden], latency_ms)."""
+
+    def __init__(self, enc: "Encoder", capacity: int = 32, deadline_ms: float = 30000.0):
+        self.lib = load()
+        self.enc = enc
+        self.hidden = enc.cfg["hidden"] if hasattr(enc, "cfg") else None
+        h = _P()
+        _check(self.lib.laya_queue_create(enc.handle, capacity, deadline_ms, ctypes.byref(h)),
+               "laya_queue_create")
+        self.handle = h
+        self._bufs = {}
+
+    def submit(self, ids, lengths, markers=None, hidden: Optional[int] = None) -> int:
+        """Queue one request; returns its ticket.  Raises LayaError (e.g.
+        LAYA_E_BUSY when the queue is full)."""
+        ids = _i32(ids)
+        lengths = _i32(lengths)
+        mk = None if markers is None else _i32(markers).reshape(-1, 2)
+        B, S = ids.shape
+        R = 0 if mk is None else mk.shape[0]
+        rows = R if R else int(lengths.sum())
+        hid = hidden or self.hidden
+        buf = np.empty((rows, hid), dtype=np.uint16)
+        t = ctypes.c_uint64()
+        rc = self.lib.laya_queue_submit(self.handle, _ptr(ids), _ptr(lengths), B, S, _ptr(mk), R,
+                                        buf.ctypes.data, buf.nbytes, ctypes.byref(t))
+        if rc != LAYA_OK:
+            raise LayaError(rc, "laya_queue_submit")
+        self._bufs[t.value] = (buf, ids, lengths, mk)
+        return t.value
+
+    def wait(self, ticket: int):
+        rows = ctypes.c_int32()
+        lat = ctypes.c_double()
+        rc = self.lib.laya_queue_wait(self.handle, ticket, ctypes.byref(rows), ctypes.byref(lat))
+        buf = self._bufs.pop(ticket, (None,))[0]
+        return rc, (buf[:rows.value] if rc == LAYA_OK else None), lat.value
+
+    def health(self) -> int:
+        return self.lib.laya_queue_health(self.handle)
+
+    def close(self):
+        if self.handle:
+            self.lib.laya_queue_destroy(self.handle)
+            self.handle = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()

@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "liblaya_encoder.so")
 
-SOURCES = ["k_elementwise.hip", "k_gemm.hip", "k_attention.hip", "engine.cpp"]
+SOURCES = ["k_elementwise.hip", "k_gemm.hip", "k_attention.hip", "engine.cpp", "queue.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

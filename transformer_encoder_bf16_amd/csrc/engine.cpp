@@ -167,6 +167,7 @@ int config_check(const laya_config *c, std::string *why) {
     if (c->vocab <= 0 || c->hidden <= 0 || c->n_heads <= 0 || c->head_dim <= 0 || c->ffn <= 0 ||
         c->n_enc_layers <= 0 || c->n_dec_layers <= 0 || c->global_every <= 0 || c->window < 0 ||
         c->max_batch <= 0 || c->max_seq <= 0 || c->max_markers < 0 || !(c->ln_eps > 0.f) ||
+        c->max_graphs <= 0 || c->workspace_budget_mib <= 0 ||
         !(c->theta_global > 1.f) || !(c->theta_local > 1.f)) {
         *why = "non-positive size or parameter in config";
         return LAYA_E_INVALID;
@@ -269,6 +270,7 @@ struct GraphEntry {
     hipGraph_t graph = nullptr;
     hipGraphExec_t exec = nullptr;
     int launches = 0;
+    uint64_t last_used = 0;  // LRU tick
 };
 
 // Offsets (in int32) of the per-run index upload for shape key (B, S, R).
@@ -342,6 +344,7 @@ struct laya_encoder {
     hipStream_t cap_stream = nullptr;
 
     std::map<std::tuple<int, int, int, int>, GraphEntry> graphs;  // (B, S, R, variant)
+    uint64_t graph_tick = 0;
 
     // per-layer captures
     void *cap_mem = nullptr;
@@ -746,6 +749,8 @@ void laya_config_init(laya_config *c) {
     c->max_batch = 16;
     c->max_seq = 512;
     c->max_markers = 2048;
+    c->max_graphs = 4;
+    c->workspace_budget_mib = 512;
 }
 
 const char *laya_last_error(void) { return g_last_error.c_str(); }
@@ -884,6 +889,9 @@ int laya_encoder_create(const laya_config *cfg, uint64_t seed, int device, laya_
     const size_t gp_off = wsz;
     wsz += al(gp_bytes);
     enc->ws_bytes = wsz;
+    if (wsz > (size_t)c.workspace_budget_mib << 20)
+        return bail(set_global_error(LAYA_E_NOMEM, "workspace of " + std::to_string(wsz >> 20) +
+                                                       " MiB exceeds workspace_budget_mib"));
     if (hipMalloc(&enc->ws, wsz) != hipSuccess)
         return bail(set_global_error(LAYA_E_NOMEM, "workspace: hipMalloc failed"));
     if (hipMemsetAsync(enc->ws, 0, wsz, s) != hipSuccess || hipStreamSynchronize(s) != hipSuccess)
@@ -1049,6 +1057,18 @@ int laya_encoder_run(laya_encoder *enc, void *stream, const int32_t *ids,
         auto key = std::make_tuple((int)B, (int)S, (int)R, rope_sa ? 1 : 0);
         auto it = enc->graphs.find(key);
         if (it == enc->graphs.end()) {
+            // LRU: make room for the new shape (every graph shares the one
+            // workspace, so the cache bounds graph objects, not memory)
+            while ((int)enc->graphs.size() >= c.max_graphs) {
+                auto lru = enc->graphs.begin();
+                for (auto g = enc->graphs.begin(); g != enc->graphs.end(); ++g)
+                    if (g->second.last_used < lru->second.last_used) lru = g;
+                HIPCHK(hipStreamSynchronize(s));  // a replay of it may still be queued
+                if (lru->second.exec) hipGraphExecDestroy(lru->second.exec);
+                if (lru->second.graph) hipGraphDestroy(lru->second.graph);
+                enc->graphs.erase(lru);
+                ++enc->stats.graph_evictions;
+            }
             auto t0 = std::chrono::steady_clock::now();
             RunShape warm{B, S, R, T, false};
             warm.rope_standalone = rope_sa;
@@ -1081,6 +1101,8 @@ int laya_encoder_run(laya_encoder *enc, void *stream, const int32_t *ids,
                     .count();
             enc->stats.graphs_cached = (int32_t)enc->graphs.size();
         }
+        it->second.last_used = ++enc->graph_tick;
+        enc->stats.graphs_cached = (int32_t)enc->graphs.size();
         HIPCHK(hipGraphLaunch(it->second.exec, s));
         enc->stats.launches_last_run = it->second.launches;
     }
@@ -1169,6 +1191,24 @@ int laya_encoder_fill_workspace(laya_encoder *enc, void *stream, uint8_t byte) {
     HIPCHK(hipMemsetAsync(enc->ws, byte, enc->ws_bytes, s));
     HIPCHK(hipStreamSynchronize(s));
     enc->have_upload = false;  // the index upload is gone with the rest
+    return LAYA_OK;
+}
+
+int laya_encoder_config(const laya_encoder *enc, laya_config *out) {
+    if (!enc || !out) return set_global_error(LAYA_E_INVALID, "NULL argument");
+    *out = enc->cfg;
+    return LAYA_OK;
+}
+
+int laya_encoder_health(const laya_encoder *enc) {
+    if (!enc) return set_global_error(LAYA_E_INVALID, "handle is NULL");
+    return enc->poisoned ? LAYA_E_POISONED : LAYA_OK;
+}
+
+int laya_encoder_inject_failure(laya_encoder *enc) {
+    if (!enc) return set_global_error(LAYA_E_INVALID, "handle is NULL");
+    enc->poisoned = true;
+    enc->err = "injected failure";
     return LAYA_OK;
 }
 

@@ -43,6 +43,8 @@ MODEL = dict(
     max_batch=16,
     max_seq=512,
     max_markers=2048,
+    max_graphs=4,              # captured graphs kept, LRU over shape keys
+    workspace_budget_mib=512,  # the workspace must fit this
 )
 
 # A tiny model of the same structure, for brute-force checks of the oracle and
@@ -63,6 +65,8 @@ TINY = dict(
     max_batch=4,
     max_seq=64,
     max_markers=64,
+    max_graphs=4,
+    workspace_budget_mib=512,
 )
 
 WEIGHT_SEED = 1
