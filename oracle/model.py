@@ -21,6 +21,14 @@ transformer layers, BF16, hidden states left for the scorer):
       after the last encoder layer:  x = R(LN_enc_final(x))
   out = R(LN_dec_final(x))
 
+With cfg["dec_head"] = 1 the decision layers are the biased head variant of
+"perf(model): exact Metal speed-ups of the forward pass": every projection
+adds a bias to its BF16 product in the same precision (the page's dense
+layer is the matmul followed by x + b in the model dtype),
+D(a, W, b) = R(R(a W^T) + b), and the FFN is 4x wide and not gated:
+      qkv = D(n, W_qkv, b_qkv)     a = D(o, W_o, b_o)
+      h   = R(GELU(D(n2, W_1, b_1)))      f = D(h, W_2, b_2)
+
 R() is float32 -> BF16 round-to-nearest-even: every stored tensor is BF16,
 every other intermediate is float32.  Separate QKV, RoPE and attention steps
 follow "[RFC]: Native Laya inference with Rust and CUDA #14", section Design.
@@ -142,19 +150,26 @@ class Oracle:
         g_attn = self.w.gamma[f"L{L}.ln_attn"]
         g_ffn = self.w.gamma[f"L{L}.ln_ffn"]
         wqkv = self.w.f32(f"L{L}.wqkv")
+        head = bool(cfg.get("dec_head", 0)) and L >= cfg["n_enc_layers"]
+        bias = (lambda name: self.w.f32(f"L{L}.{name}")) if head else (lambda name: None)
+        bqkv = bias("bqkv")
+
+        def dense(a, w, b):
+            y = R(self.lin(a, w))
+            return y if b is None else R(y + b)
 
         n = R(layer_norm(x, g_attn, eps))
         T = x.shape[0]
         if q_tok is None:
-            qkv = R(self.lin(n, wqkv))
+            qkv = dense(n, wqkv, bqkv)
             q = qkv[:, :H]
             kv = qkv[:, H:]
             q_pos = pos
             rows_q = [np.arange(row_off[b], row_off[b + 1]) for b in range(len(row_off) - 1)]
             x_q = x
         else:
-            kv = R(self.lin(n, wqkv[H:]))
-            q = R(self.lin(n[q_tok], wqkv[:H]))
+            kv = dense(n, wqkv[H:], None if bqkv is None else bqkv[H:])
+            q = dense(n[q_tok], wqkv[:H], None if bqkv is None else bqkv[:H])
             q_pos = pos[q_tok]
             x_q = x[q_tok]
             rows_q = []
@@ -173,12 +188,16 @@ class Oracle:
             o[qi] = attention(q[qi], k[ks], v[ks], q_pos[qi], pos[ks], nh, hd, hw,
                               self.rounding)
 
-        a = R(self.lin(o, self.w.f32(f"L{L}.wo")))
+        a = dense(o, self.w.f32(f"L{L}.wo"), bias("bo"))
         x1 = R(x_q + a)
         n2 = R(layer_norm(x1, g_ffn, eps))
-        ug = self.lin(n2, self.w.f32(f"L{L}.wi"))
-        h = R(gelu(ug[:, :F]) * ug[:, F:])
-        f = R(self.lin(h, self.w.f32(f"L{L}.wo2")))
+        if head:
+            h = R(gelu(dense(n2, self.w.f32(f"L{L}.w1"), bias("b1"))))
+            f = dense(h, self.w.f32(f"L{L}.w2"), bias("b2"))
+        else:
+            ug = self.lin(n2, self.w.f32(f"L{L}.wi"))
+            h = R(gelu(ug[:, :F]) * ug[:, F:])
+            f = R(self.lin(h, self.w.f32(f"L{L}.wo2")))
         return R(x1 + f)
 
     def final_norm(self, x: np.ndarray, which: str) -> np.ndarray:

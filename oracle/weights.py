@@ -15,6 +15,18 @@ Tensor numbering (nn.Linear [out][in] layout everywhere):
 Layers 0 .. n_enc-1 are the encoder, n_enc .. n_enc+n_dec-1 the decision
 layers.  Every LayerNorm gain is 1 and there are no biases (the stack is
 "pre-LayerNorm (no bias)").
+
+With cfg["dec_head"] = 1 the decision layers are the biased head variant
+("perf(model): exact Metal speed-ups of the forward pass": biased
+projections, a packed projection over every token, a 4x-wide FFN):
+  1 + 4L + 2     W_1 (FFN in)         [4*hidden, hidden]
+  1 + 4L + 3     W_2 (FFN out)        [hidden, 4*hidden]
+and after all weight tensors, for decision layer d (layer L = n_enc + d):
+  1 + 4*NL + 4d + 0   b_qkv  [3*hidden]
+  1 + 4*NL + 4d + 1   b_o    [hidden]
+  1 + 4*NL + 4d + 2   b_1    [4*hidden]
+  1 + 4*NL + 4d + 3   b_2    [hidden]
+(NL = n_enc + n_dec), drawn by the same generator as the weights.
 """
 from __future__ import annotations
 
@@ -73,15 +85,31 @@ def irwin_hall(seed: int, tensor_id: int, idx: int) -> float:
 
 
 def tensor_shapes(cfg: dict) -> list:
-    """[(tensor_id, name, (rows, cols))] in tensor-id order."""
+    """[(tensor_id, name, shape)] in tensor-id order."""
     H, F = cfg["hidden"], cfg["ffn"]
+    n_enc, n_dec = cfg["n_enc_layers"], cfg["n_dec_layers"]
+    head = bool(cfg.get("dec_head", 0))
+    NL = n_enc + n_dec
     out = [(0, "emb", (cfg["vocab"], H))]
-    for L in range(cfg["n_enc_layers"] + cfg["n_dec_layers"]):
+    for L in range(NL):
         base = 1 + 4 * L
-        out += [(base + 0, f"L{L}.wqkv", (3 * H, H)),
-                (base + 1, f"L{L}.wo", (H, H)),
-                (base + 2, f"L{L}.wi", (2 * F, H)),
-                (base + 3, f"L{L}.wo2", (H, F))]
+        if head and L >= n_enc:
+            out += [(base + 0, f"L{L}.wqkv", (3 * H, H)),
+                    (base + 1, f"L{L}.wo", (H, H)),
+                    (base + 2, f"L{L}.w1", (4 * H, H)),
+                    (base + 3, f"L{L}.w2", (H, 4 * H))]
+        else:
+            out += [(base + 0, f"L{L}.wqkv", (3 * H, H)),
+                    (base + 1, f"L{L}.wo", (H, H)),
+                    (base + 2, f"L{L}.wi", (2 * F, H)),
+                    (base + 3, f"L{L}.wo2", (H, F))]
+    if head:
+        for d in range(n_dec):
+            L, base = n_enc + d, 1 + 4 * NL + 4 * d
+            out += [(base + 0, f"L{L}.bqkv", (3 * H,)),
+                    (base + 1, f"L{L}.bo", (H,)),
+                    (base + 2, f"L{L}.b1", (4 * H,)),
+                    (base + 3, f"L{L}.b2", (H,))]
     return out
 
 

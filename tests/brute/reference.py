@@ -118,13 +118,27 @@ def forward(cfg: dict, seed: int, ids, lengths, rounding: bool = True, capture: 
         if theta not in tables:
             tables[theta] = rope_table(theta, cfg["max_seq"], d)
         c, s = tables[theta]
+        head = bool(cfg.get("dec_head", 0)) and L >= n_enc
+        NL = n_enc + n_dec
         wqkv = weights_f64(seed, 1 + 4 * L, (3 * H, H))
         wo = weights_f64(seed, 2 + 4 * L, (H, H))
-        wi = weights_f64(seed, 3 + 4 * L, (2 * F, H))
-        wo2 = weights_f64(seed, 4 + 4 * L, (H, F))
+        if head:
+            # biased head layer: 4x-wide plain-GELU FFN, biases after all weights
+            w1 = weights_f64(seed, 3 + 4 * L, (4 * H, H))
+            w2 = weights_f64(seed, 4 + 4 * L, (H, 4 * H))
+            bb = 1 + 4 * NL + 4 * (L - n_enc)
+            b_qkv = weights_f64(seed, bb, (3 * H,))
+            b_o = weights_f64(seed, bb + 1, (H,))
+            b_1 = weights_f64(seed, bb + 2, (4 * H,))
+            b_2 = weights_f64(seed, bb + 3, (H,))
+        else:
+            wi = weights_f64(seed, 3 + 4 * L, (2 * F, H))
+            wo2 = weights_f64(seed, 4 + 4 * L, (H, F))
 
         n = R(ln(x, g(f"L{L}.ln_attn")))
         qkv = R(n @ wqkv.T)
+        if head:
+            qkv = R(qkv + b_qkv)
         q, k, v = qkv[:, :H], qkv[:, H:2 * H], qkv[:, 2 * H:]
 
         def rot(m):
@@ -148,12 +162,20 @@ def forward(cfg: dict, seed: int, ids, lengths, rounding: bool = True, capture: 
                 p /= p.sum()
                 o[i, sl] = p @ v[:, sl]
         o = R(o)
-        x = R(x + R(o @ wo.T))
+        att = R(o @ wo.T)
+        if head:
+            att = R(att + b_o)
+        x = R(x + att)
         n2 = R(ln(x, g(f"L{L}.ln_ffn")))
-        u = n2 @ wi[:F].T
-        gate = n2 @ wi[F:].T
-        hmid = R(u * ndtr(u) * gate)
-        x = R(x + R(hmid @ wo2.T))
+        if head:
+            u = R(R(n2 @ w1.T) + b_1)
+            hmid = R(u * ndtr(u))
+            x = R(x + R(R(hmid @ w2.T) + b_2))
+        else:
+            u = n2 @ wi[:F].T
+            gate = n2 @ wi[F:].T
+            hmid = R(u * ndtr(u) * gate)
+            x = R(x + R(hmid @ wo2.T))
         caps.append((f"enc{L:02d}" if L < n_enc else f"dec{L - n_enc}", x.copy()))
         if L == n_enc - 1:
             x = R(ln(x, g("ln_enc_final")))

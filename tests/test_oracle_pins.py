@@ -412,3 +412,100 @@ def test_planted_mistakes_are_caught(mutation, tiny_batch, tiny_weights, brute_u
         w = _SwapGLU(tiny_weights, TINY["ffn"])
     got = omodel.Oracle(TINY, w, rounding=False).forward(tiny_batch.ids, tiny_batch.lengths, capture=True)
     assert _max_layer_nrms(got, brute_unrounded) > UNROUNDED_BOUND
+
+
+# ------------------------------------------------------- biased head variant --
+# The decision layers as the biased head of "perf(model): exact Metal
+# speed-ups of the forward pass": biased projections (bias added to the BF16
+# product in the same precision), a 4x-wide plain-GELU FFN.
+
+TINY_HEAD = dict(TINY, dec_head=1)
+
+
+@pytest.fixture(scope="module")
+def head_weights():
+    return oracle.Weights(TINY_HEAD, 1)
+
+
+@pytest.fixture(scope="module")
+def head_brute_unrounded(tiny_batch):
+    return brute.forward(TINY_HEAD, 1, tiny_batch.ids, tiny_batch.lengths, rounding=False,
+                         capture=True)
+
+
+def test_head_tensors_match_brute_generator(head_weights):
+    H = TINY["hidden"]
+    n_enc, NL = TINY["n_enc_layers"], TINY["n_enc_layers"] + TINY["n_dec_layers"]
+    shapes = {n: sh for _, n, sh in oracle.tensor_shapes(TINY_HEAD)}
+    assert shapes[f"L{n_enc}.w1"] == (4 * H, H) and shapes[f"L{n_enc}.w2"] == (H, 4 * H)
+    assert shapes[f"L{NL - 1}.b1"] == (4 * H,)
+    for tid, name, shape in oracle.tensor_shapes(TINY_HEAD):
+        if name.split(".")[-1] in ("bqkv", "bo", "b1", "b2", "w1", "w2"):
+            want = brute.weights_f64(1, tid, shape)
+            assert np.array_equal(head_weights.f32(name).astype(np.float64), want), name
+
+
+def test_head_variant_matches_brute_without_rounding(tiny_batch, head_weights,
+                                                     head_brute_unrounded):
+    got = oracle.Oracle(TINY_HEAD, head_weights, rounding=False).forward(
+        tiny_batch.ids, tiny_batch.lengths, capture=True)
+    assert _max_layer_nrms(got, head_brute_unrounded) < UNROUNDED_BOUND
+    # and it is a different model than the GeGLU decision layers
+    plain = brute.forward(TINY, 1, tiny_batch.ids, tiny_batch.lengths, rounding=False)
+    assert oracle.nrms(got["out"], plain["out"]) > 1e-2
+
+
+def test_head_variant_matches_brute_with_rounding(tiny_batch, head_weights):
+    want = brute.forward(TINY_HEAD, 1, tiny_batch.ids, tiny_batch.lengths, rounding=True,
+                         capture=True)
+    got = oracle.Oracle(TINY_HEAD, head_weights).forward(tiny_batch.ids, tiny_batch.lengths,
+                                                         capture=True)
+    assert oracle.nrms(got["out"], want["out"]) < 5e-3
+    for name, a in got["layers"]:
+        assert np.array_equal(oracle.bf16_round(a), a), name
+
+
+def test_head_variant_marker_subset_equals_full_rows(head_weights):
+    b = random_batch(TINY_HEAD, 3, 24, seed=6, len_lo=10, markers_per_row=4)
+    o = oracle.Oracle(TINY_HEAD, head_weights)
+    full = o.forward(b.ids, b.lengths)
+    sub = o.forward(b.ids, b.lengths, markers=b.markers)
+    rows = full["row_off"][b.markers[:, 0]] + b.markers[:, 1]
+    assert np.array_equal(sub["out"], full["out"][rows])
+
+
+class _DropBias:
+    """Planted mistake: one bias of the head left out."""
+
+    def __init__(self, w, suffix):
+        self.w, self.suffix = w, suffix
+        self.gamma = w.gamma
+
+    def f32(self, name):
+        a = self.w.f32(name)
+        return np.zeros_like(a) if name.endswith(self.suffix) else a
+
+
+class _GatedHead:
+    """Planted mistake: the head's FFN read as a GeGLU of two halves of W_1."""
+
+    def __init__(self, w):
+        self.w = w
+        self.gamma = w.gamma
+
+    def f32(self, name):
+        a = self.w.f32(name)
+        if name.endswith(".w1"):
+            half = a.shape[0] // 2
+            return np.concatenate([a[:half] * 0.5, a[half:]])
+        return a
+
+
+@pytest.mark.parametrize("mutation", ["b_qkv", "b_o", "b_1", "b_2", "ffn_halves"])
+def test_head_planted_mistakes_are_caught(mutation, tiny_batch, head_weights,
+                                          head_brute_unrounded):
+    w = (_GatedHead(head_weights) if mutation == "ffn_halves"
+         else _DropBias(head_weights, "." + mutation.replace("_", "")))
+    got = omodel.Oracle(TINY_HEAD, w, rounding=False).forward(tiny_batch.ids, tiny_batch.lengths,
+                                                              capture=True)
+    assert _max_layer_nrms(got, head_brute_unrounded) > UNROUNDED_BOUND
