@@ -35,7 +35,9 @@ PAGES_CALLS_PER_S = {"mixed_16": 38.7, "short_1": 358.9, "short_3": 311.0, "long
 # the GEMM tile configuration and K split follow the plan for the batch shape)
 DOMINANT_KERNEL_SYMBOL = {
     "up_geglu_gemm": "gemm_kernel<Cfg<...>, 1, ...> (GeGLU epilogue)",
-    "qkv_gemm": "gemm_kernel<Cfg<...>, 0, ...>", "down_gemm": "gemm_kernel<Cfg<...>, 0, ...>",
+    "qkv_gemm": "gemm_kernel<Cfg<...>, 2, ...> (QKV epilogue)",
+    "up_gelu_gemm": "gemm_kernel<Cfg<...>, 3, ...> (bias + GELU epilogue)",
+    "down_gemm": "gemm_kernel<Cfg<...>, 0, ...>",
     "out_proj_gemm": "gemm_kernel<Cfg<...>, 0, ...>", "attention": "attention_kernel",
     "layernorm": "layernorm_kernel", "rope": "rope_kernel",
 }
@@ -66,6 +68,9 @@ def parse():
     p.add_argument("--latency-calls", type=int, default=50)
     p.add_argument("--profile-passes", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--dec-head", action="store_true",
+                   help="decision layers as the biased head variant (biased projections, "
+                        "4*hidden GELU FFN)")
     p.add_argument("--cpu-sample-rows", type=int, default=4)
     p.add_argument("--protocol", action="store_true",
                    help="the full measurement protocol over every workload (ABBA rounds of "
@@ -205,6 +210,8 @@ def _metadata(enc, cfg):
     except OSError:
         pass
     n_tensors = 1 + 4 * (cfg["n_enc_layers"] + cfg["n_dec_layers"])
+    if cfg.get("dec_head", 0):
+        n_tensors += 4 * cfg["n_dec_layers"]
     digests = [format(enc.weight_digest(t), "016x") for t in range(n_tensors)]
     props = torch.cuda.get_device_properties(0)
     return {"git_sha": sha, "library_sha256": lib_sha, "gpu": props.name,
@@ -224,15 +231,17 @@ def protocol(args):
     standalone kernel) in ABBA order; and the CPU oracle."""
     import torch
     from transformer_encoder_bf16_amd import binding
-    from transformer_encoder_bf16_amd.inputs import ALL_WORKLOADS, MODEL, WEIGHT_SEED, make_batch
+    from transformer_encoder_bf16_amd.inputs import ALL_WORKLOADS, WEIGHT_SEED, make_batch
 
     if not os.path.exists(binding.LIB_PATH):
         from transformer_encoder_bf16_amd import build_lib
         build_lib.build()
     torch.cuda.set_device(0)
     sync = torch.cuda.synchronize
+    MODEL = model_config(args)
     enc = binding.Encoder(MODEL, seed=WEIGHT_SEED, device=0)
     meta = _metadata(enc, MODEL)
+    meta["decision_layers"] = "head" if args.dec_head else "encoder-shaped"
     meta["create_ms"] = round(enc.stats()["create_ms"], 1)
     results = {"metric": METRIC, "protocol": {"warmup": args.protocol_warmup,
                                               "calls": args.protocol_calls,
@@ -316,6 +325,12 @@ def protocol(args):
                                     for k, v in results["workloads"].items()}}), flush=True)
 
 
+def model_config(args) -> dict:
+    """The model, or with --dec-head its biased decision-head variant."""
+    from transformer_encoder_bf16_amd.inputs import MODEL
+    return dict(MODEL, dec_head=1) if args.dec_head else dict(MODEL)
+
+
 def oracle_timing(cfg, batch, calls):
     """The CPU oracle on the whole batch: one warm call, then `calls` timed."""
     import oracle
@@ -347,13 +362,14 @@ def main():
         protocol(args)
         return
     from transformer_encoder_bf16_amd import binding
-    from transformer_encoder_bf16_amd.inputs import MODEL, WEIGHT_SEED, WORKLOADS, make_batch
+    from transformer_encoder_bf16_amd.inputs import ALL_WORKLOADS, WEIGHT_SEED, make_batch
 
     if not os.path.exists(binding.LIB_PATH):
         from transformer_encoder_bf16_amd import build_lib
         build_lib.build()
     torch.cuda.set_device(0)
-    wl = WORKLOADS[args.workload]
+    MODEL = model_config(args)
+    wl = ALL_WORKLOADS[args.workload]
     batch = make_batch(MODEL, wl)
     enc = binding.Encoder(MODEL, seed=WEIGHT_SEED, device=0)
     st0 = enc.stats()
@@ -413,7 +429,8 @@ def main():
         roof = {"bound": "hbm", "achieved": round(d["_bytes"] / d["_sec"] / 1e9, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = measured_traffic(dom, args.workload)
+    # the counters were taken on the default model
+    roof["traffic"] = None if args.dec_head else measured_traffic(dom, args.workload)
     roof["op"] = dom
     roof["kernel"] = DOMINANT_KERNEL_SYMBOL.get(dom, dom)
     roof["avg_launch_us"] = d["avg_launch_us"]
@@ -428,7 +445,7 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(MODEL, batch, args.cpu_sample_rows)
 
-    pages = PAGES_CALLS_PER_S.get(args.workload)
+    pages = None if args.dec_head else PAGES_CALLS_PER_S.get(args.workload)
     line = {
         "metric": METRIC,
         "value": round(calls_per_s, 3),
@@ -447,7 +464,8 @@ def main():
         "config": {"workload": args.workload, "B": batch.B, "S": batch.S, "T": batch.T,
                    "R": 0 if mk is None else int(len(mk)), "input_seed": wl.seed,
                    "weight_seed": WEIGHT_SEED, "layers": "28+2", "mode": "hipGraph replay",
-                   "inputs": "device-resident"},
+                   "inputs": "device-resident",
+                   "decision_layers": "head" if args.dec_head else "encoder-shaped"},
         "p50_ms": round(float(np.percentile(lat, 50)), 4),
         "p95_ms": round(float(np.percentile(lat, 95)), 4),
         "host_boundary_p50_ms": round(float(np.percentile(host, 50)), 4),

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define LAYA_ABI_VERSION 3
+#define LAYA_ABI_VERSION 4
 
 #define LAYA_OK 0
 #define LAYA_E_INVALID -1     /* bad ids, lengths, markers, sizes, NULL pointers */
@@ -91,6 +91,11 @@ typedef struct laya_config {
     int32_t max_graphs;    /* captured graphs kept (LRU over shape keys), >= 1; 4 by default */
     int32_t workspace_budget_mib; /* create fails with LAYA_E_NOMEM if the workspace needs more;
                                      512 by default */
+    int32_t dec_head;      /* 0 (default): decision layers are encoder-shaped.  1: the biased
+                              head variant of the decision layers (page "perf(model): exact
+                              Metal speed-ups of the forward pass": every projection adds a
+                              bias, y = bf16(bf16(x W^T) + b), and the FFN is 4*hidden wide
+                              with plain GELU, h = bf16(GELU(y1)), f = y2) */
 } laya_config;
 
 /* Device-resident result of a run.  Owned by the handle; valid until the next
@@ -154,7 +159,12 @@ int laya_validate_run_args(const laya_config *cfg, const int32_t *token_ids,
  * (encoder layers first, then decision layers) 1+4L W_qkv [3*hidden][hidden]
  * with rows [Q | K | V], 2+4L W_o [hidden][hidden], 3+4L W_i [2*ffn][hidden]
  * with rows [GELU half | gate half], 4+4L W_o2 [hidden][ffn].  Every
- * LayerNorm gain is 1; there are no biases.
+ * LayerNorm gain is 1; there are no biases.  With dec_head = 1 the decision
+ * layers' 3+4L is W_1 [4*hidden][hidden] and 4+4L is W_2 [hidden][4*hidden],
+ * and after every weight tensor come decision layer d's biases (NL = all
+ * layers): 1+4NL+4d b_qkv [3*hidden], +1 b_o [hidden], +2 b_1 [4*hidden],
+ * +3 b_2 [hidden], drawn by the same generator (laya_encoder_weight reports
+ * a bias as 1 row).
  *
  * Rotary tables ("reproduce official BF16 rotary-table rounding", page "Laya
  * native CUDA worker", section Prepare the checkpoint and bundle; "both
@@ -231,7 +241,7 @@ int laya_encoder_layer_output(laya_encoder *enc, int32_t index, laya_output *out
  * the tensor to the host; synchronous; diagnostic only. */
 int laya_encoder_weight_digest(laya_encoder *enc, int32_t tensor_id, uint64_t *fnv64);
 
-/* Device pointer (BF16, [rows][cols]) and shape of weight tensor `tensor_id`;
+/* Device pointer (BF16, [rows][cols]) and shape of weight or bias tensor `tensor_id`;
  * diagnostic only. */
 int laya_encoder_weight(laya_encoder *enc, int32_t tensor_id, const void **dev,
                         int32_t *rows, int32_t *cols);
@@ -368,10 +378,17 @@ int laya_op_layernorm(void *stream, void *x, const void *r, void *n, const float
  * only on shapes 0..3; GeGLU not on shape 0).  Each output is the sum, in
  * order, of one MFMA chain per K range, so results depend only on `splits`.
  * With splits > 1 the call allocates its scratch and synchronises the
- * stream. */
+ * stream.
+ *
+ * bias (device BF16 [N], or NULL): the biased dense layer of the decision
+ * head ("perf(model): exact Metal speed-ups of the forward pass"), the BF16
+ * product plus the bias in BF16: epilogue 0 with a bias gives
+ * C = bf16(bf16(A W^T) + bias); epilogue 3 (bias required) gives
+ * C = bf16(GELU(bf16(bf16(A W^T) + bias))), the head's FFN input layer.
+ * Epilogue 1 takes no bias. */
 int laya_op_gemm(void *stream, const void *A, int32_t lda, const void *W, int32_t ldw,
                  void *C, int32_t ldc, int32_t M, int32_t N, int32_t K, int32_t epilogue,
-                 int32_t config, int32_t splits);
+                 int32_t config, int32_t splits, const void *bias);
 
 /* RoPE in place on `n_heads_rot` consecutive 64-wide heads starting at column
  * 0 of each of `rows` rows of buf (device BF16, row stride ld): with
@@ -398,12 +415,14 @@ int laya_op_rope(void *stream, void *buf, int32_t ld, int32_t n_heads_rot, int32
  *                            vt_tok[m]] (vt device BF16, vt_tok device int32
  *                            [M]); C is not written for these columns.
  * rope_cols and vt_col0 are multiples of 64 with rope_cols <= vt_col0 <= N.
- * cos_tab/sin_tab device BF16 [positions][32].  Not on tile shape 0. */
+ * cos_tab/sin_tab device BF16 [positions][32].  Not on tile shape 0.  With a
+ * bias (device BF16 [N], or NULL) z = bf16(bf16(A W^T) + bias) before the
+ * rotation and the transposed store, as laya_op_gemm. */
 int laya_op_gemm_qkv(void *stream, const void *A, int32_t lda, const void *W, int32_t ldw,
                      void *C, int32_t ldc, int32_t M, int32_t N, int32_t K, const int32_t *pos,
                      const void *cos_tab, const void *sin_tab, int32_t rope_cols, void *vt,
                      int32_t ldvt, const int32_t *vt_tok, int32_t vt_col0, int32_t config,
-                     int32_t splits);
+                     int32_t splits, const void *bias);
 
 /* Attention with a key-padding row and an optional sliding window, for a
  * packed batch (flash attention over the native QKV buffer, "[RFC]: Native

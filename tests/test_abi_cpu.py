@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol(lib):
     assert declared == set(b.EXPORTS)
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.laya_abi_version() == b.LAYA_ABI_VERSION == 3
+    assert lib.laya_abi_version() == b.LAYA_ABI_VERSION == 4
 
 
 def test_default_config_is_the_model(lib):
@@ -38,7 +38,7 @@ def test_default_config_is_the_model(lib):
         assert d[k] == pytest.approx(v), k
 
 
-@pytest.mark.parametrize("cfg", [MODEL, TINY])
+@pytest.mark.parametrize("cfg", [MODEL, TINY, dict(MODEL, dec_head=1), dict(TINY, dec_head=1)])
 def test_valid_configs(lib, cfg):
     assert b.validate_config(cfg) == b.LAYA_OK
 
@@ -57,6 +57,8 @@ def test_valid_configs(lib, cfg):
     (dict(ln_eps=0.0), b.LAYA_E_INVALID),
     (dict(max_graphs=0), b.LAYA_E_INVALID),
     (dict(workspace_budget_mib=0), b.LAYA_E_INVALID),
+    (dict(dec_head=2), b.LAYA_E_INVALID),
+    (dict(dec_head=-1), b.LAYA_E_INVALID),
 ])
 def test_invalid_configs(lib, change, code):
     cfg = dict(MODEL)

@@ -453,3 +453,117 @@ def _plain(B, a, w, M, N, K, cfg):
     B.op_gemm(a, w, c, M, N, K, 0, config=cfg, splits=1)
     _sync()
     return from_dev(c)
+
+
+# ------------------------------------- biased dense layers (decision head) --
+
+def _f32_of(bits):
+    return (np.asarray(bits).astype(np.uint32) << 16).view(np.float32)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 512, 128), (48, 4096, 1024), (97, 1024, 4096),
+                                   (300, 4096, 1024)])
+def test_gemm_bias_and_bias_gelu_every_tile_shape(B, M, N, K):
+    """For every tile shape and K split: epilogue 0 with a bias is bitwise
+    bf16(plain + bias) of the same shape and split, and epilogue 3 is within
+    one BF16 ulp of the oracle's GELU of that.  Against the oracle's biased
+    dense layer from the inputs: the product may differ by one ulp of the
+    product (summation order), which the bias addition carries over
+    unchanged, so y is within ulp(product) + ulp(y) of the oracle's, and
+    GELU (slope at most 1.13) keeps that."""
+    import torch
+    a_h = oracle.bf16_round(random_normal((M, K), 11 * M + K))
+    w_h = oracle.bf16_round(random_normal((N, K), 5 * N + K, 0.03))
+    b_h = oracle.bf16_round(random_normal((N,), N + 3, 0.5))
+    a, w, bias = to_dev(a_h), to_dev(w_h), to_dev(b_h)
+    p_or = oracle.bf16_round(oracle.linear(a_h, w_h))
+    y_or = oracle.bf16_round(p_or + b_h)
+    h_or = oracle.bf16_round(oracle.gelu(y_or))
+
+    def ulp(x):
+        return np.exp2(np.floor(np.log2(np.maximum(np.abs(x.astype(np.float64)), 2.0 ** -126))) - 7)
+
+    # the product's tolerance is bf16_close's: one ulp, or 2^-16 of its rms
+    y_tol = ulp(p_or) + 2.0 ** -16 * float(np.sqrt(np.mean(p_or.astype(np.float64) ** 2))) + ulp(y_or)
+    h_tol = 1.13 * y_tol + ulp(h_or) + 2.0 ** -126
+    worst = {"y": 0.0, "h": 0.0}
+    for splits in (1, 2, 4):
+        for cfg in range(7):
+            if (splits > 1 and cfg > 3) or splits > K // 64:
+                continue
+            outs = {}
+            for epi, bb in ((0, None), (0, bias), (3, bias)):
+                c = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+                B.op_gemm(a, w, c, M, N, K, epi, config=cfg, splits=splits, bias=bb)
+                _sync()
+                outs[(epi, bb is not None)] = bits_of(from_dev(c))
+            plain = _f32_of(outs[(0, False)])
+            y = _f32_of(outs[(0, True)])
+            h = _f32_of(outs[(3, True)])
+            bad, _ = bf16_close(plain, p_or)
+            assert bad == 0, (cfg, splits)
+            assert np.array_equal(bits_of(y), bits_of(oracle.bf16_round(plain + b_h))), (cfg, splits)
+            assert ulp_diff(h, oracle.bf16_round(oracle.gelu(y))).max() <= 1, (cfg, splits)
+            ey = np.abs(y.astype(np.float64) - y_or) / y_tol
+            eh = np.abs(h.astype(np.float64) - h_or) / h_tol
+            worst["y"] = max(worst["y"], float(ey.max()))
+            worst["h"] = max(worst["h"], float(eh.max()))
+            assert ey.max() <= 1.0 and eh.max() <= 1.0, (cfg, splits)
+    report("gemm_bias", {"M": M, "N": N, "K": K, "worst_frac_of_bound": worst})
+
+
+def test_gemm_bias_rules(B):
+    import torch
+    a = torch.zeros((4, 64), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((128, 64), dtype=torch.bfloat16, device="cuda")
+    c = torch.zeros((4, 64), dtype=torch.bfloat16, device="cuda")
+    bias = torch.zeros(128, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(B.LayaError):
+        B.op_gemm(a, w, c, 4, 64, 64, 3)  # bias + GELU needs a bias
+    with pytest.raises(B.LayaError):
+        B.op_gemm(a, w, c, 4, 64, 64, 1, bias=bias)  # GeGLU takes none
+
+
+@pytest.mark.parametrize("M,H,cfgs,splits", [(48, 128, (1, 2, 3), (1, 2)),
+                                             (300, 1024, (2, 3, 4, 5), (1,))])
+def test_gemm_qkv_bias_equals_biased_gemm_then_rope(B, M, H, cfgs, splits):
+    """With a bias the QKV epilogue equals the biased plain GEMM followed by
+    the RoPE kernel, and V^T holds the biased V columns, bitwise."""
+    import torch
+    K, N = 1024, 3 * H
+    a_h = oracle.bf16_round(random_normal((M, K), M + 15))
+    w_h = oracle.bf16_round(random_normal((N, K), N + 17, 0.03))
+    b_h = oracle.bf16_round(random_normal((N,), N + 19, 0.5))
+    a, w, bias = to_dev(a_h), to_dev(w_h), to_dev(b_h)
+    cb, sb = B.rope_table(160000.0, 512, 64)
+    ct = torch.from_numpy(cb.view(np.int16)).cuda()
+    st = torch.from_numpy(sb.view(np.int16)).cuda()
+    pos_h = np.random.default_rng(M + 1).integers(0, 512, M).astype(np.int32)
+    pos = torch.from_numpy(pos_h).cuda()
+    vtok_h = (np.arange(M) + 5 * (np.arange(M) // 13)).astype(np.int32)
+    vtok = torch.from_numpy(vtok_h).cuda()
+    ldvt = int(vtok_h.max()) + 9
+    for sp in splits:
+        ref = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+        B.op_gemm(a, w, ref, M, N, K, 0, config=cfgs[0], splits=sp, bias=bias)
+        _sync()
+        biased = bits_of(from_dev(ref))
+        B.op_rope(ref, 2 * H // 64, pos, ct, st)
+        _sync()
+        ref_h = bits_of(from_dev(ref))
+        for cfg in cfgs:
+            c = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+            vt = torch.full((H, ldvt), float("nan"), dtype=torch.bfloat16, device="cuda")
+            B.op_gemm_qkv(a, w, c, M, N, K, pos, ct, st, 2 * H, vt, vtok, 2 * H, config=cfg,
+                          splits=sp, bias=bias)
+            _sync()
+            got = bits_of(from_dev(c))
+            assert np.array_equal(got[:, :2 * H], ref_h[:, :2 * H]), (cfg, sp)
+            vt_h = bits_of(from_dev(vt))
+            assert np.array_equal(vt_h[:, vtok_h].T, biased[:, 2 * H:]), (cfg, sp)
+            # no rotation: the Q/K columns are the biased product itself
+            c2 = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+            B.op_gemm_qkv(a, w, c2, M, N, K, pos, ct, st, 0, vt, vtok, 2 * H, config=cfg,
+                          splits=sp, bias=bias)
+            _sync()
+            assert np.array_equal(bits_of(from_dev(c2))[:, :2 * H], biased[:, :2 * H])

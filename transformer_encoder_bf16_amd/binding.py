@@ -16,7 +16,7 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liblaya_encoder.so")
 
-LAYA_ABI_VERSION = 3
+LAYA_ABI_VERSION = 4
 LAYA_OK = 0
 LAYA_E_INVALID = -1
 LAYA_E_UNSUPPORTED = -2
@@ -69,6 +69,7 @@ class Config(ctypes.Structure):
         ("ln_eps", ctypes.c_float), ("max_batch", ctypes.c_int32),
         ("max_seq", ctypes.c_int32), ("max_markers", ctypes.c_int32),
         ("max_graphs", ctypes.c_int32), ("workspace_budget_mib", ctypes.c_int32),
+        ("dec_head", ctypes.c_int32),
     ]
 
     @classmethod
@@ -76,7 +77,9 @@ class Config(ctypes.Structure):
         c = cls()
         c.abi_version = LAYA_ABI_VERSION
         for name, _ in cls._fields_:
-            if name != "abi_version":
+            if name == "dec_head":
+                c.dec_head = int(d.get("dec_head", 0))
+            elif name != "abi_version":
                 setattr(c, name, d[name])
         return c
 
@@ -162,14 +165,14 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         "laya_op_gemm": (ctypes.c_int, [_P, _P, ctypes.c_int32, _P, ctypes.c_int32, _P,
                                         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
-                                        ctypes.c_int32]),
+                                        ctypes.c_int32, _P]),
         "laya_op_rope": (ctypes.c_int, [_P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                         _P, _P, _P, ctypes.c_int32]),
         "laya_op_gemm_qkv": (ctypes.c_int, [_P, _P, ctypes.c_int32, _P, ctypes.c_int32, _P,
                                             ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                             ctypes.c_int32, _P, _P, _P, ctypes.c_int32, _P,
                                             ctypes.c_int32, _P, ctypes.c_int32, ctypes.c_int32,
-                                            ctypes.c_int32]),
+                                            ctypes.c_int32, _P]),
         "laya_op_attention": (ctypes.c_int, [_P, _P, ctypes.c_int32, _P, ctypes.c_int32, _P,
                                              ctypes.c_int32, _P, _P, ctypes.c_int32,
                                              ctypes.c_int32, _P, ctypes.c_int32, _P,
@@ -393,10 +396,13 @@ def op_layernorm(x, r, n, gamma, eps: float, stream: Optional[int] = None):
 
 
 def op_gemm(A, W, C, M: int, N: int, K: int, epilogue: int = 0, config: int = -1,
-            splits: int = 1, stream: Optional[int] = None):
+            splits: int = 1, bias=None, stream: Optional[int] = None):
+    """C = bf16(A W^T) (epilogue 0, optionally + bias), GeGLU (1), or
+    bias then GELU (3)."""
     st = current_stream() if stream is None else stream
     _check(load().laya_op_gemm(st, _dp(A), A.stride(0), _dp(W), W.stride(0), _dp(C),
-                               C.stride(0), M, N, K, epilogue, config, splits), "laya_op_gemm")
+                               C.stride(0), M, N, K, epilogue, config, splits, _dp(bias)),
+           "laya_op_gemm")
 
 
 def op_rope(buf, n_heads_rot: int, pos, cos_tab, sin_tab, rows: Optional[int] = None,
@@ -408,7 +414,7 @@ def op_rope(buf, n_heads_rot: int, pos, cos_tab, sin_tab, rows: Optional[int] = 
 
 
 def op_gemm_qkv(A, W, C, M: int, N: int, K: int, pos, cos_tab, sin_tab, rope_cols: int,
-                vt, vt_tok, vt_col0: int, config: int = -1, splits: int = 1,
+                vt, vt_tok, vt_col0: int, config: int = -1, splits: int = 1, bias=None,
                 stream: Optional[int] = None):
     """QKV projection with RoPE on columns [0, rope_cols) and columns
     [vt_col0, N) stored transposed into vt at columns vt_tok[m]."""
@@ -416,7 +422,8 @@ def op_gemm_qkv(A, W, C, M: int, N: int, K: int, pos, cos_tab, sin_tab, rope_col
     _check(load().laya_op_gemm_qkv(st, _dp(A), A.stride(0), _dp(W), W.stride(0), _dp(C),
                                    C.stride(0), M, N, K, _dp(pos), _dp(cos_tab), _dp(sin_tab),
                                    rope_cols, _dp(vt), 0 if vt is None else vt.stride(0),
-                                   _dp(vt_tok), vt_col0, config, splits), "laya_op_gemm_qkv")
+                                   _dp(vt_tok), vt_col0, config, splits, _dp(bias)),
+           "laya_op_gemm_qkv")
 
 
 def op_attention(q, k, vt, vt_col0, o, n_heads: int, row_off, q_tok=None,

@@ -16,6 +16,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <array>
 #include <chrono>
 #include <cmath>
 #include <cstdio>
@@ -167,7 +168,7 @@ int config_check(const laya_config *c, std::string *why) {
     if (c->vocab <= 0 || c->hidden <= 0 || c->n_heads <= 0 || c->head_dim <= 0 || c->ffn <= 0 ||
         c->n_enc_layers <= 0 || c->n_dec_layers <= 0 || c->global_every <= 0 || c->window < 0 ||
         c->max_batch <= 0 || c->max_seq <= 0 || c->max_markers < 0 || !(c->ln_eps > 0.f) ||
-        c->max_graphs <= 0 || c->workspace_budget_mib <= 0 ||
+        c->max_graphs <= 0 || c->workspace_budget_mib <= 0 || c->dec_head < 0 || c->dec_head > 1 ||
         !(c->theta_global > 1.f) || !(c->theta_local > 1.f)) {
         *why = "non-positive size or parameter in config";
         return LAYA_E_INVALID;
@@ -323,6 +324,13 @@ struct laya_encoder {
     size_t wbytes = 0;
     bf16_t *emb = nullptr;
     std::vector<bf16_t *> wqkv, wo, wi, wo2;
+    // biases of the head variant's decision layers (null elsewhere)
+    std::vector<bf16_t *> bqkv, bo, b1, b2;
+    struct TensorView {
+        bf16_t *dev;
+        int32_t rows, cols;
+    };
+    std::vector<TensorView> tensors;  // by tensor id
     float *gamma_ones = nullptr;
     bf16_t *cos_g = nullptr, *sin_g = nullptr, *cos_l = nullptr, *sin_l = nullptr;
 
@@ -393,11 +401,11 @@ struct RunShape {
 // Op classes of the per-launch profile (laya_encoder_profile).
 enum OpKind {
     OP_GATHER, OP_LAYERNORM, OP_QKV, OP_ROPE, OP_ATTENTION, OP_OUT_PROJ, OP_UP_GEGLU, OP_DOWN,
-    OP_ROW_GATHER, OP_KV, OP_Q, OP_COUNT
+    OP_ROW_GATHER, OP_KV, OP_Q, OP_UP_GELU, OP_COUNT
 };
 const char *const kOpNames[OP_COUNT] = {
     "gather", "layernorm", "qkv_gemm", "rope", "attention", "out_proj_gemm",
-    "up_geglu_gemm", "down_gemm", "row_gather", "kv_gemm", "q_gemm"};
+    "up_geglu_gemm", "down_gemm", "row_gather", "kv_gemm", "q_gemm", "up_gelu_gemm"};
 
 struct ProfRec {
     int op;
@@ -419,13 +427,15 @@ int layer_count(const laya_config &c) { return c.n_enc_layers + c.n_dec_layers; 
 struct PassPlans {
     laya::GemmPlan qkv, o, up, down;              // M = B*S
     laya::GemmPlan kv_sub, q_sub, o_sub, up_sub, down_sub;  // marker layer
+    // head variant: the decision layers' 4H-wide FFN (bias + GELU, then bias)
+    laya::GemmPlan up4, down4, up4_sub, down4_sub;
 };
 
 laya::GemmPlan subset_plan(const laya::GemmPlan &full, int R, int N, int K, int epi) {
     laya::GemmPlan g;
     g.splits = full.splits;
     if (R <= 64)
-        g.config = epi ? 1 : 0;
+        g.config = (epi == 1 || epi == 2) ? 1 : 0;
     else if (R <= 256 || full.splits > 1)
         g.config = 2;  // split-capable
     else
@@ -449,6 +459,10 @@ PassPlans make_plans(const laya_config &c, int Tmax, int T, int R) {
     p.o = full_plan(Tmax, T, H, H, 0);
     p.up = full_plan(Tmax, T, F, H, 1);
     p.down = full_plan(Tmax, T, H, F, 0);
+    if (c.dec_head) {
+        p.up4 = full_plan(Tmax, T, 4 * H, H, 3);
+        p.down4 = full_plan(Tmax, T, H, 4 * H, 0);
+    }
     if (R > 0) {
         p.kv_sub = full_plan(Tmax, T, 2 * H, H, 2);
         p.kv_sub.splits = p.qkv.splits;
@@ -457,6 +471,10 @@ PassPlans make_plans(const laya_config &c, int Tmax, int T, int R) {
         p.o_sub = subset_plan(p.o, R, H, H, 0);
         p.up_sub = subset_plan(p.up, R, F, H, 1);
         p.down_sub = subset_plan(p.down, R, H, F, 0);
+        if (c.dec_head) {
+            p.up4_sub = subset_plan(p.up4, R, 4 * H, H, 3);
+            p.down4_sub = subset_plan(p.down4, R, H, 4 * H, 0);
+        }
     }
     return p;
 }
@@ -469,17 +487,22 @@ void gemm_scratch_bound(const laya_config &c, size_t *bytes) {
     auto acc = [&](const laya::GemmPlan &g, int M, int N, int epi) {
         b = std::max(b, laya::gemm_workspace_bytes(g, M, N, epi));
     };
-    int last_splits[4] = {-1, -1, -1, -1};
+    int last_splits[6] = {-1, -1, -1, -1, -1, -1};
     for (int T = 1; T <= tcap; ++T) {
         const PassPlans p = make_plans(c, T, T, 0);
         acc(p.qkv, T, 3 * H, 2);
         acc(p.o, T, H, 0);
         acc(p.up, T, F, 1);
         acc(p.down, T, H, 0);
+        if (c.dec_head) {
+            acc(p.up4, T, 4 * H, 3);
+            acc(p.down4, T, H, 0);
+        }
         // marker layer: its plans depend on T only through the K splits
-        const int sp[4] = {p.qkv.splits, p.o.splits, p.up.splits, p.down.splits};
-        if (std::equal(sp, sp + 4, last_splits)) continue;
-        std::copy(sp, sp + 4, last_splits);
+        const int sp[6] = {p.qkv.splits, p.o.splits,   p.up.splits,
+                           p.down.splits, p.up4.splits, p.down4.splits};
+        if (std::equal(sp, sp + 6, last_splits)) continue;
+        std::copy(sp, sp + 6, last_splits);
         for (int R = 1; R <= c.max_markers; ++R) {
             const PassPlans q = make_plans(c, T, T, R);
             acc(q.kv_sub, T, 2 * H, 2);
@@ -487,6 +510,10 @@ void gemm_scratch_bound(const laya_config &c, size_t *bytes) {
             acc(q.o_sub, R, H, 0);
             acc(q.up_sub, R, F, 1);
             acc(q.down_sub, R, H, 0);
+            if (c.dec_head) {
+                acc(q.up4_sub, R, 4 * H, 3);
+                acc(q.down4_sub, R, H, 0);
+            }
         }
     }
     *bytes = b;
@@ -587,6 +614,32 @@ int record(laya_encoder *enc, hipStream_t s, const RunShape &rs, Profiler *prof 
         const bf16_t *Wqkv = enc->wqkv[L], *Wo = enc->wo[L], *Wi = enc->wi[L],
                      *Wo2 = enc->wo2[L];
         const float *g1 = enc->gamma_ones;
+        // head variant: biased projections and a 4H-wide GELU FFN (W_i, W_o2
+        // then hold W_1 [4H][H] and W_2 [H][4H])
+        const bool head = c.dec_head && !is_enc;
+        const bf16_t *Bqkv = enc->bqkv[L], *Bo = enc->bo[L], *B1 = enc->b1[L], *B2 = enc->b2[L];
+        const int FW = head ? 4 * H : F;  // width of the FFN's inner activation
+        // up + activation and down projection into enc->proj (M rows, T_dev or
+        // Mmax rows when T_dev is null)
+        auto ffn = [&](const bf16_t *n_in, const int32_t *M_dev, int Mmax, double Mf,
+                       const laya::GemmPlan &pu, const laya::GemmPlan &pd) -> int {
+            if (head) {
+                L_OP(OP_UP_GELU, gemm_fl(Mf, FW, H), gemm_by(Mf, FW, FW, H) + FW * b2,
+                     laya::launch_gemm(s, n_in, H, Wi, H, enc->hid, FW, M_dev, Mmax, FW, H, 3,
+                                       pu, gp, nullptr, B1));
+                L_OP(OP_DOWN, gemm_fl(Mf, H, FW), gemm_by(Mf, H, H, FW) + H * b2,
+                     laya::launch_gemm(s, enc->hid, FW, Wo2, FW, enc->proj, H, M_dev, Mmax, H,
+                                       FW, 0, pd, gp, nullptr, B2));
+            } else {
+                L_OP(OP_UP_GEGLU, gemm_fl(Mf, 2 * F, H), gemm_by(Mf, 2 * F, F, H),
+                     laya::launch_gemm(s, n_in, H, Wi, H, enc->hid, F, M_dev, Mmax, F, H, 1,
+                                       pu, gp));
+                L_OP(OP_DOWN, gemm_fl(Mf, H, F), gemm_by(Mf, H, H, F),
+                     laya::launch_gemm(s, enc->hid, F, Wo2, F, enc->proj, H, M_dev, Mmax, H, F,
+                                       0, pd, gp));
+            }
+            return LAYA_OK;
+        };
 
         // attention sublayer: n = LN(x [+ f of the previous layer])
         L_OP(OP_LAYERNORM, 0, pending ? ln_res_by : ln_by,
@@ -605,7 +658,7 @@ int record(laya_encoder *enc, hipStream_t s, const RunShape &rs, Profiler *prof 
             const laya::QkvEpilogue qe{pos, ctab, stab, rope_cols, 2 * H, enc->vt, enc->ldvt, vtok};
             L_OP(OP_QKV, gemm_fl(T, 3 * H, H), gemm_by(T, 3 * H, 3 * H, H),
                  laya::launch_gemm(s, enc->nrm, H, Wqkv, H, enc->qkv, 3 * H, T_dev, Tmax, 3 * H,
-                                   H, 2, plans.qkv, gp, &qe));
+                                   H, 2, plans.qkv, gp, &qe, Bqkv));
             if (rs.rope_standalone)
                 L_OP(OP_ROPE, 0, 2 * T * 2 * H * b2,
                      laya::launch_rope(s, enc->qkv, 3 * H, 2 * nh, T_dev, Tmax, pos, ctab, stab));
@@ -616,16 +669,12 @@ int record(laya_encoder *enc, hipStream_t s, const RunShape &rs, Profiler *prof 
                  4 * T * H * b2, laya::launch_attention(s, ap));
             L_OP(OP_OUT_PROJ, gemm_fl(T, H, H), gemm_by(T, H, H, H),
                  laya::launch_gemm(s, enc->att, H, Wo, H, enc->proj, H, T_dev, Tmax, H, H, 0,
-                                   plans.o, gp));
+                                   plans.o, gp, nullptr, Bo));
             L_OP(OP_LAYERNORM, 0, ln_res_by,
                  laya::launch_layernorm(s, xr, enc->proj, enc->nrm, g1, T_dev, Tmax, H,
                                         c.ln_eps));
-            L_OP(OP_UP_GEGLU, gemm_fl(T, 2 * F, H), gemm_by(T, 2 * F, F, H),
-                 laya::launch_gemm(s, enc->nrm, H, Wi, H, enc->hid, F, T_dev, Tmax, F, H, 1,
-                                   plans.up, gp));
-            L_OP(OP_DOWN, gemm_fl(T, H, F), gemm_by(T, H, H, F),
-                 laya::launch_gemm(s, enc->hid, F, Wo2, F, enc->proj, H, T_dev, Tmax, H, F, 0,
-                                   plans.down, gp));
+            C_CHK(ffn(enc->nrm, T_dev, Tmax, T, head ? plans.up4 : plans.up,
+                      head ? plans.down4 : plans.down));
             pending = true;
             if (L == c.n_enc_layers - 1) {
                 // x += f; the encoder's final LayerNorm output becomes the decision stream
@@ -646,7 +695,8 @@ int record(laya_encoder *enc, hipStream_t s, const RunShape &rs, Profiler *prof 
                                           enc->ldvt, vtok};
             L_OP(OP_KV, gemm_fl(T, 2 * H, H), gemm_by(T, 2 * H, 2 * H, H),
                  laya::launch_gemm(s, enc->nrm, H, Wqkv + (size_t)H * H, H, enc->qkv, 2 * H,
-                                   T_dev, Tmax, 2 * H, H, 2, plans.kv_sub, gp, &qe_kv));
+                                   T_dev, Tmax, 2 * H, H, 2, plans.kv_sub, gp, &qe_kv,
+                                   Bqkv ? Bqkv + H : nullptr));
             if (rs.rope_standalone)
                 L_OP(OP_ROPE, 0, 2 * T * H * b2,
                      laya::launch_rope(s, enc->qkv, 2 * H, nh, T_dev, Tmax, pos, ctab, stab));
@@ -658,7 +708,7 @@ int record(laya_encoder *enc, hipStream_t s, const RunShape &rs, Profiler *prof 
                                          nullptr, 0, nullptr};
             L_OP(OP_Q, gemm_fl(R, H, H), gemm_by(R, H, H, H),
                  laya::launch_gemm(s, enc->n_sub, H, Wqkv, H, enc->q_sub, H, nullptr, Ri, H, H,
-                                   2, plans.q_sub, gp, &qe_q));
+                                   2, plans.q_sub, gp, &qe_q, Bqkv));
             if (rs.rope_standalone)
                 L_OP(OP_ROPE, 0, 2 * R * H * b2,
                      laya::launch_rope(s, enc->q_sub, H, nh, nullptr, Ri, mrk_pos, ctab, stab));
@@ -669,16 +719,12 @@ int record(laya_encoder *enc, hipStream_t s, const RunShape &rs, Profiler *prof 
                  laya::launch_attention(s, ap));
             L_OP(OP_OUT_PROJ, gemm_fl(R, H, H), gemm_by(R, H, H, H),
                  laya::launch_gemm(s, enc->att, H, Wo, H, enc->proj, H, nullptr, Ri, H, H, 0,
-                                   plans.o_sub, gp));
+                                   plans.o_sub, gp, nullptr, Bo));
             L_OP(OP_LAYERNORM, 0, 4 * R * H * b2,
                  laya::launch_layernorm(s, enc->x_sub, enc->proj, enc->n_sub, g1, nullptr, Ri,
                                         H, c.ln_eps));
-            L_OP(OP_UP_GEGLU, gemm_fl(R, 2 * F, H), gemm_by(R, 2 * F, F, H),
-                 laya::launch_gemm(s, enc->n_sub, H, Wi, H, enc->hid, F, nullptr, Ri, F, H, 1,
-                                   plans.up_sub, gp));
-            L_OP(OP_DOWN, gemm_fl(R, H, F), gemm_by(R, H, H, F),
-                 laya::launch_gemm(s, enc->hid, F, Wo2, F, enc->proj, H, nullptr, Ri, H, F, 0,
-                                   plans.down_sub, gp));
+            C_CHK(ffn(enc->n_sub, nullptr, Ri, R, head ? plans.up4_sub : plans.up_sub,
+                      head ? plans.down4_sub : plans.down_sub));
             L_OP(OP_LAYERNORM, 0, 4 * R * H * b2,
                  laya::launch_layernorm(s, enc->x_sub, enc->proj, enc->out, g1, nullptr, Ri, H,
                                         c.ln_eps));
@@ -751,6 +797,7 @@ void laya_config_init(laya_config *c) {
     c->max_markers = 2048;
     c->max_graphs = 4;
     c->workspace_budget_mib = 512;
+    c->dec_head = 0;
 }
 
 const char *laya_last_error(void) { return g_last_error.c_str(); }
@@ -810,13 +857,24 @@ int laya_encoder_create(const laya_config *cfg, uint64_t seed, int device, laya_
         tensors.push_back({off, elems});
         off += al(elems * 2);
     };
-    add((size_t)c.vocab * H);
+    // (offset, rows, cols) in tensor-id order
+    std::vector<std::array<int64_t, 2>> shapes;
+    shapes.push_back({c.vocab, H});
     for (int L = 0; L < NL; ++L) {
-        add((size_t)3 * H * H);
-        add((size_t)H * H);
-        add((size_t)2 * F * H);
-        add((size_t)H * F);
+        const bool head = c.dec_head && L >= c.n_enc_layers;
+        shapes.push_back({3 * H, H});
+        shapes.push_back({H, H});
+        shapes.push_back({head ? 4 * H : 2 * F, H});
+        shapes.push_back({H, head ? 4 * H : F});
     }
+    if (c.dec_head)
+        for (int d = 0; d < c.n_dec_layers; ++d) {
+            shapes.push_back({1, 3 * H});
+            shapes.push_back({1, H});
+            shapes.push_back({1, 4 * H});
+            shapes.push_back({1, H});
+        }
+    for (auto &sh : shapes) add((size_t)sh[0] * sh[1]);
     const size_t gamma_off = off;
     off += al((size_t)H * 4);
     const size_t tab_off = off;
@@ -826,12 +884,21 @@ int laya_encoder_create(const laya_config *cfg, uint64_t seed, int device, laya_
     if (hipMalloc(&enc->wmem, off) != hipSuccess)
         return bail(set_global_error(LAYA_E_NOMEM, "weights: hipMalloc failed"));
     char *wb = static_cast<char *>(enc->wmem);
-    enc->emb = reinterpret_cast<bf16_t *>(wb + tensors[0].first);
+    for (size_t t = 0; t < tensors.size(); ++t)
+        enc->tensors.push_back({reinterpret_cast<bf16_t *>(wb + tensors[t].first),
+                                (int32_t)shapes[t][0], (int32_t)shapes[t][1]});
+    enc->emb = enc->tensors[0].dev;
     for (int L = 0; L < NL; ++L) {
-        enc->wqkv.push_back(reinterpret_cast<bf16_t *>(wb + tensors[1 + 4 * L].first));
-        enc->wo.push_back(reinterpret_cast<bf16_t *>(wb + tensors[2 + 4 * L].first));
-        enc->wi.push_back(reinterpret_cast<bf16_t *>(wb + tensors[3 + 4 * L].first));
-        enc->wo2.push_back(reinterpret_cast<bf16_t *>(wb + tensors[4 + 4 * L].first));
+        enc->wqkv.push_back(enc->tensors[1 + 4 * L].dev);
+        enc->wo.push_back(enc->tensors[2 + 4 * L].dev);
+        enc->wi.push_back(enc->tensors[3 + 4 * L].dev);
+        enc->wo2.push_back(enc->tensors[4 + 4 * L].dev);
+        const bool head = c.dec_head && L >= c.n_enc_layers;
+        const int bt = 1 + 4 * NL + 4 * (L - c.n_enc_layers);
+        enc->bqkv.push_back(head ? enc->tensors[bt + 0].dev : nullptr);
+        enc->bo.push_back(head ? enc->tensors[bt + 1].dev : nullptr);
+        enc->b1.push_back(head ? enc->tensors[bt + 2].dev : nullptr);
+        enc->b2.push_back(head ? enc->tensors[bt + 3].dev : nullptr);
     }
     enc->gamma_ones = reinterpret_cast<float *>(wb + gamma_off);
     enc->cos_g = reinterpret_cast<bf16_t *>(wb + tab_off);
@@ -876,7 +943,8 @@ int laya_encoder_create(const laya_config *cfg, uint64_t seed, int device, laya_
         {&enc->xa, (size_t)tcap * H},      {&enc->xb, (size_t)tcap * H},
         {&enc->nrm, (size_t)tcap * H},     {&enc->qkv, (size_t)tcap * 3 * H},
         {&enc->att, (size_t)tcap * H},     {&enc->proj, (size_t)tcap * H},
-        {&enc->hid, (size_t)tcap * F},     {&enc->out, (size_t)tcap * H},
+        {&enc->hid, (size_t)tcap * (c.dec_head ? std::max(F, 4 * H) : F)},
+        {&enc->out, (size_t)tcap * H},
         {&enc->x_sub, (size_t)rcap * H},   {&enc->n_sub, (size_t)rcap * H},
         {&enc->q_sub, (size_t)rcap * H},   {&enc->vt, (size_t)H * ldvt}};
     for (auto &b : bufs) wsz += al(b.second * 2);
@@ -1134,23 +1202,11 @@ int laya_encoder_layer_output(laya_encoder *enc, int32_t index, laya_output *out
 int laya_encoder_weight(laya_encoder *enc, int32_t tid, const void **dev, int32_t *rows,
                         int32_t *cols) {
     if (!enc || !dev || !rows || !cols) return set_global_error(LAYA_E_INVALID, "NULL argument");
-    const laya_config &c = enc->cfg;
-    const int NL = layer_count(c);
-    if (tid < 0 || tid > 4 * NL) return fail(enc, LAYA_E_INVALID, "tensor id out of range");
-    const int H = c.hidden, F = c.ffn;
-    if (tid == 0) {
-        *dev = enc->emb;
-        *rows = c.vocab;
-        *cols = H;
-        return LAYA_OK;
-    }
-    const int L = (tid - 1) / 4, kind = (tid - 1) % 4;
-    switch (kind) {
-        case 0: *dev = enc->wqkv[L]; *rows = 3 * H; *cols = H; break;
-        case 1: *dev = enc->wo[L]; *rows = H; *cols = H; break;
-        case 2: *dev = enc->wi[L]; *rows = 2 * F; *cols = H; break;
-        default: *dev = enc->wo2[L]; *rows = H; *cols = F; break;
-    }
+    if (tid < 0 || tid >= (int32_t)enc->tensors.size())
+        return fail(enc, LAYA_E_INVALID, "tensor id out of range");
+    *dev = enc->tensors[tid].dev;
+    *rows = enc->tensors[tid].rows;
+    *cols = enc->tensors[tid].cols;
     return LAYA_OK;
 }
 
@@ -1337,11 +1393,11 @@ namespace {
 int op_gemm_launch(const char *who, hipStream_t s, const void *A, int32_t lda, const void *W,
                    int32_t ldw, void *C, int32_t ldc, int32_t M, int32_t N, int32_t K,
                    int32_t epilogue, int32_t config, int32_t splits,
-                   const laya::QkvEpilogue *qe) {
+                   const laya::QkvEpilogue *qe, const void *bias) {
     laya::GemmPlan plan = laya::plan_gemm(M, N, K, epilogue);
     if (config >= 0) plan = laya::GemmPlan{config, splits < 1 ? 1 : splits};
     if (plan.splits > K / 64 || plan.splits > laya::gemm_max_splits(plan.config) ||
-        (epilogue && plan.config == 0))
+        ((epilogue == 1 || epilogue == 2) && plan.config == 0))
         return set_global_error(LAYA_E_INVALID, std::string(who) + ": unsupported config/splits");
     const size_t pb = laya::gemm_workspace_bytes(plan, M, N, epilogue);
     void *scratch = nullptr;
@@ -1350,7 +1406,8 @@ int op_gemm_launch(const char *who, hipStream_t s, const void *A, int32_t lda, c
     hipError_t e = laya::launch_gemm(s, static_cast<const bf16_t *>(A), lda,
                                      static_cast<const bf16_t *>(W), ldw,
                                      static_cast<bf16_t *>(C), ldc, nullptr, M, N, K, epilogue,
-                                     plan, static_cast<float *>(scratch), qe);
+                                     plan, static_cast<float *>(scratch), qe,
+                                     static_cast<const bf16_t *>(bias));
     if (pb) {
         if (e == hipSuccess) e = hipStreamSynchronize(s);
         hipFree(scratch);
@@ -1370,20 +1427,21 @@ bool gemm_args_ok(const void *A, int32_t lda, const void *W, int32_t ldw, const 
 
 int laya_op_gemm(void *stream, const void *A, int32_t lda, const void *W, int32_t ldw, void *C,
                  int32_t ldc, int32_t M, int32_t N, int32_t K, int32_t epilogue, int32_t config,
-                 int32_t splits) {
+                 int32_t splits, const void *bias) {
     if (!gemm_args_ok(A, lda, W, ldw, C, ldc, M, N, K, config) ||
-        (epilogue != 0 && epilogue != 1))
+        (epilogue != 0 && epilogue != 1 && epilogue != 3) || (epilogue == 1 && bias) ||
+        (epilogue == 3 && M > 0 && !bias))
         return set_global_error(LAYA_E_INVALID, "laya_op_gemm: bad arguments");
     if (M == 0) return LAYA_OK;
     return op_gemm_launch("laya_op_gemm", static_cast<hipStream_t>(stream), A, lda, W, ldw, C,
-                          ldc, M, N, K, epilogue, config, splits, nullptr);
+                          ldc, M, N, K, epilogue, config, splits, nullptr, bias);
 }
 
 int laya_op_gemm_qkv(void *stream, const void *A, int32_t lda, const void *W, int32_t ldw,
                      void *C, int32_t ldc, int32_t M, int32_t N, int32_t K, const int32_t *pos,
                      const void *cos_tab, const void *sin_tab, int32_t rope_cols, void *vt,
                      int32_t ldvt, const int32_t *vt_tok, int32_t vt_col0, int32_t config,
-                     int32_t splits) {
+                     int32_t splits, const void *bias) {
     if (!gemm_args_ok(A, lda, W, ldw, C, ldc, M, N, K, config) || rope_cols < 0 ||
         rope_cols % 64 || vt_col0 % 64 || rope_cols > vt_col0 || vt_col0 > N ||
         (M > 0 && rope_cols > 0 && (!pos || !cos_tab || !sin_tab)) ||
@@ -1394,7 +1452,7 @@ int laya_op_gemm_qkv(void *stream, const void *A, int32_t lda, const void *W, in
                                static_cast<const bf16_t *>(sin_tab), rope_cols, vt_col0,
                                static_cast<bf16_t *>(vt), ldvt, vt_tok};
     return op_gemm_launch("laya_op_gemm_qkv", static_cast<hipStream_t>(stream), A, lda, W, ldw,
-                          C, ldc, M, N, K, 2, config, splits, &qe);
+                          C, ldc, M, N, K, 2, config, splits, &qe, bias);
 }
 
 int laya_op_rope(void *stream, void *buf, int32_t ld, int32_t n_heads_rot, int32_t rows,

@@ -43,6 +43,11 @@
 //
 // QKV epilogue (epilogue 2): RoPE on the Q and K heads in registers and the
 // V columns stored transposed for attention (see QkvEpilogue).
+//
+// Bias: with a bias vector, a product is rounded to BF16, the bias added and
+// the sum rounded again, y = bf16(bf16(A W^T) + b) (a biased dense layer as
+// the matmul followed by x + b in the model's precision); epilogue 3 then
+// takes GELU of that BF16 value, h = bf16(GELU(y)).
 #include "kernels.h"
 
 namespace laya {
@@ -148,8 +153,9 @@ struct GemmParams {
     const int32_t *M_dev;
     int32_t M_max, N, K;
     int32_t splits;
-    float *partial;  // [tiles][splits][BW*BT] (splits > 1)
-    QkvEpilogue qe;  // epilogue 2 only
+    float *partial;      // [tiles][splits][BW*BT] (splits > 1)
+    QkvEpilogue qe;      // epilogue 2 only
+    const bf16_t *bias;  // [N] or null (epilogues 0 and 2; required by 3)
 };
 
 // MODE 0: whole K, C written.  MODE 1: one K range per blockIdx.z, its
@@ -162,7 +168,7 @@ template <class G, int EPI, int MODE>
 __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
     constexpr int BW = G::BW, BT = G::BT, FA = G::FA, FB = G::FB, STAGES = G::STAGES;
     constexpr int BK = G::BK, CH = G::CH, RPL = G::RPL;
-    static_assert(EPI == 0 || FA % 2 == 0, "GeGLU / QKV need paired fragments");
+    static_assert(EPI == 0 || EPI >= 3 || FA % 2 == 0, "GeGLU / QKV need paired fragments");
     static_assert(EPI != 2 || G::RW % 64 == 0, "QKV epilogue: a wave's rows are whole heads");
     const int32_t M = p.M_dev ? *p.M_dev : p.M_max;
     int bx = blockIdx.x, by = blockIdx.y;
@@ -411,6 +417,14 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
             &sC[tl * BN + ((c ^ (tl & (NCH - 1))) << 3) + (fl & 4)]) = u32x2_t{lo, hi};
     };
     auto bf16r = [](float v) { return bf16_to_f32(f32_to_bf16(v)); };
+    // four consecutive bias values (f a multiple of 4; the bias is 8-byte aligned)
+    auto bias4 = [&](int32_t f, float (&bv)[4]) {
+        const u32x2_t w = *reinterpret_cast<const u32x2_t *>(p.bias + f);
+        bv[0] = bf16lo(w[0]);
+        bv[1] = bf16hi(w[0]);
+        bv[2] = bf16lo(w[1]);
+        bv[3] = bf16hi(w[1]);
+    };
 #pragma unroll
     for (int b = 0; b < FB; ++b) {
         const int tl = wc * G::RT + 32 * b + l32;  // token within the tile
@@ -442,11 +456,19 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
                         const int j = 8 * g4 + 4 * lhi;  // pair index of element 4*g4
                         const u32x2_t cv = *reinterpret_cast<const u32x2_t *>(q.cos_tab + ps + j);
                         const u32x2_t sv = *reinterpret_cast<const u32x2_t *>(q.sin_tab + ps + j);
-                        float xo[4], yo[4];
+                        float xo[4], yo[4], bx[4] = {0, 0, 0, 0}, by[4] = {0, 0, 0, 0};
+                        if (p.bias) {
+                            bias4(f0 + j, bx);
+                            bias4(f0 + 32 + j, by);
+                        }
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
-                            const float x = bf16r(acc[a][b][4 * g4 + e]);
-                            const float y = bf16r(acc[a + 1][b][4 * g4 + e]);
+                            float x = bf16r(acc[a][b][4 * g4 + e]);
+                            float y = bf16r(acc[a + 1][b][4 * g4 + e]);
+                            if (p.bias) {
+                                x = bf16r(x + bx[e]);
+                                y = bf16r(y + by[e]);
+                            }
                             const float c = (e & 1) ? bf16hi(cv[e >> 1]) : bf16lo(cv[e >> 1]);
                             const float sn = (e & 1) ? bf16hi(sv[e >> 1]) : bf16lo(sv[e >> 1]);
                             // both products of BF16 values are exact in float32
@@ -465,10 +487,17 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
 #pragma unroll
                         for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-                            for (int e = 0; e < 16; ++e) {
-                                const int32_t f = f0 + 32 * h2 + 8 * (e / 4) + 4 * lhi + e % 4;
-                                vcol[(size_t)(f - q.vt_col0) * q.ldvt] =
-                                    (bf16_t)f32_to_bf16(acc[a + h2][b][e]);
+                            for (int g = 0; g < 4; ++g) {
+                                const int32_t f4 = f0 + 32 * h2 + 8 * g + 4 * lhi;
+                                float bv[4] = {0, 0, 0, 0};
+                                if (p.bias) bias4(f4, bv);
+#pragma unroll
+                                for (int e = 0; e < 4; ++e) {
+                                    float v = acc[a + h2][b][4 * g + e];
+                                    if (p.bias) v = bf16r(v) + bv[e];
+                                    vcol[(size_t)(f4 + e - q.vt_col0) * q.ldvt] =
+                                        (bf16_t)f32_to_bf16(v);
+                                }
                             }
                     }
                 } else {
@@ -476,21 +505,39 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
                     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
                         for (int g4 = 0; g4 < 4; ++g4) {
-                            const f32x16_t &v = acc[a + h2][b];
-                            put4(tl, wrow[a] + 32 * h2 + 8 * g4 + 4 * lhi,
-                                 pack_bf16x2(v[4 * g4], v[4 * g4 + 1]),
-                                 pack_bf16x2(v[4 * g4 + 2], v[4 * g4 + 3]));
+                            const int fl = wrow[a] + 32 * h2 + 8 * g4 + 4 * lhi;
+                            float v[4], bv[4] = {0, 0, 0, 0};
+                            if (p.bias) bias4(n0 + fl, bv);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                v[e] = acc[a + h2][b][4 * g4 + e];
+                                if (p.bias) v[e] = bf16r(v[e]) + bv[e];
+                            }
+                            put4(tl, fl, pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
                         }
                 }
             }
         } else {
+            // epilogue 0 (plain), 4 (plain + bias) and 3 (bias, then GELU)
+            constexpr bool has_bias = EPI == 3 || EPI == 4;
 #pragma unroll
             for (int a = 0; a < FA; ++a)
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4) {
-                    const f32x16_t &v = acc[a][b];
-                    put4(tl, wrow[a] + 8 * g4 + 4 * lhi, pack_bf16x2(v[4 * g4], v[4 * g4 + 1]),
-                         pack_bf16x2(v[4 * g4 + 2], v[4 * g4 + 3]));
+                    const int fl = wrow[a] + 8 * g4 + 4 * lhi;
+                    float v[4], bv[4];
+                    // columns past N (clamped weight rows) are never stored; N is
+                    // a multiple of 64, so a group of 4 is wholly in or out
+                    if constexpr (has_bias) bias4(min(n0 + fl, N - 4), bv);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        v[e] = acc[a][b][4 * g4 + e];
+                        if constexpr (has_bias) {
+                            v[e] = bf16r(v[e]) + bv[e];
+                            if constexpr (EPI == 3) v[e] = gelu_erf(bf16r(v[e]));
+                        }
+                    }
+                    put4(tl, fl, pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
                 }
         }
     }
@@ -530,8 +577,15 @@ hipError_t launch_mode(hipStream_t s, const GemmParams &p, int epilogue) {
     const int bn = epilogue == 1 ? G::BW / 2 : G::BW;
     const dim3 grid((p.N + bn - 1) / bn, (p.M_max + G::BT - 1) / G::BT,
                     MODE == kPartial ? p.splits : 1);
-    if (epilogue == 0) {
-        hipLaunchKernelGGL((gemm_kernel<G, 0, MODE>), grid, dim3(G::NTHR), 0, s, p);
+    // partial tiles are the same for the plain and bias epilogues (the bias
+    // is applied by the reduce launch)
+    if (epilogue == 0 || (MODE == kPartial && epilogue == 3)) {
+        if (MODE != kPartial && p.bias)
+            hipLaunchKernelGGL((gemm_kernel<G, 4, MODE>), grid, dim3(G::NTHR), 0, s, p);
+        else
+            hipLaunchKernelGGL((gemm_kernel<G, 0, MODE>), grid, dim3(G::NTHR), 0, s, p);
+    } else if (epilogue == 3) {
+        hipLaunchKernelGGL((gemm_kernel<G, 3, MODE>), grid, dim3(G::NTHR), 0, s, p);
     } else if constexpr (G::FA % 2 == 0 && G::RW % 64 == 0) {
         if (epilogue == 1)
             hipLaunchKernelGGL((gemm_kernel<G, 1, MODE>), grid, dim3(G::NTHR), 0, s, p);
@@ -590,7 +644,7 @@ GemmPlan plan_gemm(int32_t M_max, int32_t N, int32_t K, int epilogue) {
     if (M_max <= 64) {
         // small M: stream the weights with many narrow tiles; split K until
         // about 2 workgroups per CU
-        g.config = epilogue ? 1 : 0;
+        g.config = (epilogue == 1 || epilogue == 2) ? 1 : 0;
         const int64_t tiles = (nw + kCfgs[g.config].bw - 1) / kCfgs[g.config].bw;
         int s = 1;
         while (s < 8 && tiles * s * 2 <= 512 && np / (s * 2) >= 2) s *= 2;
@@ -618,8 +672,11 @@ size_t gemm_workspace_bytes(const GemmPlan &g, int32_t M_max, int32_t N, int epi
 hipError_t launch_gemm(hipStream_t s, const bf16_t *A, int32_t lda, const bf16_t *W,
                        int32_t ldw, bf16_t *C, int32_t ldc, const int32_t *M_dev,
                        int32_t M_max, int32_t N, int32_t K, int epilogue, const GemmPlan &plan,
-                       float *partial, const QkvEpilogue *qe) {
+                       float *partial, const QkvEpilogue *qe, const bf16_t *bias) {
     if (M_max <= 0 || N <= 0) return hipSuccess;
+    if (epilogue < 0 || epilogue > 3 || (epilogue == 3 && !bias) || (epilogue == 1 && bias) ||
+        reinterpret_cast<uintptr_t>(bias) % 8 != 0)
+        return hipErrorInvalidValue;
     if (epilogue == 2 && (!qe || qe->rope_cols % 64 || qe->vt_col0 % 64 ||
                           qe->rope_cols > qe->vt_col0 || (qe->rope_cols > 0 && !qe->pos) ||
                           (qe->vt_col0 < N && (!qe->vt || !qe->vt_tok))))
@@ -629,7 +686,7 @@ hipError_t launch_gemm(hipStream_t s, const bf16_t *A, int32_t lda, const bf16_t
         return hipErrorInvalidValue;
     if (plan.splits > 1 && !partial) return hipErrorInvalidValue;
     GemmParams p{A, lda, W, ldw, C, ldc, M_dev, M_max, N, K, plan.splits, partial,
-                 epilogue == 2 ? *qe : QkvEpilogue{}};
+                 epilogue == 2 ? *qe : QkvEpilogue{}, bias};
     switch (plan.config) {
         case 0: return launch_small<CfgXS>(s, p, epilogue);
         case 1: return launch_small<CfgXSG>(s, p, epilogue);

@@ -75,12 +75,15 @@ struct QkvEpilogue {
     const int32_t *vt_tok;  // vt column of each output row
 };
 
-// C = bf16(A W^T), epilogue 0 plain, 1 GeGLU (W has 2N rows), 2 QKV (`qe`).
-// With plan.splits > 1, `partial` is required and two kernels are queued.
+// C = bf16(A W^T), epilogue 0 plain, 1 GeGLU (W has 2N rows), 2 QKV (`qe`),
+// 3 bias then GELU.  `bias` ([N], BF16, optional for 0 and 2, required for 3,
+// not allowed for 1): y = bf16(bf16(A W^T) + bias).  With plan.splits > 1,
+// `partial` is required and two kernels are queued.
 hipError_t launch_gemm(hipStream_t s, const bf16_t *A, int32_t lda, const bf16_t *W,
                        int32_t ldw, bf16_t *C, int32_t ldc, const int32_t *M_dev,
                        int32_t M_max, int32_t N, int32_t K, int epilogue, const GemmPlan &plan,
-                       float *partial, const QkvEpilogue *qe = nullptr);
+                       float *partial, const QkvEpilogue *qe = nullptr,
+                       const bf16_t *bias = nullptr);
 
 hipError_t launch_rope(hipStream_t s, bf16_t *buf, int32_t ld, int32_t n_heads_rot,
                        const int32_t *count_dev, int32_t rows_max, const int32_t *pos,

@@ -45,6 +45,7 @@ MODEL = dict(
     max_markers=2048,
     max_graphs=4,              # captured graphs kept, LRU over shape keys
     workspace_budget_mib=512,  # the workspace must fit this
+    dec_head=0,                # 1: biased head variant of the decision layers
 )
 
 # A tiny model of the same structure, for brute-force checks of the oracle and
@@ -67,6 +68,7 @@ TINY = dict(
     max_markers=64,
     max_graphs=4,
     workspace_budget_mib=512,
+    dec_head=0,
 )
 
 WEIGHT_SEED = 1
