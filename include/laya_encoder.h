@@ -373,8 +373,9 @@ int laya_op_layernorm(void *stream, void *x, const void *r, void *n, const float
  * [M][lda], W device BF16 [N or 2N][ldw], C device BF16 [M][ldc]; K a multiple
  * of 64, N a multiple of 64, lda/ldw/ldc multiples of 8 (16-byte rows).
  * config -1 picks the tile shape and K split the pass itself would use for M
- * rows; config 0..5 (tile shapes 32x64, 64x64, 128x64, 128x128, 256x128,
- * 256x256 weight rows x tokens) with `splits` K ranges forces one (split K
+ * rows; config 0..6 (tile shapes 32x64, 64x64, 128x64, 128x128, 256x128,
+ * 256x256, and 128x128 with a shallower ring that fits two per compute unit;
+ * weight rows x tokens) with `splits` K ranges forces one (split K
  * only on shapes 0..3; GeGLU not on shape 0).  Each output is the sum, in
  * order, of one MFMA chain per K range, so results depend only on `splits`.
  * With splits > 1 the call allocates its scratch and synchronises the

@@ -368,7 +368,7 @@ def test_gemm_every_tile_shape_and_split(B, M, N, K, epi):
         want = oracle.bf16_round(oracle.linear(a_h, w_h))
     for splits in (1, 2, 5):
         outs = []
-        for cfg in range(6):
+        for cfg in range(7):
             if (epi and cfg == 0) or (splits > 1 and cfg > 3):
                 continue
             c = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
@@ -400,7 +400,7 @@ def test_gemm_split_k_repeats_bitwise(B):
 # ------------------------------------------------------- QKV epilogue (fused) --
 
 @pytest.mark.parametrize("M,H,cfgs,splits", [(48, 128, (1, 2, 3), (1, 2, 5)),
-                                             (300, 1024, (2, 3, 4, 5), (1,)),
+                                             (300, 1024, (2, 3, 4, 5, 6), (1,)),
                                              (97, 256, (1, 2, 3), (1, 4))])
 def test_gemm_qkv_epilogue_equals_gemm_then_rope(B, M, H, cfgs, splits):
     """The QKV epilogue gives bitwise the plain GEMM followed by the RoPE

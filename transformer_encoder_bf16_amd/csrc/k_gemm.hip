@@ -562,7 +562,7 @@ using CfgS = Cfg<128, 64, 2, 2, 64, 4>;    // 4 waves of 64 rows x 32 tokens
 using CfgM = Cfg<128, 128, 2, 2, 64, 4>;   // 4 waves of 64 x 64
 using CfgL = Cfg<256, 128, 2, 4, 64, 3>;   // 8 waves of 128 x 32
 using CfgXL = Cfg<256, 256, 2, 4, 64, 2>;  // 8 waves of 128 x 64
-using CfgXL4 = Cfg<256, 256, 2, 2, 64, 2>;  // 4 waves of 128 x 128
+using CfgM2 = Cfg<128, 128, 2, 2, 64, 2>;   // M with a 2-stage ring: 64 KB, two per CU
 
 struct CfgInfo {
     int bw, bt;
@@ -570,7 +570,7 @@ struct CfgInfo {
 constexpr CfgInfo kCfgs[kGemmConfigs] = {{CfgXS::BW, CfgXS::BT}, {CfgXSG::BW, CfgXSG::BT},
                                          {CfgS::BW, CfgS::BT},   {CfgM::BW, CfgM::BT},
                                          {CfgL::BW, CfgL::BT},   {CfgXL::BW, CfgXL::BT},
-                                         {CfgXL4::BW, CfgXL4::BT}};
+                                         {CfgM2::BW, CfgM2::BT}};
 
 template <class G, int MODE>
 hipError_t launch_mode(hipStream_t s, const GemmParams &p, int epilogue) {
@@ -615,19 +615,24 @@ hipError_t launch_large(hipStream_t s, const GemmParams &p, int epilogue) {
 int gemm_max_splits(int config) { return config <= 3 ? 8 : 1; }
 
 GemmPlan plan_gemm_tiles(int32_t M, int32_t N, int32_t K, int epilogue) {
-    // Tile shape with the least estimated time: whole waves of workgroups
-    // over the 256 compute units times the per-tile cost, with the relative
-    // per-CU throughput of each shape.
+    // Tile shape with the least estimated time: the tiles the busiest of the
+    // 256 compute units gets, times the per-tile cost, with each shape's
+    // relative per-CU throughput (measured on the pass's shapes, weights
+    // streamed from HBM).  The 2-stage 128x128 shape fits two workgroups per
+    // CU, which hide each other's waits, but its shallow ring cannot cover
+    // HBM latency on its own: it pays only where every CU runs a long queue
+    // of tiles (at least 4).
     const int64_t nw = epilogue == 1 ? 2LL * N : N;
-    const int cand[4] = {2, 3, 4, 5};
-    const double eff[4] = {0.45, 0.70, 0.85, 1.0};
+    const int cand[5] = {2, 3, 4, 5, 6};
+    const double eff[5] = {0.45, 0.70, 0.85, 1.0, 1.0};
     GemmPlan g{3, 1};
     double best = 1e30;
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 5; ++i) {
         const CfgInfo &c = kCfgs[cand[i]];
         const int64_t tiles = ((nw + c.bw - 1) / c.bw) * ((M + c.bt - 1) / c.bt);
-        const int64_t waves = (tiles + 255) / 256;
-        const double t = (double)waves * c.bw * c.bt / eff[i];
+        const int64_t per_cu = (tiles + 255) / 256;
+        const double e = (cand[i] == 6 && per_cu < 4) ? 0.50 : eff[i];
+        const double t = (double)per_cu * c.bw * c.bt / e;
         if (t < best) {
             best = t;
             g.config = cand[i];
@@ -694,7 +699,7 @@ hipError_t launch_gemm(hipStream_t s, const bf16_t *A, int32_t lda, const bf16_t
         case 3: return launch_small<CfgM>(s, p, epilogue);
         case 4: return launch_large<CfgL>(s, p, epilogue);
         case 5: return launch_large<CfgXL>(s, p, epilogue);
-        default: return launch_large<CfgXL4>(s, p, epilogue);
+        default: return launch_large<CfgM2>(s, p, epilogue);
     }
 }
 

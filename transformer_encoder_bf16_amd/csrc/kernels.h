@@ -48,7 +48,7 @@ hipError_t launch_layernorm(hipStream_t s, bf16_t *x, const bf16_t *r, bf16_t *n
 constexpr int kGemmConfigs = 7;
 struct GemmPlan {
     int config;  // 0 XS 32x64, 1 XSG 64x64, 2 S 128x64, 3 M 128x128, 4 L 256x128, 5 XL 256x256,
-                 // 6 XL4 256x256 (4 waves)
+                 // 6 M2 128x128 with a 2-stage ring (two workgroups per CU)
     int splits;  // K ranges (>= 1)
 };
 // plan for a GEMM launched with a grid for M_max rows (the K split depends
