@@ -48,6 +48,8 @@
 // the sum rounded again, y = bf16(bf16(A W^T) + b) (a biased dense layer as
 // the matmul followed by x + b in the model's precision); epilogue 3 then
 // takes GELU of that BF16 value, h = bf16(GELU(y)).
+#include <algorithm>
+
 #include "kernels.h"
 
 namespace laya {
@@ -124,6 +126,58 @@ __device__ __forceinline__ bool tile_order(int live_by, int &bx, int &by) {
     return true;
 }
 
+// Two-dimensional split of the tile grid over the 8 XCDs: XCD x takes the
+// block of weight tiles xk = x % xw and token tiles xt = x / xw (xw * xt
+// ranges = 8 blocks), so its L2 fetches 1/xw of the weights and xw/8 of the
+// activations instead of all of the weights; inside the block the tiles go
+// in groups of 4 token tiles as above.  The j-th workgroup dispatched to XCD
+// x takes the j-th tile of the block; the host pads the grid so that every
+// XCD has a slot for each tile of the largest block, whichever split the
+// live token count selects.
+//
+// The split (xw weight ranges, 1 = the 1-D order) minimises the rows one XCD
+// reads, weight rows / xw + token rows * xw / 8, among the splits whose
+// largest block needs no more rounds of the XCD's 32 CUs (occ workgroups
+// each) than the even 1-D share: a block a few tiles over a round doubles
+// the time of the whole launch.
+__device__ __forceinline__ int pick_xw(int nbx, int live_by, int bw, int bt, int occ) {
+    const int slots = 32 * occ;
+    const int r1 = ((nbx * live_by + 7) / 8 + slots - 1) / slots;
+    int best = 1;
+    int64_t cost = (int64_t)nbx * bw * 8 + (int64_t)live_by * bt;
+    for (int xw = 2; xw <= 8; xw *= 2) {
+        const int xtn = 8 / xw;
+        const int bmax = ((live_by + xtn - 1) / xtn) * ((nbx + xw - 1) / xw);
+        if ((bmax + slots - 1) / slots > r1) continue;
+        const int64_t c = (int64_t)nbx * bw * 8 / xw + (int64_t)live_by * bt * xw;
+        if (c < cost) {
+            cost = c;
+            best = xw;
+        }
+    }
+    return best;
+}
+
+__device__ __forceinline__ bool tile_order_2d(int live_by, int xw, int &bx, int &by) {
+    const int nbx = gridDim.x;
+    const int d = blockIdx.y * nbx + blockIdx.x;
+    const int xtn = 8 / xw;
+    const int x = d & 7, j = d >> 3;
+    const int xt = x / xw, xk = x % xw;
+    const int t_lo = xt * live_by / xtn, t_hi = (xt + 1) * live_by / xtn;
+    const int w_lo = xk * nbx / xw, w_hi = (xk + 1) * nbx / xw;
+    const int nt = t_hi - t_lo, nw = w_hi - w_lo;
+    if (j >= nt * nw) return false;
+    constexpr int GT = 4;
+    const int group = j / (GT * nw);
+    const int first = group * GT;
+    const int gsize = min(nt - first, GT);
+    const int idx = j - group * GT * nw;
+    bx = w_lo + idx / gsize;
+    by = t_lo + first + idx % gsize;
+    return true;
+}
+
 template <int BW_, int BT_, int WW_, int WT_, int BK_, int STAGES_>
 struct Cfg {
     static constexpr int BW = BW_, BT = BT_, WW = WW_, WT = WT_, BK = BK_, STAGES = STAGES_;
@@ -131,6 +185,8 @@ struct Cfg {
     static constexpr int RW = BW / WW, RT = BT / WT;  // rows / tokens per wave
     static constexpr int FA = RW / 32, FB = RT / 32;  // 32x32 fragments per wave
     static constexpr int STAGE_ELEMS = (BW + BT) * BK;
+    // workgroups per CU that the ring's LDS allows (at most 2 used)
+    static constexpr int OCC = (160 * 1024) / (STAGES * STAGE_ELEMS * 2) >= 2 ? 2 : 1;
     static constexpr int CH = BK / 8;                      // 16-byte chunks per row
     static constexpr int RPL = 64 / CH;                    // rows per 1 KB DMA load
     static constexpr int LOADS = (BW + BT) / RPL / NWAVE;  // DMA loads per wave per stage
@@ -156,6 +212,7 @@ struct GemmParams {
     float *partial;      // [tiles][splits][BW*BT] (splits > 1)
     QkvEpilogue qe;      // epilogue 2 only
     const bf16_t *bias;  // [N] or null (epilogues 0 and 2; required by 3)
+    int32_t split2d;     // whole K: 1 if the grid is padded for the 2-D XCD split
 };
 
 // MODE 0: whole K, C written.  MODE 1: one K range per blockIdx.z, its
@@ -173,7 +230,10 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
     const int32_t M = p.M_dev ? *p.M_dev : p.M_max;
     int bx = blockIdx.x, by = blockIdx.y;
     if (MODE == kWholeK) {
-        if (!tile_order((M + BT - 1) / BT, bx, by)) return;
+        const int live_by = (M + BT - 1) / BT;
+        const int xw = p.split2d ? pick_xw(gridDim.x, live_by, BW, BT, G::OCC) : 1;
+        if (!(xw > 1 ? tile_order_2d(live_by, xw, bx, by) : tile_order(live_by, bx, by)))
+            return;
     }
     const int32_t t0 = by * BT;
     if (t0 >= M) return;
@@ -573,10 +633,23 @@ constexpr CfgInfo kCfgs[kGemmConfigs] = {{CfgXS::BW, CfgXS::BT}, {CfgXSG::BW, Cf
                                          {CfgM2::BW, CfgM2::BT}};
 
 template <class G, int MODE>
-hipError_t launch_mode(hipStream_t s, const GemmParams &p, int epilogue) {
+hipError_t launch_mode(hipStream_t s, GemmParams p, int epilogue) {
     const int bn = epilogue == 1 ? G::BW / 2 : G::BW;
-    const dim3 grid((p.N + bn - 1) / bn, (p.M_max + G::BT - 1) / G::BT,
-                    MODE == kPartial ? p.splits : 1);
+    const int nbx = (p.N + bn - 1) / bn, nby = (p.M_max + G::BT - 1) / G::BT;
+    int gy = nby;
+    // whole-K grids of at least 512 tiles may take the 2-D XCD split (on
+    // smaller grids it gained nothing and the padding cost a little): pad
+    // the grid so every XCD has a slot per tile of the largest block of any
+    // split (blocks only shrink with fewer live tokens)
+    p.split2d = MODE == kWholeK && nbx * nby >= 512;
+    if (p.split2d) {
+        for (int xw = 2; xw <= 8; xw *= 2) {
+            const int xtn = 8 / xw;
+            const int64_t bmax = (int64_t)((nby + xtn - 1) / xtn) * ((nbx + xw - 1) / xw);
+            gy = (int)std::max<int64_t>(gy, (8 * bmax + nbx - 1) / nbx);
+        }
+    }
+    const dim3 grid(nbx, gy, MODE == kPartial ? p.splits : 1);
     // partial tiles are the same for the plain and bias epilogues (the bias
     // is applied by the reduce launch)
     if (epilogue == 0 || (MODE == kPartial && epilogue == 3)) {
@@ -698,7 +771,7 @@ hipError_t launch_gemm(hipStream_t s, const bf16_t *A, int32_t lda, const bf16_t
         return hipErrorInvalidValue;
     if (plan.splits > 1 && !partial) return hipErrorInvalidValue;
     GemmParams p{A, lda, W, ldw, C, ldc, M_dev, M_max, N, K, plan.splits, partial,
-                 epilogue == 2 ? *qe : QkvEpilogue{}, bias};
+                 epilogue == 2 ? *qe : QkvEpilogue{}, bias, 0};
     switch (plan.config) {
         case 0: return launch_small<CfgXS>(s, p, epilogue);
         case 1: return launch_small<CfgXSG>(s, p, epilogue);
