@@ -52,7 +52,7 @@ DOMINANT_KERNEL_SYMBOL = {
 # kernels.h); after any change to them the traffic is reported as null.
 TRAFFIC = {"op": "up_geglu_gemm", "workload": "mixed_16", "fetch_kib": 51988.7,
            "write_kib": 20756.2, "fetch_per_byte": 0.5000, "write_per_byte": 1.0000,
-           "sources_sha256": "42d8a405fb9af3404fa1e83a510d7eb70db4504b0505bd9ccf252cf0f75b45bf"}
+           "sources_sha256": "5a8de7e878f452fe919c0d8f150fc45ed51ad1f3a6b05dab96dea2f7ce1587ba"}
 TRAFFIC_SOURCES = ("k_gemm.hip", "common.h", "kernels.h")
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense BF16 MFMA

@@ -197,6 +197,8 @@ struct Cfg {
     static_assert(STAGES >= 2 && (STAGES - 1) * LOADS < 64, "vmcnt range");
     static_assert(STAGES * STAGE_ELEMS * 2 <= 160 * 1024, "LDS");
     static_assert(FA + FB <= 15, "lgkmcnt range");
+    static_assert((BW & (BW - 1)) == 0 && (BT & (BT - 1)) == 0,
+                  "power-of-two tiles (the output staging swizzles 16-byte chunks by XOR)");
 };
 
 struct GemmParams {
