@@ -567,3 +567,38 @@ def test_gemm_qkv_bias_equals_biased_gemm_then_rope(B, M, H, cfgs, splits):
                           splits=sp, bias=bias)
             _sync()
             assert np.array_equal(bits_of(from_dev(c2))[:, :2 * H], biased[:, :2 * H])
+
+
+# ------------------------------------------- 2-D XCD split of large grids --
+
+@pytest.mark.parametrize("M,N,K,epi,cfgs", [(4049, 2624, 1024, 1, (3, 4, 5, 6)),
+                                            (4050, 3072, 1024, 0, (3, 5, 6)),
+                                            (2049, 4096, 1024, 0, (3, 6))])
+def test_gemm_two_dimensional_xcd_split_writes_every_tile(B, M, N, K, epi, cfgs):
+    """Grids of >= 512 tiles take the 2-D split of the tile grid over the
+    XCDs (a padded grid, tile blocks chosen on the device from the row
+    count).  Every output element is written (the output starts as NaN),
+    every tile shape gives the same bits, and the result is the oracle's
+    within one BF16 ulp."""
+    import torch
+    a_h = oracle.bf16_round(random_normal((M, K), M + 3 * K))
+    rows = 2 * N if epi else N
+    w_h = oracle.bf16_round(random_normal((rows, K), N + 7, 0.03))
+    a, w = to_dev(a_h), to_dev(w_h)
+    if epi:
+        ug = oracle.linear(a_h, w_h)
+        want = oracle.bf16_round(oracle.gelu(ug[:, :N]) * ug[:, N:])
+    else:
+        want = oracle.bf16_round(oracle.linear(a_h, w_h))
+    outs = []
+    for cfg in cfgs:
+        c = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+        B.op_gemm(a, w, c, M, N, K, epi, config=cfg, splits=1)
+        _sync()
+        got = from_dev(c)
+        assert not np.isnan(got).any(), cfg
+        outs.append(bits_of(got))
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+    bad, frac = bf16_close((outs[0].astype(np.uint32) << 16).view(np.float32), want)
+    assert bad == 0, (bad, frac)
