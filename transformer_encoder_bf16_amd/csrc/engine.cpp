@@ -95,6 +95,18 @@ void build_rope_table(double theta, int max_pos, int head_dim, uint16_t *c, uint
 // ---------------------------------------------------------------------------
 int align_down(int k) { return k - k % 64; }
 
+// Heaviest blocks first (most key tiles), ties in list order.  The kernel
+// runs as long as its busiest compute unit, and workgroups are handed out
+// in dispatch order, breadth first over the CUs: with the longest chains
+// dispatched first each CU gets one heavy block per round, instead of some
+// CUs drawing several of a 16x512 batch's 512-key rows.  Blocks are
+// independent, so the order changes no result.
+void heaviest_first(AttnBlock *blocks, int n) {
+    std::stable_sort(blocks, blocks + n, [](const AttnBlock &a, const AttnBlock &b) {
+        return a.k_hi - a.k_lo > b.k_hi - b.k_lo;
+    });
+}
+
 void build_blocks_full(const int32_t *row_off, const int32_t *vcol0, int B, int half_window,
                        AttnBlock *out, int *n_out) {
     int n = 0;
@@ -118,6 +130,7 @@ void build_blocks_full(const int32_t *row_off, const int32_t *vcol0, int B, int 
             out[n++] = a;
         }
     }
+    heaviest_first(out, n);
     *n_out = n;
 }
 
@@ -153,6 +166,7 @@ void build_blocks_list(const int32_t *row_off, const int32_t *vcol0, const int32
         out[n++] = a;
         r = e;
     }
+    heaviest_first(out, n);
     *n_out = n;
 }
 
