@@ -283,3 +283,38 @@ def test_unknown_run_flags_are_rejected(binding, enc):
     with pytest.raises(binding.LayaError) as ei:
         enc.run(batch.ids, batch.lengths, flags=64)
     assert ei.value.code == binding.LAYA_E_INVALID
+
+
+@pytest.mark.timeout(900)
+def test_maximum_batch_and_markers_match_oracle(binding, enc, orc, orc64):
+    """The handle's limits: 16 rows of 512 tokens (T = 8192, every row full)
+    and 2048 marker rows (128 per row).  Per layer within the pages' 0.005 on
+    the GPU's own inputs, end to end within 1.5x the oracle's float32/float64
+    spread, graph equal to eager, marker rows bitwise equal to the full
+    pass's rows."""
+    batch = random_batch(MODEL, 16, 512, seed=77, len_lo=512, markers_per_row=128)
+    mk = batch.markers
+    assert batch.T == 8192 and len(mk) == 2048
+    print("[max] B=16 S=512 T=8192 R=2048", flush=True)
+    enc.run(batch.ids, batch.lengths, flags=binding.RUN_CAPTURE_LAYERS)
+    _sync()
+    caps = dict(enc.layer_outputs())
+    lw = orc.forward_layerwise(batch.ids, batch.lengths, caps)
+    per_layer = {n: oracle.nrms(caps[n], y) for n, y in lw.items()}
+    ref = orc.forward(batch.ids, batch.lengths)
+    final = oracle.nrms(caps["out"], ref["out"])
+    floor = oracle.nrms(orc64.forward(batch.ids, batch.lengths)["out"], ref["out"])
+    print(f"[max] per-layer worst {max(per_layer.values()):.3g}, final {final:.3g} "
+          f"(floor {floor:.3g})", flush=True)
+    report("maximum_batch", {"per_layer_nrms": per_layer, "final_nrms": final,
+                             "oracle_f32_vs_f64_final_nrms": floor})
+    for n, e in per_layer.items():
+        assert e <= NRMS_LIMIT, (n, e)
+    assert final <= max(NRMS_LIMIT, FLOOR_FACTOR * floor)
+    eager, _ = _run_bits(binding, enc, batch, binding.RUN_EAGER)
+    graph, _ = _run_bits(binding, enc, batch, 0)
+    assert np.array_equal(eager, bits_of(caps["out"])) and np.array_equal(graph, eager)
+    sub_e, _ = _run_bits(binding, enc, batch, binding.RUN_EAGER, mk)
+    sub_g, _ = _run_bits(binding, enc, batch, 0, mk)
+    rows = ref["row_off"][mk[:, 0]] + mk[:, 1]
+    assert np.array_equal(sub_e, eager[rows]) and np.array_equal(sub_g, sub_e)
