@@ -52,7 +52,7 @@ DOMINANT_KERNEL_SYMBOL = {
 # kernels.h); after any change to them the traffic is reported as null.
 TRAFFIC = {"op": "up_geglu_gemm", "workload": "mixed_16", "fetch_kib": 51988.7,
            "write_kib": 20756.2, "fetch_per_byte": 0.5000, "write_per_byte": 1.0000,
-           "sources_sha256": "5a8de7e878f452fe919c0d8f150fc45ed51ad1f3a6b05dab96dea2f7ce1587ba"}
+           "sources_sha256": "ab1fe44cd39006143edc6d82cd188c4b204ecfd3fd99b8c49bce75fdc9f77c75"}
 TRAFFIC_SOURCES = ("k_gemm.hip", "common.h", "kernels.h")
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense BF16 MFMA

@@ -621,7 +621,7 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
 using CfgXS = Cfg<32, 64, 1, 1, 64, 6>;    // small M, 1 wave (plain only)
 using CfgXSG = Cfg<64, 64, 1, 1, 64, 4>;   // small M, 1 wave (GeGLU-capable)
 using CfgS = Cfg<128, 64, 2, 2, 64, 4>;    // 4 waves of 64 rows x 32 tokens
-using CfgM = Cfg<128, 128, 2, 2, 64, 4>;   // 4 waves of 64 x 64
+using CfgM = Cfg<128, 128, 2, 4, 64, 4>;   // 8 waves of 64 x 32 (two per SIMD)
 using CfgL = Cfg<256, 128, 2, 4, 64, 3>;   // 8 waves of 128 x 32
 using CfgXL = Cfg<256, 256, 2, 4, 64, 2>;  // 8 waves of 128 x 64
 using CfgM2 = Cfg<128, 128, 2, 2, 64, 2>;   // M with a 2-stage ring: 64 KB, two per CU
