@@ -52,7 +52,7 @@ DOMINANT_KERNEL_SYMBOL = {
 # kernels.h); after any change to them the traffic is reported as null.
 TRAFFIC = {"op": "up_geglu_gemm", "workload": "mixed_16", "fetch_kib": 51988.7,
            "write_kib": 20756.2, "fetch_per_byte": 0.5000, "write_per_byte": 1.0000,
-           "sources_sha256": "ab1fe44cd39006143edc6d82cd188c4b204ecfd3fd99b8c49bce75fdc9f77c75"}
+           "sources_sha256": "329c906eb1555336594053fb14b3acb88c6250b662697c8972c391d36bf0f90a"}
 TRAFFIC_SOURCES = ("k_gemm.hip", "common.h", "kernels.h")
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense BF16 MFMA

@@ -28,7 +28,9 @@
 //   - the output tile is assembled in LDS and written with 16-byte stores
 //     along whole row segments.
 //
-// Split-K (small M, where only a few weight tiles exist): the K range is cut
+// Split-K (few tokens and a long K, where a whole-K chain of few tiles
+// would be a long serial wait on loads; at short K the second launch costs
+// more than the split saves): the K range is cut
 // into S contiguous pieces (multiples of 64); one launch writes each piece's
 // float32 partial tile, a second launch adds the partials in piece order
 // 0..S-1 and runs the epilogue.  The sum order is fixed, so results are
