@@ -52,7 +52,7 @@ DOMINANT_KERNEL_SYMBOL = {
 # kernels.h); after any change to them the traffic is reported as null.
 TRAFFIC = {"op": "up_geglu_gemm", "workload": "mixed_16", "fetch_kib": 51988.7,
            "write_kib": 20756.2, "fetch_per_byte": 0.5000, "write_per_byte": 1.0000,
-           "sources_sha256": "329c906eb1555336594053fb14b3acb88c6250b662697c8972c391d36bf0f90a"}
+           "sources_sha256": "be64124e1d54b85a085fddd30659bf18bec2ad314e155491606cf0d0f9864bf2"}
 TRAFFIC_SOURCES = ("k_gemm.hip", "common.h", "kernels.h")
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense BF16 MFMA

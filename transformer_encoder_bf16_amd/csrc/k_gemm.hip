@@ -728,7 +728,10 @@ GemmPlan plan_gemm(int32_t M_max, int32_t N, int32_t K, int epilogue) {
         // weight stream over more workgroups but costs a second launch,
         // which at these sizes takes longer than the split saves (measured
         // in the pass: 1x48 1.79 -> 1.59 ms, 4x64 2.07 -> 1.71 ms).
-        g.config = (M_max <= 64 && epilogue == 0) ? 0 : 2;
+        // (the plain epilogue on 32-row tiles, three times as many workgroups:
+        // 1x187 1.77 -> 1.71 ms; the 128-row tiles stay for the others, whose
+        // 64-row alternative was slower in the pass)
+        g.config = epilogue == 0 ? 0 : 2;
         g.splits = 1;
     } else if (M_max <= 64) {
         // small M, long K: stream the weights with many narrow tiles; split K
