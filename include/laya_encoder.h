@@ -373,10 +373,11 @@ int laya_op_layernorm(void *stream, void *x, const void *r, void *n, const float
  * [M][lda], W device BF16 [N or 2N][ldw], C device BF16 [M][ldc]; K a multiple
  * of 64, N a multiple of 64, lda/ldw/ldc multiples of 8 (16-byte rows).
  * config -1 picks the tile shape and K split the pass itself would use for M
- * rows; config 0..6 (tile shapes 32x64, 64x64, 128x64, 128x128, 256x128,
- * 256x256, and 128x128 with a shallower ring that fits two per compute unit;
- * weight rows x tokens) with `splits` K ranges forces one (split K
- * only on shapes 0..3; GeGLU not on shape 0).  Each output is the sum, in
+ * rows; config 0..8 (tile shapes 32x64, 64x64, 128x64, 128x128, 256x128,
+ * 256x256, 128x128 with a shallower ring that fits two per compute unit, and
+ * 32x64 and 64x64 on two waves with deep rings; weight rows x tokens) with
+ * `splits` K ranges forces one (split K only on shapes 0..3, 7 and 8; GeGLU
+ * not on shapes 0 and 7).  Each output is the sum, in
  * order, of one MFMA chain per K range, so results depend only on `splits`.
  * With splits > 1 the call allocates its scratch and synchronises the
  * stream.
@@ -390,6 +391,24 @@ int laya_op_layernorm(void *stream, void *x, const void *r, void *n, const float
 int laya_op_gemm(void *stream, const void *A, int32_t lda, const void *W, int32_t ldw,
                  void *C, int32_t ldc, int32_t M, int32_t N, int32_t K, int32_t epilogue,
                  int32_t config, int32_t splits, const void *bias);
+
+/* A projection onto the hidden width followed by the residual add and the
+ * LayerNorm of the next sublayer (pre-norm stack, "[RFC]: Native Laya
+ * inference with Rust and CUDA #14", section Design; fused residual and
+ * LayerNorm as asked for short requests in "[Performance]: Optimize native
+ * Rust/CUDA Laya inference #66", section Implementation priorities):
+ *   f = bf16(A W^T) (with a bias: bf16(bf16(A W^T) + bias)),
+ *   x <- bf16(x + f),  n <- bf16((x - mean) / sqrt(var + eps) * gamma),
+ * computed with `splits` >= 2 K ranges on tile shape `config` (0..3, 7, 8),
+ * the split's reduce launch doing the residual and the LayerNorm: bitwise
+ * laya_op_gemm(config, splits) into r followed by laya_op_layernorm(x, r, n).
+ * A device BF16 [M][lda], W device BF16 [N][ldw] (N <= 1024, a multiple of
+ * 64), x device BF16 [M][N] (updated in place), n device BF16 [M][N] (not
+ * aliasing x), gamma device float32 [N], bias device BF16 [N] 16-byte aligned
+ * or NULL.  The call allocates its scratch and synchronises the stream. */
+int laya_op_gemm_layernorm(void *stream, const void *A, int32_t lda, const void *W, int32_t ldw,
+                           void *x, void *n, const float *gamma, int32_t M, int32_t N, int32_t K,
+                           int32_t config, int32_t splits, const void *bias, float eps);
 
 /* RoPE in place on `n_heads_rot` consecutive 64-wide heads starting at column
  * 0 of each of `rows` rows of buf (device BF16, row stride ld): with

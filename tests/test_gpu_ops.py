@@ -368,8 +368,8 @@ def test_gemm_every_tile_shape_and_split(B, M, N, K, epi):
         want = oracle.bf16_round(oracle.linear(a_h, w_h))
     for splits in (1, 2, 5):
         outs = []
-        for cfg in range(7):
-            if (epi and cfg == 0) or (splits > 1 and cfg > 3):
+        for cfg in range(9):
+            if (epi and cfg in (0, 7)) or (splits > 1 and cfg in (4, 5, 6)):
                 continue
             c = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
             B.op_gemm(a, w, c, M, N, K, epi, config=cfg, splits=splits)
@@ -380,6 +380,45 @@ def test_gemm_every_tile_shape_and_split(B, M, N, K, epi):
         got = (outs[0][1].astype(np.uint32) << 16).view(np.float32)
         bad, frac = bf16_close(got, want)
         assert bad == 0 and frac < 0.02, (splits, bad, frac)
+
+
+@pytest.mark.parametrize("M,N,K,cfg,splits,bias", [
+    (48, 1024, 1024, 7, 4, False), (48, 1024, 2624, 7, 8, False), (64, 1024, 2624, 0, 8, False),
+    (200, 1024, 2624, 2, 4, False), (97, 1024, 4096, 8, 8, True), (33, 512, 1024, 3, 2, True),
+    (1, 1024, 1024, 1, 3, False)])
+def test_gemm_layernorm_equals_gemm_then_layernorm(B, M, N, K, cfg, splits, bias):
+    """The split reduce with the residual add and LayerNorm fused in is bitwise
+    the split GEMM followed by the LayerNorm kernel, and matches the oracle."""
+    import torch
+    a_h = oracle.bf16_round(random_normal((M, K), 11 * M + K))
+    w_h = oracle.bf16_round(random_normal((N, K), 5 * N + K, 0.03))
+    x_h = oracle.bf16_round(random_normal((M, N), M + 3 * N, 1.5))
+    g_h = oracle.bf16_round(random_gamma(N, N + 1))
+    b_h = oracle.bf16_round(random_normal((N,), N + 7, 0.5)) if bias else None
+    a, w, g = to_dev(a_h), to_dev(w_h), torch.from_numpy(g_h).cuda()
+    bb = to_dev(b_h) if bias else None
+    # reference: split GEMM into r, then the LayerNorm kernel on a copy of x
+    r = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    B.op_gemm(a, w, r, M, N, K, 0, config=cfg, splits=splits, bias=bb)
+    x_ref, n_ref = to_dev(x_h), torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    B.op_layernorm(x_ref, r, n_ref, g, 1e-5)
+    x, n = to_dev(x_h), torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    B.op_gemm_layernorm(a, w, x, n, g, M, N, K, cfg, splits, bias=bb)
+    _sync()
+    assert np.array_equal(bits_of(from_dev(x)), bits_of(from_dev(x_ref)))
+    assert np.array_equal(bits_of(from_dev(n)), bits_of(from_dev(n_ref)))
+    # against the oracle: the product within one BF16 ulp (the biased product
+    # has its own bound, pinned by the bias tests above), then the residual
+    # and the LayerNorm of the GPU's own product
+    if not bias:
+        bad, frac = bf16_close(from_dev(r), oracle.bf16_round(oracle.linear(a_h, w_h)))
+        assert bad == 0 and frac < 0.02, (bad, frac)
+    xs = oracle.bf16_round(x_h + from_dev(r))
+    assert np.array_equal(bits_of(from_dev(x)), bits_of(xs))
+    d = ulp_diff(from_dev(n), oracle.bf16_round(oracle.layer_norm(xs, g_h, 1e-5)))
+    assert d.max() <= 1 and (d > 0).mean() < 0.005
+    report("gemm_layernorm", {"M": M, "N": N, "K": K, "config": cfg, "splits": splits,
+                              "bias": bias, "max_ulp": int(d.max())})
 
 
 def test_gemm_split_k_repeats_bitwise(B):

@@ -48,7 +48,7 @@ EXPORTS = [
     "laya_encoder_profile", "laya_encoder_fill_workspace", "laya_encoder_config",
     "laya_encoder_health", "laya_encoder_inject_failure", "laya_queue_create", "laya_queue_submit",
     "laya_queue_wait", "laya_queue_health", "laya_queue_destroy", "laya_rope_table", "laya_memcpy", "laya_op_gather", "laya_op_layernorm", "laya_op_gemm",
-    "laya_op_gemm_qkv", "laya_op_rope", "laya_op_attention",
+    "laya_op_gemm_layernorm", "laya_op_gemm_qkv", "laya_op_rope", "laya_op_attention",
 ]
 
 
@@ -166,6 +166,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
                                         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                         ctypes.c_int32, _P]),
+        "laya_op_gemm_layernorm": (ctypes.c_int, [_P, _P, ctypes.c_int32, _P, ctypes.c_int32,
+                                                  _P, _P, _P, ctypes.c_int32, ctypes.c_int32,
+                                                  ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                  _P, ctypes.c_float]),
         "laya_op_rope": (ctypes.c_int, [_P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                         _P, _P, _P, ctypes.c_int32]),
         "laya_op_gemm_qkv": (ctypes.c_int, [_P, _P, ctypes.c_int32, _P, ctypes.c_int32, _P,
@@ -403,6 +407,16 @@ def op_gemm(A, W, C, M: int, N: int, K: int, epilogue: int = 0, config: int = -1
     _check(load().laya_op_gemm(st, _dp(A), A.stride(0), _dp(W), W.stride(0), _dp(C),
                                C.stride(0), M, N, K, epilogue, config, splits, _dp(bias)),
            "laya_op_gemm")
+
+
+def op_gemm_layernorm(A, W, x, n, gamma, M: int, N: int, K: int, config: int, splits: int,
+                      bias=None, eps: float = 1e-5, stream: Optional[int] = None):
+    """x <- bf16(x + bf16(A W^T) [+ bias]), n <- LN(x) * gamma, on a K split whose
+    reduce launch does the residual and the LayerNorm."""
+    st = current_stream() if stream is None else stream
+    _check(load().laya_op_gemm_layernorm(st, _dp(A), A.stride(0), _dp(W), W.stride(0), _dp(x),
+                                         _dp(n), _dp(gamma), M, N, K, config, splits, _dp(bias),
+                                         eps), "laya_op_gemm_layernorm")
 
 
 def op_rope(buf, n_heads_rot: int, pos, cos_tab, sin_tab, rows: Optional[int] = None,

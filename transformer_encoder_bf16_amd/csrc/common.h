@@ -54,6 +54,50 @@ LAYA_DEV float group16_max(float v) {
 LAYA_DEV u32x4_t ld16(const void *p) { return *reinterpret_cast<const u32x4_t *>(p); }
 LAYA_DEV void st16(void *p, u32x4_t v) { *reinterpret_cast<u32x4_t *>(p) = v; }
 
+// LayerNorm of one row held by one 64-lane wave, shared by every kernel that
+// ends in a LayerNorm so they round alike: lane L holds the 8 values of
+// chunks L, L + 64, ... (v[c] for chunk lane + 64 c < nch) and `sum`, their
+// running sum in chunk order.  Mean and biased variance in float32 (two
+// passes over the registers, butterfly sums over the wave), then
+// n = bf16((v - mean) / sqrt(var + eps) * gamma) with a true division.
+template <int MAXC>
+LAYA_DEV void layernorm_row_store(const float (&v)[MAXC][8], float sum, int lane, int nch,
+                                  int hidden, float eps, const float *__restrict__ gamma,
+                                  uint16_t *__restrict__ n_row) {
+    const float inv_h = 1.0f / (float)hidden;
+    const float mean = wave_sum(sum) * inv_h;
+    float sq = 0.f;
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+        if (lane + c * 64 < nch) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float d = v[c][e] - mean;
+                sq += d * d;
+            }
+        }
+    }
+    const float var = wave_sum(sq) * inv_h;
+    const float sd = sqrtf(var + eps);
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+        const int ch = lane + c * 64;
+        if (ch < nch) {
+            const f32x4_t g0 = *reinterpret_cast<const f32x4_t *>(gamma + ch * 8);
+            const f32x4_t g1 = *reinterpret_cast<const f32x4_t *>(gamma + ch * 8 + 4);
+            float g[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
+            u32x4_t o;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float lo = ((v[c][2 * q] - mean) / sd) * g[2 * q];
+                const float hi = ((v[c][2 * q + 1] - mean) / sd) * g[2 * q + 1];
+                o[q] = pack_bf16x2(lo, hi);
+            }
+            st16(n_row + ch * 8, o);
+        }
+    }
+}
+
 LAYA_DEV bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 
 // ---------------------------------------------------------------------------

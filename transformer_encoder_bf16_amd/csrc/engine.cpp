@@ -415,11 +415,12 @@ struct RunShape {
 // Op classes of the per-launch profile (laya_encoder_profile).
 enum OpKind {
     OP_GATHER, OP_LAYERNORM, OP_QKV, OP_ROPE, OP_ATTENTION, OP_OUT_PROJ, OP_UP_GEGLU, OP_DOWN,
-    OP_ROW_GATHER, OP_KV, OP_Q, OP_UP_GELU, OP_COUNT
+    OP_ROW_GATHER, OP_KV, OP_Q, OP_UP_GELU, OP_OUT_PROJ_LN, OP_DOWN_LN, OP_COUNT
 };
 const char *const kOpNames[OP_COUNT] = {
     "gather", "layernorm", "qkv_gemm", "rope", "attention", "out_proj_gemm",
-    "up_geglu_gemm", "down_gemm", "row_gather", "kv_gemm", "q_gemm", "up_gelu_gemm"};
+    "up_geglu_gemm", "down_gemm", "row_gather", "kv_gemm", "q_gemm", "up_gelu_gemm",
+    "out_proj_gemm_layernorm", "down_gemm_layernorm"};
 
 struct ProfRec {
     int op;
@@ -449,7 +450,7 @@ laya::GemmPlan subset_plan(const laya::GemmPlan &full, int R, int N, int K, int 
     laya::GemmPlan g;
     g.splits = full.splits;
     if (R <= 64)
-        g.config = (epi == 1 || epi == 2) ? 1 : 0;
+        g.config = (epi == 1 || epi == 2) ? 8 : 7;
     else if (R <= 256 || full.splits > 1)
         g.config = 2;  // split-capable
     else
@@ -601,6 +602,9 @@ int record(laya_encoder *enc, hipStream_t s, const RunShape &rs, Profiler *prof 
         return b2 * (M * K + Nw * K + M * N);
     };
     const double ln_res_by = 4 * T * H * b2, ln_by = 2 * T * H * b2;
+    // a projection onto H whose split reduce also does the residual and the
+    // LayerNorm: reads A, W and x, writes x and n (f is never stored)
+    auto proj_ln_by = [&](double M, double K) { return b2 * (M * K + H * K + 3 * M * H); };
     const double attn_fl_per_pair = 4.0 * c.head_dim * nh;
 
     // bytes the attention kernel may read from a K column block of row
@@ -614,7 +618,8 @@ int record(laya_encoder *enc, hipStream_t s, const RunShape &rs, Profiler *prof 
     L_OP(OP_GATHER, 0, 2 * T * H * b2 + 4 * T,
          laya::launch_gather(s, enc->emb, ids, T_dev, Tmax, H, xr));
     C_CHK(cap("emb", xr, rs.T));
-    bool pending = false;  // the down projection of the previous layer waits in proj
+    bool pending = false;   // the down projection of the previous layer waits in proj
+    bool ln_ready = false;  // ... or was fused with the residual and the next LayerNorm
     char name[32];
     for (int L = 0; L < NL; ++L) {
         const bool is_enc = L < c.n_enc_layers;
@@ -635,36 +640,64 @@ int record(laya_encoder *enc, hipStream_t s, const RunShape &rs, Profiler *prof 
         const int FW = head ? 4 * H : F;  // width of the FFN's inner activation
         // up + activation and down projection into enc->proj (M rows, T_dev or
         // Mmax rows when T_dev is null)
+        // With a K split, the down projection's reduce launch also does the
+        // residual add into x_res and the LayerNorm that follows it, into
+        // n_next (*fused set); otherwise f is left in enc->proj.
         auto ffn = [&](const bf16_t *n_in, const int32_t *M_dev, int Mmax, double Mf,
-                       const laya::GemmPlan &pu, const laya::GemmPlan &pd) -> int {
+                       const laya::GemmPlan &pu, const laya::GemmPlan &pd, bf16_t *x_res,
+                       bf16_t *n_next, bool *fused) -> int {
             if (head) {
                 L_OP(OP_UP_GELU, gemm_fl(Mf, FW, H), gemm_by(Mf, FW, FW, H) + FW * b2,
                      laya::launch_gemm(s, n_in, H, Wi, H, enc->hid, FW, M_dev, Mmax, FW, H, 3,
                                        pu, gp, nullptr, B1));
-                L_OP(OP_DOWN, gemm_fl(Mf, H, FW), gemm_by(Mf, H, H, FW) + H * b2,
-                     laya::launch_gemm(s, enc->hid, FW, Wo2, FW, enc->proj, H, M_dev, Mmax, H,
-                                       FW, 0, pd, gp, nullptr, B2));
             } else {
                 L_OP(OP_UP_GEGLU, gemm_fl(Mf, 2 * F, H), gemm_by(Mf, 2 * F, F, H),
                      laya::launch_gemm(s, n_in, H, Wi, H, enc->hid, F, M_dev, Mmax, F, H, 1,
                                        pu, gp));
-                L_OP(OP_DOWN, gemm_fl(Mf, H, F), gemm_by(Mf, H, H, F),
-                     laya::launch_gemm(s, enc->hid, F, Wo2, F, enc->proj, H, M_dev, Mmax, H, F,
-                                       0, pd, gp));
+            }
+            const bf16_t *Bd = head ? B2 : nullptr;
+            const double bias_by = head ? H * b2 : 0.0;
+            *fused = pd.splits > 1;
+            if (*fused)
+                L_OP(OP_DOWN_LN, gemm_fl(Mf, H, FW), proj_ln_by(Mf, FW) + bias_by,
+                     laya::launch_gemm_layernorm(s, enc->hid, FW, Wo2, FW, M_dev, Mmax, H, FW,
+                                                 pd, gp, Bd, x_res, n_next, g1, c.ln_eps));
+            else
+                L_OP(OP_DOWN, gemm_fl(Mf, H, FW), gemm_by(Mf, H, H, FW) + bias_by,
+                     laya::launch_gemm(s, enc->hid, FW, Wo2, FW, enc->proj, H, M_dev, Mmax, H,
+                                       FW, 0, pd, gp, nullptr, Bd));
+            return LAYA_OK;
+        };
+        // output projection followed by x += a, n_out = LN(x)
+        auto attn_out = [&](const int32_t *M_dev, int Mmax, double Mf, const laya::GemmPlan &po,
+                            bf16_t *x_res, bf16_t *n_out) -> int {
+            if (po.splits > 1) {
+                L_OP(OP_OUT_PROJ_LN, gemm_fl(Mf, H, H), proj_ln_by(Mf, H) + (Bo ? H * b2 : 0.0),
+                     laya::launch_gemm_layernorm(s, enc->att, H, Wo, H, M_dev, Mmax, H, H, po, gp,
+                                                 Bo, x_res, n_out, g1, c.ln_eps));
+            } else {
+                L_OP(OP_OUT_PROJ, gemm_fl(Mf, H, H), gemm_by(Mf, H, H, H),
+                     laya::launch_gemm(s, enc->att, H, Wo, H, enc->proj, H, M_dev, Mmax, H, H, 0,
+                                       po, gp, nullptr, Bo));
+                L_OP(OP_LAYERNORM, 0, 4 * Mf * H * b2,
+                     laya::launch_layernorm(s, x_res, enc->proj, n_out, g1, M_dev, Mmax, H,
+                                            c.ln_eps));
             }
             return LAYA_OK;
         };
 
-        // attention sublayer: n = LN(x [+ f of the previous layer])
-        L_OP(OP_LAYERNORM, 0, pending ? ln_res_by : ln_by,
-             laya::launch_layernorm(s, xr, pending ? enc->proj : nullptr, enc->nrm, g1, T_dev,
-                                    Tmax, H, c.ln_eps));
-        if (pending) {
+        // attention sublayer: n = LN(x [+ f of the previous layer]), unless the
+        // previous layer's down projection already produced it
+        if (!ln_ready)
+            L_OP(OP_LAYERNORM, 0, pending ? ln_res_by : ln_by,
+                 laya::launch_layernorm(s, xr, pending ? enc->proj : nullptr, enc->nrm, g1,
+                                        T_dev, Tmax, H, c.ln_eps));
+        if (pending || ln_ready) {
             std::snprintf(name, sizeof name, (L - 1) < c.n_enc_layers ? "enc%02d" : "dec%d",
                           (L - 1) < c.n_enc_layers ? L - 1 : L - 1 - c.n_enc_layers);
             C_CHK(cap(name, xr, rs.T));
         }
-        pending = false;
+        pending = ln_ready = false;
         if (!subset) {
             // Q, K rotated in the epilogue (or by the RoPE kernel after it); V
             // stored transposed for attention
@@ -681,25 +714,27 @@ int record(laya_encoder *enc, hipStream_t s, const RunShape &rs, Profiler *prof 
                                       ml.nblk_full_max, pos, nh, half};
             L_OP(OP_ATTENTION, attn_fl_per_pair * (glob ? rs.pairs_global : rs.pairs_local),
                  4 * T * H * b2, laya::launch_attention(s, ap));
-            L_OP(OP_OUT_PROJ, gemm_fl(T, H, H), gemm_by(T, H, H, H),
-                 laya::launch_gemm(s, enc->att, H, Wo, H, enc->proj, H, T_dev, Tmax, H, H, 0,
-                                   plans.o, gp, nullptr, Bo));
-            L_OP(OP_LAYERNORM, 0, ln_res_by,
-                 laya::launch_layernorm(s, xr, enc->proj, enc->nrm, g1, T_dev, Tmax, H,
-                                        c.ln_eps));
+            C_CHK(attn_out(T_dev, Tmax, T, plans.o, xr, enc->nrm));
+            // the LayerNorm after this layer: the next layer's attention norm,
+            // the encoder's final norm, or the closing norm
+            bf16_t *n_next = L == NL - 1 ? enc->out
+                                         : (L == c.n_enc_layers - 1 ? xalt : enc->nrm);
+            bool fused = false;
             C_CHK(ffn(enc->nrm, T_dev, Tmax, T, head ? plans.up4 : plans.up,
-                      head ? plans.down4 : plans.down));
-            pending = true;
+                      head ? plans.down4 : plans.down, xr, n_next, &fused));
+            pending = !fused;
+            ln_ready = fused;
             if (L == c.n_enc_layers - 1) {
                 // x += f; the encoder's final LayerNorm output becomes the decision stream
-                L_OP(OP_LAYERNORM, 0, ln_res_by,
-                     laya::launch_layernorm(s, xr, enc->proj, xalt, g1, T_dev, Tmax, H,
-                                            c.ln_eps));
+                if (!fused)
+                    L_OP(OP_LAYERNORM, 0, ln_res_by,
+                         laya::launch_layernorm(s, xr, enc->proj, xalt, g1, T_dev, Tmax, H,
+                                                c.ln_eps));
                 std::snprintf(name, sizeof name, "enc%02d", L);
                 C_CHK(cap(name, xr, rs.T));
                 C_CHK(cap("enc_final", xalt, rs.T));
                 std::swap(xr, xalt);
-                pending = false;
+                pending = ln_ready = false;
             }
         } else {
             // keys/values for every token, queries only for the marker rows
@@ -731,17 +766,14 @@ int record(laya_encoder *enc, hipStream_t s, const RunShape &rs, Profiler *prof 
                                       ml.nblk_sub_max, mrk_pos, nh, half};
             L_OP(OP_ATTENTION, attn_fl_per_pair * rs.pairs_subset, (2 * R + 2 * T) * H * b2,
                  laya::launch_attention(s, ap));
-            L_OP(OP_OUT_PROJ, gemm_fl(R, H, H), gemm_by(R, H, H, H),
-                 laya::launch_gemm(s, enc->att, H, Wo, H, enc->proj, H, nullptr, Ri, H, H, 0,
-                                   plans.o_sub, gp, nullptr, Bo));
-            L_OP(OP_LAYERNORM, 0, 4 * R * H * b2,
-                 laya::launch_layernorm(s, enc->x_sub, enc->proj, enc->n_sub, g1, nullptr, Ri,
-                                        H, c.ln_eps));
+            C_CHK(attn_out(nullptr, Ri, R, plans.o_sub, enc->x_sub, enc->n_sub));
+            bool fused = false;
             C_CHK(ffn(enc->n_sub, nullptr, Ri, R, head ? plans.up4_sub : plans.up_sub,
-                      head ? plans.down4_sub : plans.down_sub));
-            L_OP(OP_LAYERNORM, 0, 4 * R * H * b2,
-                 laya::launch_layernorm(s, enc->x_sub, enc->proj, enc->out, g1, nullptr, Ri, H,
-                                        c.ln_eps));
+                      head ? plans.down4_sub : plans.down_sub, enc->x_sub, enc->out, &fused));
+            if (!fused)
+                L_OP(OP_LAYERNORM, 0, 4 * R * H * b2,
+                     laya::launch_layernorm(s, enc->x_sub, enc->proj, enc->out, g1, nullptr, Ri,
+                                            H, c.ln_eps));
             std::snprintf(name, sizeof name, L < c.n_enc_layers ? "enc%02d" : "dec%d",
                           L < c.n_enc_layers ? L : L - c.n_enc_layers);
             C_CHK(cap(name, enc->x_sub, Ri));
@@ -749,11 +781,13 @@ int record(laya_encoder *enc, hipStream_t s, const RunShape &rs, Profiler *prof 
             return LAYA_OK;
         }
     }
-    // closing LayerNorm over the decision stream
-    L_OP(OP_LAYERNORM, 0, pending ? ln_res_by : ln_by,
-         laya::launch_layernorm(s, xr, pending ? enc->proj : nullptr, enc->out, enc->gamma_ones,
-                                T_dev, Tmax, H, c.ln_eps));
-    if (pending) {
+    // closing LayerNorm over the decision stream (already done by a fused down
+    // projection)
+    if (!ln_ready)
+        L_OP(OP_LAYERNORM, 0, pending ? ln_res_by : ln_by,
+             laya::launch_layernorm(s, xr, pending ? enc->proj : nullptr, enc->out,
+                                    enc->gamma_ones, T_dev, Tmax, H, c.ln_eps));
+    if (pending || ln_ready) {
         std::snprintf(name, sizeof name, (NL - 1) < c.n_enc_layers ? "enc%02d" : "dec%d",
                       (NL - 1) < c.n_enc_layers ? NL - 1 : NL - 1 - c.n_enc_layers);
         C_CHK(cap(name, xr, rs.T));
@@ -1411,7 +1445,7 @@ int op_gemm_launch(const char *who, hipStream_t s, const void *A, int32_t lda, c
     laya::GemmPlan plan = laya::plan_gemm(M, N, K, epilogue);
     if (config >= 0) plan = laya::GemmPlan{config, splits < 1 ? 1 : splits};
     if (plan.splits > K / 64 || plan.splits > laya::gemm_max_splits(plan.config) ||
-        ((epilogue == 1 || epilogue == 2) && plan.config == 0))
+        ((epilogue == 1 || epilogue == 2) && (plan.config == 0 || plan.config == 7)))
         return set_global_error(LAYA_E_INVALID, std::string(who) + ": unsupported config/splits");
     const size_t pb = laya::gemm_workspace_bytes(plan, M, N, epilogue);
     void *scratch = nullptr;
@@ -1449,6 +1483,33 @@ int laya_op_gemm(void *stream, const void *A, int32_t lda, const void *W, int32_
     if (M == 0) return LAYA_OK;
     return op_gemm_launch("laya_op_gemm", static_cast<hipStream_t>(stream), A, lda, W, ldw, C,
                           ldc, M, N, K, epilogue, config, splits, nullptr, bias);
+}
+
+int laya_op_gemm_layernorm(void *stream, const void *A, int32_t lda, const void *W, int32_t ldw,
+                           void *x, void *n, const float *gamma, int32_t M, int32_t N, int32_t K,
+                           int32_t config, int32_t splits, const void *bias, float eps) {
+    if (!gemm_args_ok(A, lda, W, ldw, x, N, M, N, K, config) || N > 1024 || !(eps > 0.f) ||
+        config < 0 || (config > 3 && config < 7) || splits < 2 || splits > K / 64 ||
+        splits > laya::gemm_max_splits(config) || (M > 0 && (!n || !gamma || n == x)) ||
+        reinterpret_cast<uintptr_t>(bias) % 16 != 0)
+        return set_global_error(LAYA_E_INVALID, "laya_op_gemm_layernorm: bad arguments");
+    if (M == 0) return LAYA_OK;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const laya::GemmPlan plan{config, splits};
+    const size_t pb = laya::gemm_workspace_bytes(plan, M, N, 0);
+    void *scratch = nullptr;
+    if (hipMalloc(&scratch, pb) != hipSuccess)
+        return set_global_error(LAYA_E_NOMEM, "laya_op_gemm_layernorm: scratch hipMalloc failed");
+    hipError_t e = laya::launch_gemm_layernorm(
+        s, static_cast<const bf16_t *>(A), lda, static_cast<const bf16_t *>(W), ldw, nullptr, M, N,
+        K, plan, static_cast<float *>(scratch), static_cast<const bf16_t *>(bias),
+        static_cast<bf16_t *>(x), static_cast<bf16_t *>(n), gamma, eps);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    hipFree(scratch);
+    if (e != hipSuccess)
+        return set_global_error(LAYA_E_DEVICE,
+                                std::string("laya_op_gemm_layernorm: ") + hipGetErrorString(e));
+    return LAYA_OK;
 }
 
 int laya_op_gemm_qkv(void *stream, const void *A, int32_t lda, const void *W, int32_t ldw,

@@ -158,38 +158,8 @@ __global__ __launch_bounds__(256) void layernorm_kernel(bf16_t *__restrict__ x,
             for (int e = 0; e < 8; ++e) sum += v[c][e];
         }
     }
-    const float inv_h = 1.0f / (float)hidden;
-    const float mean = wave_sum(sum) * inv_h;
-    float sq = 0.f;
-#pragma unroll
-    for (int c = 0; c < MAXC; ++c) {
-        if (lane + c * 64 < nch) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float d = v[c][e] - mean;
-                sq += d * d;
-            }
-        }
-    }
-    const float var = wave_sum(sq) * inv_h;
-    const float sd = sqrtf(var + eps);
-#pragma unroll
-    for (int c = 0; c < MAXC; ++c) {
-        const int ch = lane + c * 64;
-        if (ch < nch) {
-            const f32x4_t g0 = *reinterpret_cast<const f32x4_t *>(gamma + ch * 8);
-            const f32x4_t g1 = *reinterpret_cast<const f32x4_t *>(gamma + ch * 8 + 4);
-            float g[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
-            u32x4_t o;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float lo = ((v[c][2 * q] - mean) / sd) * g[2 * q];
-                const float hi = ((v[c][2 * q + 1] - mean) / sd) * g[2 * q + 1];
-                o[q] = pack_bf16x2(lo, hi);
-            }
-            st16(n + (uint32_t)row * (uint32_t)hidden + ch * 8, o);
-        }
-    }
+    layernorm_row_store<MAXC>(v, sum, lane, nch, hidden, eps, gamma,
+                              n + (uint32_t)row * (uint32_t)hidden);
 }
 
 hipError_t launch_layernorm(hipStream_t s, bf16_t *x, const bf16_t *r, bf16_t *n,

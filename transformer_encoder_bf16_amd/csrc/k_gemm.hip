@@ -59,6 +59,7 @@ namespace laya {
 namespace {
 
 constexpr int KMULT = 64;  // K and every split piece are multiples of 64
+constexpr int kMaxSplits = 8;  // K ranges of a split launch
 
 // Physical 16-byte chunk of logical chunk `c` in stage row `r` (rows of BK
 // bf16): XOR with the row's index among the rows that share one 256-byte
@@ -294,9 +295,11 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
             }
             off[j] = (uint32_t)(grow * p.ldw + kbase + c * 8) * 2u;
         } else {
-            int trow = t0 + (r - BW);
-            if (trow >= M) trow = M - 1;
-            off[j] = (uint32_t)(trow * p.lda + kbase + c * 8) * 2u;
+            // token rows past the live count are never stored: their lanes
+            // take an offset past the resource's end, so the hardware fetches
+            // nothing and their stage rows read as zero
+            const int trow = t0 + (r - BW);
+            off[j] = trow < M ? (uint32_t)(trow * p.lda + kbase + c * 8) * 2u : a_bytes;
         }
     }
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
@@ -619,6 +622,104 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
     }
 }
 
+// Split-K reduce fused with the residual add and LayerNorm that follow a
+// projection onto the hidden width (the output and down projections), one
+// 64-lane wave per token row:
+//   f = bf16(sum of the K ranges' float32 partials, in range order)
+//       (with a bias: f = bf16(f + bias), as the biased epilogue rounds),
+//   x <- bf16(x + f),  n <- bf16(LN(x) * gamma).
+// The partials are those of the split launch (layout [tile][range][wave][a]
+// [b][e4][lane][4], geometry below); the sums, roundings and the LayerNorm
+// are those of the reduce launch and of the LayerNorm kernel, in the same
+// order, so the results are bitwise theirs with one launch fewer.
+struct SplitGeom {
+    int32_t bw, bt, rw, rt, wt, fa, fb, nbx;  // tile, per-wave sub-tile, wave grid, tiles in N
+};
+template <int MAXC>
+__global__ __launch_bounds__(64) void splitk_layernorm_kernel(
+    const float *__restrict__ partial, int32_t splits, SplitGeom g,
+    const bf16_t *__restrict__ bias, bf16_t *__restrict__ x, bf16_t *__restrict__ n,
+    const float *__restrict__ gamma, const int32_t *count_dev, int32_t count_max,
+    int32_t hidden, float eps) {
+    const int32_t T = count_dev ? *count_dev : count_max;
+    const int32_t row = blockIdx.x;
+    const int lane = threadIdx.x;
+    if (row >= T) return;
+    const int nch = hidden >> 3;
+    // the token's place in its tile: wave column, fragment, fragment column
+    const int by = row / g.bt, tl = row - by * g.bt;
+    const int wc = tl / g.rt, b = (tl % g.rt) >> 5, c32 = tl & 31;
+    const size_t tile_el = (size_t)g.bw * g.bt;
+    bf16_t *xr = x + (size_t)row * hidden;
+    // every partial of the row's chunks is loaded before any is added, so the
+    // loads are in flight together (a load-add chain would wait on each)
+    f32x4_t pt[MAXC][kMaxSplits][2];
+    u32x4_t xa[MAXC];
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+        const int ch = lane + c * 64;
+        if (ch < nch) {
+            // features f0..f0+7: rows 8 e4 .. 8 e4 + 7 of fragment a of wave
+            // row wr; the first four in lane c32, the next four in lane c32 + 32
+            const int f0 = ch * 8;
+            const int bx = f0 / g.bw, fl = f0 - bx * g.bw;
+            const int wr = fl / g.rw, a = (fl % g.rw) >> 5, e4 = (fl & 31) >> 3;
+            const int blk = (((wr * g.wt + wc) * g.fa + a) * g.fb + b) * 4 + e4;
+            const float *pp = partial + (size_t)(by * g.nbx + bx) * splits * tile_el +
+                              (size_t)blk * 256;
+#pragma unroll
+            for (int sp = 0; sp < kMaxSplits; ++sp) {
+                if (sp < splits) {
+                    pt[c][sp][0] = *reinterpret_cast<const f32x4_t *>(pp + c32 * 4);
+                    pt[c][sp][1] = *reinterpret_cast<const f32x4_t *>(pp + (c32 + 32) * 4);
+                }
+                pp += tile_el;
+            }
+            xa[c] = ld16(xr + ch * 8);
+        }
+    }
+    float v[MAXC][8];
+    float sum = 0.f;
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+        const int ch = lane + c * 64;
+        if (ch < nch) {
+            f32x4_t s0 = pt[c][0][0], s1 = pt[c][0][1];
+#pragma unroll
+            for (int sp = 1; sp < kMaxSplits; ++sp) {
+                if (sp < splits) {
+                    s0 += pt[c][sp][0];
+                    s1 += pt[c][sp][1];
+                }
+            }
+            float f[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) f[e] = bf16_to_f32(f32_to_bf16(f[e]));
+            if (bias != nullptr) {
+                const u32x4_t bw4 = ld16(bias + ch * 8);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    f[2 * q] = bf16_to_f32(f32_to_bf16(f[2 * q] + bf16lo(bw4[q])));
+                    f[2 * q + 1] = bf16_to_f32(f32_to_bf16(f[2 * q + 1] + bf16hi(bw4[q])));
+                }
+            }
+            u32x4_t o;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float lo = bf16_to_f32(f32_to_bf16(bf16lo(xa[c][q]) + f[2 * q]));
+                const float hi = bf16_to_f32(f32_to_bf16(bf16hi(xa[c][q]) + f[2 * q + 1]));
+                v[c][2 * q] = lo;
+                v[c][2 * q + 1] = hi;
+                o[q] = pack_bf16x2(lo, hi);
+            }
+            st16(xr + ch * 8, o);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sum += v[c][e];
+        }
+    }
+    layernorm_row_store<MAXC>(v, sum, lane, nch, hidden, eps, gamma, n + (size_t)row * hidden);
+}
+
 // Tile configurations: weight rows x tokens, wave grid, K step, stages.
 using CfgXS = Cfg<32, 64, 1, 1, 64, 6>;    // small M, 1 wave (plain only)
 using CfgXSG = Cfg<64, 64, 1, 1, 64, 4>;   // small M, 1 wave (GeGLU-capable)
@@ -627,6 +728,8 @@ using CfgM = Cfg<128, 128, 2, 4, 64, 4>;   // 8 waves of 64 x 32 (two per SIMD)
 using CfgL = Cfg<256, 128, 2, 4, 64, 3>;   // 8 waves of 128 x 32
 using CfgXL = Cfg<256, 256, 2, 4, 64, 2>;  // 8 waves of 128 x 64
 using CfgM2 = Cfg<128, 128, 2, 2, 64, 2>;   // M with a 2-stage ring: 64 KB, two per CU
+using CfgXS2 = Cfg<32, 64, 1, 2, 64, 11>;  // small M, 2 waves of 32 x 32, deep ring (plain only)
+using CfgXSG2 = Cfg<64, 64, 1, 2, 64, 8>;  // small M, 2 waves of 64 x 32, deep ring
 
 struct CfgInfo {
     int bw, bt;
@@ -634,7 +737,8 @@ struct CfgInfo {
 constexpr CfgInfo kCfgs[kGemmConfigs] = {{CfgXS::BW, CfgXS::BT}, {CfgXSG::BW, CfgXSG::BT},
                                          {CfgS::BW, CfgS::BT},   {CfgM::BW, CfgM::BT},
                                          {CfgL::BW, CfgL::BT},   {CfgXL::BW, CfgXL::BT},
-                                         {CfgM2::BW, CfgM2::BT}};
+                                         {CfgM2::BW, CfgM2::BT}, {CfgXS2::BW, CfgXS2::BT},
+                                         {CfgXSG2::BW, CfgXSG2::BT}};
 
 template <class G, int MODE>
 hipError_t launch_mode(hipStream_t s, GemmParams p, int epilogue) {
@@ -687,9 +791,21 @@ hipError_t launch_large(hipStream_t s, const GemmParams &p, int epilogue) {
     return p.splits > 1 ? hipErrorInvalidValue : launch_mode<G, kWholeK>(s, p, epilogue);
 }
 
+// The split launch's partials, then the fused reduce + residual + LayerNorm.
+template <class G>
+hipError_t launch_split_layernorm(hipStream_t s, const GemmParams &p, bf16_t *x, bf16_t *n,
+                                  const float *gamma, float eps) {
+    const hipError_t e = launch_mode<G, kPartial>(s, p, 0);
+    if (e != hipSuccess) return e;
+    const SplitGeom g{G::BW, G::BT, G::RW, G::RT, G::WT, G::FA, G::FB, (p.N + G::BW - 1) / G::BW};
+    hipLaunchKernelGGL(splitk_layernorm_kernel<2>, dim3(p.M_max), dim3(64), 0, s, p.partial,
+                       p.splits, g, p.bias, x, n, gamma, p.M_dev, p.M_max, p.N, eps);
+    return hipGetLastError();
+}
+
 }  // namespace
 
-int gemm_max_splits(int config) { return config <= 3 ? 8 : 1; }
+int gemm_max_splits(int config) { return (config <= 3 || config >= 7) ? kMaxSplits : 1; }
 
 GemmPlan plan_gemm_tiles(int32_t M, int32_t N, int32_t K, int epilogue) {
     // Tile shape with the least estimated time: the tiles the busiest of the
@@ -723,20 +839,28 @@ GemmPlan plan_gemm(int32_t M_max, int32_t N, int32_t K, int epilogue) {
     const int64_t nw = epilogue == 1 ? 2LL * N : N;  // weight rows read
     const int np = K / KMULT;                   // 64-wide K pieces
     GemmPlan g{};
-    if (M_max <= 256 && K <= 1024) {
+    if (M_max <= 64 && K <= 1024 && epilogue == 0 && N <= 1024) {
+        // the output projection of a short call: four K ranges on 32-row
+        // tiles; the split's reduce launch also takes the residual add and
+        // the LayerNorm that follow (launch_gemm_layernorm), so the split
+        // costs no extra launch
+        g.config = 7;
+        g.splits = std::min(4, np);
+    } else if (M_max <= 256 && K <= 1024) {
         // few tokens, short K: whole K in one launch.  A K split spreads the
         // weight stream over more workgroups but costs a second launch,
         // which at these sizes takes longer than the split saves (measured
         // in the pass: 1x48 1.79 -> 1.59 ms, 4x64 2.07 -> 1.71 ms).
         // (the plain epilogue on 32-row tiles, three times as many workgroups:
         // 1x187 1.77 -> 1.71 ms; the 128-row tiles stay for the others, whose
-        // 64-row alternative was slower in the pass)
-        g.config = epilogue == 0 ? 0 : 2;
+        // 64-row alternative was slower in the pass.)  Up to 64 tokens the
+        // two-wave deep-ring tiles keep more of the weight stream in flight.
+        g.config = M_max <= 64 ? (epilogue == 0 ? 7 : 8) : (epilogue == 0 ? 0 : 2);
         g.splits = 1;
     } else if (M_max <= 64) {
         // small M, long K: stream the weights with many narrow tiles; split K
         // until about 2 workgroups per CU
-        g.config = (epilogue == 1 || epilogue == 2) ? 1 : 0;
+        g.config = (epilogue == 1 || epilogue == 2) ? 1 : 7;
         const int64_t tiles = (nw + kCfgs[g.config].bw - 1) / kCfgs[g.config].bw;
         int s = 1;
         while (s < 8 && tiles * s * 2 <= 512 && np / (s * 2) >= 2) s *= 2;
@@ -786,7 +910,33 @@ hipError_t launch_gemm(hipStream_t s, const bf16_t *A, int32_t lda, const bf16_t
         case 3: return launch_small<CfgM>(s, p, epilogue);
         case 4: return launch_large<CfgL>(s, p, epilogue);
         case 5: return launch_large<CfgXL>(s, p, epilogue);
-        default: return launch_large<CfgM2>(s, p, epilogue);
+        case 6: return launch_large<CfgM2>(s, p, epilogue);
+        case 7: return launch_small<CfgXS2>(s, p, epilogue);
+        default: return launch_small<CfgXSG2>(s, p, epilogue);
+    }
+}
+
+hipError_t launch_gemm_layernorm(hipStream_t s, const bf16_t *A, int32_t lda, const bf16_t *W,
+                                 int32_t ldw, const int32_t *M_dev, int32_t M_max, int32_t N,
+                                 int32_t K, const GemmPlan &plan, float *partial,
+                                 const bf16_t *bias, bf16_t *x, bf16_t *n, const float *gamma,
+                                 float eps) {
+    if (M_max <= 0) return hipSuccess;
+    // one wave per row holds 16 values per lane: widths up to 1024, multiples of 64
+    if (N % 64 != 0 || N > 1024 || K % KMULT != 0 || plan.splits < 2 ||
+        plan.splits > K / KMULT || plan.splits > gemm_max_splits(plan.config) || !partial ||
+        !x || !n || !gamma || reinterpret_cast<uintptr_t>(bias) % 16 != 0)
+        return hipErrorInvalidValue;
+    GemmParams p{A, lda, W, ldw, nullptr, 0, M_dev, M_max, N, K, plan.splits, partial,
+                 QkvEpilogue{}, bias, 0};
+    switch (plan.config) {
+        case 0: return launch_split_layernorm<CfgXS>(s, p, x, n, gamma, eps);
+        case 1: return launch_split_layernorm<CfgXSG>(s, p, x, n, gamma, eps);
+        case 2: return launch_split_layernorm<CfgS>(s, p, x, n, gamma, eps);
+        case 3: return launch_split_layernorm<CfgM>(s, p, x, n, gamma, eps);
+        case 7: return launch_split_layernorm<CfgXS2>(s, p, x, n, gamma, eps);
+        case 8: return launch_split_layernorm<CfgXSG2>(s, p, x, n, gamma, eps);
+        default: return hipErrorInvalidValue;
     }
 }
 

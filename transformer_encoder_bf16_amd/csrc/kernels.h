@@ -45,10 +45,11 @@ hipError_t launch_layernorm(hipStream_t s, bf16_t *x, const bf16_t *r, bf16_t *n
 // GEMM tile configuration and K split.  Every output element is one MFMA
 // chain per K range, the ranges summed in order, so a result depends only on
 // `splits` (never on the tile shape).
-constexpr int kGemmConfigs = 7;
+constexpr int kGemmConfigs = 9;
 struct GemmPlan {
     int config;  // 0 XS 32x64, 1 XSG 64x64, 2 S 128x64, 3 M 128x128, 4 L 256x128, 5 XL 256x256,
-                 // 6 M2 128x128 with a 2-stage ring (two workgroups per CU)
+                 // 6 M2 128x128 with a 2-stage ring (two workgroups per CU),
+                 // 7 XS2 32x64 and 8 XSG2 64x64 (two waves each, deep rings)
     int splits;  // K ranges (>= 1)
 };
 // plan for a GEMM launched with a grid for M_max rows (the K split depends
@@ -84,6 +85,17 @@ hipError_t launch_gemm(hipStream_t s, const bf16_t *A, int32_t lda, const bf16_t
                        int32_t M_max, int32_t N, int32_t K, int epilogue, const GemmPlan &plan,
                        float *partial, const QkvEpilogue *qe = nullptr,
                        const bf16_t *bias = nullptr);
+
+// A projection onto the hidden width with a K split (plan.splits >= 2, N <=
+// 1024) whose reduce launch also does the residual add and LayerNorm that
+// follow it: x <- bf16(x + bf16(A W^T) [+ bias, rounded again]),
+// n <- bf16(LN(x) * gamma).  Bitwise the same as launch_gemm with this plan
+// (C = r) followed by launch_layernorm(x, r, n), with one launch fewer.
+hipError_t launch_gemm_layernorm(hipStream_t s, const bf16_t *A, int32_t lda, const bf16_t *W,
+                                 int32_t ldw, const int32_t *M_dev, int32_t M_max, int32_t N,
+                                 int32_t K, const GemmPlan &plan, float *partial,
+                                 const bf16_t *bias, bf16_t *x, bf16_t *n, const float *gamma,
+                                 float eps);
 
 hipError_t launch_rope(hipStream_t s, bf16_t *buf, int32_t ld, int32_t n_heads_rot,
                        const int32_t *count_dev, int32_t rows_max, const int32_t *pos,
