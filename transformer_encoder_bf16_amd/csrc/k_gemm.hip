@@ -223,8 +223,10 @@ struct GemmParams {
 // MODE 0: whole K, C written.  MODE 1: one K range per blockIdx.z, its
 // float32 partial tile written to p.partial.  MODE 2: the partials of each
 // tile summed in range order, then the epilogue (a second launch, so the
-// partials are visible without any cross-XCD fence).
-enum { kWholeK = 0, kPartial = 1, kReduce = 2 };
+// partials are visible without any cross-XCD fence).  MODE 3: as MODE 1, but
+// the partials are written row-major, [range][M_max][N], through LDS, for the
+// fused reduce + LayerNorm kernel, which reads whole token rows.
+enum { kWholeK = 0, kPartial = 1, kReduce = 2, kPartialRows = 3 };
 
 template <class G, int EPI, int MODE>
 __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
@@ -409,6 +411,39 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
       }
     }
 
+    if constexpr (MODE == kPartialRows) {
+        // the float32 tile in LDS as [token][feature] (16-byte chunks
+        // XOR-swizzled by token), then 16-byte stores along the rows of
+        // p.partial + split * M_max * N
+        constexpr int NC4 = BW / 4;  // 16-byte chunks per tile row
+        static_assert(BT * BW * 4 <= STAGES * G::STAGE_ELEMS * 2, "float32 tile fits the ring");
+        __syncthreads();  // every wave is done with the ring
+        float *sP = reinterpret_cast<float *>(smem);
+#pragma unroll
+        for (int a = 0; a < FA; ++a)
+#pragma unroll
+            for (int b = 0; b < FB; ++b) {
+                const int tl = wc * G::RT + 32 * b + l32;
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int c = (wrow[a] + 8 * g4 + 4 * lhi) >> 2;
+                    *reinterpret_cast<f32x4_t *>(&sP[tl * BW + ((c ^ (tl & (NC4 - 1))) << 2)]) =
+                        f32x4_t{acc[a][b][4 * g4], acc[a][b][4 * g4 + 1], acc[a][b][4 * g4 + 2],
+                                acc[a][b][4 * g4 + 3]};
+                }
+            }
+        __syncthreads();
+        float *dst = p.partial + (size_t)split * p.M_max * N;
+#pragma unroll 4
+        for (int idx = tid; idx < BT * NC4; idx += G::NTHR) {
+            const int tl = idx / NC4, c = idx % NC4;
+            const int32_t tok = t0 + tl, f = n0 + 4 * c;
+            if (tok < M && f < N)
+                *reinterpret_cast<f32x4_t *>(dst + (size_t)tok * N + f) =
+                    *reinterpret_cast<const f32x4_t *>(&sP[tl * BW + ((c ^ (tl & (NC4 - 1))) << 2)]);
+        }
+        return;
+    }
     // Partial tiles: [tile][split][wave][a][b][e4][lane][4] float32, so each
     // lane moves 16 contiguous bytes.
     const int tile = blockIdx.y * gridDim.x + blockIdx.x;
@@ -628,28 +663,21 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
 //   f = bf16(sum of the K ranges' float32 partials, in range order)
 //       (with a bias: f = bf16(f + bias), as the biased epilogue rounds),
 //   x <- bf16(x + f),  n <- bf16(LN(x) * gamma).
-// The partials are those of the split launch (layout [tile][range][wave][a]
-// [b][e4][lane][4], geometry below); the sums, roundings and the LayerNorm
-// are those of the reduce launch and of the LayerNorm kernel, in the same
-// order, so the results are bitwise theirs with one launch fewer.
-struct SplitGeom {
-    int32_t bw, bt, rw, rt, wt, fa, fb, nbx;  // tile, per-wave sub-tile, wave grid, tiles in N
-};
+// The partials are the row-major ones of the split launch (MODE 3); the sums,
+// roundings and the LayerNorm are those of the reduce launch and of the
+// LayerNorm kernel, in the same order, so the results are bitwise theirs
+// with one launch fewer.
 template <int MAXC>
 __global__ __launch_bounds__(64) void splitk_layernorm_kernel(
-    const float *__restrict__ partial, int32_t splits, SplitGeom g,
-    const bf16_t *__restrict__ bias, bf16_t *__restrict__ x, bf16_t *__restrict__ n,
-    const float *__restrict__ gamma, const int32_t *count_dev, int32_t count_max,
-    int32_t hidden, float eps) {
+    const float *__restrict__ partial, int32_t splits, const bf16_t *__restrict__ bias,
+    bf16_t *__restrict__ x, bf16_t *__restrict__ n, const float *__restrict__ gamma,
+    const int32_t *count_dev, int32_t count_max, int32_t hidden, float eps) {
     const int32_t T = count_dev ? *count_dev : count_max;
     const int32_t row = blockIdx.x;
     const int lane = threadIdx.x;
     if (row >= T) return;
     const int nch = hidden >> 3;
-    // the token's place in its tile: wave column, fragment, fragment column
-    const int by = row / g.bt, tl = row - by * g.bt;
-    const int wc = tl / g.rt, b = (tl % g.rt) >> 5, c32 = tl & 31;
-    const size_t tile_el = (size_t)g.bw * g.bt;
+    const size_t range_el = (size_t)count_max * hidden;  // floats per K range
     bf16_t *xr = x + (size_t)row * hidden;
     // every partial of the row's chunks is loaded before any is added, so the
     // loads are in flight together (a load-add chain would wait on each)
@@ -659,21 +687,14 @@ __global__ __launch_bounds__(64) void splitk_layernorm_kernel(
     for (int c = 0; c < MAXC; ++c) {
         const int ch = lane + c * 64;
         if (ch < nch) {
-            // features f0..f0+7: rows 8 e4 .. 8 e4 + 7 of fragment a of wave
-            // row wr; the first four in lane c32, the next four in lane c32 + 32
-            const int f0 = ch * 8;
-            const int bx = f0 / g.bw, fl = f0 - bx * g.bw;
-            const int wr = fl / g.rw, a = (fl % g.rw) >> 5, e4 = (fl & 31) >> 3;
-            const int blk = (((wr * g.wt + wc) * g.fa + a) * g.fb + b) * 4 + e4;
-            const float *pp = partial + (size_t)(by * g.nbx + bx) * splits * tile_el +
-                              (size_t)blk * 256;
+            const float *pp = partial + (size_t)row * hidden + ch * 8;
 #pragma unroll
             for (int sp = 0; sp < kMaxSplits; ++sp) {
                 if (sp < splits) {
-                    pt[c][sp][0] = *reinterpret_cast<const f32x4_t *>(pp + c32 * 4);
-                    pt[c][sp][1] = *reinterpret_cast<const f32x4_t *>(pp + (c32 + 32) * 4);
+                    pt[c][sp][0] = *reinterpret_cast<const f32x4_t *>(pp);
+                    pt[c][sp][1] = *reinterpret_cast<const f32x4_t *>(pp + 4);
                 }
-                pp += tile_el;
+                pp += range_el;
             }
             xa[c] = ld16(xr + ch * 8);
         }
@@ -757,10 +778,12 @@ hipError_t launch_mode(hipStream_t s, GemmParams p, int epilogue) {
             gy = (int)std::max<int64_t>(gy, (8 * bmax + nbx - 1) / nbx);
         }
     }
-    const dim3 grid(nbx, gy, MODE == kPartial ? p.splits : 1);
+    const dim3 grid(nbx, gy, (MODE == kPartial || MODE == kPartialRows) ? p.splits : 1);
     // partial tiles are the same for the plain and bias epilogues (the bias
     // is applied by the reduce launch)
-    if (epilogue == 0 || (MODE == kPartial && epilogue == 3)) {
+    if constexpr (MODE == kPartialRows) {
+        hipLaunchKernelGGL((gemm_kernel<G, 0, kPartialRows>), grid, dim3(G::NTHR), 0, s, p);
+    } else if (epilogue == 0 || (MODE == kPartial && epilogue == 3)) {
         if (MODE != kPartial && p.bias)
             hipLaunchKernelGGL((gemm_kernel<G, 4, MODE>), grid, dim3(G::NTHR), 0, s, p);
         else
@@ -795,11 +818,10 @@ hipError_t launch_large(hipStream_t s, const GemmParams &p, int epilogue) {
 template <class G>
 hipError_t launch_split_layernorm(hipStream_t s, const GemmParams &p, bf16_t *x, bf16_t *n,
                                   const float *gamma, float eps) {
-    const hipError_t e = launch_mode<G, kPartial>(s, p, 0);
+    const hipError_t e = launch_mode<G, kPartialRows>(s, p, 0);
     if (e != hipSuccess) return e;
-    const SplitGeom g{G::BW, G::BT, G::RW, G::RT, G::WT, G::FA, G::FB, (p.N + G::BW - 1) / G::BW};
     hipLaunchKernelGGL(splitk_layernorm_kernel<2>, dim3(p.M_max), dim3(64), 0, s, p.partial,
-                       p.splits, g, p.bias, x, n, gamma, p.M_dev, p.M_max, p.N, eps);
+                       p.splits, p.bias, x, n, gamma, p.M_dev, p.M_max, p.N, eps);
     return hipGetLastError();
 }
 
