@@ -375,7 +375,8 @@ int laya_op_layernorm(void *stream, void *x, const void *r, void *n, const float
  * config -1 picks the tile shape and K split the pass itself would use for M
  * rows; config 0..8 (tile shapes 32x64, 64x64, 128x64, 128x128, 256x128,
  * 256x256, 128x128 with a shallower ring that fits two per compute unit, and
- * 32x64 and 64x64 on two waves with deep rings; weight rows x tokens) with
+ * 32x64 and 64x64 for short calls, two computing waves with deep rings;
+ * weight rows x tokens) with
  * `splits` K ranges forces one (split K only on shapes 0..3, 7 and 8; GeGLU
  * not on shapes 0 and 7).  Each output is the sum, in
  * order, of one MFMA chain per K range, so results depend only on `splits`.

@@ -181,10 +181,16 @@ __device__ __forceinline__ bool tile_order_2d(int live_by, int xw, int &bx, int 
     return true;
 }
 
-template <int BW_, int BT_, int WW_, int WT_, int BK_, int STAGES_>
+// XW extra waves only move operands: they issue their share of the ring's
+// loads and meet the barriers, but read no fragments and run no MFMAs (more
+// loads in flight per CU for the small tiles, whose one or two computing
+// waves cannot issue them fast enough).
+template <int BW_, int BT_, int WW_, int WT_, int BK_, int STAGES_, int XW_ = 0>
 struct Cfg {
     static constexpr int BW = BW_, BT = BT_, WW = WW_, WT = WT_, BK = BK_, STAGES = STAGES_;
-    static constexpr int NWAVE = WW * WT, NTHR = NWAVE * 64;
+    static constexpr int XW = XW_;
+    static constexpr int NWAVE_C = WW * WT;                 // waves that compute
+    static constexpr int NWAVE = NWAVE_C + XW, NTHR = NWAVE * 64;  // waves that load
     static constexpr int RW = BW / WW, RT = BT / WT;  // rows / tokens per wave
     static constexpr int FA = RW / 32, FB = RT / 32;  // 32x32 fragments per wave
     static constexpr int STAGE_ELEMS = (BW + BT) * BK;
@@ -253,6 +259,7 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
+    const bool compute = G::XW == 0 || wave < G::NWAVE_C;  // else a loading-only wave
     const int wr = wave / G::WT;  // wave row (weight rows)
     const int wc = wave % G::WT;  // wave column (tokens)
 
@@ -379,6 +386,17 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
       wait_lgkmcnt<0>();  // no scalar loads left in flight, so
                                            // the loop's LDS reads can be waited on in order
       ring_barrier();
+      if (!compute) {
+          // the same waits, barriers and refills as the computing waves
+          for (int i = 0; i < nk; ++i) {
+              if (i + STAGES <= nk)
+                  wait_vmcnt<(STAGES - 2) * G::LOADS>();
+              else
+                  wait_vmcnt<0>();
+              ring_barrier();
+              if (i + STAGES < nk) issue(i + STAGES, i % STAGES);
+          }
+      } else {
       if (nk > 0) read_frags(0, 0, 0);
   
       for (int i = 0; i < nk; ++i) {
@@ -409,6 +427,7 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
               __builtin_amdgcn_sched_barrier(0);
           }
       }
+      }
     }
 
     if constexpr (MODE == kPartialRows) {
@@ -419,6 +438,7 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
         static_assert(BT * BW * 4 <= STAGES * G::STAGE_ELEMS * 2, "float32 tile fits the ring");
         __syncthreads();  // every wave is done with the ring
         float *sP = reinterpret_cast<float *>(smem);
+        if (compute)
 #pragma unroll
         for (int a = 0; a < FA; ++a)
 #pragma unroll
@@ -449,6 +469,7 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
     const int tile = blockIdx.y * gridDim.x + blockIdx.x;
     if constexpr (MODE == kPartial) {
         float *mine = p.partial + ((size_t)tile * p.splits + split) * (BW * BT);
+        if (compute)
 #pragma unroll
         for (int a = 0; a < FA; ++a)
 #pragma unroll
@@ -463,6 +484,7 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
         return;
     }
     if constexpr (MODE == kReduce) {
+      if (compute) {
         // sum of the K ranges' partials, in range order; each range's whole
         // share of the tile is loaded before it is added, so a wave has all
         // of its loads for one range in flight at once
@@ -500,6 +522,7 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
             for (int b = 0; b < FB; ++b)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) acc[a][b][e] = sum[a][b][e / 4][e % 4];
+      }
     }
 
     // Epilogue.  Accumulator element e of lane l in a 32x32 block holds
@@ -527,6 +550,7 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
         bv[2] = bf16lo(w[1]);
         bv[3] = bf16hi(w[1]);
     };
+    if (compute)
 #pragma unroll
     for (int b = 0; b < FB; ++b) {
         const int tl = wc * G::RT + 32 * b + l32;  // token within the tile
@@ -749,7 +773,7 @@ using CfgM = Cfg<128, 128, 2, 4, 64, 4>;   // 8 waves of 64 x 32 (two per SIMD)
 using CfgL = Cfg<256, 128, 2, 4, 64, 3>;   // 8 waves of 128 x 32
 using CfgXL = Cfg<256, 256, 2, 4, 64, 2>;  // 8 waves of 128 x 64
 using CfgM2 = Cfg<128, 128, 2, 2, 64, 2>;   // M with a 2-stage ring: 64 KB, two per CU
-using CfgXS2 = Cfg<32, 64, 1, 2, 64, 11>;  // small M, 2 waves of 32 x 32, deep ring (plain only)
+using CfgXS2 = Cfg<32, 64, 1, 2, 64, 13, 2>;  // small M, 2 waves of 32 x 32 + 2 loading, deep ring
 using CfgXSG2 = Cfg<64, 64, 1, 2, 64, 8>;  // small M, 2 waves of 64 x 32, deep ring
 
 struct CfgInfo {
@@ -861,7 +885,7 @@ GemmPlan plan_gemm(int32_t M_max, int32_t N, int32_t K, int epilogue) {
     const int64_t nw = epilogue == 1 ? 2LL * N : N;  // weight rows read
     const int np = K / KMULT;                   // 64-wide K pieces
     GemmPlan g{};
-    if (M_max <= 64 && K <= 1024 && epilogue == 0 && N <= 1024) {
+    if (M_max <= 256 && K <= 1024 && epilogue == 0 && N <= 1024) {
         // the output projection of a short call: four K ranges on 32-row
         // tiles; the split's reduce launch also takes the residual add and
         // the LayerNorm that follow (launch_gemm_layernorm), so the split

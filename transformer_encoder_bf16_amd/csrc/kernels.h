@@ -49,7 +49,8 @@ constexpr int kGemmConfigs = 9;
 struct GemmPlan {
     int config;  // 0 XS 32x64, 1 XSG 64x64, 2 S 128x64, 3 M 128x128, 4 L 256x128, 5 XL 256x256,
                  // 6 M2 128x128 with a 2-stage ring (two workgroups per CU),
-                 // 7 XS2 32x64 and 8 XSG2 64x64 (two waves each, deep rings)
+                 // 7 XS2 32x64 and 8 XSG2 64x64 (two computing waves each, deep
+                 // rings; XS2 with two more waves that only load)
     int splits;  // K ranges (>= 1)
 };
 // plan for a GEMM launched with a grid for M_max rows (the K split depends
