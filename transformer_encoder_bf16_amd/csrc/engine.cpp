@@ -450,7 +450,7 @@ laya::GemmPlan subset_plan(const laya::GemmPlan &full, int R, int N, int K, int 
     laya::GemmPlan g;
     g.splits = full.splits;
     if (R <= 64)
-        g.config = (epi == 1 || epi == 2) ? 8 : 7;
+        g.config = 7;
     else if (R <= 256 || full.splits > 1)
         g.config = 2;  // split-capable
     else
@@ -1445,7 +1445,7 @@ int op_gemm_launch(const char *who, hipStream_t s, const void *A, int32_t lda, c
     laya::GemmPlan plan = laya::plan_gemm(M, N, K, epilogue);
     if (config >= 0) plan = laya::GemmPlan{config, splits < 1 ? 1 : splits};
     if (plan.splits > K / 64 || plan.splits > laya::gemm_max_splits(plan.config) ||
-        ((epilogue == 1 || epilogue == 2) && (plan.config == 0 || plan.config == 7)))
+        ((epilogue == 1 || epilogue == 2) && plan.config == 0))
         return set_global_error(LAYA_E_INVALID, std::string(who) + ": unsupported config/splits");
     const size_t pb = laya::gemm_workspace_bytes(plan, M, N, epilogue);
     void *scratch = nullptr;

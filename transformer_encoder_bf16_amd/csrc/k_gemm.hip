@@ -238,8 +238,11 @@ template <class G, int EPI, int MODE>
 __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
     constexpr int BW = G::BW, BT = G::BT, FA = G::FA, FB = G::FB, STAGES = G::STAGES;
     constexpr int BK = G::BK, CH = G::CH, RPL = G::RPL;
-    static_assert(EPI == 0 || EPI >= 3 || FA % 2 == 0, "GeGLU / QKV need paired fragments");
-    static_assert(EPI != 2 || G::RW % 64 == 0, "QKV epilogue: a wave's rows are whole heads");
+    // GeGLU / QKV pair rows (u with g, dimension i with i + 32): in paired
+    // fragments, or, on 32-row tiles, within one fragment (rows r and r + 16)
+    constexpr bool HALF = G::RW == 32 && G::WW == 1 && (EPI == 1 || EPI == 2);
+    static_assert(EPI == 0 || EPI >= 3 || FA % 2 == 0 || HALF, "GeGLU / QKV need paired rows");
+    static_assert(EPI != 2 || G::RW % 64 == 0 || HALF, "QKV epilogue: whole or half heads");
     const int32_t M = p.M_dev ? *p.M_dev : p.M_max;
     int bx = blockIdx.x, by = blockIdx.y;
     if (MODE == kWholeK) {
@@ -298,6 +301,10 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
                 int f = n0 + (r % half);
                 if (f >= N) f = N - 1;  // clamp: rows past N are computed, never stored
                 grow = (r < half) ? f : N + f;
+            } else if (EPI == 2 && HALF) {
+                // half a head: dimensions 16p .. 16p+15, then 32+16p .. 32+16p+15
+                const int p16 = (bx & 1) * 16;
+                grow = (bx >> 1) * 64 + (r < 16 ? p16 + r : 32 + p16 + (r - 16));
             } else {
                 grow = n0 + r;
                 if (grow >= N) grow = N - 1;
@@ -336,7 +343,7 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
     int wrow[FA];
 #pragma unroll
     for (int a = 0; a < FA; ++a) {
-        if (EPI == 1)
+        if (EPI == 1 && !HALF)
             wrow[a] = (a < FA / 2) ? (wr * (G::RW / 2) + 32 * a)
                                    : (BW / 2 + wr * (G::RW / 2) + 32 * (a - FA / 2));
         else
@@ -555,7 +562,18 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
     for (int b = 0; b < FB; ++b) {
         const int tl = wc * G::RT + 32 * b + l32;  // token within the tile
         const int32_t tok = t0 + tl;
-        if constexpr (EPI == 1) {
+        if constexpr (EPI == 1 && HALF) {
+            // tile rows 0..15 are u, rows 16..31 the matching g: accumulator
+            // element 4 g4 + e (row 8 g4 + 4 lhi + e) pairs with 4 (g4 + 2) + e
+#pragma unroll
+            for (int g4 = 0; g4 < 2; ++g4) {
+                float h[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    h[e] = gelu_erf(acc[0][b][4 * g4 + e]) * acc[0][b][4 * (g4 + 2) + e];
+                put4(tl, 8 * g4 + 4 * lhi, pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
+            }
+        } else if constexpr (EPI == 1) {
 #pragma unroll
             for (int a = 0; a < FA / 2; ++a)
 #pragma unroll
@@ -567,6 +585,80 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
                         h[e] = gelu_erf(acc[a][b][4 * g4 + e]) * acc[a + FA / 2][b][4 * g4 + e];
                     put4(tl, fl, pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
                 }
+        } else if constexpr (EPI == 2 && HALF) {
+            // Half a head per tile: accumulator element 4 g4 + e (g4 < 2) is
+            // dimension 16p + 8 g4 + 4 lhi + e, element 4 (g4 + 2) + e the
+            // dimension 32 above it, so each rotation pair is in one lane.  The
+            // staged tile holds the 16 low dimensions, then the 16 high ones.
+            const QkvEpilogue &q = p.qe;
+            const int32_t hcol = (bx >> 1) * 64;  // first column of the head
+            const int p16 = (bx & 1) * 16;
+            if (hcol < q.rope_cols) {
+                const uint32_t ps = (uint32_t)q.pos[tok < M ? tok : M - 1] * 32u;
+#pragma unroll
+                for (int g4 = 0; g4 < 2; ++g4) {
+                    const int j = p16 + 8 * g4 + 4 * lhi;  // pair index of element 4*g4
+                    const u32x2_t cv = *reinterpret_cast<const u32x2_t *>(q.cos_tab + ps + j);
+                    const u32x2_t sv = *reinterpret_cast<const u32x2_t *>(q.sin_tab + ps + j);
+                    float xo[4], yo[4], bx4[4] = {0, 0, 0, 0}, by4[4] = {0, 0, 0, 0};
+                    if (p.bias) {
+                        bias4(hcol + j, bx4);
+                        bias4(hcol + 32 + j, by4);
+                    }
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        float x = bf16r(acc[0][b][4 * g4 + e]);
+                        float y = bf16r(acc[0][b][4 * (g4 + 2) + e]);
+                        if (p.bias) {
+                            x = bf16r(x + bx4[e]);
+                            y = bf16r(y + by4[e]);
+                        }
+                        const float c = (e & 1) ? bf16hi(cv[e >> 1]) : bf16lo(cv[e >> 1]);
+                        const float sn = (e & 1) ? bf16hi(sv[e >> 1]) : bf16lo(sv[e >> 1]);
+                        // both products of BF16 values are exact in float32
+                        xo[e] = fmaf(x, c, -(y * sn));
+                        yo[e] = fmaf(y, c, x * sn);
+                    }
+                    put4(tl, 8 * g4 + 4 * lhi, pack_bf16x2(xo[0], xo[1]),
+                         pack_bf16x2(xo[2], xo[3]));
+                    put4(tl, 16 + 8 * g4 + 4 * lhi, pack_bf16x2(yo[0], yo[1]),
+                         pack_bf16x2(yo[2], yo[3]));
+                }
+            } else if (hcol >= q.vt_col0) {
+                if (tok < M) {
+                    bf16_t *vcol = q.vt + q.vt_tok[tok];
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                        for (int g = 0; g < 2; ++g) {
+                            const int32_t f4 = hcol + 32 * h2 + p16 + 8 * g + 4 * lhi;
+                            float bv[4] = {0, 0, 0, 0};
+                            if (p.bias) bias4(f4, bv);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                float v = acc[0][b][4 * (g + 2 * h2) + e];
+                                if (p.bias) v = bf16r(v) + bv[e];
+                                vcol[(size_t)(f4 + e - q.vt_col0) * q.ldvt] =
+                                    (bf16_t)f32_to_bf16(v);
+                            }
+                        }
+                }
+            } else {
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                    for (int g4 = 0; g4 < 2; ++g4) {
+                        float v[4], bv[4] = {0, 0, 0, 0};
+                        if (p.bias) bias4(hcol + 32 * h2 + p16 + 8 * g4 + 4 * lhi, bv);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            v[e] = acc[0][b][4 * (g4 + 2 * h2) + e];
+                            if (p.bias) v[e] = bf16r(v[e]) + bv[e];
+                        }
+                        put4(tl, 16 * h2 + 8 * g4 + 4 * lhi, pack_bf16x2(v[0], v[1]),
+                             pack_bf16x2(v[2], v[3]));
+                    }
+            }
         } else if constexpr (EPI == 2) {
             // Fragments a (dims 0..31 of a head) and a+1 (dims 32..63) sit in
             // the same lanes, so the rotation pairs (i, i+32) are in registers.
@@ -671,10 +763,15 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
     // columns this tile writes to C: [n0, min(N, n0 + BN), and below vt_col0)
     int32_t n_end = min(N, n0 + BN);
     if constexpr (EPI == 2) n_end = min(n_end, max(p.qe.vt_col0, n0));
+    if constexpr (EPI == 2 && HALF) n_end = min(N, p.qe.vt_col0);
 #pragma unroll 4
     for (int idx = tid; idx < BT * NCH; idx += G::NTHR) {
         const int tl = idx / NCH, c = idx % NCH;
-        const int32_t tok = t0 + tl, f = n0 + 8 * c;
+        // half-head tiles: chunks 0, 1 are dimensions 16p.., chunks 2, 3 are 32+16p..
+        const int32_t f = (EPI == 2 && HALF)
+                              ? (bx >> 1) * 64 + (bx & 1) * 16 + (c < 2 ? 8 * c : 32 + 8 * (c - 2))
+                              : n0 + 8 * c;
+        const int32_t tok = t0 + tl;
         if (tok < M && f < n_end)
             st16(p.C + (size_t)tok * p.ldc + f,
                  *reinterpret_cast<const u32x4_t *>(&sC[tl * BN + ((c ^ (tl & (NCH - 1))) << 3)]));
@@ -814,7 +911,7 @@ hipError_t launch_mode(hipStream_t s, GemmParams p, int epilogue) {
             hipLaunchKernelGGL((gemm_kernel<G, 0, MODE>), grid, dim3(G::NTHR), 0, s, p);
     } else if (epilogue == 3) {
         hipLaunchKernelGGL((gemm_kernel<G, 3, MODE>), grid, dim3(G::NTHR), 0, s, p);
-    } else if constexpr (G::FA % 2 == 0 && G::RW % 64 == 0) {
+    } else if constexpr ((G::FA % 2 == 0 && G::RW % 64 == 0) || (G::RW == 32 && G::WW == 1)) {
         if (epilogue == 1)
             hipLaunchKernelGGL((gemm_kernel<G, 1, MODE>), grid, dim3(G::NTHR), 0, s, p);
         else
@@ -901,7 +998,7 @@ GemmPlan plan_gemm(int32_t M_max, int32_t N, int32_t K, int epilogue) {
         // 1x187 1.77 -> 1.71 ms; the 128-row tiles stay for the others, whose
         // 64-row alternative was slower in the pass.)  Up to 64 tokens the
         // two-wave deep-ring tiles keep more of the weight stream in flight.
-        g.config = M_max <= 64 ? (epilogue == 0 ? 7 : 8) : (epilogue == 0 ? 0 : 2);
+        g.config = M_max <= 64 ? 7 : (epilogue == 0 ? 0 : 2);
         g.splits = 1;
     } else if (M_max <= 64) {
         // small M, long K: stream the weights with many narrow tiles; split K
