@@ -140,3 +140,23 @@ def test_queue_and_health_reject_null_handles(lib):
     assert lib.laya_queue_destroy(None) == b.LAYA_OK
     assert lib.laya_encoder_health(None) == b.LAYA_E_INVALID
     assert lib.laya_encoder_inject_failure(None) == b.LAYA_E_INVALID
+
+
+def test_gemm_layernorm_rejects_bad_arguments(lib):
+    """The fused split projection + LayerNorm validates on the host before any
+    device call (dummy aligned addresses are never dereferenced)."""
+    P = ctypes.c_void_p
+    A, W, x, n, g = P(0x1000), P(0x2000), P(0x3000), P(0x4000), P(0x5000)
+
+    def call(M=48, N=1024, K=1024, config=7, splits=4, bias=None, x_=x, n_=n, eps=1e-5):
+        return lib.laya_op_gemm_layernorm(None, A, K, W, K, x_, n_, g, M, N, K, config, splits,
+                                          bias, eps)
+    assert call(splits=1) == b.LAYA_E_INVALID          # needs a K split
+    assert call(splits=17) == b.LAYA_E_INVALID         # more ranges than 64-wide K pieces
+    assert call(N=2048) == b.LAYA_E_INVALID            # one wave per row: N <= 1024
+    assert call(config=4) == b.LAYA_E_INVALID          # whole-K-only tile shape
+    assert call(n_=x) == b.LAYA_E_INVALID              # n must not alias x
+    assert call(bias=P(0x6008)) == b.LAYA_E_INVALID    # bias must be 16-byte aligned
+    assert call(K=1000) == b.LAYA_E_INVALID            # K a multiple of 64
+    assert call(eps=0.0) == b.LAYA_E_INVALID
+    assert call(M=0) == b.LAYA_OK                      # nothing to do, no device call
