@@ -1014,6 +1014,16 @@ GemmPlan plan_gemm(int32_t M_max, int32_t N, int32_t K, int epilogue) {
         int s = 1;
         while (s < 4 && tiles * s * 2 <= 512 && np / (s * 2) >= 4) s *= 2;
         g.splits = s;
+    } else if (epilogue == 0 && N <= 1024 && M_max <= 1024) {
+        // output and down projections up to 1024 rows: whole-K grids hold
+        // only 64-128 tiles; up to 4 K ranges on the 128x64 tile, reduced by
+        // the fused residual + LayerNorm launch (1x464 2.047 -> 1.703 ms; at
+        // 1496 and 1856 rows the split was slower)
+        g.config = 2;
+        const int64_t tiles = ((nw + 127) / 128) * ((M_max + 63) / 64);
+        int s = 1;
+        while (s < 4 && tiles * s * 2 <= 512 && np / (s * 2) >= 4) s *= 2;
+        g.splits = s;
     } else {
         g = plan_gemm_tiles(M_max, N, K, epilogue);
     }
