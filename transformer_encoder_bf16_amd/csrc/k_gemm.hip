@@ -1024,6 +1024,14 @@ GemmPlan plan_gemm(int32_t M_max, int32_t N, int32_t K, int epilogue) {
         int s = 1;
         while (s < 4 && tiles * s * 2 <= 512 && np / (s * 2) >= 4) s *= 2;
         g.splits = s;
+    } else if (epilogue == 0 && N <= 1024 && K > 1024 && M_max <= 2048) {
+        // the down projection up to 2048 rows: 96-116 whole-K 128x128 tiles
+        // of 41 K steps leave most CUs idle; two K ranges, reduced by the
+        // fused residual + LayerNorm launch (8x187 2.741 -> 2.729 ms, 4x464
+        // 3.185 -> 3.174 ms; four ranges, or splitting the output projection
+        // too, were slower)
+        g.config = 3;
+        g.splits = 2;
     } else {
         g = plan_gemm_tiles(M_max, N, K, epilogue);
     }
