@@ -116,8 +116,22 @@ def _run_bits(binding, enc, batch, flags=0, markers=None):
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", list(ALL_WORKLOADS))
 def test_workload_matches_oracle(binding, enc, orc, orc64, name):
-    wl = ALL_WORKLOADS[name]
-    batch = make_batch(MODEL, wl)
+    _check_batch(binding, enc, orc, orc64, make_batch(MODEL, ALL_WORKLOADS[name]), name)
+
+
+# Batch sizes B*S on either side of where the GEMM plans change (split output
+# and down projections with the fused residual + LayerNorm up to 256 and 1024
+# rows, the split down projection up to 2048, whole K above), one with
+# markers so the marker layer's fused splits run too.
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("B,S,lo,mpr", [(1, 65, 65, 0), (1, 257, 257, 0), (2, 512, 400, 0),
+                                        (5, 205, 150, 3), (9, 228, 180, 0)])
+def test_plan_boundaries_match_oracle(binding, enc, orc, orc64, B, S, lo, mpr):
+    batch = random_batch(MODEL, B, S, seed=B * 1000 + S, len_lo=lo, markers_per_row=mpr)
+    _check_batch(binding, enc, orc, orc64, batch, f"{B}x{S}")
+
+
+def _check_batch(binding, enc, orc, orc64, batch, name):
     markers = batch.markers
     print(f"[{name}] B={batch.B} S={batch.S} T={batch.T} R={0 if markers is None else len(markers)}",
           flush=True)
