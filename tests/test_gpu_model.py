@@ -131,6 +131,17 @@ def test_plan_boundaries_match_oracle(binding, enc, orc, orc64, B, S, lo, mpr):
     _check_batch(binding, enc, orc, orc64, batch, f"{B}x{S}")
 
 
+# Short calls with markers: the full pass's last layer runs the 32-row tiles
+# and the split projections with the fused residual + LayerNorm over all
+# tokens, the marker layer the same K ranges over the marker rows on other
+# tiles; marker rows must equal the full pass's rows bit for bit.
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("B,S,lo,mpr", [(1, 48, 48, 12), (4, 16, 5, 4)])
+def test_short_call_markers_match_full_rows(binding, enc, orc, orc64, B, S, lo, mpr):
+    batch = random_batch(MODEL, B, S, seed=77 + B, len_lo=lo, markers_per_row=mpr)
+    _check_batch(binding, enc, orc, orc64, batch, f"{B}x{S}+markers")
+
+
 def _check_batch(binding, enc, orc, orc64, batch, name):
     markers = batch.markers
     print(f"[{name}] B={batch.B} S={batch.S} T={batch.T} R={0 if markers is None else len(markers)}",
