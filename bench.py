@@ -52,7 +52,7 @@ DOMINANT_KERNEL_SYMBOL = {
 # kernels.h); after any change to them the traffic is reported as null.
 TRAFFIC = {"op": "up_geglu_gemm", "workload": "mixed_16", "fetch_kib": 52104.1,
            "write_kib": 20756.2, "fetch_per_byte": 0.5000, "write_per_byte": 1.0000,
-           "sources_sha256": "40e70113967281cbcacf7ea9b6be00459cb372074946b5d322aaa38ef7e4fcb7"}
+           "sources_sha256": "519bbd7151515a8d72b6b74f8df107826d3394c62ceeb2807fc98545c2bb18b3"}
 TRAFFIC_SOURCES = ("k_gemm.hip", "common.h", "kernels.h")
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense BF16 MFMA

@@ -36,15 +36,21 @@
 // 0..S-1 and runs the epilogue.  The sum order is fixed, so results are
 // deterministic.  Two launches rather than a last-arriving workgroup: on a
 // multi-XCD part a device-scope fence writes back the XCD's whole L2, which
-// cost tens of microseconds when every workgroup issued one.
+// cost tens of microseconds when every workgroup issued one.  A projection
+// onto the hidden width is always followed by the residual add and a
+// LayerNorm: there the split launch writes its partials row-major and the
+// second launch is the fused reduce + residual + LayerNorm
+// (splitk_layernorm_kernel), so the split costs no extra launch.
 //
 // GeGLU epilogue (epilogue 1): the first BW/2 rows of the weight tile are
 // rows n0.. of W (the GELU half), the last BW/2 rows are rows N+n0.. (the
-// gate half); each wave holds matching u and g fragments, so
-// h = bf16(GELU(u) * g) is formed from unrounded float32 u and g.
+// gate half); each wave holds matching u and g fragments (on 32-row tiles,
+// accumulator rows r and r + 16 of one fragment), so h = bf16(GELU(u) * g)
+// is formed from unrounded float32 u and g.
 //
 // QKV epilogue (epilogue 2): RoPE on the Q and K heads in registers and the
-// V columns stored transposed for attention (see QkvEpilogue).
+// V columns stored transposed for attention (see QkvEpilogue); a 32-row tile
+// takes half a head, dimensions 16p..16p+15 and their rotation partners.
 //
 // Bias: with a bias vector, a product is rounded to BF16, the bias added and
 // the sum rounded again, y = bf16(bf16(A W^T) + b) (a biased dense layer as
