@@ -105,9 +105,21 @@ def test_head_tensor_digests(enc):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("name", ["short_3", "marker_subset", "long_3"])
+@pytest.mark.parametrize("name", ["short_1", "short_3", "marker_subset", "long_3"])
 def test_head_workload_matches_oracle(binding, enc, orc, orc64, name):
-    batch = make_batch(HEAD, WORKLOADS[name])
+    _check_head(binding, enc, orc, orc64, make_batch(HEAD, WORKLOADS[name]), name)
+
+
+# A short call with markers: the biased output and 4H-wide down projections run
+# split with the bias in the fused reduce + LayerNorm, in the full pass and in
+# the marker layer alike.
+@pytest.mark.timeout(900)
+def test_head_short_call_with_markers(binding, enc, orc, orc64):
+    batch = random_batch(HEAD, 1, 48, seed=91, len_lo=48, markers_per_row=12)
+    _check_head(binding, enc, orc, orc64, batch, "1x48+markers")
+
+
+def _check_head(binding, enc, orc, orc64, batch, name):
     markers = batch.markers
     print(f"[head {name}] B={batch.B} S={batch.S} T={batch.T}", flush=True)
     enc.run(batch.ids, batch.lengths, markers=markers, flags=binding.RUN_CAPTURE_LAYERS)
