@@ -59,12 +59,23 @@ LAYA_DEV void st16(void *p, u32x4_t v) { *reinterpret_cast<u32x4_t *>(p) = v; }
 // chunks L, L + 64, ... (v[c] for chunk lane + 64 c < nch) and `sum`, their
 // running sum in chunk order.  Mean and biased variance in float32 (two
 // passes over the registers, butterfly sums over the wave), then
-// n = bf16((v - mean) / sqrt(var + eps) * gamma) with a true division.
+// n = bf16((v - mean) * rs * gamma) with rs = 1 / sqrt(var + eps), one
+// division per row.  gamma is loaded before the reductions, so its latency
+// overlaps them.
 template <int MAXC>
 LAYA_DEV void layernorm_row_store(const float (&v)[MAXC][8], float sum, int lane, int nch,
                                   int hidden, float eps, const float *__restrict__ gamma,
                                   uint16_t *__restrict__ n_row) {
     const float inv_h = 1.0f / (float)hidden;
+    f32x4_t gv[MAXC][2];
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+        const int ch = lane + c * 64;
+        if (ch < nch) {
+            gv[c][0] = *reinterpret_cast<const f32x4_t *>(gamma + ch * 8);
+            gv[c][1] = *reinterpret_cast<const f32x4_t *>(gamma + ch * 8 + 4);
+        }
+    }
     const float mean = wave_sum(sum) * inv_h;
     float sq = 0.f;
 #pragma unroll
@@ -78,19 +89,19 @@ LAYA_DEV void layernorm_row_store(const float (&v)[MAXC][8], float sum, int lane
         }
     }
     const float var = wave_sum(sq) * inv_h;
-    const float sd = sqrtf(var + eps);
+    const float rs = 1.0f / sqrtf(var + eps);
 #pragma unroll
     for (int c = 0; c < MAXC; ++c) {
         const int ch = lane + c * 64;
         if (ch < nch) {
-            const f32x4_t g0 = *reinterpret_cast<const f32x4_t *>(gamma + ch * 8);
-            const f32x4_t g1 = *reinterpret_cast<const f32x4_t *>(gamma + ch * 8 + 4);
+            const f32x4_t g0 = gv[c][0];
+            const f32x4_t g1 = gv[c][1];
             float g[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
             u32x4_t o;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const float lo = ((v[c][2 * q] - mean) / sd) * g[2 * q];
-                const float hi = ((v[c][2 * q + 1] - mean) / sd) * g[2 * q + 1];
+                const float lo = ((v[c][2 * q] - mean) * rs) * g[2 * q];
+                const float hi = ((v[c][2 * q + 1] - mean) * rs) * g[2 * q + 1];
                 o[q] = pack_bf16x2(lo, hi);
             }
             st16(n_row + ch * 8, o);
