@@ -31,11 +31,26 @@ LAYA_DEV uint32_t f32_to_bf16(float f) {
 }
 LAYA_DEV uint32_t pack_bf16x2(float lo, float hi) { return cvt_pk_bf16(lo, hi); }
 
-// Wave-wide (64 lanes) butterfly sums / maxima.
+// Sum over a 64-lane wave, the same value in every lane.  DPP moves within
+// each 16-lane row (quad_perm [1,0,3,2], quad_perm [2,3,0,1], row half
+// mirror, row mirror: pairs, quads, eights, rows), then the four row sums are
+// read into scalar registers and added as (r0 + r1) + (r2 + r3).  No LDS
+// round trip: a lane shuffle through ds_bpermute costs a full LDS latency per
+// step, and the row statistics sit on every row's critical path.
+template <int CTRL>
+LAYA_DEV float dpp_f32(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                 CTRL, 0xF, 0xF, false));
+}
+LAYA_DEV float lane_f32(float v, int lane) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
 LAYA_DEV float wave_sum(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
+    v += dpp_f32<0xB1>(v);
+    v += dpp_f32<0x4E>(v);
+    v += dpp_f32<0x141>(v);
+    v += dpp_f32<0x140>(v);
+    return (lane_f32(v, 0) + lane_f32(v, 16)) + (lane_f32(v, 32) + lane_f32(v, 48));
 }
 
 // Reduction across the 16 lanes that share (lane / 16), i.e. xor 1, 2, 4, 8.
@@ -58,7 +73,7 @@ LAYA_DEV void st16(void *p, u32x4_t v) { *reinterpret_cast<u32x4_t *>(p) = v; }
 // ends in a LayerNorm so they round alike: lane L holds the 8 values of
 // chunks L, L + 64, ... (v[c] for chunk lane + 64 c < nch) and `sum`, their
 // running sum in chunk order.  Mean and biased variance in float32 (two
-// passes over the registers, butterfly sums over the wave), then
+// passes over the registers, DPP and readlane sums over the wave), then
 // n = bf16((v - mean) * rs * gamma) with rs = 1 / sqrt(var + eps), one
 // division per row.  gamma is loaded before the reductions, so its latency
 // overlaps them.
