@@ -385,8 +385,8 @@ def oracle_timing(cfg, batch, calls):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the pass is not "
-              f"sharded across GPUs in this build", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the pass has no "
+              f"multi-GPU sharding", file=sys.stderr)
         sys.exit(2)
     import torch
     if args.copy_calibration_mib:

@@ -51,10 +51,10 @@ def bf16_close(got: np.ndarray, want: np.ndarray, ulps: float = 1.0,
 
 
 def report(name: str, payload: dict):
-    """Append a parity record to <report dir>/parity_report.jsonl when the
-    report directory exists (gpurun_out/ on a GPU run)."""
-    d = os.environ.get("LAYA_REPORT_DIR", os.path.join(ROOT, "gpurun_out"))
-    if not os.path.isdir(d):
+    """Append a parity record to $LAYA_REPORT_DIR/parity_report.jsonl when
+    that variable names an existing directory (no report otherwise)."""
+    d = os.environ.get("LAYA_REPORT_DIR")
+    if not d or not os.path.isdir(d):
         return
     with open(os.path.join(d, "parity_report.jsonl"), "a") as f:
         f.write(json.dumps({"test": name, **payload}) + "\n")
