@@ -114,12 +114,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void a
     const int32_t q_hi =
         p.half_window < 0 ? blk.k_hi : min(blk.k_hi, my_pos + p.half_window + 1);
     const uint32_t q_span = (uint32_t)(q_hi - q_lo);
+    // Reduced over each 16-lane row (one lane per query) by DPP moves:
+    // quad_perm [1,0,3,2], quad_perm [2,3,0,1], row half mirror, row mirror.
+    // All 64 lanes are active here (invalid queries are clamped, not
+    // masked off), so no DPP source lane is disabled.
     int32_t w_lo = q_lo, w_hi = q_hi;
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) {
-        w_lo = max(w_lo, __shfl_xor(w_lo, off, 64));
-        w_hi = min(w_hi, __shfl_xor(w_hi, off, 64));
-    }
+    w_lo = max(w_lo, __builtin_amdgcn_update_dpp(0, w_lo, 0xB1, 0xF, 0xF, false));
+    w_hi = min(w_hi, __builtin_amdgcn_update_dpp(0, w_hi, 0xB1, 0xF, 0xF, false));
+    w_lo = max(w_lo, __builtin_amdgcn_update_dpp(0, w_lo, 0x4E, 0xF, 0xF, false));
+    w_hi = min(w_hi, __builtin_amdgcn_update_dpp(0, w_hi, 0x4E, 0xF, 0xF, false));
+    w_lo = max(w_lo, __builtin_amdgcn_update_dpp(0, w_lo, 0x141, 0xF, 0xF, false));
+    w_hi = min(w_hi, __builtin_amdgcn_update_dpp(0, w_hi, 0x141, 0xF, 0xF, false));
+    w_lo = max(w_lo, __builtin_amdgcn_update_dpp(0, w_lo, 0x140, 0xF, 0xF, false));
+    w_hi = min(w_hi, __builtin_amdgcn_update_dpp(0, w_hi, 0x140, 0xF, 0xF, false));
     w_lo = __builtin_amdgcn_readfirstlane(w_lo);
     w_hi = __builtin_amdgcn_readfirstlane(w_hi);
 
