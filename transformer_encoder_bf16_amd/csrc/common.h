@@ -53,18 +53,6 @@ LAYA_DEV float wave_sum(float v) {
     return (lane_f32(v, 0) + lane_f32(v, 16)) + (lane_f32(v, 32) + lane_f32(v, 48));
 }
 
-// Reduction across the 16 lanes that share (lane / 16), i.e. xor 1, 2, 4, 8.
-LAYA_DEV float group16_sum(float v) {
-#pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
-}
-LAYA_DEV float group16_max(float v) {
-#pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-    return v;
-}
-
 // 16-byte global load / store helpers.
 LAYA_DEV u32x4_t ld16(const void *p) { return *reinterpret_cast<const u32x4_t *>(p); }
 LAYA_DEV void st16(void *p, u32x4_t v) { *reinterpret_cast<u32x4_t *>(p) = v; }
