@@ -361,7 +361,8 @@ int laya_op_gather(void *stream, const void *emb, int32_t vocab, int32_t hidden,
 /* Fused residual add + LayerNorm over T rows of `hidden` values:
  *   if r != NULL:  x[t] <- bf16(x[t] + r[t])   (written back to x)
  *   n[t] <- bf16((x[t] - mean) / sqrt(var + eps) * gamma)
- * with mean and biased variance of row t in float32, no bias.  x, r, n device
+ * with mean and biased variance of row t in float32, no bias; the division is
+ * a multiply by the row's float32 1 / sqrt(var + eps).  x, r, n device
  * BF16 [T][hidden] (n must not alias x or r); gamma device float32 [hidden]. */
 int laya_op_layernorm(void *stream, void *x, const void *r, void *n, const float *gamma,
                       int32_t T, int32_t hidden, float eps);
