@@ -71,7 +71,11 @@ def parse():
     p.add_argument("--dec-head", action="store_true",
                    help="decision layers as the biased head variant (biased projections, "
                         "4*hidden GELU FFN)")
-    p.add_argument("--cpu-sample-rows", type=int, default=4)
+    p.add_argument("--cpu-calls", type=int, default=3,
+                   help="timed oracle calls on the whole batch after one warm call")
+    p.add_argument("--short-workload", default="short_1",
+                   help="the second shape the metric is quoted on, measured in the same run "
+                        "(graph replays); 'none' to skip")
     p.add_argument("--protocol", action="store_true",
                    help="the full measurement protocol over every workload (ABBA rounds of "
                         "eager and graph calls, device timer, capture cost, per-op shares, "
@@ -101,11 +105,11 @@ def copy_calibration(mib):
     print(json.dumps({"copy_bytes_per_launch": n, "launches": 3}), flush=True)
 
 
-def op_table(enc, batch, mk, repeats):
+def op_table(enc, batch, mk, repeats, flags=0):
     """Per-op-class average of `repeats` event-bracketed eager passes."""
     acc, tot = {}, 0.0
     for _ in range(repeats):
-        ops, t = enc.profile(batch.ids, batch.lengths, markers=mk)
+        ops, t = enc.profile(batch.ids, batch.lengths, markers=mk, flags=flags)
         tot += t
         for k, v in ops.items():
             a = acc.setdefault(k, {"calls": 0, "ms": 0.0, "flops": 0.0, "bytes": 0.0})
@@ -180,7 +184,9 @@ def measured_traffic(op, workload):
                  TRAFFIC["write_kib"] * 1024 / TRAFFIC["write_per_byte"])
 
 
-def cpu_baseline(cfg, batch, rows):
+def cpu_baseline(cfg, batch, calls):
+    """The CPU oracle on the whole benchmarked batch: one warm call, then
+    `calls` timed calls; calls/s = calls / their total time, with the p50."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -189,18 +195,23 @@ def cpu_baseline(cfg, batch, rows):
         cores = os.cpu_count()
     w = oracle.Weights(cfg, 1)
     o = oracle.Oracle(cfg, w)
-    o.forward(batch.ids[:1, :4], np.array([4], np.int32))  # widen weights (untimed)
-    rows = min(rows, batch.B)
-    ids, lens = batch.ids[:rows], batch.lengths[:rows]
-    t0 = time.perf_counter()
-    o.forward(ids, lens)
-    dt = time.perf_counter() - t0
-    frac = float(lens.sum()) / float(batch.lengths.sum())
-    return {"value": round(frac / dt, 4), "unit": "calls/s", "cores": int(cores),
-            "kind": "oracle",
-            "sample": f"first {rows} of {batch.B} rows ({int(lens.sum())} of {batch.T} tokens) "
-                      f"of the same batch, one full 30-layer pass in {dt:.1f} s; calls/s scaled "
-                      f"by the token fraction"}
+    o.forward(batch.ids, batch.lengths, markers=batch.markers)  # warm (weights widened)
+    ts = []
+    for _ in range(calls):
+        t0 = time.perf_counter()
+        o.forward(batch.ids, batch.lengths, markers=batch.markers)
+        ts.append(time.perf_counter() - t0)
+    cpu = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), None)
+    except OSError:
+        pass
+    return {"value": round(calls / sum(ts), 4), "unit": "calls/s", "cores": int(cores),
+            "kind": "oracle", "p50_ms": round(float(np.percentile(ts, 50)) * 1e3, 1),
+            "host_cpu": cpu,
+            "sample": f"the whole {batch.B}x{batch.S} batch ({batch.T} tokens), one warm call "
+                      f"then {calls} timed full 30-layer passes"}
 
 
 def _host_calls(enc, batch, flags, n, sync):
@@ -324,10 +335,13 @@ def protocol(args):
         res["graph_p50_over_roofline"] = round(res["graph_host"]["p50_ms"] / (t_roof * 1e3), 2)
         res["ops"] = {k: {f: v for f, v in row.items() if not f.startswith("_")}
                       for k, row in table.items()}
-        # RoPE variants, ABBA: fused, standalone, standalone, fused (graph replays)
+        # RoPE variants in mirrored order (original, standalone, fused, fused,
+        # standalone, original), graph replays
         ab = []
-        for variant in ("fused", "standalone", "standalone", "fused"):
-            flags = binding.RUN_ROPE_STANDALONE if variant == "standalone" else 0
+        rope_flags = {"original": binding.RUN_ROPE_ORIGINAL,
+                      "standalone": binding.RUN_ROPE_STANDALONE, "fused": 0}
+        for variant in ("original", "standalone", "fused", "fused", "standalone", "original"):
+            flags = rope_flags[variant]
             enc.run(batch.ids, batch.lengths, markers=batch.markers, flags=flags)
             sync()
             _host_calls(enc, batch, flags | binding.RUN_RESIDENT, args.protocol_warmup, sync)
@@ -335,13 +349,21 @@ def protocol(args):
                                   args.protocol_calls, sync)
             ab.append({"variant": variant, **_summ(samples)})
         bits = {}
-        for variant, flags in (("fused", binding.RUN_EAGER),
-                               ("standalone", binding.RUN_EAGER | binding.RUN_ROPE_STANDALONE)):
-            out = enc.run(batch.ids, batch.lengths, markers=batch.markers, flags=flags)
+        for variant, flags in rope_flags.items():
+            out = enc.run(batch.ids, batch.lengths, markers=batch.markers,
+                          flags=flags | binding.RUN_EAGER)
             sync()
             bits[variant] = enc.hidden_bits(out)
         res["rope_ab"] = {"rounds": ab,
-                          "bitwise_equal": bool(np.array_equal(bits["fused"], bits["standalone"]))}
+                          "bitwise_equal": bool(np.array_equal(bits["fused"], bits["standalone"]) and
+                                                np.array_equal(bits["fused"], bits["original"]))}
+        # the standalone kernels' own time, from one event-profiled eager pass each
+        for variant in ("original", "standalone"):
+            t_ops, _ = op_table(enc, batch, batch.markers, 1, flags=rope_flags[variant])
+            key = "rope_original" if variant == "original" else "rope"
+            if key in t_ops:
+                res["rope_ab"][f"{variant}_kernel_us"] = t_ops[key]["avg_launch_us"]
+                res["rope_ab"][f"{variant}_kernel_gbs"] = t_ops[key]["hbm_gbs"]
         if args.protocol_oracle_calls > 0:
             res["oracle"] = oracle_timing(MODEL, batch, args.protocol_oracle_calls)
         results["workloads"][name] = res
@@ -349,7 +371,8 @@ def protocol(args):
               f"({res['graph_host']['calls_per_s']:8.1f} calls/s)  eager p50 "
               f"{res['eager_host']['p50_ms']:8.3f}  device p50 {res['device_graph']['p50_ms']:8.3f}  "
               f"roofline {res['roofline_time_ms']:7.3f} ms  capture {res['capture_ms']:7.1f} ms  "
-              f"rope fused/standalone p50 {ab[0]['p50_ms']:.3f}/{ab[1]['p50_ms']:.3f}", flush=True)
+              f"rope original/standalone/fused p50 {ab[0]['p50_ms']:.3f}/{ab[1]['p50_ms']:.3f}/"
+              f"{ab[2]['p50_ms']:.3f}", flush=True)
     enc.close()
     with open(args.protocol_out, "w") as f:
         json.dump(results, f)
@@ -382,6 +405,53 @@ def oracle_timing(cfg, batch, calls):
             "calls_per_s": round(calls / (sum(ts) / 1e3), 4), "cores": os.cpu_count()}
 
 
+def graph_replays(enc, batch, steps, warmup, latency_calls, sync):
+    """First call (upload + graph capture), then `warmup` and `steps` timed
+    back-to-back graph replays on device-resident indices, then per-call
+    latencies (synchronised per call), the pages' host boundary (pack + upload
+    + replay + sync) and eager calls."""
+    from transformer_encoder_bf16_amd import binding
+    mk = batch.markers
+    t = time.perf_counter()
+    enc.run(batch.ids, batch.lengths, markers=mk)
+    sync()
+    first_ms = (time.perf_counter() - t) * 1e3
+    capture_ms = enc.stats()["last_capture_ms"]
+    flags = binding.RUN_RESIDENT
+    for _ in range(warmup):
+        enc.run(batch.ids, batch.lengths, markers=mk, flags=flags)
+    sync()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        enc.run(batch.ids, batch.lengths, markers=mk, flags=flags)
+    sync()
+    elapsed = time.perf_counter() - t0
+    lat, host, eager = [], [], []
+    for _ in range(latency_calls):
+        t = time.perf_counter()
+        enc.run(batch.ids, batch.lengths, markers=mk, flags=flags)
+        sync()
+        lat.append((time.perf_counter() - t) * 1e3)
+    for _ in range(latency_calls):
+        t = time.perf_counter()
+        enc.run(batch.ids, batch.lengths, markers=mk)
+        sync()
+        host.append((time.perf_counter() - t) * 1e3)
+    for _ in range(max(5, latency_calls // 5)):
+        t = time.perf_counter()
+        enc.run(batch.ids, batch.lengths, markers=mk, flags=binding.RUN_EAGER)
+        sync()
+        eager.append((time.perf_counter() - t) * 1e3)
+    launches = enc.stats()["launches_last_run"]
+    return {"calls_per_s": steps / elapsed, "ms_per_call": elapsed / steps * 1e3,
+            "p50_ms": round(float(np.percentile(lat, 50)), 4),
+            "p95_ms": round(float(np.percentile(lat, 95)), 4),
+            "host_boundary_p50_ms": round(float(np.percentile(host, 50)), 4),
+            "eager_host_boundary_p50_ms": round(float(np.percentile(eager, 50)), 4),
+            "first_call_ms": round(first_ms, 2), "capture_ms": round(capture_ms, 2),
+            "launches_per_call": launches}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -411,46 +481,20 @@ def main():
     mk = batch.markers
     sync = torch.cuda.synchronize
 
-    # first call: upload + graph capture (2 warmups inside), reported separately
-    t = time.perf_counter()
-    enc.run(batch.ids, batch.lengths, markers=mk)
-    sync()
-    first_ms = (time.perf_counter() - t) * 1e3
-    capture_ms = enc.stats()["last_capture_ms"]
+    main_run = graph_replays(enc, batch, args.steps, args.warmup, args.latency_calls, sync)
+    calls_per_s = main_run["calls_per_s"]
 
-    flags = binding.RUN_RESIDENT
-    for _ in range(args.warmup):
-        enc.run(batch.ids, batch.lengths, markers=mk, flags=flags)
-    sync()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        enc.run(batch.ids, batch.lengths, markers=mk, flags=flags)
-    sync()
-    elapsed = time.perf_counter() - t0
-    calls_per_s = args.steps / elapsed
-
-    # per-call latency, device-resident inputs, synchronised per call
-    lat = []
-    for _ in range(args.latency_calls):
-        t = time.perf_counter()
-        enc.run(batch.ids, batch.lengths, markers=mk, flags=flags)
-        sync()
-        lat.append((time.perf_counter() - t) * 1e3)
-    # the pages' host boundary: pack + upload + replay + completion sync
-    host = []
-    for _ in range(args.latency_calls):
-        t = time.perf_counter()
-        enc.run(batch.ids, batch.lengths, markers=mk)
-        sync()
-        host.append((time.perf_counter() - t) * 1e3)
-    # eager (no graph), host boundary
-    eager = []
-    for _ in range(max(5, args.latency_calls // 5)):
-        t = time.perf_counter()
-        enc.run(batch.ids, batch.lengths, markers=mk, flags=binding.RUN_EAGER)
-        sync()
-        eager.append((time.perf_counter() - t) * 1e3)
-    launches = enc.stats()["launches_last_run"]
+    # the second shape the metric is quoted on, the same way
+    short = None
+    if args.short_workload != "none" and args.short_workload != args.workload:
+        sb = make_batch(MODEL, ALL_WORKLOADS[args.short_workload])
+        r = graph_replays(enc, sb, max(args.steps, 200), args.warmup, args.latency_calls, sync)
+        short = {"workload": args.short_workload, "B": sb.B, "S": sb.S, "T": sb.T,
+                 "calls_per_s": round(r["calls_per_s"], 3),
+                 "ms_per_call": round(r["ms_per_call"], 4),
+                 **{k: r[k] for k in ("p50_ms", "p95_ms", "host_boundary_p50_ms",
+                                      "eager_host_boundary_p50_ms", "capture_ms",
+                                      "launches_per_call")}}
 
     # per-op table from event-bracketed eager passes (HIP events on the launch stream)
     table, pass_ms = op_table(enc, batch, mk, args.profile_passes)
@@ -487,7 +531,11 @@ def main():
         roof["avg_launch_us"] = d["avg_launch_us"]
         roof["timing"] = "HIP events around each launch of an eager pass"
         roof["per_launch_algorithmic"] = (d["_bytes"] if hbm_bound else d["_flops"]) / d["_calls"]
+    # the same kernel inside the pass: HIP events around each of its launches
     roof["avg_launch_us_in_pass_events"] = d["avg_launch_us"]
+    in_pass = (d["_bytes"] / d["_sec"] / 1e9) if hbm_bound else (d["_flops"] / d["_sec"] / 1e12)
+    roof["achieved_in_pass"] = round(in_pass, 2)
+    roof["frac_in_pass"] = round(in_pass / roof["peak"], 4)
     gemm_ops = [k for k in table if "_gemm" in k]
     gemm_frac = (sum(table[k]["_flops"] for k in gemm_ops) /
                  sum(table[k]["_sec"] for k in gemm_ops) / 1e12 / PEAK_BF16_TFLOPS)
@@ -496,7 +544,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(MODEL, batch, args.cpu_sample_rows)
+        cpu = cpu_baseline(MODEL, batch, args.cpu_calls)
 
     pages = None if args.dec_head else PAGES_CALLS_PER_S.get(args.workload)
     line = {
@@ -506,7 +554,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(elapsed / args.steps * 1e3, 4),
+        "ms_per_step": round(main_run["ms_per_call"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": round(calls_per_s / pages, 3) if pages else None,
@@ -519,14 +567,11 @@ def main():
                    "weight_seed": WEIGHT_SEED, "layers": "28+2", "mode": "hipGraph replay",
                    "inputs": "device-resident",
                    "decision_layers": "head" if args.dec_head else "encoder-shaped"},
-        "p50_ms": round(float(np.percentile(lat, 50)), 4),
-        "p95_ms": round(float(np.percentile(lat, 95)), 4),
-        "host_boundary_p50_ms": round(float(np.percentile(host, 50)), 4),
-        "eager_host_boundary_p50_ms": round(float(np.percentile(eager, 50)), 4),
-        "first_call_ms": round(first_ms, 2),
-        "capture_ms": round(capture_ms, 2),
+        **{k: main_run[k] for k in ("p50_ms", "p95_ms", "host_boundary_p50_ms",
+                                    "eager_host_boundary_p50_ms", "first_call_ms", "capture_ms",
+                                    "launches_per_call")},
         "create_ms": round(st0["create_ms"], 1),
-        "launches_per_call": launches,
+        "short_call": short,
         "roofline": roof,
         "gemm_mfma_frac": round(gemm_frac, 4),
         "profiled_pass_ms": round(pass_ms, 4),

@@ -1,21 +1,22 @@
 /*
  * laya_encoder.h -- C ABI of the MI355X (gfx950) BF16 encoder forward pass.
  *
- * What the library computes: the forward pass of an encoder-only transformer,
- * "28 encoder layers and two decision transformer layers" after a token
- * embedding, in BF16, with the final hidden states left in device memory for
- * a scorer (page "Run Laya encoder and decision layers on CUDA", section
- * Purpose).  Each layer is pre-LayerNorm (no bias) with rotary position
+ * What the library computes: the forward pass of an encoder-only transformer
+ * (a token embedding, then the encoder stack of 28 layers, then the two
+ * decision layers), in BF16, with the final hidden states kept in device
+ * memory for the scorer that consumes them (page "Run Laya encoder and
+ * decision layers on CUDA", section Purpose).  Each layer is pre-LayerNorm (no bias) with rotary position
  * embedding, bidirectional attention that is global on every 3rd encoder
- * layer and a 128-token sliding window otherwise, and a GeGLU FFN; separate
- * QKV, RoPE and attention steps ("[RFC]: Native Laya inference with Rust and
- * CUDA #14", section Design).  Optionally the last decision layer runs only
+ * layer and a 128-token sliding window otherwise, and a GeGLU FFN; the QKV
+ * projection, the rotation and attention are distinct steps ("[RFC]: Native
+ * Laya inference with Rust and CUDA #14", section Design).  Optionally the last decision layer runs only
  * for a list of marker rows, with keys and values still computed for every
  * token (page "perf(model): exact Metal speed-ups of the forward pass").
  *
  * Conventions (the "ops.h"-style C ABI of the RFC's build discussion: an ABI
- * version query, int return codes, work queued on a caller-supplied stream so
- * that it can be captured into a graph, resolved handles reused):
+ * version query, int return codes, device work placed on a stream the caller
+ * passes in so that the caller can capture it into a graph, resolved handles
+ * reused):
  *   - every function returns LAYA_OK (0) or a negative LAYA_E_* code;
  *   - `stream` arguments are hipStream_t values passed as void* (NULL = the
  *     null stream); all device work is queued on that stream and nothing
@@ -42,7 +43,7 @@
 extern "C" {
 #endif
 
-#define LAYA_ABI_VERSION 4
+#define LAYA_ABI_VERSION 5
 
 #define LAYA_OK 0
 #define LAYA_E_INVALID -1     /* bad ids, lengths, markers, sizes, NULL pointers */
@@ -63,18 +64,24 @@ extern "C" {
                                       token_ids/lengths/markers are not read */
 #define LAYA_RUN_ROPE_STANDALONE 8u /* RoPE by its own kernel after the QKV projection
                                       instead of in the projection's epilogue (the
-                                      pages' original step order; the two variants give
-                                      bitwise equal outputs and have separate graphs) */
+                                      pages' step order: projection, rotation, attention) */
+#define LAYA_RUN_ROPE_ORIGINAL 16u /* RoPE by its own kernel in the original launch
+                                      geometry (one thread per rotation pair, 64-bit index
+                                      division), the reference arm of the RoPE comparison of
+                                      "[Performance]: Optimize native Rust/CUDA Laya
+                                      inference #66", section Starting evidence.  All three
+                                      variants give bitwise equal outputs; each has its own
+                                      graphs; at most one of the two flags may be set */
 
 /* Model and limit configuration.  laya_config_init() fills the 421M-parameter
  * shape: vocab 50368, hidden 1024, 16 heads of 64, GeGLU inner width 2624,
- * 28 encoder + 2 decision layers, global attention on encoder layers with
+ * 28 encoder layers then 2 decision layers, global attention on encoder layers with
  * l % 3 == 0 (RoPE theta 160000), a 128-token window elsewhere (theta 10000),
  * LayerNorm eps 1e-5, limits 16 rows x 512 tokens, 2048 markers. */
 typedef struct laya_config {
     int32_t abi_version;   /* must be LAYA_ABI_VERSION */
     int32_t vocab;
-    int32_t hidden;        /* n_heads * head_dim; multiple of 128, <= 2048 */
+    int32_t hidden;        /* n_heads * head_dim; multiple of 128, <= 1024 */
     int32_t n_heads;
     int32_t head_dim;      /* must be 64 */
     int32_t ffn;           /* GeGLU inner width F: W_i has 2F rows, W_o2 has F columns; multiple of 64 */
@@ -129,11 +136,35 @@ void laya_config_init(laya_config *cfg);
 /* Checks a configuration without touching the device.  Returns LAYA_OK,
  * LAYA_E_ABI, LAYA_E_INVALID (non-positive or inconsistent sizes) or
  * LAYA_E_UNSUPPORTED (head_dim != 64, hidden not a multiple of 128 or above
- * 2048, ffn not a multiple of 64, limits above 16 x 512 / 2048). */
+ * 1024, ffn not a multiple of 64, limits above 16 x 512 / 2048, or a shape
+ * for which some planned GEMM launch would be unsupported). */
 int laya_validate_config(const laya_config *cfg);
 
+/* Host-only diagnostic: the GEMM plans of a pass over T live tokens and R
+ * marker rows.  A plan is a tile shape (laya_op_gemm's `config`) and a number
+ * of K ranges; every plan follows T alone, never the padded B x S, so padding
+ * never changes a result.  Plans are piecewise constant in T: *t_first and
+ * *t_last bound the token counts that share this pass's plans, and one
+ * captured graph of a (B, S, R) serves exactly such a range.  out (host,
+ * `cap` entries) receives the plans in the order QKV, output, up, down, then
+ * (dec_head) head up, head down, then (R > 0) the marker layer's K/V, Q,
+ * output, up, down (and head up, head down); *n_out is the full count.
+ * fused = 1 marks a split projection whose reduce launch also does the
+ * residual add and the next LayerNorm.  Returns LAYA_E_INVALID for T outside
+ * [1, max_batch x max_seq] or R outside [0, max_markers]. */
+typedef struct laya_gemm_plan {
+    int32_t config;
+    int32_t splits;
+    int32_t fused;
+} laya_gemm_plan;
+
+int laya_pass_plans(const laya_config *cfg, int32_t T, int32_t R, int32_t *t_first,
+                    int32_t *t_last, laya_gemm_plan *out, int32_t cap, int32_t *n_out);
+
 /* Checks run arguments without touching the device (the host half of
- * laya_encoder_run's validation).  token_ids: host int32 [B][S] row-major,
+ * laya_encoder_run's validation; the worker's input limits, and the refusal
+ * of invalid input before any model work, of page "Laya native CUDA worker",
+ * section Start and check).  token_ids: host int32 [B][S] row-major,
  * right-padded, each valid id in [0, vocab); lengths: host int32 [B], each in
  * [1, S]; markers: host int32 [R][2] (row, position) pairs with position <
  * lengths[row], or NULL when R == 0.  B == 0 is valid (empty batch).  Limits:
@@ -166,10 +197,11 @@ int laya_validate_run_args(const laya_config *cfg, const int32_t *token_ids,
  * +3 b_2 [hidden], drawn by the same generator (laya_encoder_weight reports
  * a bias as 1 row).
  *
- * Rotary tables ("reproduce official BF16 rotary-table rounding", page "Laya
- * native CUDA worker", section Prepare the checkpoint and bundle; "both
- * global/local tables", page "[Performance]...#66", section Starting
- * evidence): cos and sin of p * theta^(-2i/head_dim), p < max_seq,
+ * Rotary tables (BF16-rounded tables exported once and then fixed, page
+ * "Laya native CUDA worker", section Prepare the checkpoint and bundle; one
+ * table for the global layers and one for the local ones, page
+ * "[Performance]: Optimize native Rust/CUDA Laya inference #66", section
+ * Starting evidence): cos and sin of p * theta^(-2i/head_dim), p < max_seq,
  * i < head_dim/2, evaluated in double and rounded once to BF16.
  *
  * On success *out owns all device memory it allocated.  Errors: LAYA_E_ABI,
@@ -204,8 +236,8 @@ int laya_encoder_create(const laya_config *cfg, uint64_t weight_seed, int device
  *
  * With LAYA_RUN_RESIDENT the pass reruns on the device copy of the previous
  * run's indices (same B, S, R; LAYA_E_INVALID otherwise): inputs already in
- * device memory, nothing crosses the host link ("repeat each workspace
- * without intermediate readbacks", page "Run Laya encoder and decision layers
+ * device memory, nothing crosses the host link (the reused-workspace reruns
+ * with no readback in between of page "Run Laya encoder and decision layers
  * on CUDA", section Test Plan).
  *
  * The caller synchronises `stream` before reading out->hidden, and must not
@@ -215,19 +247,33 @@ int laya_encoder_run(laya_encoder *enc, void *stream, const int32_t *token_ids,
                      const int32_t *markers, int32_t R, uint32_t flags,
                      laya_output *out);
 
-/* Frees every resource of the handle (waits for its device work).  NULL is a
- * no-op.  Works on a poisoned handle. */
+/* Frees every resource of the handle (waits for its device work): the
+ * resident weights and the shape workspaces the executor owns (page "Laya
+ * native CUDA worker", section Prepare the checkpoint and bundle) and the
+ * cached graphs ("[RFC]: Native Laya inference with Rust and CUDA #14",
+ * section Design).  NULL is a no-op.  Works on a poisoned handle, which a
+ * native failure leaves stopped but still to be released (the same page's
+ * section Start and check). */
 int laya_encoder_destroy(laya_encoder *enc);
 
-/* Message of the last failure on this handle ("" if none).  The string is
- * owned by the handle. */
+/* Message of the last failure on this handle ("" if none): the text behind
+ * the error classes of page "Laya native CUDA worker", section Start and
+ * check (invalid input, unsupported shape, a native failure that stops the
+ * executor).  The string is owned by the handle. */
 const char *laya_encoder_last_error(const laya_encoder *enc);
 
 /* Message of the last failure in this thread that had no handle to attach
- * to (laya_encoder_create, laya_validate_*, laya_op_*). */
+ * to (laya_encoder_create, laya_validate_*, laya_op_*): a refused
+ * configuration at startup, which the pages check before anything is loaded
+ * (page "Run Laya encoder and decision layers on CUDA", section Purpose). */
 const char *laya_last_error(void);
 
-/* After a run with LAYA_RUN_CAPTURE_LAYERS: layer output `index` (0 = "emb",
+/* The per-layer hidden states that the pages compare against their
+ * reference, intermediate states as well as final ones (page "Run Laya
+ * encoder and decision layers on CUDA", section Test Plan; the comparison at
+ * "encoder27" of "[Performance]: Optimize native Rust/CUDA Laya inference
+ * #66", section Starting evidence).
+ * After a run with LAYA_RUN_CAPTURE_LAYERS: layer output `index` (0 = "emb",
  * then "enc00".."enc<n_enc-1>" (residual stream after each encoder layer),
  * "enc_final", "dec0".., and "out"), as a device BF16 [rows][hidden] view
  * owned by the handle and valid until the next run.  name_out (host, may be
@@ -237,8 +283,13 @@ int laya_encoder_layer_output(laya_encoder *enc, int32_t index, laya_output *out
                               char *name_out, size_t name_cap);
 
 /* FNV-1a-64 over the BF16 bytes (little-endian, logical [out][in] order) of
- * weight tensor `tensor_id` (numbering as in laya_encoder_create).  Copies
- * the tensor to the host; synchronous; diagnostic only. */
+ * weight tensor `tensor_id` (numbering as in laya_encoder_create): the
+ * weight-parity check of the pages, here between the library and the
+ * oracle's independent generator ("[RFC]: Native Laya inference with Rust
+ * and CUDA #14", section Implementation and checks; frozen checkpoint hashes,
+ * "[Performance]: Optimize native Rust/CUDA Laya inference #66", section
+ * Validation and acceptance).  Copies the tensor to the host; synchronous;
+ * diagnostic only. */
 int laya_encoder_weight_digest(laya_encoder *enc, int32_t tensor_id, uint64_t *fnv64);
 
 /* Device pointer (BF16, [rows][cols]) and shape of weight or bias tensor `tensor_id`;
@@ -246,6 +297,13 @@ int laya_encoder_weight_digest(laya_encoder *enc, int32_t tensor_id, uint64_t *f
 int laya_encoder_weight(laya_encoder *enc, int32_t tensor_id, const void **dev,
                         int32_t *rows, int32_t *cols);
 
+/* Copies the handle's counters into *stats (host only): creation time, the
+ * cost of the last graph capture and the graph cache's state, reported apart
+ * from replay latency as "[Performance]: Optimize native Rust/CUDA Laya
+ * inference #66", section Implementation priorities, asks (first-shape and
+ * capture costs measured separately), with the LRU of captured shapes of
+ * "[RFC]: Native Laya inference with Rust and CUDA #14", section Design.
+ * LAYA_E_INVALID for NULL arguments. */
 int laya_encoder_stats(const laya_encoder *enc, laya_stats *stats);
 
 /* Diagnostic: fill every byte of the handle's workspace (activations,
@@ -321,7 +379,9 @@ int laya_queue_destroy(laya_queue *q);
  * HIP events on `stream`, aggregated by op class.  flops and bytes are the
  * algorithmic work of the class's launches (GEMMs 2*M*N*K; attention
  * 4*64*heads per visible (query, key) pair; bytes = the tensors each launch
- * must read and write once, in BF16).  Arguments as laya_encoder_run;
+ * must read and write once, in BF16).  Arguments as laya_encoder_run (flags:
+ * only LAYA_RUN_ROPE_STANDALONE or LAYA_RUN_ROPE_ORIGINAL, to time a RoPE
+ * variant);
  * synchronous; out receives up to `cap` classes, *n_out how many, *total_ms
  * (may be NULL) the event span of the whole pass.  Diagnostic only. */
 typedef struct laya_op_time {
@@ -334,8 +394,8 @@ typedef struct laya_op_time {
 
 int laya_encoder_profile(laya_encoder *enc, void *stream, const int32_t *token_ids,
                          const int32_t *lengths, int32_t B, int32_t S,
-                         const int32_t *markers, int32_t R, laya_op_time *out, int32_t cap,
-                         int32_t *n_out, double *total_ms);
+                         const int32_t *markers, int32_t R, uint32_t flags, laya_op_time *out,
+                         int32_t cap, int32_t *n_out, double *total_ms);
 
 /* Rotary table of laya_encoder_create, on the host: cos_bits/sin_bits receive
  * max_pos * head_dim/2 BF16 bit patterns ([p][i] row-major).  Host only. */
@@ -374,9 +434,10 @@ int laya_op_layernorm(void *stream, void *x, const void *r, void *n, const float
  * [M][lda], W device BF16 [N or 2N][ldw], C device BF16 [M][ldc]; K a multiple
  * of 64, N a multiple of 64, lda/ldw/ldc multiples of 8 (16-byte rows).
  * config -1 picks the tile shape and K split the pass itself would use for M
- * rows; config 0..8 (tile shapes 32x64, 64x64, 128x64, 128x128, 256x128,
- * 256x256, 128x128 with a shallower ring that fits two per compute unit, and
- * 32x64 and 64x64 for short calls, two computing waves with deep rings;
+ * rows; config 0..9 (tile shapes 32x64, 64x64, 128x64, 128x128, 256x128,
+ * 256x256, 128x128 with a shallower ring that fits two per compute unit,
+ * 32x64 and 64x64 for short calls, two computing waves with deep rings, and
+ * 256x256 with two wave groups alternating between multiplying and loading;
  * weight rows x tokens) with
  * `splits` K ranges forces one (split K only on shapes 0..3, 7 and 8; GeGLU
  * not on shapes 0 and 7).  Each output is the sum, in
@@ -423,8 +484,17 @@ int laya_op_rope(void *stream, void *buf, int32_t ld, int32_t n_heads_rot, int32
                  const int32_t *pos, const void *cos_tab, const void *sin_tab,
                  int32_t max_pos);
 
+/* laya_op_rope in the original launch geometry of the pages' rotary kernel
+ * (page "perf(model): exact Metal speed-ups of the forward pass": the kernel it
+ * replaced derived each element's coordinates by 64-bit integer division):
+ * one thread per rotation pair, its (row, head, pair) recovered from a flat
+ * 64-bit index.  Arguments, result and errors as laya_op_rope, bitwise. */
+int laya_op_rope_original(void *stream, void *buf, int32_t ld, int32_t n_heads_rot,
+                          int32_t rows, const int32_t *pos, const void *cos_tab,
+                          const void *sin_tab, int32_t max_pos);
+
 /* The QKV projection with its two consumers' layouts fused into the epilogue
- * (the separate QKV, RoPE and attention steps of "[RFC]: Native Laya
+ * (the QKV projection that feeds the rotation and attention steps of "[RFC]: Native Laya
  * inference with Rust and CUDA #14", section Design; RoPE fused as the
  * optimised variant of "[Performance]: Optimize native Rust/CUDA Laya
  * inference #66", section Implementation priorities).  Computes

@@ -3,8 +3,8 @@
 TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
 
 What is computed (the stack of page "Run Laya encoder and decision layers on
-CUDA", section Purpose: an embedding, 28 encoder layers and two decision
-transformer layers, BF16, hidden states left for the scorer):
+CUDA", section Purpose: a token embedding, the 28-layer encoder, then the two
+decision layers, in BF16, the final hidden states kept for the scorer):
 
   x = Emb[id]                                          (exact copy)
   for every layer L (encoder 0..n_enc-1, then decision layers):
@@ -30,8 +30,8 @@ D(a, W, b) = R(R(a W^T) + b), and the FFN is 4x wide and not gated:
       h   = R(GELU(D(n2, W_1, b_1)))      f = D(h, W_2, b_2)
 
 R() is float32 -> BF16 round-to-nearest-even: every stored tensor is BF16,
-every other intermediate is float32.  Separate QKV, RoPE and attention steps
-follow "[RFC]: Native Laya inference with Rust and CUDA #14", section Design.
+every other intermediate is float32.  The QKV projection, the rotation and
+attention as distinct steps follow "[RFC]: Native Laya inference with Rust and CUDA #14", section Design.
 Encoder layer l is global iff l % global_every == 0; decision layers are
 global; global layers use the theta_global table, local ones theta_local.
 LayerNorm: mean and biased variance in float32 (two passes), eps 1e-5, gain
@@ -81,10 +81,19 @@ def linear(a: np.ndarray, w: np.ndarray, accumulate: str = "float32") -> np.ndar
     float32.  The sum is accumulated in float32 (the pass's stated precision)
     or, with accumulate="float64", in float64 and rounded once to float32: the
     same definition with a different accumulation error, used to measure how
-    far two valid implementations of the BF16 pass drift apart."""
+    far two valid implementations of the BF16 pass drift apart.
+    accumulate="chunk16" is a third valid order: the K range in consecutive
+    pieces of 16, each piece's float32 sum added to a float32 running total
+    in K order (the shape of a chain of 16-deep matrix-core steps)."""
     if accumulate == "float64":
         return np.matmul(np.asarray(a, np.float64), np.asarray(w, np.float64).T).astype(np.float32)
-    return np.matmul(np.asarray(a, np.float32), np.asarray(w, np.float32).T)
+    a32, w32 = np.asarray(a, np.float32), np.asarray(w, np.float32)
+    if accumulate == "chunk16":
+        y = np.zeros((a32.shape[0], w32.shape[0]), np.float32)
+        for k0 in range(0, a32.shape[1], 16):
+            y += np.matmul(a32[:, k0:k0 + 16], w32[:, k0:k0 + 16].T)
+        return y
+    return np.matmul(a32, w32.T)
 
 
 def attention(q, k, v, q_pos, k_pos, n_heads, head_dim, half_window, rounding=True):

@@ -2,9 +2,9 @@
 
 TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
 
-BF16 is the storage format of every tensor of the forward pass ("28 encoder
-layers and two decision transformer layers" run in BF16, page "Run Laya
-encoder and decision layers on CUDA", section Purpose); arithmetic between
+BF16 is the storage format of every tensor of the forward pass (the encoder
+and decision layers run in BF16, page "Run Laya encoder and decision layers
+on CUDA", section Purpose); arithmetic between
 two stored tensors happens in float32 and its result is rounded once, to
 nearest-even, when it is stored again.
 """

@@ -3,14 +3,15 @@
 TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
 
 Tables.  The pages keep four rotary tables -- global and local, cos and sin --
-whose entries carry the BF16 rounding of the official model ("Table export
-... reproduce official BF16 rotary-table rounding", page "Laya native CUDA
-worker", section Prepare the checkpoint and bundle; "both global/local
-tables", page "[Performance]: Optimize native Rust/CUDA Laya inference #66",
-section Starting evidence).  Reading taken here: the angle of pair i at
+whose entries carry the BF16 rounding of the official model (exported once
+with that rounding and then fixed: page "Laya native CUDA worker", section
+Prepare the checkpoint and bundle; one table pair for the global layers and
+one for the local ones: page "[Performance]: Optimize native Rust/CUDA Laya
+inference #66", section Starting evidence).  Reading taken here: the angle of pair i at
 position p is p * theta^(-2i/d) with d = head_dim; cos and sin are evaluated
 in float64 and rounded once to BF16 (nearest even).  Positions run 0..511
-("maximum 512 tokens", same page, section Recorded baseline and environment).
+(the 512-token maximum of the issue's section Recorded baseline and
+environment).
 
 Rotation.  Pairs are (i, i + d/2) ("rotate half").  For one head vector v of
 length d, with x = v[i], y = v[i + d/2] and c, s the table entries of the
@@ -19,7 +20,7 @@ token's position:
     v[i + d/2] <- bf16( fl32(y*c + x*s) )
 Both products of BF16 values are exact in float32, so the only roundings are
 the float32 difference/sum and the BF16 store.  Only query and key heads are
-rotated; value bytes are left as they were ("preserving V bytes", section
+rotated; value bytes are left as they were (V's bytes kept, section
 Starting evidence of the same issue).
 """
 from __future__ import annotations

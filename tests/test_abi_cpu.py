@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol(lib):
     assert declared == set(b.EXPORTS)
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.laya_abi_version() == b.LAYA_ABI_VERSION == 4
+    assert lib.laya_abi_version() == b.LAYA_ABI_VERSION == 5
 
 
 def test_default_config_is_the_model(lib):
@@ -47,6 +47,8 @@ def test_valid_configs(lib, cfg):
     (dict(head_dim=32, n_heads=32), b.LAYA_E_UNSUPPORTED),
     (dict(hidden=1000), b.LAYA_E_INVALID),
     (dict(hidden=960, n_heads=15), b.LAYA_E_UNSUPPORTED),
+    (dict(hidden=1152, n_heads=18), b.LAYA_E_UNSUPPORTED),
+    (dict(hidden=2048, n_heads=32), b.LAYA_E_UNSUPPORTED),
     (dict(ffn=2600), b.LAYA_E_UNSUPPORTED),
     (dict(max_batch=17), b.LAYA_E_UNSUPPORTED),
     (dict(max_seq=513), b.LAYA_E_UNSUPPORTED),
@@ -64,6 +66,70 @@ def test_invalid_configs(lib, change, code):
     cfg = dict(MODEL)
     cfg.update(change)
     assert b.validate_config(cfg) == code
+
+
+# split-capable tile shapes and the most K ranges each takes (laya_op_gemm)
+SPLIT_MAX = {0: 8, 1: 8, 2: 8, 3: 8, 7: 8, 8: 8}
+
+
+def _launchable(cfg_id, splits, K, epi, N, fused):
+    if not 0 <= cfg_id <= 9 or splits < 1 or splits > K // 64:
+        return False
+    if splits > SPLIT_MAX.get(cfg_id, 1):
+        return False
+    if epi in (1, 2) and cfg_id == 0:
+        return False
+    if fused and (N > 1024 or cfg_id not in SPLIT_MAX):
+        return False
+    return True
+
+
+@pytest.mark.parametrize("hidden", list(range(128, 1025, 128)))
+def test_every_accepted_width_plans_launchable_gemms(lib, hidden):
+    """Every hidden width the handle accepts: at every token count the pass
+    can see, with and without markers, each planned GEMM launch is one the
+    kernels support (tile shape, K split within the shape's limit, paired
+    epilogues on paired shapes, the fused reduce + LayerNorm only on
+    split-capable shapes and rows of at most 1024 values)."""
+    cfg = dict(MODEL, hidden=hidden, n_heads=hidden // 64, ffn=(hidden * 41 // 16) // 64 * 64)
+    assert b.validate_config(cfg) == b.LAYA_OK
+    H, F = cfg["hidden"], cfg["ffn"]
+    shapes = [(3 * H, H, 2), (H, H, 0), (F, H, 1), (H, F, 0)]
+    marker = [(2 * H, H, 2), (H, H, 2), (H, H, 0), (F, H, 1), (H, F, 0)]
+    T = 1
+    while T <= cfg["max_batch"] * cfg["max_seq"]:
+        lo, hi, plans = b.pass_plans(cfg, T, 96)
+        assert lo == T
+        for (cid, sp, fused), (N, K, epi) in zip(plans, shapes + marker):
+            assert _launchable(cid, sp, K, epi, N, fused), (T, N, K, cid, sp, fused)
+        T = hi + 1
+
+
+def test_plans_follow_the_token_count_in_buckets(lib):
+    """Plans depend on the live token count alone, through fixed buckets whose
+    edges include the K-split thresholds: inside a bucket every count has the
+    same plans (one captured graph serves it), and the splits of the marker
+    layer are those of the full pass."""
+    edges = []
+    T = 1
+    while T <= 8192:
+        lo, hi, plans = b.pass_plans(MODEL, T)
+        for t in sorted({lo, hi, (lo + hi) // 2, min(hi, lo + 1)}):
+            assert b.pass_plans(MODEL, t) == (lo, hi, plans), t
+        _, _, with_markers = b.pass_plans(MODEL, hi, 37)
+        assert with_markers[:4] == plans
+        assert [p[1] for p in with_markers[4:]] == [plans[0][1], plans[0][1], plans[1][1],
+                                                   plans[2][1], plans[3][1]]
+        edges.append(hi)
+        T = hi + 1
+    assert edges == [64, 256, 512, 1024, 1536, 2048, 3072, 4096, 8192]
+    # the configs' token counts
+    assert b.pass_plans(MODEL, 48)[:2] == (1, 64)
+    assert b.pass_plans(MODEL, 4050)[:2] == (3073, 4096)
+    with pytest.raises(b.LayaError):
+        b.pass_plans(MODEL, 0)
+    with pytest.raises(b.LayaError):
+        b.pass_plans(MODEL, 8193)
 
 
 def test_abi_mismatch(lib):

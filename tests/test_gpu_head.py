@@ -5,7 +5,7 @@ Variant of "perf(model): exact Metal speed-ups of the forward pass": every
 projection of the two decision layers adds a bias to its BF16 product in
 BF16, and their FFN is 4*hidden wide with plain GELU.  The same bars as the
 default model: per layer on the GPU's own inputs within the pages' nRMS
-0.005, end to end within 1.5x the oracle's float32-vs-float64 spread, graph
+0.005, end to end within 1.1x the oracle's float32-vs-float64 spread, graph
 replay bitwise equal to eager, marker rows bitwise equal to the full pass's
 rows, and no dependence on stale workspace contents.
 """
@@ -20,7 +20,7 @@ from transformer_encoder_bf16_amd.inputs import (MODEL, TINY, WEIGHT_SEED, WORKL
 pytestmark = pytest.mark.gpu
 
 NRMS_LIMIT = 5e-3
-FLOOR_FACTOR = 1.5
+FLOOR_FACTOR = 1.1
 TINY_NRMS_LIMIT = 1e-2
 HEAD = dict(MODEL, dec_head=1)
 TINY_HEAD = dict(TINY, dec_head=1)
@@ -105,7 +105,7 @@ def test_head_tensor_digests(enc):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("name", ["short_1", "short_3", "marker_subset", "long_3"])
+@pytest.mark.parametrize("name", ["short_1", "short_3", "marker_subset", "long_3", "mixed_16"])
 def test_head_workload_matches_oracle(binding, enc, orc, orc64, name):
     _check_head(binding, enc, orc, orc64, make_batch(HEAD, WORKLOADS[name]), name)
 
@@ -139,7 +139,7 @@ def _check_head(binding, enc, orc, orc64, batch, name):
                              "end_to_end_nrms": e2e, "oracle_f32_vs_f64_final_nrms": floor})
     for n, e in per_layer.items():
         assert e <= NRMS_LIMIT, (n, e)
-    assert e2e["out"] <= max(NRMS_LIMIT, FLOOR_FACTOR * floor)
+    assert e2e["out"] <= FLOOR_FACTOR * floor, (e2e["out"], floor)
 
     eager, _ = _run_bits(enc, batch, binding.RUN_EAGER, markers)
     assert np.array_equal(eager, bits_of(caps["out"]))

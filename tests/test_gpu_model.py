@@ -11,8 +11,11 @@ it are checked for every workload:
   BF16 pass a single rounding decision that comes out differently (any
   change of float32 summation order does that) grows until the two runs'
   rounding noise is decorrelated; the oracle against itself with a float64
-  accumulator ends ~1.4% apart.  The GPU must stay within 1.5x of that floor,
-  measured in the same test.
+  accumulator ends ~1.4% apart.  The GPU must stay within 1.1x of that floor,
+  measured in the same test.  The pages' absolute 0.005 is NOT met end to end
+  (final nRMS ~0.014 on every workload); test_end_to_end_absolute_limit
+  records that as an expected failure, and every report says whether a
+  batch met it.
 
 The embedding must be bit-exact, graph replay must equal the eager run bit
 for bit, repeated runs must be bitwise repeatable, and the invariants the
@@ -30,7 +33,7 @@ from transformer_encoder_bf16_amd.inputs import (ALL_WORKLOADS, MODEL, TINY, WEI
 pytestmark = pytest.mark.gpu
 
 NRMS_LIMIT = 5e-3
-FLOOR_FACTOR = 1.5
+FLOOR_FACTOR = 1.1
 
 
 @pytest.fixture(scope="module")
@@ -169,15 +172,19 @@ def _check_batch(binding, enc, orc, orc64, batch, name):
     ref64 = orc64.forward(batch.ids, batch.lengths, markers=markers)["out"]
     floor = oracle.nrms(ref64, ref["out"])
     final = e2e["out"]
+    final64 = oracle.nrms(caps["out"], ref64)
     max_abs = float(np.abs(caps["out"] - ref["out"]).max())
     print(f"[{name}] end-to-end final nRMS {final:.3g} (oracle float32 vs float64 accumulation: "
-          f"{floor:.3g}), max_abs {max_abs:.3g}", flush=True)
+          f"{floor:.3g}; GPU vs the float64 oracle {final64:.3g}), max_abs {max_abs:.3g}",
+          flush=True)
     report("workload", {"workload": name, "T": batch.T, "per_layer_nrms": per_layer,
                         "end_to_end_nrms": e2e, "final_nrms": final, "max_abs": max_abs,
-                        "oracle_f32_vs_f64_final_nrms": floor})
+                        "oracle_f32_vs_f64_final_nrms": floor, "final_nrms_vs_f64_oracle": final64,
+                        "final_over_floor": final / floor if floor else None,
+                        "end_to_end_within_0.005": bool(final <= NRMS_LIMIT)})
     for n, e in per_layer.items():
         assert e <= NRMS_LIMIT, (n, e)
-    assert final <= max(NRMS_LIMIT, FLOOR_FACTOR * floor)
+    assert final <= FLOOR_FACTOR * floor, (final, floor)
 
     # eager (no capture), graph replay, repeat: all bitwise equal
     eager, _ = _run_bits(binding, enc, batch, binding.RUN_EAGER, markers)
@@ -197,6 +204,23 @@ def _check_batch(binding, enc, orc, orc64, batch, name):
         e = oracle.nrms(to_f(eager), to_f(full[rows]))
         report("marker_subset_vs_full", {"rows": int(len(rows)), "bitwise": bitwise, "nrms": e})
         assert bitwise, e
+
+
+@pytest.mark.xfail(strict=True, reason=(
+    "the pages' nRMS <= 0.005 is not met end to end: the BF16 pass is chaotic, any "
+    "change of float32 summation order (the oracle's own float64 accumulation "
+    "included) ends ~0.014 apart at the output; see the floor-relative checks"))
+def test_end_to_end_absolute_limit(binding, enc, orc):
+    """The pages' limit read as an absolute end-to-end bound on the final
+    hidden states of the 1x48 call.  Expected to fail (strict): if it ever
+    passes, the parity claims must be revisited."""
+    batch = make_batch(MODEL, WORKLOADS["short_1"])
+    out = enc.run(batch.ids, batch.lengths, flags=binding.RUN_EAGER)
+    _sync()
+    got = (enc.hidden_bits(out).astype(np.uint32) << 16).view(np.float32)
+    final = oracle.nrms(got, orc.forward(batch.ids, batch.lengths)["out"])
+    print(f"[short_1] end-to-end final nRMS {final:.4g} against the absolute 0.005", flush=True)
+    assert final <= NRMS_LIMIT, final
 
 
 def test_reversed_rows_and_padding_are_bitwise_invariant(binding, enc):
@@ -219,25 +243,30 @@ def test_reversed_rows_and_padding_are_bitwise_invariant(binding, enc):
     assert np.array_equal(base, pbits)
     gbits, _ = _run_bits(binding, enc, pad, 0)
     assert np.array_equal(base, gbits)
-    # a wider padded S with the same lengths: B*S picks the GEMMs' K split, so
-    # the result is bitwise equal while the split is unchanged and otherwise
-    # within the drift of a different summation order
-    ids3 = np.full((batch.B, 96), 7, np.int32)
-    for b in range(batch.B):
-        ids3[b, :batch.lengths[b]] = batch.ids[b, :batch.lengths[b]]
-    wide = type(batch)(ids=ids3, lengths=batch.lengths.copy())
-    wbits, _ = _run_bits(binding, enc, wide, binding.RUN_EAGER)
-    to_f = lambda u: (u.astype(np.uint32) << 16).view(np.float32)
-    e = oracle.nrms(to_f(wbits), to_f(base))
-    report("wider_padding", {"S": [batch.S, 96], "bitwise": bool(np.array_equal(base, wbits)),
-                             "nrms": e})
-    assert e < 0.03
+    # the same rows padded to a wider S (4x64 -> 4x96 and 4x512, where B*S
+    # crosses several GEMM plan thresholds): plans follow the live token count
+    # only, so every valid output is bitwise the same, eager and graph
+    for width in (96, 512):
+        ids3 = np.full((batch.B, width), 7, np.int32)
+        for b in range(batch.B):
+            ids3[b, :batch.lengths[b]] = batch.ids[b, :batch.lengths[b]]
+        wide = type(batch)(ids=ids3, lengths=batch.lengths.copy())
+        wbits, _ = _run_bits(binding, enc, wide, binding.RUN_EAGER)
+        wgraph, _ = _run_bits(binding, enc, wide, 0)
+        report("wider_padding", {"S": [batch.S, width],
+                                 "bitwise": bool(np.array_equal(base, wbits))})
+        assert np.array_equal(base, wbits), width
+        assert np.array_equal(base, wgraph), width
 
 
 def test_one_graph_serves_every_length_pattern(binding, enc):
+    """Two length patterns of one (B, S) whose token counts fall in the same
+    plan bucket replay one graph; a third pattern in another bucket gets its
+    own graph; every replay equals its eager run bitwise."""
     wl = WORKLOADS["short_3"]
     b1 = make_batch(MODEL, wl)
     b2 = random_batch(MODEL, wl.B, wl.S, seed=99, len_lo=wl.len_lo)
+    assert binding.pass_plans(MODEL, b1.T)[:2] == binding.pass_plans(MODEL, b2.T)[:2]
     e1, _ = _run_bits(binding, enc, b1, binding.RUN_EAGER)
     e2, _ = _run_bits(binding, enc, b2, binding.RUN_EAGER)
     g1, _ = _run_bits(binding, enc, b1, 0)
@@ -245,6 +274,12 @@ def test_one_graph_serves_every_length_pattern(binding, enc):
     g2, _ = _run_bits(binding, enc, b2, 0)
     assert enc.stats()["graphs_cached"] == n_graphs
     assert np.array_equal(g1, e1) and np.array_equal(g2, e2)
+    # 4 rows of 8..16 tokens: T <= 64, another plan bucket of the same (B, S)
+    b3 = random_batch(MODEL, wl.B, wl.S, seed=98, len_lo=8, len_hi=16)
+    assert b3.T <= 64 < b1.T
+    e3, _ = _run_bits(binding, enc, b3, binding.RUN_EAGER)
+    g3, _ = _run_bits(binding, enc, b3, 0)
+    assert np.array_equal(g3, e3)
 
 
 def test_empty_batch_and_invalid_args(binding, enc):
@@ -291,30 +326,33 @@ def test_nan_poisoned_workspace_changes_nothing(binding, enc, name):
 
 @pytest.mark.parametrize("name", ["short_1", "long_3", "marker_subset"])
 def test_rope_variants_are_bitwise_equal(binding, enc, name):
-    """RoPE in the QKV projection's epilogue (the default) and RoPE by its own
-    kernel after the projection give bitwise equal outputs, eager and graph."""
+    """RoPE in the QKV projection's epilogue (the default), by its own kernel
+    after the projection, and by its own kernel in the original launch
+    geometry give bitwise equal outputs, eager and graph."""
     batch = make_batch(MODEL, WORKLOADS[name])
     fused, _ = _run_bits(binding, enc, batch, binding.RUN_EAGER, batch.markers)
-    alone, _ = _run_bits(binding, enc, batch, binding.RUN_EAGER | binding.RUN_ROPE_STANDALONE,
-                         batch.markers)
-    alone_g, _ = _run_bits(binding, enc, batch, binding.RUN_ROPE_STANDALONE, batch.markers)
     fused_g, _ = _run_bits(binding, enc, batch, 0, batch.markers)
-    assert np.array_equal(fused, alone)
-    assert np.array_equal(alone_g, alone) and np.array_equal(fused_g, fused)
+    assert np.array_equal(fused_g, fused)
+    for flag in (binding.RUN_ROPE_STANDALONE, binding.RUN_ROPE_ORIGINAL):
+        alone, _ = _run_bits(binding, enc, batch, binding.RUN_EAGER | flag, batch.markers)
+        alone_g, _ = _run_bits(binding, enc, batch, flag, batch.markers)
+        assert np.array_equal(fused, alone), flag
+        assert np.array_equal(alone_g, alone), flag
 
 
 def test_unknown_run_flags_are_rejected(binding, enc):
     batch = make_batch(MODEL, WORKLOADS["short_1"])
-    with pytest.raises(binding.LayaError) as ei:
-        enc.run(batch.ids, batch.lengths, flags=64)
-    assert ei.value.code == binding.LAYA_E_INVALID
+    for flags in (64, binding.RUN_ROPE_STANDALONE | binding.RUN_ROPE_ORIGINAL):
+        with pytest.raises(binding.LayaError) as ei:
+            enc.run(batch.ids, batch.lengths, flags=flags)
+        assert ei.value.code == binding.LAYA_E_INVALID
 
 
 @pytest.mark.timeout(900)
 def test_maximum_batch_and_markers_match_oracle(binding, enc, orc, orc64):
     """The handle's limits: 16 rows of 512 tokens (T = 8192, every row full)
     and 2048 marker rows (128 per row).  Per layer within the pages' 0.005 on
-    the GPU's own inputs, end to end within 1.5x the oracle's float32/float64
+    the GPU's own inputs, end to end within 1.1x the oracle's float32/float64
     spread, graph equal to eager, marker rows bitwise equal to the full
     pass's rows."""
     batch = random_batch(MODEL, 16, 512, seed=77, len_lo=512, markers_per_row=128)
@@ -335,7 +373,7 @@ def test_maximum_batch_and_markers_match_oracle(binding, enc, orc, orc64):
                              "oracle_f32_vs_f64_final_nrms": floor})
     for n, e in per_layer.items():
         assert e <= NRMS_LIMIT, (n, e)
-    assert final <= max(NRMS_LIMIT, FLOOR_FACTOR * floor)
+    assert final <= FLOOR_FACTOR * floor, (final, floor)
     eager, _ = _run_bits(binding, enc, batch, binding.RUN_EAGER)
     graph, _ = _run_bits(binding, enc, batch, 0)
     assert np.array_equal(eager, bits_of(caps["out"])) and np.array_equal(graph, eager)

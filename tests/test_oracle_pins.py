@@ -294,14 +294,39 @@ def test_model_with_random_gammas_matches_brute(tiny_batch):
     assert oracle.nrms(got["out"], want["out"]) < 1e-5
 
 
-def test_marker_subset_equals_full_rows(tiny_weights):
-    b = random_batch(TINY, 3, 24, seed=6, len_lo=10, markers_per_row=4)
+@pytest.mark.parametrize("seed", range(8))
+def test_marker_subset_equals_full_rows(tiny_weights, seed):
+    """The marker path (last layer on the marker rows only, keys and values
+    over every token) gives bitwise the full pass's rows: each row's products
+    are the same sums whichever rows are in the matrix."""
+    b = random_batch(TINY, 1 + seed % 4, 24, seed=6 + seed, len_lo=3,
+                     markers_per_row=1 + seed % 5)
     o = oracle.Oracle(TINY, tiny_weights)
     full = o.forward(b.ids, b.lengths)
     sub = o.forward(b.ids, b.lengths, markers=b.markers)
     rows = full["row_off"][b.markers[:, 0]] + b.markers[:, 1]
     assert sub["out"].shape == (len(b.markers), TINY["hidden"])
-    assert oracle.nrms(sub["out"], full["out"][rows]) < 1e-3
+    assert np.array_equal(sub["out"], full["out"][rows])
+
+
+def test_nrms_closed_forms():
+    """nRMS(g, o) = |g - o|_2 / |o|_2 in float64: a uniform relative error e
+    gives |e| whatever o is; it is 0 for g = o, 1 for g = 0 and 2 for g = -o;
+    it is invariant under a common scale; a hand example: g = (3, 5) against
+    o = (3, 4) gives 1 / 5."""
+    rng = np.random.default_rng(5)
+    o = rng.standard_normal((37, 64)).astype(np.float32)
+    for eps in (1e-3, -2.5e-2, 0.5):
+        g = o.astype(np.float64) * (1.0 + eps)
+        assert oracle.nrms(g, o) == pytest.approx(abs(eps), rel=1e-12)
+    assert oracle.nrms(o, o) == 0.0
+    assert oracle.nrms(np.zeros_like(o), o) == pytest.approx(1.0, rel=1e-15)
+    assert oracle.nrms(-o, o) == pytest.approx(2.0, rel=1e-15)
+    g = o + 0.01 * rng.standard_normal(o.shape).astype(np.float32)
+    assert oracle.nrms(8.0 * g, 8.0 * o) == pytest.approx(oracle.nrms(g, o), rel=1e-12)
+    assert oracle.nrms(np.array([3.0, 5.0]), np.array([3.0, 4.0])) == pytest.approx(0.2, rel=1e-15)
+    assert oracle.nrms(np.zeros(3), np.zeros(3)) == 0.0
+    assert oracle.nrms(np.ones(3), np.zeros(3)) == float("inf")
 
 
 def test_layerwise_on_own_captures_reproduces_forward(tiny_weights):

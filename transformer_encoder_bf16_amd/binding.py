@@ -16,7 +16,7 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liblaya_encoder.so")
 
-LAYA_ABI_VERSION = 4
+LAYA_ABI_VERSION = 5
 LAYA_OK = 0
 LAYA_E_INVALID = -1
 LAYA_E_UNSUPPORTED = -2
@@ -31,6 +31,7 @@ RUN_EAGER = 1
 RUN_CAPTURE_LAYERS = 2
 RUN_RESIDENT = 4
 RUN_ROPE_STANDALONE = 8
+RUN_ROPE_ORIGINAL = 16
 
 ERROR_NAMES = {
     LAYA_E_INVALID: "LAYA_E_INVALID", LAYA_E_UNSUPPORTED: "LAYA_E_UNSUPPORTED",
@@ -42,13 +43,15 @@ ERROR_NAMES = {
 # Every symbol the header declares (checked by the CPU tests).
 EXPORTS = [
     "laya_abi_version", "laya_config_init", "laya_validate_config", "laya_validate_run_args",
+    "laya_pass_plans",
     "laya_encoder_create", "laya_encoder_run", "laya_encoder_destroy",
     "laya_encoder_last_error", "laya_last_error", "laya_encoder_layer_output",
     "laya_encoder_weight_digest", "laya_encoder_weight", "laya_encoder_stats",
     "laya_encoder_profile", "laya_encoder_fill_workspace", "laya_encoder_config",
     "laya_encoder_health", "laya_encoder_inject_failure", "laya_queue_create", "laya_queue_submit",
     "laya_queue_wait", "laya_queue_health", "laya_queue_destroy", "laya_rope_table", "laya_memcpy", "laya_op_gather", "laya_op_layernorm", "laya_op_gemm",
-    "laya_op_gemm_layernorm", "laya_op_gemm_qkv", "laya_op_rope", "laya_op_attention",
+    "laya_op_gemm_layernorm", "laya_op_gemm_qkv", "laya_op_rope", "laya_op_rope_original",
+    "laya_op_attention",
 ]
 
 
@@ -102,6 +105,10 @@ class Stats(ctypes.Structure):
                 ("weight_bytes", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64)]
 
 
+class GemmPlanC(ctypes.Structure):
+    _fields_ = [("config", ctypes.c_int32), ("splits", ctypes.c_int32), ("fused", ctypes.c_int32)]
+
+
 _lib = None
 _P = ctypes.c_void_p
 _I32P = ctypes.POINTER(ctypes.c_int32)
@@ -121,6 +128,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         "laya_abi_version": (ctypes.c_int, []),
         "laya_config_init": (None, [ctypes.POINTER(Config)]),
         "laya_validate_config": (ctypes.c_int, [ctypes.POINTER(Config)]),
+        "laya_pass_plans": (ctypes.c_int, [ctypes.POINTER(Config), ctypes.c_int32,
+                                           ctypes.c_int32, _I32P, _I32P,
+                                           ctypes.POINTER(GemmPlanC), ctypes.c_int32, _I32P]),
         "laya_validate_run_args": (ctypes.c_int, [ctypes.POINTER(Config), _P, _P, ctypes.c_int32,
                                                   ctypes.c_int32, _P, ctypes.c_int32]),
         "laya_encoder_create": (ctypes.c_int, [ctypes.POINTER(Config), ctypes.c_uint64,
@@ -152,7 +162,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         "laya_queue_health": (ctypes.c_int, [_P]),
         "laya_queue_destroy": (ctypes.c_int, [_P]),
         "laya_encoder_profile": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32,
-                                                _P, ctypes.c_int32, ctypes.POINTER(OpTime),
+                                                _P, ctypes.c_int32, ctypes.c_uint32,
+                                                ctypes.POINTER(OpTime),
                                                 ctypes.c_int32, _I32P,
                                                 ctypes.POINTER(ctypes.c_double)]),
         "laya_rope_table": (ctypes.c_int, [ctypes.c_float, ctypes.c_int32, ctypes.c_int32, _P,
@@ -172,6 +183,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
                                                   _P, ctypes.c_float]),
         "laya_op_rope": (ctypes.c_int, [_P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                         _P, _P, _P, ctypes.c_int32]),
+        "laya_op_rope_original": (ctypes.c_int, [_P, _P, ctypes.c_int32, ctypes.c_int32,
+                                                 ctypes.c_int32, _P, _P, _P, ctypes.c_int32]),
         "laya_op_gemm_qkv": (ctypes.c_int, [_P, _P, ctypes.c_int32, _P, ctypes.c_int32, _P,
                                             ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                             ctypes.c_int32, _P, _P, _P, ctypes.c_int32, _P,
@@ -214,6 +227,17 @@ def default_config() -> dict:
 def validate_config(cfg: dict) -> int:
     c = Config.from_dict(cfg)
     return load().laya_validate_config(ctypes.byref(c))
+
+
+def pass_plans(cfg: dict, T: int, R: int = 0):
+    """(t_first, t_last, [(config, splits, fused)]) of laya_pass_plans."""
+    c = Config.from_dict(cfg)
+    lo, hi, n = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    out = (GemmPlanC * 16)()
+    _check(load().laya_pass_plans(ctypes.byref(c), T, R, ctypes.byref(lo), ctypes.byref(hi), out,
+                                  16, ctypes.byref(n)), "laya_pass_plans")
+    return lo.value, hi.value, [(out[i].config, out[i].splits, out[i].fused)
+                                for i in range(min(n.value, 16))]
 
 
 def validate_run_args(cfg: dict, ids, lengths, markers=None) -> int:
@@ -337,7 +361,7 @@ class Encoder:
         return copy_to_host(p.value, r.value * c.value * 2, 0).view(np.uint16).reshape(
             r.value, c.value)
 
-    def profile(self, ids, lengths, markers=None, stream: Optional[int] = None):
+    def profile(self, ids, lengths, markers=None, stream: Optional[int] = None, flags: int = 0):
         """Per-op-class event times of one eager pass: ({name: {calls, ms, flops,
         bytes}}, total_ms)."""
         ids = _i32(ids)
@@ -351,7 +375,7 @@ class Encoder:
         tot = ctypes.c_double()
         st = current_stream() if stream is None else stream
         _check(self.lib.laya_encoder_profile(self.handle, st, _ptr(ids), _ptr(lengths), B, S,
-                                             _ptr(mk), R, arr, 32, ctypes.byref(n),
+                                             _ptr(mk), R, flags, arr, 32, ctypes.byref(n),
                                              ctypes.byref(tot)),
                "laya_encoder_profile", self.handle)
         res = {}
@@ -420,11 +444,13 @@ def op_gemm_layernorm(A, W, x, n, gamma, M: int, N: int, K: int, config: int, sp
 
 
 def op_rope(buf, n_heads_rot: int, pos, cos_tab, sin_tab, rows: Optional[int] = None,
-            stream: Optional[int] = None):
+            stream: Optional[int] = None, original: bool = False):
+    """RoPE in place; original=True runs the original-geometry kernel."""
     st = current_stream() if stream is None else stream
-    _check(load().laya_op_rope(st, _dp(buf), buf.stride(0), n_heads_rot,
-                               buf.shape[0] if rows is None else rows, _dp(pos), _dp(cos_tab),
-                               _dp(sin_tab), cos_tab.shape[0]), "laya_op_rope")
+    fn = load().laya_op_rope_original if original else load().laya_op_rope
+    _check(fn(st, _dp(buf), buf.stride(0), n_heads_rot, buf.shape[0] if rows is None else rows,
+              _dp(pos), _dp(cos_tab), _dp(sin_tab), cos_tab.shape[0]),
+           "laya_op_rope_original" if original else "laya_op_rope")
 
 
 def op_gemm_qkv(A, W, C, M: int, N: int, K: int, pos, cos_tab, sin_tab, rope_cols: int,

@@ -1,14 +1,15 @@
 // Host engine of the encoder pass: the C ABI of include/laya_encoder.h.
 //
-// The engine owns resident weights, the rotary tables, one activation
-// workspace sized for max_batch x max_seq tokens, pinned staging memory for
-// the per-run index upload, and a cache of per-shape hipGraphs ("The executor
-// owns resident weights and bounded shape workspaces", page "Laya native CUDA
-// worker", section Prepare the checkpoint and bundle; "A new shape allocates
-// buffers, runs two warmups, and captures synchronously", "[RFC]: Native Laya
-// inference with Rust and CUDA #14", section Design).  A run packs the valid
-// tokens of all rows on the host, uploads the packed indices with one copy
-// ("group uploads with safe host-buffer lifetimes", "[Performance]: Optimize
+// The engine keeps the weights resident on the device, together with the
+// rotary tables, one activation workspace sized for max_batch x max_seq
+// tokens, pinned staging memory for the per-run index upload, and a cache of
+// per-shape hipGraphs (the executor design of page "Laya native CUDA worker",
+// section Prepare the checkpoint and bundle, and of "[RFC]: Native Laya
+// inference with Rust and CUDA #14", section Design: a shape seen for the
+// first time gets its buffers, two warm-up passes and a synchronous capture).
+// A run packs the valid tokens of all rows on the host and moves the packed
+// indices to the device in a single copy whose host source the caller may
+// free on return (the upload batching asked for in "[Performance]: Optimize
 // native Rust/CUDA Laya inference #66", section Implementation priorities),
 // then queues the layer schedule: gather; per layer LayerNorm(+residual),
 // QKV GEMM, RoPE, attention, output GEMM, LayerNorm(+residual), GeGLU-up
@@ -195,8 +196,10 @@ int config_check(const laya_config *c, std::string *why) {
         *why = "head_dim must be 64";
         return LAYA_E_UNSUPPORTED;
     }
-    if (c->hidden % 128 != 0 || c->hidden > 2048) {
-        *why = "hidden must be a multiple of 128 and <= 2048";
+    // one 64-lane wave holds a whole row in the fused split reduce + LayerNorm
+    // that follows the output and down projections (16 values per lane)
+    if (c->hidden % 128 != 0 || c->hidden > 1024) {
+        *why = "hidden must be a multiple of 128 and <= 1024";
         return LAYA_E_UNSUPPORTED;
     }
     if (c->ffn % 64 != 0) {
@@ -365,7 +368,11 @@ struct laya_encoder {
     bool upload_pending = false;
     hipStream_t cap_stream = nullptr;
 
-    std::map<std::tuple<int, int, int, int>, GraphEntry> graphs;  // (B, S, R, variant)
+    // GEMM plan range of each token count (see plan_ranges)
+    std::vector<int16_t> plan_id;                 // [T], 1 <= T <= tcap
+    std::vector<std::pair<int, int>> plan_range;  // [id] -> (first T, last T)
+
+    std::map<std::tuple<int, int, int, int, int>, GraphEntry> graphs;  // (B, S, R, variant, plan)
     uint64_t graph_tick = 0;
 
     // per-layer captures
@@ -407,7 +414,10 @@ struct RunShape {
     int B, S, R;
     int T;  // actual tokens (host value; used only for captures in eager mode)
     bool capture_layers;
-    bool rope_standalone = false;  // RoPE by its own kernel instead of the QKV epilogue
+    // RoPE: 0 in the QKV projection's epilogue, 1 by its own kernel after the
+    // projection, 2 by its own kernel in the original launch geometry
+    int rope_variant = 0;
+    bool rope_standalone() const { return rope_variant != 0; }
     // host-side algorithmic counts, used only when profiling
     double pairs_global = 0, pairs_local = 0, pairs_subset = 0;
 };
@@ -415,12 +425,12 @@ struct RunShape {
 // Op classes of the per-launch profile (laya_encoder_profile).
 enum OpKind {
     OP_GATHER, OP_LAYERNORM, OP_QKV, OP_ROPE, OP_ATTENTION, OP_OUT_PROJ, OP_UP_GEGLU, OP_DOWN,
-    OP_ROW_GATHER, OP_KV, OP_Q, OP_UP_GELU, OP_OUT_PROJ_LN, OP_DOWN_LN, OP_COUNT
+    OP_ROW_GATHER, OP_KV, OP_Q, OP_UP_GELU, OP_OUT_PROJ_LN, OP_DOWN_LN, OP_ROPE_ORIGINAL, OP_COUNT
 };
 const char *const kOpNames[OP_COUNT] = {
     "gather", "layernorm", "qkv_gemm", "rope", "attention", "out_proj_gemm",
     "up_geglu_gemm", "down_gemm", "row_gather", "kv_gemm", "q_gemm", "up_gelu_gemm",
-    "out_proj_gemm_layernorm", "down_gemm_layernorm"};
+    "out_proj_gemm_layernorm", "down_gemm_layernorm", "rope_original"};
 
 struct ProfRec {
     int op;
@@ -435,12 +445,14 @@ struct Profiler {
 
 int layer_count(const laya_config &c) { return c.n_enc_layers + c.n_dec_layers; }
 
-// GEMM plans of one pass.  The four projections over the packed tokens are
-// planned from B*S; the marker layer's GEMMs over R rows keep the K split of
-// the matching full-pass GEMM (so marker rows are bitwise the full pass's
-// rows) and choose their own tile shape.
+// GEMM plans of one pass.  Every plan (tile shape and K split) follows the
+// live token count T alone, never the padded B*S, so the same rows padded to
+// a wider S add in the same order and give bitwise the same states.  The
+// marker layer's GEMMs over R rows keep the K split of the matching
+// full-pass GEMM (so marker rows are bitwise the full pass's rows) and choose
+// their own tile shape.
 struct PassPlans {
-    laya::GemmPlan qkv, o, up, down;              // M = B*S
+    laya::GemmPlan qkv, o, up, down;              // over the T packed tokens
     laya::GemmPlan kv_sub, q_sub, o_sub, up_sub, down_sub;  // marker layer
     // head variant: the decision layers' 4H-wide FFN (bias + GELU, then bias)
     laya::GemmPlan up4, down4, up4_sub, down4_sub;
@@ -458,28 +470,38 @@ laya::GemmPlan subset_plan(const laya::GemmPlan &full, int R, int N, int K, int 
     return g;
 }
 
-// K splits follow B*S (so eager and graph runs of one key add in the same
-// order); with whole K, the tile shape follows the tokens T of the run that
-// records the launches (any shape gives the same result).
-laya::GemmPlan full_plan(int Tmax, int T, int N, int K, int epi) {
-    laya::GemmPlan g = laya::plan_gemm(Tmax, N, K, epi);
-    if (g.splits == 1 && T > 0 && T < Tmax) g = laya::plan_gemm_tiles(T, N, K, epi);
-    return g;
+// Plan buckets of the live token count T.  Every GEMM of a pass is planned
+// for the largest count of T's bucket (its grid is sized for that count
+// anyway), so one plan, and one captured graph, serves the whole bucket, and
+// the plan depends on T alone, never on the padded B*S.  The split
+// thresholds of laya::plan_gemm (64, 256, 1024, 2048) are bucket edges; the
+// others halve the span over which one whole-K tile shape must serve.
+constexpr int kPlanEdges[] = {64, 256, 512, 1024, 1536, 2048, 3072, 4096};
+std::pair<int, int> plan_bucket(const laya_config &c, int T) {
+    const int tcap = c.max_batch * c.max_seq;
+    int lo = 1;
+    for (int e : kPlanEdges) {
+        if (T <= e) return {lo, std::min(e, tcap)};
+        lo = e + 1;
+    }
+    return {lo, tcap};
 }
 
-PassPlans make_plans(const laya_config &c, int Tmax, int T, int R) {
+PassPlans make_plans(const laya_config &c, int T, int R) {
     const int H = c.hidden, F = c.ffn;
+    const std::pair<int, int> b = plan_bucket(c, T);
+    auto plan = [&](int N, int K, int epi) { return laya::plan_gemm(b.second, N, K, epi); };
     PassPlans p{};
-    p.qkv = full_plan(Tmax, T, 3 * H, H, 2);
-    p.o = full_plan(Tmax, T, H, H, 0);
-    p.up = full_plan(Tmax, T, F, H, 1);
-    p.down = full_plan(Tmax, T, H, F, 0);
+    p.qkv = plan(3 * H, H, 2);
+    p.o = plan(H, H, 0);
+    p.up = plan(F, H, 1);
+    p.down = plan(H, F, 0);
     if (c.dec_head) {
-        p.up4 = full_plan(Tmax, T, 4 * H, H, 3);
-        p.down4 = full_plan(Tmax, T, H, 4 * H, 0);
+        p.up4 = plan(4 * H, H, 3);
+        p.down4 = plan(H, 4 * H, 0);
     }
     if (R > 0) {
-        p.kv_sub = full_plan(Tmax, T, 2 * H, H, 2);
+        p.kv_sub = plan(2 * H, H, 2);
         p.kv_sub.splits = p.qkv.splits;
         if (p.kv_sub.splits > laya::gemm_max_splits(p.kv_sub.config)) p.kv_sub.config = 2;
         p.q_sub = subset_plan(p.qkv, R, H, H, 2);
@@ -494,17 +516,96 @@ PassPlans make_plans(const laya_config &c, int Tmax, int T, int R) {
     return p;
 }
 
-// Largest split-K partial buffer (bytes) over every shape the handle accepts.
-void gemm_scratch_bound(const laya_config &c, size_t *bytes) {
-    const int H = c.hidden, F = c.ffn;
+bool same_plan(const laya::GemmPlan &a, const laya::GemmPlan &b) {
+    return a.config == b.config && a.splits == b.splits;
+}
+// full-pass plans (R = 0) equal: the marker layer's plans follow from them and R
+bool same_full_plans(const PassPlans &a, const PassPlans &b) {
+    return same_plan(a.qkv, b.qkv) && same_plan(a.o, b.o) && same_plan(a.up, b.up) &&
+           same_plan(a.down, b.down) && same_plan(a.up4, b.up4) && same_plan(a.down4, b.down4);
+}
+
+// A captured graph serves one plan bucket of its (B, S, R); its GEMM grids
+// are sized for the bucket's largest count (or B*S if smaller).
+struct PlanRanges {
+    std::vector<int16_t> id;                 // [T] for 1 <= T <= tcap
+    std::vector<std::pair<int, int>> range;  // [id] -> (first T, last T)
+};
+
+PlanRanges plan_ranges(const laya_config &c) {
     const int tcap = c.max_batch * c.max_seq;
+    PlanRanges r;
+    r.id.assign((size_t)tcap + 1, 0);
+    for (int T = 1; T <= tcap; ++T) {
+        const std::pair<int, int> b = plan_bucket(c, T);
+        if (r.range.empty() || r.range.back() != b) r.range.push_back(b);
+        r.id[T] = (int16_t)(r.range.size() - 1);
+    }
+    return r;
+}
+
+// Why a planned launch could not run, or "" (checked for every plan a handle
+// can use when its configuration is validated): the fused split reduce +
+// LayerNorm holds a row of at most 1024 values and runs on the split-capable
+// tile shapes; a split must fit the shape's range limit and K; the paired
+// epilogues (GeGLU, QKV) need shapes with paired weight rows.
+std::string plan_problem(const laya::GemmPlan &g, int N, int K, int epi, bool fused) {
+    if (g.config < 0 || g.config >= laya::kGemmConfigs) return "tile shape out of range";
+    if (g.splits < 1 || g.splits > K / 64 || g.splits > laya::gemm_max_splits(g.config))
+        return "K split not supported by the tile shape";
+    if ((epi == 1 || epi == 2) && g.config == 0) return "paired epilogue on the 32x64 plain tile";
+    if (fused && (N > 1024 || N % 64 != 0)) return "fused reduce + LayerNorm wider than 1024";
+    if (fused && g.config > 3 && g.config != 7 && g.config != 8)
+        return "fused reduce + LayerNorm on a whole-K tile shape";
+    return "";
+}
+
+std::string plans_problem(const laya_config &c, const PassPlans &p, int R) {
+    const int H = c.hidden, F = c.ffn;
+    struct Item {
+        const laya::GemmPlan *g;
+        int N, K, epi;
+        bool fused_if_split;
+        const char *what;
+    };
+    std::vector<Item> items = {{&p.qkv, 3 * H, H, 2, false, "QKV"}, {&p.o, H, H, 0, true, "output"},
+                               {&p.up, F, H, 1, false, "up"},       {&p.down, H, F, 0, true, "down"}};
+    if (c.dec_head) {
+        items.push_back({&p.up4, 4 * H, H, 3, false, "head up"});
+        items.push_back({&p.down4, H, 4 * H, 0, true, "head down"});
+    }
+    if (R > 0) {
+        items.push_back({&p.kv_sub, 2 * H, H, 2, false, "marker K/V"});
+        items.push_back({&p.q_sub, H, H, 2, false, "marker Q"});
+        items.push_back({&p.o_sub, H, H, 0, true, "marker output"});
+        items.push_back({&p.up_sub, F, H, 1, false, "marker up"});
+        items.push_back({&p.down_sub, H, F, 0, true, "marker down"});
+        if (c.dec_head) {
+            items.push_back({&p.up4_sub, 4 * H, H, 3, false, "marker head up"});
+            items.push_back({&p.down4_sub, H, 4 * H, 0, true, "marker head down"});
+        }
+    }
+    for (const Item &it : items) {
+        const std::string why =
+            plan_problem(*it.g, it.N, it.K, it.epi, it.fused_if_split && it.g->splits > 1);
+        if (!why.empty()) return std::string(it.what) + " GEMM: " + why;
+    }
+    return "";
+}
+
+// Largest split-K partial buffer (bytes) over every shape the handle accepts,
+// and the first planned launch that could not run ("" if none).
+void gemm_scratch_bound(const laya_config &c, const PlanRanges &pr, size_t *bytes,
+                        std::string *problem) {
+    const int H = c.hidden, F = c.ffn;
     size_t b = 0;
     auto acc = [&](const laya::GemmPlan &g, int M, int N, int epi) {
         b = std::max(b, laya::gemm_workspace_bytes(g, M, N, epi));
     };
-    int last_splits[6] = {-1, -1, -1, -1, -1, -1};
-    for (int T = 1; T <= tcap; ++T) {
-        const PassPlans p = make_plans(c, T, T, 0);
+    problem->clear();
+    for (const auto &rg : pr.range) {
+        const int T = rg.second;  // grids are sized for the range's largest count
+        const PassPlans p = make_plans(c, T, 0);
         acc(p.qkv, T, 3 * H, 2);
         acc(p.o, T, H, 0);
         acc(p.up, T, F, 1);
@@ -513,13 +614,9 @@ void gemm_scratch_bound(const laya_config &c, size_t *bytes) {
             acc(p.up4, T, 4 * H, 3);
             acc(p.down4, T, H, 0);
         }
-        // marker layer: its plans depend on T only through the K splits
-        const int sp[6] = {p.qkv.splits, p.o.splits,   p.up.splits,
-                           p.down.splits, p.up4.splits, p.down4.splits};
-        if (std::equal(sp, sp + 6, last_splits)) continue;
-        std::copy(sp, sp + 6, last_splits);
+        if (problem->empty()) *problem = plans_problem(c, p, 0);
         for (int R = 1; R <= c.max_markers; ++R) {
-            const PassPlans q = make_plans(c, T, T, R);
+            const PassPlans q = make_plans(c, T, R);
             acc(q.kv_sub, T, 2 * H, 2);
             acc(q.q_sub, R, H, 2);
             acc(q.o_sub, R, H, 0);
@@ -529,6 +626,7 @@ void gemm_scratch_bound(const laya_config &c, size_t *bytes) {
                 acc(q.up4_sub, R, 4 * H, 3);
                 acc(q.down4_sub, R, H, 0);
             }
+            if (problem->empty()) *problem = plans_problem(c, q, R);
         }
     }
     *bytes = b;
@@ -556,7 +654,14 @@ int record(laya_encoder *enc, hipStream_t s, const RunShape &rs, Profiler *prof 
     const int32_t *mrk_tok = md + ml.mrk_tok;
     const int32_t *mrk_pos = md + ml.mrk_pos;
     const int hw = c.window / 2;
-    const PassPlans plans = make_plans(c, Tmax, rs.T, rs.R);
+    // the standalone RoPE launch of the chosen variant
+    auto rope = rs.rope_variant == 2 ? laya::launch_rope_original : laya::launch_rope;
+    const int rope_op = rs.rope_variant == 2 ? OP_ROPE_ORIGINAL : OP_ROPE;
+    // plans follow the live count; GEMM grids cover the largest count of its
+    // plan range (kernels read the live count from the device)
+    const int T_run = std::max(1, rs.T);
+    const PassPlans plans = make_plans(c, T_run, rs.R);
+    const int Mg = std::min(Tmax, enc->plan_range[enc->plan_id[T_run]].second);
     float *gp = enc->gemm_partial;
     enc->launches = 0;
 
@@ -701,26 +806,26 @@ int record(laya_encoder *enc, hipStream_t s, const RunShape &rs, Profiler *prof 
         if (!subset) {
             // Q, K rotated in the epilogue (or by the RoPE kernel after it); V
             // stored transposed for attention
-            const int rope_cols = rs.rope_standalone ? 0 : 2 * H;
+            const int rope_cols = rs.rope_standalone() ? 0 : 2 * H;
             const laya::QkvEpilogue qe{pos, ctab, stab, rope_cols, 2 * H, enc->vt, enc->ldvt, vtok};
             L_OP(OP_QKV, gemm_fl(T, 3 * H, H), gemm_by(T, 3 * H, 3 * H, H),
-                 laya::launch_gemm(s, enc->nrm, H, Wqkv, H, enc->qkv, 3 * H, T_dev, Tmax, 3 * H,
+                 laya::launch_gemm(s, enc->nrm, H, Wqkv, H, enc->qkv, 3 * H, T_dev, Mg, 3 * H,
                                    H, 2, plans.qkv, gp, &qe, Bqkv));
-            if (rs.rope_standalone)
-                L_OP(OP_ROPE, 0, 2 * T * 2 * H * b2,
-                     laya::launch_rope(s, enc->qkv, 3 * H, 2 * nh, T_dev, Tmax, pos, ctab, stab));
+            if (rs.rope_standalone())
+                L_OP(rope_op, 0, 2 * T * 2 * H * b2,
+                     rope(s, enc->qkv, 3 * H, 2 * nh, T_dev, Tmax, pos, ctab, stab));
             const laya::AttnParams ap{enc->qkv, 3 * H, enc->qkv + H, 3 * H, k_bytes(3 * H),
                                       enc->vt, enc->ldvt, vt_bytes, enc->att, H, blk, nblk,
                                       ml.nblk_full_max, pos, nh, half};
             L_OP(OP_ATTENTION, attn_fl_per_pair * (glob ? rs.pairs_global : rs.pairs_local),
                  4 * T * H * b2, laya::launch_attention(s, ap));
-            C_CHK(attn_out(T_dev, Tmax, T, plans.o, xr, enc->nrm));
+            C_CHK(attn_out(T_dev, Mg, T, plans.o, xr, enc->nrm));
             // the LayerNorm after this layer: the next layer's attention norm,
             // the encoder's final norm, or the closing norm
             bf16_t *n_next = L == NL - 1 ? enc->out
                                          : (L == c.n_enc_layers - 1 ? xalt : enc->nrm);
             bool fused = false;
-            C_CHK(ffn(enc->nrm, T_dev, Tmax, T, head ? plans.up4 : plans.up,
+            C_CHK(ffn(enc->nrm, T_dev, Mg, T, head ? plans.up4 : plans.up,
                       head ? plans.down4 : plans.down, xr, n_next, &fused));
             pending = !fused;
             ln_ready = fused;
@@ -740,27 +845,27 @@ int record(laya_encoder *enc, hipStream_t s, const RunShape &rs, Profiler *prof 
             // keys/values for every token, queries only for the marker rows
             const int Ri = rs.R;
             const laya::QkvEpilogue qe_kv{pos,      ctab,          stab,
-                                          rs.rope_standalone ? 0 : H, H, enc->vt,
+                                          rs.rope_standalone() ? 0 : H, H, enc->vt,
                                           enc->ldvt, vtok};
             L_OP(OP_KV, gemm_fl(T, 2 * H, H), gemm_by(T, 2 * H, 2 * H, H),
                  laya::launch_gemm(s, enc->nrm, H, Wqkv + (size_t)H * H, H, enc->qkv, 2 * H,
-                                   T_dev, Tmax, 2 * H, H, 2, plans.kv_sub, gp, &qe_kv,
+                                   T_dev, Mg, 2 * H, H, 2, plans.kv_sub, gp, &qe_kv,
                                    Bqkv ? Bqkv + H : nullptr));
-            if (rs.rope_standalone)
-                L_OP(OP_ROPE, 0, 2 * T * H * b2,
-                     laya::launch_rope(s, enc->qkv, 2 * H, nh, T_dev, Tmax, pos, ctab, stab));
+            if (rs.rope_standalone())
+                L_OP(rope_op, 0, 2 * T * H * b2,
+                     rope(s, enc->qkv, 2 * H, nh, T_dev, Tmax, pos, ctab, stab));
             L_OP(OP_ROW_GATHER, 0, 2 * R * H * b2,
                  laya::launch_gather_rows(s, enc->nrm, H, mrk_tok, Ri, H, enc->n_sub, H));
             L_OP(OP_ROW_GATHER, 0, 2 * R * H * b2,
                  laya::launch_gather_rows(s, xr, H, mrk_tok, Ri, H, enc->x_sub, H));
-            const laya::QkvEpilogue qe_q{mrk_pos, ctab, stab, rs.rope_standalone ? 0 : H, H,
+            const laya::QkvEpilogue qe_q{mrk_pos, ctab, stab, rs.rope_standalone() ? 0 : H, H,
                                          nullptr, 0, nullptr};
             L_OP(OP_Q, gemm_fl(R, H, H), gemm_by(R, H, H, H),
                  laya::launch_gemm(s, enc->n_sub, H, Wqkv, H, enc->q_sub, H, nullptr, Ri, H, H,
                                    2, plans.q_sub, gp, &qe_q, Bqkv));
-            if (rs.rope_standalone)
-                L_OP(OP_ROPE, 0, 2 * R * H * b2,
-                     laya::launch_rope(s, enc->q_sub, H, nh, nullptr, Ri, mrk_pos, ctab, stab));
+            if (rs.rope_standalone())
+                L_OP(rope_op, 0, 2 * R * H * b2,
+                     rope(s, enc->q_sub, H, nh, nullptr, Ri, mrk_pos, ctab, stab));
             const laya::AttnParams ap{enc->q_sub, H, enc->qkv, 2 * H, k_bytes(2 * H),
                                       enc->vt, enc->ldvt, vt_bytes, enc->att, H, blk_s, nblk_s,
                                       ml.nblk_sub_max, mrk_pos, nh, half};
@@ -853,8 +958,58 @@ const char *laya_last_error(void) { return g_last_error.c_str(); }
 int laya_validate_config(const laya_config *cfg) {
     std::string why;
     int rc = config_check(cfg, &why);
+    if (rc == LAYA_OK) {
+        size_t bytes = 0;
+        gemm_scratch_bound(*cfg, plan_ranges(*cfg), &bytes, &why);
+        if (!why.empty()) {
+            why = "unsupported plan: " + why;
+            rc = LAYA_E_UNSUPPORTED;
+        }
+    }
     if (rc != LAYA_OK) g_last_error = why;
     return rc;
+}
+
+int laya_pass_plans(const laya_config *cfg, int32_t T, int32_t R, int32_t *t_first,
+                    int32_t *t_last, laya_gemm_plan *out, int32_t cap, int32_t *n_out) {
+    std::string why;
+    int rc = config_check(cfg, &why);
+    if (rc != LAYA_OK) return set_global_error(rc, why);
+    const int tcap = cfg->max_batch * cfg->max_seq;
+    if (T < 1 || T > tcap || R < 0 || R > cfg->max_markers || !t_first || !t_last || !n_out ||
+        cap < 0 || (cap > 0 && !out))
+        return set_global_error(LAYA_E_INVALID, "laya_pass_plans: bad arguments");
+    const PassPlans p = make_plans(*cfg, T, R);
+    const std::pair<int, int> b = plan_bucket(*cfg, T);
+    *t_first = b.first;
+    *t_last = b.second;
+    std::vector<std::pair<const laya::GemmPlan *, int>> list = {
+        {&p.qkv, 0}, {&p.o, 1}, {&p.up, 0}, {&p.down, 1}};
+    if (cfg->dec_head) {
+        list.push_back({&p.up4, 0});
+        list.push_back({&p.down4, 1});
+    }
+    if (R > 0) {
+        list.push_back({&p.kv_sub, 0});
+        list.push_back({&p.q_sub, 0});
+        list.push_back({&p.o_sub, 1});
+        list.push_back({&p.up_sub, 0});
+        list.push_back({&p.down_sub, 1});
+        if (cfg->dec_head) {
+            list.push_back({&p.up4_sub, 0});
+            list.push_back({&p.down4_sub, 1});
+        }
+    }
+    int n = 0;
+    for (const auto &it : list) {
+        if (n >= cap) break;
+        out[n].config = it.first->config;
+        out[n].splits = it.first->splits;
+        out[n].fused = it.second && it.first->splits > 1 ? 1 : 0;
+        ++n;
+    }
+    *n_out = (int32_t)list.size();
+    return LAYA_OK;
 }
 
 int laya_validate_run_args(const laya_config *cfg, const int32_t *ids, const int32_t *lengths,
@@ -1001,7 +1156,15 @@ int laya_encoder_create(const laya_config *cfg, uint64_t seed, int device, laya_
     const size_t meta_off = wsz;
     wsz += al((size_t)enc->meta_cap * 4);
     size_t gp_bytes = 0;
-    gemm_scratch_bound(c, &gp_bytes);
+    {
+        const PlanRanges pr = plan_ranges(c);
+        enc->plan_id = pr.id;
+        enc->plan_range = pr.range;
+        std::string problem;
+        gemm_scratch_bound(c, pr, &gp_bytes, &problem);
+        if (!problem.empty())
+            return bail(set_global_error(LAYA_E_UNSUPPORTED, "unsupported plan: " + problem));
+    }
     const size_t gp_off = wsz;
     wsz += al(gp_bytes);
     enc->ws_bytes = wsz;
@@ -1069,8 +1232,10 @@ int laya_encoder_run(laya_encoder *enc, void *stream, const int32_t *ids,
     if (enc->poisoned) return fail(enc, LAYA_E_POISONED, "handle poisoned by an earlier device failure");
     if (!out) return fail(enc, LAYA_E_INVALID, "out is NULL");
     if (flags & ~(LAYA_RUN_EAGER | LAYA_RUN_CAPTURE_LAYERS | LAYA_RUN_RESIDENT |
-                  LAYA_RUN_ROPE_STANDALONE))
+                  LAYA_RUN_ROPE_STANDALONE | LAYA_RUN_ROPE_ORIGINAL))
         return fail(enc, LAYA_E_INVALID, "unknown run flags");
+    if ((flags & LAYA_RUN_ROPE_STANDALONE) && (flags & LAYA_RUN_ROPE_ORIGINAL))
+        return fail(enc, LAYA_E_INVALID, "two RoPE variants requested");
     const bool resident = (flags & LAYA_RUN_RESIDENT) != 0;
     std::string why;
     int rc = LAYA_OK;
@@ -1156,9 +1321,9 @@ int laya_encoder_run(laya_encoder *enc, void *stream, const int32_t *ids,
 
     const bool capture = (flags & LAYA_RUN_CAPTURE_LAYERS) != 0;
     const bool eager = capture || (flags & LAYA_RUN_EAGER) != 0;
-    const bool rope_sa = (flags & LAYA_RUN_ROPE_STANDALONE) != 0;
+    const int rope_var = (flags & LAYA_RUN_ROPE_ORIGINAL) ? 2 : (flags & LAYA_RUN_ROPE_STANDALONE) ? 1 : 0;
     RunShape rs{B, S, R, T, capture};
-    rs.rope_standalone = rope_sa;
+    rs.rope_variant = rope_var;
     if (capture) {
         int r2 = ensure_captures(enc);
         if (r2 != LAYA_OK) return r2;
@@ -1170,7 +1335,8 @@ int laya_encoder_run(laya_encoder *enc, void *stream, const int32_t *ids,
         enc->stats.launches_last_run = enc->launches;
         enc->have_caps = capture;
     } else {
-        auto key = std::make_tuple((int)B, (int)S, (int)R, rope_sa ? 1 : 0);
+        auto key = std::make_tuple((int)B, (int)S, (int)R, rope_var,
+                                   (int)enc->plan_id[std::max(1, T)]);
         auto it = enc->graphs.find(key);
         if (it == enc->graphs.end()) {
             // LRU: make room for the new shape (every graph shares the one
@@ -1187,7 +1353,7 @@ int laya_encoder_run(laya_encoder *enc, void *stream, const int32_t *ids,
             }
             auto t0 = std::chrono::steady_clock::now();
             RunShape warm{B, S, R, T, false};
-            warm.rope_standalone = rope_sa;
+            warm.rope_variant = rope_var;
             for (int w = 0; w < 2; ++w) {
                 int r2 = record(enc, s, warm);
                 if (r2 != LAYA_OK) return r2;
@@ -1333,13 +1499,16 @@ int laya_memcpy(void *dst, const void *src, size_t bytes, int32_t kind, void *st
 
 int laya_encoder_profile(laya_encoder *enc, void *stream, const int32_t *ids,
                          const int32_t *lengths, int32_t B, int32_t S, const int32_t *markers,
-                         int32_t R, laya_op_time *out, int32_t cap, int32_t *n_out,
-                         double *total_ms) {
+                         int32_t R, uint32_t flags, laya_op_time *out, int32_t cap,
+                         int32_t *n_out, double *total_ms) {
     if (!enc || !out || !n_out || cap < 0) return set_global_error(LAYA_E_INVALID, "NULL argument");
     if (enc->poisoned) return fail(enc, LAYA_E_POISONED, "handle poisoned");
+    if (flags & ~(LAYA_RUN_ROPE_STANDALONE | LAYA_RUN_ROPE_ORIGINAL))
+        return fail(enc, LAYA_E_INVALID, "laya_encoder_profile: only RoPE variant flags");
     laya_output o;
     // upload the indices (and validate) with an ordinary eager run first
-    int rc = laya_encoder_run(enc, stream, ids, lengths, B, S, markers, R, LAYA_RUN_EAGER, &o);
+    int rc = laya_encoder_run(enc, stream, ids, lengths, B, S, markers, R,
+                              LAYA_RUN_EAGER | flags, &o);
     if (rc != LAYA_OK) return rc;
     *n_out = 0;
     if (total_ms) *total_ms = 0;
@@ -1347,6 +1516,7 @@ int laya_encoder_profile(laya_encoder *enc, void *stream, const int32_t *ids,
     hipStream_t s = static_cast<hipStream_t>(stream);
     const laya_config &c = enc->cfg;
     RunShape rs{B, S, R, enc->up_T, false};
+    rs.rope_variant = (flags & LAYA_RUN_ROPE_ORIGINAL) ? 2 : (flags & LAYA_RUN_ROPE_STANDALONE) ? 1 : 0;
     const int hw = c.window / 2;
     for (int b = 0; b < B; ++b) {
         const double len = lengths[b];
@@ -1538,6 +1708,19 @@ int laya_op_rope(void *stream, void *buf, int32_t ld, int32_t n_heads_rot, int32
     OPCHK(laya::launch_rope(static_cast<hipStream_t>(stream), static_cast<bf16_t *>(buf), ld,
                             n_heads_rot, nullptr, rows, pos, static_cast<const bf16_t *>(cos_tab),
                             static_cast<const bf16_t *>(sin_tab)));
+    return LAYA_OK;
+}
+
+int laya_op_rope_original(void *stream, void *buf, int32_t ld, int32_t n_heads_rot, int32_t rows,
+                          const int32_t *pos, const void *cos_tab, const void *sin_tab,
+                          int32_t max_pos) {
+    if (rows < 0 || n_heads_rot <= 0 || ld % 8 || ld < n_heads_rot * 64 || max_pos <= 0 ||
+        (rows > 0 && (!buf || !pos || !cos_tab || !sin_tab)))
+        return set_global_error(LAYA_E_INVALID, "laya_op_rope_original: bad arguments");
+    OPCHK(laya::launch_rope_original(static_cast<hipStream_t>(stream), static_cast<bf16_t *>(buf),
+                                     ld, n_heads_rot, nullptr, rows, pos,
+                                     static_cast<const bf16_t *>(cos_tab),
+                                     static_cast<const bf16_t *>(sin_tab)));
     return LAYA_OK;
 }
 

@@ -231,6 +231,43 @@ __global__ __launch_bounds__(256) void rope_kernel(bf16_t *__restrict__ buf, int
     st16(hp + 32, yo);
 }
 
+// RoPE in the pages' original launch geometry, kept as the reference arm of
+// the RoPE comparison ("perf(model): exact Metal speed-ups of the forward
+// pass": the rotary kernel it replaced found every element's coordinates by
+// 64-bit integer division, a software routine on the GPU).  One thread
+// per rotation pair over a flat 64-bit index, split back into (row, head,
+// pair) with 64-bit division and remainder; the same arithmetic per pair as
+// rope_kernel, so the two give bitwise equal results.
+__global__ __launch_bounds__(256) void rope_original_kernel(
+    bf16_t *__restrict__ buf, int32_t ld, int32_t n_rot, const int32_t *count_dev,
+    int32_t rows_max, const int32_t *__restrict__ pos, const bf16_t *__restrict__ cos_tab,
+    const bf16_t *__restrict__ sin_tab) {
+    const uint64_t rows = (uint64_t)(count_dev ? *count_dev : rows_max);
+    const uint64_t idx = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const uint64_t per_row = (uint64_t)n_rot * 32u;
+    const uint64_t row = idx / per_row;
+    const uint64_t rem = idx % per_row;
+    const uint64_t head = rem / 32u, i = rem % 32u;
+    if (row >= rows) return;
+    const uint64_t p = (uint64_t)pos[row];
+    bf16_t *hp = buf + row * (uint64_t)ld + head * 64u + i;
+    const float x = bf16_to_f32(hp[0]), y = bf16_to_f32(hp[32]);
+    const float c = bf16_to_f32(cos_tab[p * 32u + i]), sn = bf16_to_f32(sin_tab[p * 32u + i]);
+    // both products of BF16 values are exact in float32
+    hp[0] = (bf16_t)f32_to_bf16(fmaf(x, c, -(y * sn)));
+    hp[32] = (bf16_t)f32_to_bf16(fmaf(y, c, x * sn));
+}
+
+hipError_t launch_rope_original(hipStream_t s, bf16_t *buf, int32_t ld, int32_t n_heads_rot,
+                                const int32_t *count_dev, int32_t rows_max, const int32_t *pos,
+                                const bf16_t *cos_tab, const bf16_t *sin_tab) {
+    if (rows_max <= 0) return hipSuccess;
+    const int64_t threads = (int64_t)rows_max * n_heads_rot * 32;
+    hipLaunchKernelGGL(rope_original_kernel, dim3((uint32_t)((threads + 255) / 256)), dim3(256), 0,
+                       s, buf, ld, n_heads_rot, count_dev, rows_max, pos, cos_tab, sin_tab);
+    return hipGetLastError();
+}
+
 hipError_t launch_rope(hipStream_t s, bf16_t *buf, int32_t ld, int32_t n_heads_rot,
                        const int32_t *count_dev, int32_t rows_max, const int32_t *pos,
                        const bf16_t *cos_tab, const bf16_t *sin_tab) {

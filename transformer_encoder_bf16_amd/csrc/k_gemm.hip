@@ -868,6 +868,358 @@ __global__ __launch_bounds__(64) void splitk_layernorm_kernel(
     layernorm_row_store<MAXC>(v, sum, lane, nch, hidden, eps, gamma, n + (size_t)row * hidden);
 }
 
+// ---------------------------------------------------------------------------
+// 256 x 256 tiles for the large projections: two wave groups in ping-pong.
+//
+// One workgroup of 8 waves per compute unit, two per SIMD.  The waves form
+// two groups of four (one wave of each group per SIMD) that take turns: while
+// one group multiplies (16 MFMAs per wave on fragments already in registers),
+// the other reads the fragments of its next K step from LDS and issues its
+// share of the global -> LDS loads, and a workgroup barrier ends every phase.
+// Each SIMD's matrix core thus always has one wave with MFMAs to issue; in the
+// lock-step kernel above both waves of a SIMD wait at the same barrier and the
+// matrix core idles there.
+//
+// K steps of 32 in a 4-slot ring (128 KB): the loads of step k + 3 are issued
+// while step k is read, 5 to 6 phases before they are needed.  Group 0 loads
+// the weight half of every step and group 1 the token half; a wave waits
+// (vmcnt) for its own loads of a step before the barrier that precedes the
+// step's first reader.  The remaining 32 KB of LDS gives each wave a private
+// 4 KB area in which its output fragments are transposed to token rows, so
+// the epilogue needs no workgroup barrier and writes 64-byte row segments.
+//
+// Each wave owns 128 weight rows x 64 tokens (4 x 2 fragments of 32 x 32);
+// every output element is one chain of v_mfma_f32_32x32x16_bf16 over K in
+// order, as in the other tile shapes, so the results are bitwise theirs.
+// ---------------------------------------------------------------------------
+namespace pp {
+constexpr int BW = 256, BT = 256, BK = 32, SLOTS = 4;
+constexpr int SLOT = (BW + BT) * BK;  // bf16 elements per ring slot (32 KB)
+constexpr int FA = 4, FB = 2;         // fragments per wave (weight rows, tokens)
+constexpr int D = 4;                  // loads (1 KB each) per wave per half step
+constexpr int SCR = 2048;             // bf16 elements of scratch per wave (4 KB)
+}  // namespace pp
+
+// scratch chunk swizzle of a 32 x 32 BF16 fragment stored as [token][feature]
+__device__ __forceinline__ int pp_sc(int tok, int chunk) {
+    return tok * 32 + ((chunk ^ (tok & 3)) << 3);
+}
+
+template <int EPI>
+__global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
+    using namespace pp;
+    const int32_t M = p.M_dev ? *p.M_dev : p.M_max;
+    int bx = blockIdx.x, by = blockIdx.y;
+    {
+        const int live_by = (M + BT - 1) / BT;
+        const int xw = p.split2d ? pick_xw(gridDim.x, live_by, BW, BT, 1) : 1;
+        if (!(xw > 1 ? tile_order_2d(live_by, xw, bx, by) : tile_order(live_by, bx, by))) return;
+    }
+    const int32_t t0 = by * BT;
+    if (t0 >= M) return;
+    constexpr int BN = EPI == 1 ? BW / 2 : BW;  // output features per tile
+    const int32_t n0 = bx * BN;
+    const int N = p.N;
+
+    __shared__ __attribute__((aligned(16))) bf16_t ring[SLOTS * SLOT];
+    __shared__ __attribute__((aligned(16))) bf16_t scratch[8 * SCR];
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int grp = wave >> 2, q = wave & 3;
+    const int grp_u = __builtin_amdgcn_readfirstlane(grp);
+    const int q_u = __builtin_amdgcn_readfirstlane(q);
+    const int nk = p.K / BK;
+
+    // Loads: group 0 fills the weight rows of a step, group 1 the token rows;
+    // wave q covers 1 KB blocks q + 4 j (16 rows of 64 bytes each), lane L
+    // physical chunk L % 4 of row 16 (q + 4 j) + L / 4.
+    const uint32_t w_rows = EPI == 1 ? 2u * (uint32_t)N : (uint32_t)N;
+    const uint32_t w_bytes = ((w_rows - 1) * (uint32_t)p.ldw + (uint32_t)p.K) * 2u;
+    const uint32_t a_bytes = (((uint32_t)p.M_max - 1) * (uint32_t)p.lda + (uint32_t)p.K) * 2u;
+    const bf16_t *src = grp_u == 0 ? p.W : p.A;
+    const uint32_t src_bytes = grp_u == 0 ? w_bytes : a_bytes;
+    uint32_t off[D];
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+        const int r = 16 * (q + 4 * j) + (lane >> 2);  // row within the operand's 256
+        const int c = pchunk<BK>(r, lane & 3);
+        if (grp == 0) {
+            int grow;
+            if (EPI == 1) {
+                int f = n0 + (r & 127);
+                if (f >= N) f = N - 1;  // clamp: rows past N are computed, never stored
+                grow = r < 128 ? f : N + f;
+            } else {
+                grow = n0 + r;
+                if (grow >= N) grow = N - 1;
+            }
+            off[j] = (uint32_t)(grow * p.ldw + c * 8) * 2u;
+        } else {
+            const int trow = t0 + r;
+            off[j] = trow < M ? (uint32_t)(trow * p.lda + c * 8) * 2u : a_bytes;
+        }
+    }
+    auto issue = [&](int k) {
+        bf16_t *base = ring + (k & (SLOTS - 1)) * SLOT + grp_u * (BW * BK) + q_u * 512;
+#pragma unroll
+        for (int j = 0; j < D; ++j)
+            dma16(src, src_bytes, (lds_ptr_t)(base + j * 4 * 512), off[j], (uint32_t)(k * BK * 2));
+    };
+
+    // stage-row base of each weight fragment of this wave, and of its tokens
+    int wrow[FA];
+#pragma unroll
+    for (int a = 0; a < FA; ++a)
+        wrow[a] = EPI == 1 ? (a < 2 ? 64 * grp + 32 * a : 128 + 64 * grp + 32 * (a - 2))
+                           : 128 * grp + 32 * a;
+    const int tcol = 64 * q;
+    const int l32 = lane & 31, lhi = lane >> 5;
+
+    f32x16_t acc[FA][FB];
+#pragma unroll
+    for (int a = 0; a < FA; ++a)
+#pragma unroll
+        for (int b = 0; b < FB; ++b)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
+    bf16x8_t fw[2][FA], fa[2][FB];
+
+    // prologue: steps 0..2 in flight, step 0 published
+#pragma unroll
+    for (int k = 0; k < 3; ++k)
+        if (k < nk) issue(k);
+    if (nk >= 3)
+        wait_vmcnt<2 * D>();
+    else if (nk == 2)
+        wait_vmcnt<D>();
+    else
+        wait_vmcnt<0>();
+    wait_lgkmcnt<0>();
+    ring_barrier();
+
+    // Phases, each ended by a workgroup barrier: in phase 2k group 0 reads
+    // step k and group 1 multiplies step k - 1; in phase 2k + 1 group 0
+    // multiplies step k and group 1 reads step k.  So both groups run the same
+    // loop, read(k) then multiply(k), group 1 one phase behind (an extra
+    // barrier before its loop, group 0's after).  A group that reads step k
+    // also issues its half of step k + 3, into the slot of step k - 1, which
+    // both groups have read by then.
+    //
+    // Before the barrier that ends a phase, each wave waits for its own loads
+    // of the step read in the next phase, (phase + 1) / 2; `later` counts its
+    // loads issued after those (steps are issued in order, D loads each).
+    auto wait_later = [&](int later) {
+        if (later >= 3)
+            wait_vmcnt<3 * D>();
+        else if (later == 2)
+            wait_vmcnt<2 * D>();
+        else if (later == 1)
+            wait_vmcnt<D>();
+        else
+            wait_vmcnt<0>();
+    };
+    auto read_step = [&](int k) {
+        const bf16_t *sw = ring + (k & (SLOTS - 1)) * SLOT;
+        const bf16_t *sa = sw + BW * BK;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int ch = 2 * s + lhi;
+#pragma unroll
+            for (int a = 0; a < FA; ++a)
+                fw[s][a] = *reinterpret_cast<const bf16x8_t *>(&sw[swz<BK>(wrow[a] + l32, ch)]);
+#pragma unroll
+            for (int b = 0; b < FB; ++b)
+                fa[s][b] = *reinterpret_cast<const bf16x8_t *>(&sa[swz<BK>(tcol + 32 * b + l32, ch)]);
+        }
+    };
+    auto multiply = [&]() {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int a = 0; a < FA; ++a)
+#pragma unroll
+                for (int b = 0; b < FB; ++b)
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[s][a], fa[s][b],
+                                                                        acc[a][b], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    if (grp_u == 1) {
+        // phase 0: group 1 has nothing to multiply yet; step 0 must be visible
+        // for its read in phase 1
+        wait_later(min(2, nk - 1));
+        ring_barrier();
+    }
+    for (int k = 0; k < nk; ++k) {
+        read_step(k);
+        if (k + 3 < nk) issue(k + 3);
+        // next phase: group 0 multiplies (group 1 reads step k): step k needed
+        // from group 0's loads; group 1's next phase reads step k + 1
+        if (grp_u == 0)
+            wait_later(min(3, nk - 1 - k));
+        else if (k + 1 < nk)
+            wait_later(min(2, nk - 2 - k));
+        wait_lgkmcnt<0>();
+        ring_barrier();
+        multiply();
+        // next phase reads step k + 1 (group 0) or is group 1's read of k + 1
+        if (k + 1 < nk) wait_later(min(2, nk - 2 - k));
+        ring_barrier();
+    }
+    if (grp_u == 0) ring_barrier();  // group 1's last multiply
+
+    // Epilogue.  Accumulator element 4 g + e of lane l holds weight row
+    // 8 g + 4 (l / 32) + e and token l % 32 of its fragment.  Each output
+    // fragment goes through this wave's scratch as [token][feature] and is
+    // stored as 16-byte pieces, four lanes per 64-byte token row segment.
+    bf16_t *scr = scratch + wave * SCR;
+    auto bf16r = [](float v) { return bf16_to_f32(f32_to_bf16(v)); };
+    auto bias4 = [&](int32_t f, float (&bv)[4]) {
+        const u32x2_t w = *reinterpret_cast<const u32x2_t *>(p.bias + f);
+        bv[0] = bf16lo(w[0]);
+        bv[1] = bf16hi(w[0]);
+        bv[2] = bf16lo(w[1]);
+        bv[3] = bf16hi(w[1]);
+    };
+    int buf = 0;
+    // one 32 x 32 output fragment: values h[g][e] (feature 8 g + 4 lhi + e of
+    // token l32), first column col0 of C, token tiles' first row trow0
+    auto store_frag = [&](const float (&h)[4][4], int32_t col0, int32_t trow0) {
+        bf16_t *s = scr + buf * 1024;
+        buf ^= 1;
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+            *reinterpret_cast<u32x2_t *>(&s[pp_sc(l32, g) + 4 * lhi]) =
+                u32x2_t{pack_bf16x2(h[g][0], h[g][1]), pack_bf16x2(h[g][2], h[g][3])};
+        wait_lgkmcnt<0>();
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int tl = 16 * r + (lane >> 2), c = lane & 3;
+            const u32x4_t v = *reinterpret_cast<const u32x4_t *>(&s[pp_sc(tl, c)]);
+            const int32_t tok = trow0 + tl;
+            if (tok < M) st16(p.C + (size_t)tok * p.ldc + col0 + 8 * c, v);
+        }
+    };
+#pragma unroll
+    for (int b = 0; b < FB; ++b) {
+        const int32_t trow0 = t0 + tcol + 32 * b;
+        const int32_t tok = trow0 + l32;
+        if constexpr (EPI == 1) {
+#pragma unroll
+            for (int a = 0; a < 2; ++a) {
+                const int32_t col0 = n0 + 64 * grp + 32 * a;
+                if (col0 >= N) continue;
+                float h[4][4];
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        h[g][e] = gelu_erf(acc[a][b][4 * g + e]) * acc[a + 2][b][4 * g + e];
+                store_frag(h, col0, trow0);
+            }
+        } else if constexpr (EPI == 2) {
+            const QkvEpilogue &qe = p.qe;
+#pragma unroll
+            for (int a = 0; a < FA; a += 2) {
+                const int32_t f0 = n0 + wrow[a];  // first column of the head
+                if (f0 >= N) continue;
+                if (f0 < qe.rope_cols) {
+                    const uint32_t ps = (uint32_t)qe.pos[tok < M ? tok : M - 1] * 32u;
+                    float xo[4][4], yo[4][4];
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int j = 8 * g + 4 * lhi;  // pair index of element 4 g
+                        const u32x2_t cv = *reinterpret_cast<const u32x2_t *>(qe.cos_tab + ps + j);
+                        const u32x2_t sv = *reinterpret_cast<const u32x2_t *>(qe.sin_tab + ps + j);
+                        float bxv[4] = {0, 0, 0, 0}, byv[4] = {0, 0, 0, 0};
+                        if (p.bias) {
+                            bias4(f0 + j, bxv);
+                            bias4(f0 + 32 + j, byv);
+                        }
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            float x = bf16r(acc[a][b][4 * g + e]);
+                            float y = bf16r(acc[a + 1][b][4 * g + e]);
+                            if (p.bias) {
+                                x = bf16r(x + bxv[e]);
+                                y = bf16r(y + byv[e]);
+                            }
+                            const float c = (e & 1) ? bf16hi(cv[e >> 1]) : bf16lo(cv[e >> 1]);
+                            const float sn = (e & 1) ? bf16hi(sv[e >> 1]) : bf16lo(sv[e >> 1]);
+                            // both products of BF16 values are exact in float32
+                            xo[g][e] = fmaf(x, c, -(y * sn));
+                            yo[g][e] = fmaf(y, c, x * sn);
+                        }
+                    }
+                    store_frag(xo, f0, trow0);
+                    store_frag(yo, f0 + 32, trow0);
+                } else if (f0 >= qe.vt_col0) {
+                    // transposed: row f - vt_col0 of vt holds this token at
+                    // column vt_tok[tok] (32 lanes write 32 consecutive tokens)
+                    if (tok < M) {
+                        bf16_t *vcol = qe.vt + qe.vt_tok[tok];
+#pragma unroll
+                        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                            for (int g = 0; g < 4; ++g) {
+                                const int32_t f4 = f0 + 32 * h2 + 8 * g + 4 * lhi;
+                                float bv[4] = {0, 0, 0, 0};
+                                if (p.bias) bias4(f4, bv);
+#pragma unroll
+                                for (int e = 0; e < 4; ++e) {
+                                    float v = acc[a + h2][b][4 * g + e];
+                                    if (p.bias) v = bf16r(v) + bv[e];
+                                    vcol[(size_t)(f4 + e - qe.vt_col0) * qe.ldvt] =
+                                        (bf16_t)f32_to_bf16(v);
+                                }
+                            }
+                    }
+                } else {
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2) {
+                        float v[4][4];
+#pragma unroll
+                        for (int g = 0; g < 4; ++g) {
+                            float bv[4] = {0, 0, 0, 0};
+                            if (p.bias) bias4(f0 + 32 * h2 + 8 * g + 4 * lhi, bv);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                v[g][e] = acc[a + h2][b][4 * g + e];
+                                if (p.bias) v[g][e] = bf16r(v[g][e]) + bv[e];
+                            }
+                        }
+                        store_frag(v, f0 + 32 * h2, trow0);
+                    }
+                }
+            }
+        } else {
+            // epilogue 0 (plain), 4 (plain + bias) and 3 (bias, then GELU)
+            constexpr bool has_bias = EPI == 3 || EPI == 4;
+#pragma unroll
+            for (int a = 0; a < FA; ++a) {
+                const int32_t col0 = n0 + wrow[a];
+                if (col0 >= N) continue;
+                float v[4][4];
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    float bv[4];
+                    if constexpr (has_bias) bias4(col0 + 8 * g + 4 * lhi, bv);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        v[g][e] = acc[a][b][4 * g + e];
+                        if constexpr (has_bias) {
+                            v[g][e] = bf16r(v[g][e]) + bv[e];
+                            if constexpr (EPI == 3) v[g][e] = gelu_erf(bf16r(v[g][e]));
+                        }
+                    }
+                }
+                store_frag(v, col0, trow0);
+            }
+        }
+    }
+}
+
 // Tile configurations: weight rows x tokens, wave grid, K step, stages.
 using CfgXS = Cfg<32, 64, 1, 1, 64, 6>;    // small M, 1 wave (plain only)
 using CfgXSG = Cfg<64, 64, 1, 1, 64, 4>;   // small M, 1 wave (GeGLU-capable)
@@ -886,25 +1238,28 @@ constexpr CfgInfo kCfgs[kGemmConfigs] = {{CfgXS::BW, CfgXS::BT}, {CfgXSG::BW, Cf
                                          {CfgS::BW, CfgS::BT},   {CfgM::BW, CfgM::BT},
                                          {CfgL::BW, CfgL::BT},   {CfgXL::BW, CfgXL::BT},
                                          {CfgM2::BW, CfgM2::BT}, {CfgXS2::BW, CfgXS2::BT},
-                                         {CfgXSG2::BW, CfgXSG2::BT}};
+                                         {CfgXSG2::BW, CfgXSG2::BT}, {pp::BW, pp::BT}};
+
+// Whole-K grids of at least 512 tiles may take the 2-D XCD split (on smaller
+// grids it gained nothing and the padding cost a little): the grid rows
+// that give every XCD a slot per tile of the largest block of any split
+// (blocks only shrink with fewer live tokens).
+int grid_rows_2d(int nbx, int nby) {
+    int gy = nby;
+    for (int xw = 2; xw <= 8; xw *= 2) {
+        const int xtn = 8 / xw;
+        const int64_t bmax = (int64_t)((nby + xtn - 1) / xtn) * ((nbx + xw - 1) / xw);
+        gy = (int)std::max<int64_t>(gy, (8 * bmax + nbx - 1) / nbx);
+    }
+    return gy;
+}
 
 template <class G, int MODE>
 hipError_t launch_mode(hipStream_t s, GemmParams p, int epilogue) {
     const int bn = epilogue == 1 ? G::BW / 2 : G::BW;
     const int nbx = (p.N + bn - 1) / bn, nby = (p.M_max + G::BT - 1) / G::BT;
-    int gy = nby;
-    // whole-K grids of at least 512 tiles may take the 2-D XCD split (on
-    // smaller grids it gained nothing and the padding cost a little): pad
-    // the grid so every XCD has a slot per tile of the largest block of any
-    // split (blocks only shrink with fewer live tokens)
     p.split2d = MODE == kWholeK && nbx * nby >= 512;
-    if (p.split2d) {
-        for (int xw = 2; xw <= 8; xw *= 2) {
-            const int xtn = 8 / xw;
-            const int64_t bmax = (int64_t)((nby + xtn - 1) / xtn) * ((nbx + xw - 1) / xw);
-            gy = (int)std::max<int64_t>(gy, (8 * bmax + nbx - 1) / nbx);
-        }
-    }
+    const int gy = p.split2d ? grid_rows_2d(nbx, nby) : nby;
     const dim3 grid(nbx, gy, (MODE == kPartial || MODE == kPartialRows) ? p.splits : 1);
     // partial tiles are the same for the plain and bias epilogues (the bias
     // is applied by the reduce launch)
@@ -941,6 +1296,29 @@ hipError_t launch_large(hipStream_t s, const GemmParams &p, int epilogue) {
     return p.splits > 1 ? hipErrorInvalidValue : launch_mode<G, kWholeK>(s, p, epilogue);
 }
 
+// The ping-pong 256 x 256 tiles: whole K only.
+hipError_t launch_pp(hipStream_t s, GemmParams p, int epilogue) {
+    if (p.splits != 1 || p.K % pp::BK != 0) return hipErrorInvalidValue;
+    const int bn = epilogue == 1 ? pp::BW / 2 : pp::BW;
+    const int nbx = (p.N + bn - 1) / bn, nby = (p.M_max + pp::BT - 1) / pp::BT;
+    p.split2d = nbx * nby >= 512;
+    const dim3 grid(nbx, p.split2d ? grid_rows_2d(nbx, nby) : nby);
+    const dim3 block(512);
+    switch (epilogue) {
+        case 0:
+            if (p.bias)
+                hipLaunchKernelGGL(gemm_pp_kernel<4>, grid, block, 0, s, p);
+            else
+                hipLaunchKernelGGL(gemm_pp_kernel<0>, grid, block, 0, s, p);
+            break;
+        case 1: hipLaunchKernelGGL(gemm_pp_kernel<1>, grid, block, 0, s, p); break;
+        case 2: hipLaunchKernelGGL(gemm_pp_kernel<2>, grid, block, 0, s, p); break;
+        case 3: hipLaunchKernelGGL(gemm_pp_kernel<3>, grid, block, 0, s, p); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 // The split launch's partials, then the fused reduce + residual + LayerNorm.
 template <class G>
 hipError_t launch_split_layernorm(hipStream_t s, const GemmParams &p, bf16_t *x, bf16_t *n,
@@ -954,7 +1332,9 @@ hipError_t launch_split_layernorm(hipStream_t s, const GemmParams &p, bf16_t *x,
 
 }  // namespace
 
-int gemm_max_splits(int config) { return (config <= 3 || config >= 7) ? kMaxSplits : 1; }
+int gemm_max_splits(int config) {
+    return (config <= 3 || config == 7 || config == 8) ? kMaxSplits : 1;
+}
 
 GemmPlan plan_gemm_tiles(int32_t M, int32_t N, int32_t K, int epilogue) {
     // Tile shape with the least estimated time: the tiles the busiest of the
@@ -1079,7 +1459,8 @@ hipError_t launch_gemm(hipStream_t s, const bf16_t *A, int32_t lda, const bf16_t
         case 5: return launch_large<CfgXL>(s, p, epilogue);
         case 6: return launch_large<CfgM2>(s, p, epilogue);
         case 7: return launch_small<CfgXS2>(s, p, epilogue);
-        default: return launch_small<CfgXSG2>(s, p, epilogue);
+        case 8: return launch_small<CfgXSG2>(s, p, epilogue);
+        default: return launch_pp(s, p, epilogue);
     }
 }
 

@@ -45,16 +45,18 @@ hipError_t launch_layernorm(hipStream_t s, bf16_t *x, const bf16_t *r, bf16_t *n
 // GEMM tile configuration and K split.  Every output element is one MFMA
 // chain per K range, the ranges summed in order, so a result depends only on
 // `splits` (never on the tile shape).
-constexpr int kGemmConfigs = 9;
+constexpr int kGemmConfigs = 10;
 struct GemmPlan {
     int config;  // 0 XS 32x64, 1 XSG 64x64, 2 S 128x64, 3 M 128x128, 4 L 256x128, 5 XL 256x256,
                  // 6 M2 128x128 with a 2-stage ring (two workgroups per CU),
                  // 7 XS2 32x64 and 8 XSG2 64x64 (two computing waves each, deep
-                 // rings; XS2 with two more waves that only load)
+                 // rings; XS2 with two more waves that only load),
+                 // 9 P 256x256 with two wave groups in ping-pong (whole K)
     int splits;  // K ranges (>= 1)
 };
-// plan for a GEMM launched with a grid for M_max rows (the K split depends
-// only on M_max); plan_gemm_tiles: the best whole-K tile shape for M rows.
+// plan for a GEMM of up to M_max rows (its K split and tile shape; the split
+// thresholds are 64, 256, 1024 and 2048 rows); plan_gemm_tiles: the best
+// whole-K tile shape for M rows.
 GemmPlan plan_gemm(int32_t M_max, int32_t N, int32_t K, int epilogue);
 GemmPlan plan_gemm_tiles(int32_t M, int32_t N, int32_t K, int epilogue);
 int gemm_max_splits(int config);
@@ -101,6 +103,11 @@ hipError_t launch_gemm_layernorm(hipStream_t s, const bf16_t *A, int32_t lda, co
 hipError_t launch_rope(hipStream_t s, bf16_t *buf, int32_t ld, int32_t n_heads_rot,
                        const int32_t *count_dev, int32_t rows_max, const int32_t *pos,
                        const bf16_t *cos_tab, const bf16_t *sin_tab);
+// The same rotation in the original launch geometry (one thread per pair,
+// 64-bit index division); bitwise equal to launch_rope.
+hipError_t launch_rope_original(hipStream_t s, bf16_t *buf, int32_t ld, int32_t n_heads_rot,
+                                const int32_t *count_dev, int32_t rows_max, const int32_t *pos,
+                                const bf16_t *cos_tab, const bf16_t *sin_tab);
 
 // Attention over packed rows.  q [rows][ldq] (head h at columns h*64..),
 // k [rows][ldk] likewise, vt [n_heads*64][ldvt] (row h*64+d holds

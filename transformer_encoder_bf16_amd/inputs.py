@@ -6,12 +6,12 @@ very same arrays.  Everything here is plain data (model shapes, workload
 shapes, seeds) plus numpy ``default_rng`` draws.
 
 Model shapes: the synthetic Laya-sized encoder (hidden 1024, 16 heads of 64,
-GeGLU inner width 2624, 28 encoder + 2 decision layers, vocab 50368, global
+GeGLU inner width 2624, 28 encoder layers then 2 decision layers, vocab 50368, global
 attention on every 3rd encoder layer with RoPE theta 160000, the others a
-128-token window with theta 10000).  The pages describe the same stack as
-"28 encoder layers and two decision transformer layers" in BF16 (page
-"Run Laya encoder and decision layers on CUDA", section Purpose) and its
-input limits of 16 questions, 512 tokens per sequence and 2048 markers
+128-token window with theta 10000).  The pages describe the same stack, an
+encoder of 28 layers followed by two decision layers, run in BF16 (page
+"Run Laya encoder and decision layers on CUDA", section Purpose), and the
+worker's limits of at most 16 rows, 512 tokens per row and 2048 markers
 (page "Laya native CUDA worker", section Start and check).
 
 Workload shapes follow the batch shapes the pages time (the table in the
