@@ -455,6 +455,22 @@ int laya_op_gemm(void *stream, const void *A, int32_t lda, const void *W, int32_
                  void *C, int32_t ldc, int32_t M, int32_t N, int32_t K, int32_t epilogue,
                  int32_t config, int32_t splits, const void *bias);
 
+/* laya_op_gemm for callers that cannot allocate device memory (code under
+ * graph capture, tight serving loops, harnesses that forbid allocation):
+ * arguments, plan choice, results and errors as laya_op_gemm, bitwise, but
+ * the split-K partials (splits > 1) go to a buffer the library holds for the
+ * life of the process on each GPU it runs on (16 MiB; the bytes a plan needs
+ * are 4 x tiles x splits x tile area), the call allocates and frees nothing,
+ * and it does not synchronise: it only queues the launches on `stream`.
+ * LAYA_E_INVALID, before any device work, when the split needs more than the
+ * buffer.  Every call on one GPU shares that buffer, which keeps the last
+ * call's contents (nothing in it needs clearing: each call writes every
+ * partial it reads): calls that may overlap on one GPU, on different streams
+ * or from different threads, race; the caller orders them. */
+int laya_op_gemm_noalloc(void *stream, const void *A, int32_t lda, const void *W, int32_t ldw,
+                         void *C, int32_t ldc, int32_t M, int32_t N, int32_t K, int32_t epilogue,
+                         int32_t config, int32_t splits, const void *bias);
+
 /* A projection onto the hidden width followed by the residual add and the
  * LayerNorm of the next sublayer (pre-norm stack, "[RFC]: Native Laya
  * inference with Rust and CUDA #14", section Design; fused residual and

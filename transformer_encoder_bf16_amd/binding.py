@@ -50,7 +50,8 @@ EXPORTS = [
     "laya_encoder_profile", "laya_encoder_fill_workspace", "laya_encoder_config",
     "laya_encoder_health", "laya_encoder_inject_failure", "laya_queue_create", "laya_queue_submit",
     "laya_queue_wait", "laya_queue_health", "laya_queue_destroy", "laya_rope_table", "laya_memcpy", "laya_op_gather", "laya_op_layernorm", "laya_op_gemm",
-    "laya_op_gemm_layernorm", "laya_op_gemm_qkv", "laya_op_rope", "laya_op_rope_original",
+    "laya_op_gemm_noalloc", "laya_op_gemm_layernorm", "laya_op_gemm_qkv", "laya_op_rope",
+    "laya_op_rope_original",
     "laya_op_attention",
 ]
 
@@ -177,6 +178,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
                                         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                         ctypes.c_int32, _P]),
+        "laya_op_gemm_noalloc": (ctypes.c_int, [_P, _P, ctypes.c_int32, _P, ctypes.c_int32, _P,
+                                                ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                ctypes.c_int32, _P]),
         "laya_op_gemm_layernorm": (ctypes.c_int, [_P, _P, ctypes.c_int32, _P, ctypes.c_int32,
                                                   _P, _P, _P, ctypes.c_int32, ctypes.c_int32,
                                                   ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
@@ -431,6 +436,16 @@ def op_gemm(A, W, C, M: int, N: int, K: int, epilogue: int = 0, config: int = -1
     _check(load().laya_op_gemm(st, _dp(A), A.stride(0), _dp(W), W.stride(0), _dp(C),
                                C.stride(0), M, N, K, epilogue, config, splits, _dp(bias)),
            "laya_op_gemm")
+
+
+def op_gemm_noalloc(A, W, C, M: int, N: int, K: int, epilogue: int = 0, config: int = -1,
+                    splits: int = 1, bias=None, stream: Optional[int] = None):
+    """op_gemm without any allocation (split-K partials in the library's own
+    per-device buffer); queues only, does not synchronise."""
+    st = current_stream() if stream is None else stream
+    _check(load().laya_op_gemm_noalloc(st, _dp(A), A.stride(0), _dp(W), W.stride(0), _dp(C),
+                                       C.stride(0), M, N, K, epilogue, config, splits, _dp(bias)),
+           "laya_op_gemm_noalloc")
 
 
 def op_gemm_layernorm(A, W, x, n, gamma, M: int, N: int, K: int, config: int, splits: int,

@@ -1655,6 +1655,34 @@ int laya_op_gemm(void *stream, const void *A, int32_t lda, const void *W, int32_
                           ldc, M, N, K, epilogue, config, splits, nullptr, bias);
 }
 
+int laya_op_gemm_noalloc(void *stream, const void *A, int32_t lda, const void *W, int32_t ldw,
+                         void *C, int32_t ldc, int32_t M, int32_t N, int32_t K, int32_t epilogue,
+                         int32_t config, int32_t splits, const void *bias) {
+    if (!gemm_args_ok(A, lda, W, ldw, C, ldc, M, N, K, config) ||
+        (epilogue != 0 && epilogue != 1 && epilogue != 3) || (epilogue == 1 && bias) ||
+        (epilogue == 3 && M > 0 && !bias))
+        return set_global_error(LAYA_E_INVALID, "laya_op_gemm_noalloc: bad arguments");
+    if (M == 0) return LAYA_OK;
+    laya::GemmPlan plan = laya::plan_gemm(M, N, K, epilogue);
+    if (config >= 0) plan = laya::GemmPlan{config, splits < 1 ? 1 : splits};
+    if (plan.splits > K / 64 || plan.splits > laya::gemm_max_splits(plan.config) ||
+        ((epilogue == 1 || epilogue == 2) && plan.config == 0))
+        return set_global_error(LAYA_E_INVALID, "laya_op_gemm_noalloc: unsupported config/splits");
+    const size_t pb = laya::gemm_workspace_bytes(plan, M, N, epilogue);
+    if (pb > laya::gemm_static_scratch_bytes())
+        return set_global_error(
+            LAYA_E_INVALID, "laya_op_gemm_noalloc: the K split needs " + std::to_string(pb) +
+                                " bytes of scratch, more than the library's " +
+                                std::to_string(laya::gemm_static_scratch_bytes()));
+    float *scratch = nullptr;
+    if (pb) OPCHK(laya::gemm_static_scratch(&scratch));
+    OPCHK(laya::launch_gemm(static_cast<hipStream_t>(stream), static_cast<const bf16_t *>(A), lda,
+                            static_cast<const bf16_t *>(W), ldw, static_cast<bf16_t *>(C), ldc,
+                            nullptr, M, N, K, epilogue, plan, scratch, nullptr,
+                            static_cast<const bf16_t *>(bias)));
+    return LAYA_OK;
+}
+
 int laya_op_gemm_layernorm(void *stream, const void *A, int32_t lda, const void *W, int32_t ldw,
                            void *x, void *n, const float *gamma, int32_t M, int32_t N, int32_t K,
                            int32_t config, int32_t splits, const void *bias, float eps) {

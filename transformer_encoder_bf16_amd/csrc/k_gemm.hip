@@ -57,8 +57,15 @@
 // the matmul followed by x + b in the model's precision); epilogue 3 then
 // takes GELU of that BF16 value, h = bf16(GELU(y)).
 #include <algorithm>
+#include <mutex>
 
 #include "kernels.h"
+
+// Split-K partials of the allocation-free GEMM entry point: device memory the
+// library holds for the life of the process on each GPU it runs on, shared by
+// every such call on that GPU.
+constexpr size_t kStaticScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) float scratch[kStaticScratchBytes / sizeof(float)];
 
 namespace laya {
 
@@ -1430,6 +1437,29 @@ size_t gemm_workspace_bytes(const GemmPlan &g, int32_t M_max, int32_t N, int epi
     const int bn = epilogue == 1 ? c.bw / 2 : c.bw;
     const size_t tiles = (size_t)((N + bn - 1) / bn) * ((M_max + c.bt - 1) / c.bt);
     return tiles * g.splits * c.bw * c.bt * 4;
+}
+
+size_t gemm_static_scratch_bytes() { return kStaticScratchBytes; }
+
+// The address of this device's copy of `scratch`, looked up once per device
+// with that device current (the array's name is only a host-side stand-in;
+// kernels must get the device address).
+hipError_t gemm_static_scratch(float **ptr) {
+    static std::mutex mu;
+    static float *addr[64] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = static_cast<float *>(p);
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_gemm(hipStream_t s, const bf16_t *A, int32_t lda, const bf16_t *W,

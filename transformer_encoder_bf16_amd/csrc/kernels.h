@@ -62,6 +62,11 @@ GemmPlan plan_gemm_tiles(int32_t M, int32_t N, int32_t K, int epilogue);
 int gemm_max_splits(int config);
 // float32 partial-tile bytes a plan needs (0 when splits == 1)
 size_t gemm_workspace_bytes(const GemmPlan &g, int32_t M_max, int32_t N, int epilogue);
+// The library's own split-K scratch on the current device (for callers that
+// cannot allocate): its size, and its device address (looked up once per
+// device; every call on one device shares it).
+size_t gemm_static_scratch_bytes();
+hipError_t gemm_static_scratch(float **ptr);
 
 // Epilogue 2 (QKV projection): output columns [0, rope_cols) are heads of
 // 64 that are rotated (RoPE, rotate-half pairs (i, i+32), c/s = tab[pos][i])
