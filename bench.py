@@ -68,6 +68,16 @@ def parse():
     p.add_argument("--latency-calls", type=int, default=50)
     p.add_argument("--profile-passes", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--rope", choices=("fused", "standalone", "original"), default="fused",
+                   help="RoPE variant of the measured pass: in the QKV epilogue (default), by its "
+                        "own kernel, or by its own kernel in the original launch geometry")
+    p.add_argument("--summarize-counters", nargs="+", metavar="DIR",
+                   help="only print a per-kernel markdown table of the rocprofv3 counter runs "
+                        "written to these directories (counter_collection.csv), then exit")
+    p.add_argument("--copy-fetch-per-byte", type=float, default=None,
+                   help="FETCH_SIZE KiB per KiB of a plain device copy (scales HBM reads)")
+    p.add_argument("--copy-write-per-byte", type=float, default=None,
+                   help="WRITE_SIZE KiB per KiB of a plain device copy (scales HBM writes)")
     p.add_argument("--dec-head", action="store_true",
                    help="decision layers as the biased head variant (biased projections, "
                         "4*hidden GELU FFN)")
@@ -405,7 +415,96 @@ def oracle_timing(cfg, batch, calls):
             "calls_per_s": round(calls / (sum(ts) / 1e3), 4), "cores": os.cpu_count()}
 
 
-def graph_replays(enc, batch, steps, warmup, latency_calls, sync):
+def summarize_counters(dirs, fetch_per_byte=None, write_per_byte=None):
+    """Per-kernel averages of rocprofv3 --pmc runs, as a markdown table.
+
+    Each dispatch's duration comes from its timestamps.  GRBM_GUI_ACTIVE is
+    summed over the 8 XCDs and carries a fixed overhead per dispatch, so the
+    clock and that overhead are fitted over every dispatch of a run
+    (GRBM/8 = clock * duration + overhead); busy fractions are then per SIMD
+    (1024) or per CU (256) over duration x fitted clock.  MFMA TFLOP/s comes
+    from SQ_INSTS_VALU_MFMA_MOPS_BF16 (512 FLOP each).  HBM bytes: FETCH_SIZE
+    and WRITE_SIZE (KiB) divided by what they read per byte of a plain copy."""
+    import csv
+    import re
+    import collections
+    kern = collections.defaultdict(lambda: collections.defaultdict(list))
+    durs = collections.defaultdict(dict)
+    fits = []
+    for d in dirs:
+        path = None
+        for root, _, files in os.walk(d):
+            for f in files:
+                if f.endswith("counter_collection.csv"):
+                    path = os.path.join(root, f)
+        if path is None:
+            continue
+        per_dispatch = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                name = r["Kernel_Name"]
+                m = re.search(r"gemm_kernel<laya::\(anonymous namespace\)::Cfg<([^>]*)>, (\d+), (\d+)>", name)
+                if m:
+                    short = f"gemm_kernel<Cfg<{m.group(1)}>, {m.group(2)}, {m.group(3)}>"
+                else:
+                    short = re.sub(r"\(.*", "", name.replace("laya::(anonymous namespace)::", "")
+                                   .replace("void ", "").replace("laya::", ""))
+                key = (short, int(r["Grid_Size"]))
+                us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+                kern[key][r["Counter_Name"]].append(float(r["Counter_Value"]))
+                durs[key][(d, r["Dispatch_Id"])] = us
+                if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+                    per_dispatch[r["Dispatch_Id"]] = (us, float(r["Counter_Value"]) / 8)
+        if len(per_dispatch) >= 2:
+            x = np.array([v[0] for v in per_dispatch.values()])
+            y = np.array([v[1] for v in per_dispatch.values()])
+            fits.append(np.polyfit(x, y, 1))
+    clock_mhz, overhead = (np.mean([f[0] for f in fits]), np.mean([f[1] for f in fits])) if fits \
+        else (2100.0, 0.0)
+    print(f"Fitted over every dispatch: clock {clock_mhz / 1e3:.2f} GHz, GRBM overhead "
+          f"{overhead:.0f} cycles per dispatch.\n")
+    cols = ["Kernel", "Grid", "Dispatches", "Avg µs"]
+    rows = []
+    for key, cs in kern.items():
+        a = {c: sum(v) / len(v) for c, v in cs.items()}
+        us = sum(durs[key].values()) / len(durs[key])
+        cyc = us * clock_mhz
+        row = {"Kernel": f"`{key[0]}`", "Grid": key[1], "Dispatches": len(durs[key]),
+               "Avg µs": f"{us:.2f}"}
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in a:
+            row["MFMA busy %"] = f"{100 * a['SQ_VALU_MFMA_BUSY_CYCLES'] / 1024 / cyc:.1f}"
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in a:
+            row["MFMA TFLOP/s"] = f"{a['SQ_INSTS_VALU_MFMA_MOPS_BF16'] * 512 / us / 1e6:.0f}"
+        if "SQ_ACTIVE_INST_VALU" in a:
+            row["VALU busy %"] = f"{100 * a['SQ_ACTIVE_INST_VALU'] * 4 / 1024 / cyc:.1f}"
+        if "SQ_INSTS_MFMA" in a and a["SQ_INSTS_MFMA"] and "SQ_INSTS_VALU" in a:
+            row["VALU instr / MFMA"] = f"{(a['SQ_INSTS_VALU'] - a['SQ_INSTS_MFMA']) / a['SQ_INSTS_MFMA']:.2f}"
+        if "SQ_LDS_BANK_CONFLICT" in a:
+            row["LDS bank-conflict %"] = f"{100 * a['SQ_LDS_BANK_CONFLICT'] / 256 / cyc:.2f}"
+        if "SQ_WAVE_CYCLES" in a and a["SQ_WAVE_CYCLES"]:
+            for c in ("SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY"):
+                if c in a:
+                    row[c[3:] + " % of wave cycles"] = f"{100 * a[c] / a['SQ_WAVE_CYCLES']:.1f}"
+        if "FETCH_SIZE" in a:
+            b = a["FETCH_SIZE"] * 1024 / (fetch_per_byte or 1.0)
+            row["HBM read MB"] = f"{b / 1e6:.2f}"
+            row["read GB/s"] = f"{b / us / 1e3:.0f}"
+        if "WRITE_SIZE" in a:
+            b = a["WRITE_SIZE"] * 1024 / (write_per_byte or 1.0)
+            row["HBM write MB"] = f"{b / 1e6:.2f}"
+            row["write GB/s"] = f"{b / us / 1e3:.0f}"
+        rows.append((us * len(durs[key]), row))
+        for k in row:
+            if k not in cols:
+                cols.append(k)
+    rows.sort(key=lambda t: -t[0])
+    print("| " + " | ".join(cols) + " |")
+    print("|" + "---|" * len(cols))
+    for _, row in rows:
+        print("| " + " | ".join(str(row.get(c, "")) for c in cols) + " |")
+
+
+def graph_replays(enc, batch, steps, warmup, latency_calls, sync, vflags=0):
     """First call (upload + graph capture), then `warmup` and `steps` timed
     back-to-back graph replays on device-resident indices, then per-call
     latencies (synchronised per call), the pages' host boundary (pack + upload
@@ -413,11 +512,11 @@ def graph_replays(enc, batch, steps, warmup, latency_calls, sync):
     from transformer_encoder_bf16_amd import binding
     mk = batch.markers
     t = time.perf_counter()
-    enc.run(batch.ids, batch.lengths, markers=mk)
+    enc.run(batch.ids, batch.lengths, markers=mk, flags=vflags)
     sync()
     first_ms = (time.perf_counter() - t) * 1e3
     capture_ms = enc.stats()["last_capture_ms"]
-    flags = binding.RUN_RESIDENT
+    flags = binding.RUN_RESIDENT | vflags
     for _ in range(warmup):
         enc.run(batch.ids, batch.lengths, markers=mk, flags=flags)
     sync()
@@ -434,12 +533,12 @@ def graph_replays(enc, batch, steps, warmup, latency_calls, sync):
         lat.append((time.perf_counter() - t) * 1e3)
     for _ in range(latency_calls):
         t = time.perf_counter()
-        enc.run(batch.ids, batch.lengths, markers=mk)
+        enc.run(batch.ids, batch.lengths, markers=mk, flags=vflags)
         sync()
         host.append((time.perf_counter() - t) * 1e3)
     for _ in range(max(5, latency_calls // 5)):
         t = time.perf_counter()
-        enc.run(batch.ids, batch.lengths, markers=mk, flags=binding.RUN_EAGER)
+        enc.run(batch.ids, batch.lengths, markers=mk, flags=binding.RUN_EAGER | vflags)
         sync()
         eager.append((time.perf_counter() - t) * 1e3)
     launches = enc.stats()["launches_last_run"]
@@ -454,6 +553,10 @@ def graph_replays(enc, batch, steps, warmup, latency_calls, sync):
 
 def main():
     args = parse()
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.copy_fetch_per_byte,
+                           args.copy_write_per_byte)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the pass has no "
               f"multi-GPU sharding", file=sys.stderr)
@@ -481,7 +584,10 @@ def main():
     mk = batch.markers
     sync = torch.cuda.synchronize
 
-    main_run = graph_replays(enc, batch, args.steps, args.warmup, args.latency_calls, sync)
+    vflags = {"fused": 0, "standalone": binding.RUN_ROPE_STANDALONE,
+              "original": binding.RUN_ROPE_ORIGINAL}[args.rope]
+    main_run = graph_replays(enc, batch, args.steps, args.warmup, args.latency_calls, sync,
+                             vflags)
     calls_per_s = main_run["calls_per_s"]
 
     # the second shape the metric is quoted on, the same way
@@ -497,7 +603,7 @@ def main():
                                       "launches_per_call")}}
 
     # per-op table from event-bracketed eager passes (HIP events on the launch stream)
-    table, pass_ms = op_table(enc, batch, mk, args.profile_passes)
+    table, pass_ms = op_table(enc, batch, mk, args.profile_passes, flags=vflags)
     enc.close()
     dom = max(table, key=lambda k: table[k]["ms_per_pass"])
     d = table[dom]
@@ -566,7 +672,8 @@ def main():
                    "R": 0 if mk is None else int(len(mk)), "input_seed": wl.seed,
                    "weight_seed": WEIGHT_SEED, "layers": "28+2", "mode": "hipGraph replay",
                    "inputs": "device-resident",
-                   "decision_layers": "head" if args.dec_head else "encoder-shaped"},
+                   "decision_layers": "head" if args.dec_head else "encoder-shaped",
+                   "rope": args.rope},
         **{k: main_run[k] for k in ("p50_ms", "p95_ms", "host_boundary_p50_ms",
                                     "eager_host_boundary_p50_ms", "first_call_ms", "capture_ms",
                                     "launches_per_call")},
