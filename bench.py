@@ -47,12 +47,12 @@ DOMINANT_KERNEL_SYMBOL = {
 # rocprofv3 --pmc runs of this script, each divided by what the same counter
 # reads per byte moved by a plain 1 GiB device copy (this script's
 # --copy-calibration-mib mode).  Commands and figures:
-# profiles/up_geglu_gemm_mixed_16_traffic.md.  The figure holds only for the
+# profiles/pass_traffic_mixed_16.md.  The figure holds only for the
 # GEMM sources it was taken with (SHA-256 over k_gemm.hip, common.h,
 # kernels.h); after any change to them the traffic is reported as null.
-TRAFFIC = {"op": "up_geglu_gemm", "workload": "mixed_16", "fetch_kib": 52254.5,
+TRAFFIC = {"op": "up_geglu_gemm", "workload": "mixed_16", "fetch_kib": 52217.7,
            "write_kib": 20756.2, "fetch_per_byte": 0.5000, "write_per_byte": 1.0000,
-           "sources_sha256": "9dd9c7b3d3567048537c80119243ebe254bb05965efb41637dc5a94f45bd6625"}
+           "sources_sha256": "27f59a41869dbc19d314efe14ca958803078cea57ed87fd2a3dae6f04be791e5"}
 TRAFFIC_SOURCES = ("k_gemm.hip", "common.h", "kernels.h")
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense BF16 MFMA
