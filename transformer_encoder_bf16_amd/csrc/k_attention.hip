@@ -16,9 +16,13 @@
 //   - S^T = K Q^T with v_mfma_f32_16x16x32_bf16: keys are the MFMA rows and
 //     queries the columns, so each lane ends up with 16 scores of ONE query
 //     (lane l: query l%16, keys 8*(l/16)+0..7 of each 32-key half);
-//   - online softmax in float32, exp2 domain, the row maximum reduced over
-//     the 4 lanes of a query (two xor shuffles); tiles inside every window
-//     of the wave skip the mask;
+//   - online softmax in float32, exp2 domain: each tile's maximum is
+//     reduced over the 4 lanes of a query with the gfx950 lane swaps
+//     (v_permlane16_swap, v_permlane32_swap: plain VALU moves, no LDS round
+//     trip), and the reference maximum that the weights are taken against
+//     moves only when a score passes it by more than 2^8, so the
+//     accumulators are rarely rescaled; tiles inside every window of the
+//     wave skip the mask;
 //   - O^T += V^T P^T: P^T is the MFMA B operand, whose lane layout (query
 //     l%16, 8 consecutive k slots per lane) is exactly the lane's own scores
 //     once the K rows of S^T are fed in the matching order, so P never leaves
@@ -131,7 +135,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void a
     w_hi = __builtin_amdgcn_readfirstlane(w_hi);
 
     const float sl2 = 0.125f * 1.44269504088896341f;  // 1/sqrt(64) * log2(e)
-    float m = -INFINITY;  // running maximum, raw score units
+    float m = -INFINITY;  // reference maximum, raw score units
     f32x4_t oacc[4];       // O^T rows 16 dblk + 4 g + i, column c16
 #pragma unroll
     for (int d = 0; d < 4; ++d) oacc[d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -195,18 +199,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void a
                     s[b][i] = rel < q_span ? s[b][i] : -INFINITY;
                 }
         }
-        // running maximum in raw score units (the scale is positive)
+        // this tile's maximum in raw score units (the scale is positive),
+        // reduced over the 4 lanes of a query (rows of 16 lanes swapped
+        // pairwise, then the two halves of the wave)
         float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
                          fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
         mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(s[2][0], s[2][1]), fmaxf(s[2][2], s[2][3])),
                              fmaxf(fmaxf(s[3][0], s[3][1]), fmaxf(s[3][2], s[3][3]))));
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float mnew = fmaxf(m, mx);
-        const bool none = mnew == -INFINITY;  // every key so far masked
-        const float alpha = none ? 1.f : __builtin_amdgcn_exp2f((m - mnew) * sl2);
-        const float neg = none ? 0.f : -mnew * sl2;
-        m = mnew;
+        {
+            const uint32_t xb = __float_as_uint(mx);
+            const auto r16 = __builtin_amdgcn_permlane16_swap(xb, xb, false, false);
+            mx = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+            const uint32_t yb = __float_as_uint(mx);
+            const auto r32 = __builtin_amdgcn_permlane32_swap(yb, yb, false, false);
+            mx = fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+        }
+        // The reference maximum m follows the scores lazily: it moves only
+        // when a score exceeds it by more than 8 after scaling (2^8 in the
+        // weights), or at the first unmasked keys, so rescaling the
+        // accumulators is rare and the weights stay at most 2^8.  The
+        // normalisation by the row sum makes the result independent of m.
+        float alpha = 1.f;
+        if (mx * sl2 > fmaf(m, sl2, 8.f)) {
+            if (m != -INFINITY) alpha = __builtin_amdgcn_exp2f((m - mx) * sl2);
+            m = mx;
+        }
+        const float neg = m == -INFINITY ? 0.f : -m * sl2;
         // P = 2^(s * scale - m * scale), split into BF16 hi + lo and packed
         // as the B operand of each 32-key half: slot 4 e + i <- block 2 ks + e,
         // element i (masked keys: 2^-inf = 0).
@@ -222,7 +240,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void a
                 ph[ks][qd] = hi;
                 pl[ks][qd] = cvt_pk_bf16(p0 - bf16lo(hi), p1 - bf16hi(hi));  // exact tails
             }
-        if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {  // the maximum moved for some query
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {  // the reference moved for some query
 #pragma unroll
             for (int d = 0; d < 4; ++d) oacc[d] *= alpha;
             lacc *= alpha;
