@@ -96,6 +96,9 @@ def parse():
     p.add_argument("--protocol-calls", type=int, default=100)
     p.add_argument("--protocol-oracle-calls", type=int, default=3,
                    help="oracle calls per workload in --protocol (0: skip the oracle)")
+    p.add_argument("--plan-check", action="store_true",
+                   help="time each projection at the first token count of every plan range, "
+                        "with the range's plan and with the plan for exactly that count")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="only run a plain device-to-device copy of this many MiB three times "
                         "(the reference for scaling HBM byte counters), then exit")
@@ -393,6 +396,89 @@ def protocol(args):
                                     for k, v in results["workloads"].items()}}), flush=True)
 
 
+CONFIG_NAMES = ["XS", "XSG", "S", "M", "L", "XL", "M2", "XS2", "XSG2", "PP"]
+
+
+def plan_check():
+    """A captured graph serves the run of live token counts whose GEMM plans
+    agree (laya_pass_plans).  For the first count of every such run, each
+    projection is timed with the pass's plan and with the planner evaluated
+    at exactly that count (laya_plan_gemm; the two agree when the pass plans
+    per count), as back-to-back launches in a captured graph with the weights
+    rotated through copies larger than the MALL.  Split plans run with their
+    own reduce launch here (laya_op_gemm_noalloc; the pass fuses that reduce
+    with the LayerNorm).  Prints a markdown table."""
+    import torch
+    from transformer_encoder_bf16_amd import binding as B
+    from transformer_encoder_bf16_amd.inputs import MODEL
+    torch.cuda.set_device(0)
+    dev = "cuda"
+    H, F = MODEL["hidden"], MODEL["ffn"]
+    gemms = [("qkv", 3 * H, H, 2), ("out", H, H, 0), ("up", F, H, 1), ("down", H, F, 0)]
+    cb, sb = B.rope_table(160000.0, 512, 64)
+    ct = torch.from_numpy(cb.view(np.int16)).to(dev)
+    st = torch.from_numpy(sb.view(np.int16)).to(dev)
+
+    def graph_us(fn, n_inner, reps=5):
+        s = torch.cuda.Stream()
+        with torch.cuda.stream(s):
+            fn()
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                fn()
+            g.replay()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            for _ in range(reps):
+                g.replay()
+            e1.record(s)
+            torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (reps * n_inner)
+
+    ranges = []
+    T = 1
+    while T <= MODEL["max_batch"] * MODEL["max_seq"]:
+        lo, hi, plans = B.pass_plans(MODEL, T)
+        ranges.append((max(lo, 48), lo, hi, plans))
+        T = hi + 1
+    print("| T | Range | GEMM | Range plan (tile, K ranges) | µs | Plan at T | µs | Range / at-T |")
+    print("|---|---|---|---|---|---|---|---|")
+    for T, lo, hi, plans in ranges:
+        pos = torch.from_numpy((np.arange(T) % 512).astype(np.int32)).to(dev)
+        vtok = torch.arange(T, dtype=torch.int32, device=dev)
+        vt = torch.empty(H, T + 64, dtype=torch.bfloat16, device=dev)
+        for (name, N, K, epi), pl in zip(gemms, plans[:4]):
+            wr = 2 * N if epi == 1 else N
+            A = (torch.randn(T, K, device=dev) * 0.5).bfloat16()
+            W = (torch.randn(wr, K, device=dev) * 0.03).bfloat16()
+            C = torch.empty(T, N, device=dev, dtype=torch.bfloat16)
+            ncopy = max(8, int(600e6 // (wr * K * 2)))
+            Ws = [W.clone() for _ in range(ncopy)]
+            del W
+
+            def timed(cfg, sp):
+                def fn():
+                    for w in Ws:
+                        if epi == 2:
+                            B.op_gemm_qkv(A, w, C, T, N, K, pos, ct, st, 2 * H, vt, vtok, 2 * H,
+                                          config=cfg, splits=sp)
+                        else:
+                            B.op_gemm_noalloc(A, w, C, T, N, K, epi, cfg, sp)
+                return graph_us(fn, ncopy)
+
+            at = B.plan_gemm(T, N, K, epi)
+            rng = (pl[0], pl[1])
+            us_r = timed(*rng)
+            us_t = us_r if at == rng else timed(*at)
+            print(f"| {T} | {lo}–{hi} | {name} | {CONFIG_NAMES[rng[0]]}, {rng[1]} | {us_r:.2f} | "
+                  f"{'same' if at == rng else f'{CONFIG_NAMES[at[0]]}, {at[1]}'} | {us_t:.2f} | "
+                  f"{us_r / us_t:.3f} |", flush=True)
+            del Ws
+
+
 def model_config(args) -> dict:
     """The model, or with --dec-head its biased decision-head variant."""
     from transformer_encoder_bf16_amd.inputs import MODEL
@@ -568,6 +654,9 @@ def main():
         return
     if args.protocol:
         protocol(args)
+        return
+    if args.plan_check:
+        plan_check()
         return
     from transformer_encoder_bf16_amd import binding
     from transformer_encoder_bf16_amd.inputs import ALL_WORKLOADS, WEIGHT_SEED, make_batch

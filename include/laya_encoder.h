@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define LAYA_ABI_VERSION 5
+#define LAYA_ABI_VERSION 6
 
 #define LAYA_OK 0
 #define LAYA_E_INVALID -1     /* bad ids, lengths, markers, sizes, NULL pointers */
@@ -142,10 +142,11 @@ int laya_validate_config(const laya_config *cfg);
 
 /* Host-only diagnostic: the GEMM plans of a pass over T live tokens and R
  * marker rows.  A plan is a tile shape (laya_op_gemm's `config`) and a number
- * of K ranges; every plan follows T alone, never the padded B x S, so padding
- * never changes a result.  Plans are piecewise constant in T: *t_first and
- * *t_last bound the token counts that share this pass's plans, and one
- * captured graph of a (B, S, R) serves exactly such a range.  out (host,
+ * of K ranges; every plan is the planner's choice for exactly T
+ * (laya_plan_gemm), never for the padded B x S, so padding never changes a
+ * result.  Plans are piecewise constant in T: *t_first and *t_last bound the
+ * maximal run of token counts that share this pass's plans, and one captured
+ * graph of a (B, S, R) serves exactly such a run.  out (host,
  * `cap` entries) receives the plans in the order QKV, output, up, down, then
  * (dec_head) head up, head down, then (R > 0) the marker layer's K/V, Q,
  * output, up, down (and head up, head down); *n_out is the full count.
@@ -160,6 +161,15 @@ typedef struct laya_gemm_plan {
 
 int laya_pass_plans(const laya_config *cfg, int32_t T, int32_t R, int32_t *t_first,
                     int32_t *t_last, laya_gemm_plan *out, int32_t cap, int32_t *n_out);
+
+/* Host-only diagnostic: the plan that laya_op_gemm (config -1) uses for an
+ * M x N x K product with the given epilogue (0 plain, 1 GeGLU, 2 QKV, 3 bias
+ * then GELU): the planner evaluated at exactly M rows.  A pass over T live
+ * tokens uses exactly these plans for its projections; laya_pass_plans
+ * reports them with the run of token counts that share them.  out->fused is
+ * 0.  Returns LAYA_E_INVALID for M, N or K below 1, K not a multiple of 64,
+ * an unknown epilogue, or a null out. */
+int laya_plan_gemm(int32_t M, int32_t N, int32_t K, int32_t epilogue, laya_gemm_plan *out);
 
 /* Checks run arguments without touching the device (the host half of
  * laya_encoder_run's validation; the worker's input limits, and the refusal

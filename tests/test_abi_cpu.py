@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol(lib):
     assert declared == set(b.EXPORTS)
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.laya_abi_version() == b.LAYA_ABI_VERSION == 5
+    assert lib.laya_abi_version() == b.LAYA_ABI_VERSION == 6
 
 
 def test_default_config_is_the_model(lib):
@@ -105,24 +105,38 @@ def test_every_accepted_width_plans_launchable_gemms(lib, hidden):
         T = hi + 1
 
 
-def test_plans_follow_the_token_count_in_buckets(lib):
-    """Plans depend on the live token count alone, through fixed buckets whose
-    edges include the K-split thresholds: inside a bucket every count has the
-    same plans (one captured graph serves it), and the splits of the marker
-    layer are those of the full pass."""
+def test_plans_are_the_planners_choice_for_the_exact_token_count(lib):
+    """A pass over T live tokens uses the planner's plans for exactly T
+    (laya_plan_gemm), reported with the maximal run of counts that share them
+    (one captured graph serves such a run); runs split wherever any
+    projection's plan changes, which includes the K-split thresholds; the
+    splits of the marker layer are those of the full pass."""
+    H, F = MODEL["hidden"], MODEL["ffn"]
+    shapes = [(3 * H, H, 2), (H, H, 0), (F, H, 1), (H, F, 0)]
     edges = []
+    prev = None
     T = 1
     while T <= 8192:
         lo, hi, plans = b.pass_plans(MODEL, T)
+        assert lo == T
         for t in sorted({lo, hi, (lo + hi) // 2, min(hi, lo + 1)}):
             assert b.pass_plans(MODEL, t) == (lo, hi, plans), t
+            assert [b.plan_gemm(t, N, K, e) for N, K, e in shapes] == \
+                [(p[0], p[1]) for p in plans[:4]], t
+        assert plans != prev  # maximal runs
+        prev = plans
         _, _, with_markers = b.pass_plans(MODEL, hi, 37)
         assert with_markers[:4] == plans
         assert [p[1] for p in with_markers[4:]] == [plans[0][1], plans[0][1], plans[1][1],
                                                    plans[2][1], plans[3][1]]
         edges.append(hi)
         T = hi + 1
-    assert edges == [64, 256, 512, 1024, 1536, 2048, 3072, 4096, 8192]
+    for split_edge in (64, 256, 1024, 2048):
+        assert split_edge in edges
+    # every count, not only the samples above
+    for t in range(1, 8193, 7):
+        lo, hi, plans = b.pass_plans(MODEL, t)
+        assert [b.plan_gemm(t, N, K, e) for N, K, e in shapes] == [(p[0], p[1]) for p in plans[:4]]
     # the configs' token counts
     assert b.pass_plans(MODEL, 48)[:2] == (1, 64)
     assert b.pass_plans(MODEL, 4050)[:2] == (3073, 4096)
@@ -130,6 +144,15 @@ def test_plans_follow_the_token_count_in_buckets(lib):
         b.pass_plans(MODEL, 0)
     with pytest.raises(b.LayaError):
         b.pass_plans(MODEL, 8193)
+
+
+def test_plan_gemm_arguments(lib):
+    """laya_plan_gemm is host-only and refuses shapes the GEMMs cannot run."""
+    H = MODEL["hidden"]
+    assert b.plan_gemm(48, 3 * H, H, 2) == b.pass_plans(MODEL, 48)[2][0][:2]
+    for bad in ((0, H, H, 0), (1, 0, H, 0), (1, H, 100, 0), (1, H, H, 4), (1, H, H, -1)):
+        with pytest.raises(b.LayaError):
+            b.plan_gemm(*bad)
 
 
 def test_abi_mismatch(lib):

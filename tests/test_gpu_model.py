@@ -261,8 +261,9 @@ def test_reversed_rows_and_padding_are_bitwise_invariant(binding, enc):
 
 def test_one_graph_serves_every_length_pattern(binding, enc):
     """Two length patterns of one (B, S) whose token counts fall in the same
-    plan bucket replay one graph; a third pattern in another bucket gets its
-    own graph; every replay equals its eager run bitwise."""
+    plan segment (a run of counts with equal GEMM plans) replay one graph; a
+    third pattern in another segment gets its own graph; every replay equals
+    its eager run bitwise."""
     wl = WORKLOADS["short_3"]
     b1 = make_batch(MODEL, wl)
     b2 = random_batch(MODEL, wl.B, wl.S, seed=99, len_lo=wl.len_lo)
@@ -274,7 +275,7 @@ def test_one_graph_serves_every_length_pattern(binding, enc):
     g2, _ = _run_bits(binding, enc, b2, 0)
     assert enc.stats()["graphs_cached"] == n_graphs
     assert np.array_equal(g1, e1) and np.array_equal(g2, e2)
-    # 4 rows of 8..16 tokens: T <= 64, another plan bucket of the same (B, S)
+    # 4 rows of 8..16 tokens: T <= 64, another plan segment of the same (B, S)
     b3 = random_batch(MODEL, wl.B, wl.S, seed=98, len_lo=8, len_hi=16)
     assert b3.T <= 64 < b1.T
     e3, _ = _run_bits(binding, enc, b3, binding.RUN_EAGER)

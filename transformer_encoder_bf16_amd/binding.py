@@ -16,7 +16,7 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liblaya_encoder.so")
 
-LAYA_ABI_VERSION = 5
+LAYA_ABI_VERSION = 6
 LAYA_OK = 0
 LAYA_E_INVALID = -1
 LAYA_E_UNSUPPORTED = -2
@@ -44,6 +44,7 @@ ERROR_NAMES = {
 EXPORTS = [
     "laya_abi_version", "laya_config_init", "laya_validate_config", "laya_validate_run_args",
     "laya_pass_plans",
+    "laya_plan_gemm",
     "laya_encoder_create", "laya_encoder_run", "laya_encoder_destroy",
     "laya_encoder_last_error", "laya_last_error", "laya_encoder_layer_output",
     "laya_encoder_weight_digest", "laya_encoder_weight", "laya_encoder_stats",
@@ -132,6 +133,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         "laya_pass_plans": (ctypes.c_int, [ctypes.POINTER(Config), ctypes.c_int32,
                                            ctypes.c_int32, _I32P, _I32P,
                                            ctypes.POINTER(GemmPlanC), ctypes.c_int32, _I32P]),
+        "laya_plan_gemm": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                          ctypes.c_int32, ctypes.POINTER(GemmPlanC)]),
         "laya_validate_run_args": (ctypes.c_int, [ctypes.POINTER(Config), _P, _P, ctypes.c_int32,
                                                   ctypes.c_int32, _P, ctypes.c_int32]),
         "laya_encoder_create": (ctypes.c_int, [ctypes.POINTER(Config), ctypes.c_uint64,
@@ -243,6 +246,13 @@ def pass_plans(cfg: dict, T: int, R: int = 0):
                                   16, ctypes.byref(n)), "laya_pass_plans")
     return lo.value, hi.value, [(out[i].config, out[i].splits, out[i].fused)
                                 for i in range(min(n.value, 16))]
+
+
+def plan_gemm(M: int, N: int, K: int, epilogue: int = 0):
+    """(config, splits) that laya_op_gemm uses for exactly M rows."""
+    out = GemmPlanC()
+    _check(load().laya_plan_gemm(M, N, K, epilogue, ctypes.byref(out)), "laya_plan_gemm")
+    return out.config, out.splits
 
 
 def validate_run_args(cfg: dict, ids, lengths, markers=None) -> int:

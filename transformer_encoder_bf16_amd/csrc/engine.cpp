@@ -23,6 +23,7 @@
 #include <cstdio>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <new>
 #include <string>
 #include <tuple>
@@ -470,26 +471,60 @@ laya::GemmPlan subset_plan(const laya::GemmPlan &full, int R, int N, int K, int 
     return g;
 }
 
-// Plan buckets of the live token count T.  Every GEMM of a pass is planned
-// for the largest count of T's bucket (its grid is sized for that count
-// anyway), so one plan, and one captured graph, serves the whole bucket, and
-// the plan depends on T alone, never on the padded B*S.  The split
-// thresholds of laya::plan_gemm (64, 256, 1024, 2048) are bucket edges; the
-// others halve the span over which one whole-K tile shape must serve.
-constexpr int kPlanEdges[] = {64, 256, 512, 1024, 1536, 2048, 3072, 4096};
-std::pair<int, int> plan_bucket(const laya_config &c, int T) {
-    const int tcap = c.max_batch * c.max_seq;
-    int lo = 1;
-    for (int e : kPlanEdges) {
-        if (T <= e) return {lo, std::min(e, tcap)};
-        lo = e + 1;
+// Plan segments of the live token count T.  The GEMM planner, evaluated at
+// exactly T, is piecewise constant in T; a segment is a maximal run of
+// counts whose projections (QKV, output, up, down, and the head's two) all
+// get the same tile shape and K split.  A pass over T tokens therefore uses
+// the plans for exactly T, one captured graph of a (B, S, R) serves one
+// segment, and the plan depends on T alone, never on the padded B*S.  The
+// segment ends are computed once per model width, FFN width, head variant
+// and token capacity.
+std::vector<int> compute_segment_ends(const laya_config &c) {
+    const int H = c.hidden, F = c.ffn, tcap = c.max_batch * c.max_seq;
+    auto key_at = [&](int T) {
+        std::array<int, 12> k{};
+        const laya::GemmPlan g[6] = {laya::plan_gemm(T, 3 * H, H, 2), laya::plan_gemm(T, H, H, 0),
+                                     laya::plan_gemm(T, F, H, 1), laya::plan_gemm(T, H, F, 0),
+                                     c.dec_head ? laya::plan_gemm(T, 4 * H, H, 3) : laya::GemmPlan{},
+                                     c.dec_head ? laya::plan_gemm(T, H, 4 * H, 0) : laya::GemmPlan{}};
+        for (int i = 0; i < 6; ++i) {
+            k[2 * i] = g[i].config;
+            k[2 * i + 1] = g[i].splits;
+        }
+        return k;
+    };
+    std::vector<int> ends;
+    std::array<int, 12> prev = key_at(1);
+    for (int T = 2; T <= tcap; ++T) {
+        const std::array<int, 12> k = key_at(T);
+        if (k != prev) ends.push_back(T - 1);
+        prev = k;
     }
-    return {lo, tcap};
+    ends.push_back(tcap);
+    return ends;
+}
+
+const std::vector<int> &plan_segment_ends(const laya_config &c) {
+    static std::mutex mu;
+    static std::map<std::array<int, 4>, std::vector<int>> cache;
+    const std::array<int, 4> key = {c.hidden, c.ffn, c.dec_head, c.max_batch * c.max_seq};
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find(key);
+    if (it == cache.end()) it = cache.emplace(key, compute_segment_ends(c)).first;
+    return it->second;
+}
+
+std::pair<int, int> plan_segment(const laya_config &c, int T) {
+    const std::vector<int> &ends = plan_segment_ends(c);
+    const auto it = std::lower_bound(ends.begin(), ends.end(), T);
+    const int hi = it == ends.end() ? ends.back() : *it;
+    const int lo = it == ends.begin() ? 1 : *(it - 1) + 1;
+    return {lo, hi};
 }
 
 PassPlans make_plans(const laya_config &c, int T, int R) {
     const int H = c.hidden, F = c.ffn;
-    const std::pair<int, int> b = plan_bucket(c, T);
+    const std::pair<int, int> b = plan_segment(c, T);
     auto plan = [&](int N, int K, int epi) { return laya::plan_gemm(b.second, N, K, epi); };
     PassPlans p{};
     p.qkv = plan(3 * H, H, 2);
@@ -525,8 +560,8 @@ bool same_full_plans(const PassPlans &a, const PassPlans &b) {
            same_plan(a.down, b.down) && same_plan(a.up4, b.up4) && same_plan(a.down4, b.down4);
 }
 
-// A captured graph serves one plan bucket of its (B, S, R); its GEMM grids
-// are sized for the bucket's largest count (or B*S if smaller).
+// A captured graph serves one plan segment of its (B, S, R); its GEMM grids
+// are sized for the segment's largest count (or B*S if smaller).
 struct PlanRanges {
     std::vector<int16_t> id;                 // [T] for 1 <= T <= tcap
     std::vector<std::pair<int, int>> range;  // [id] -> (first T, last T)
@@ -537,7 +572,7 @@ PlanRanges plan_ranges(const laya_config &c) {
     PlanRanges r;
     r.id.assign((size_t)tcap + 1, 0);
     for (int T = 1; T <= tcap; ++T) {
-        const std::pair<int, int> b = plan_bucket(c, T);
+        const std::pair<int, int> b = plan_segment(c, T);
         if (r.range.empty() || r.range.back() != b) r.range.push_back(b);
         r.id[T] = (int16_t)(r.range.size() - 1);
     }
@@ -980,7 +1015,7 @@ int laya_pass_plans(const laya_config *cfg, int32_t T, int32_t R, int32_t *t_fir
         cap < 0 || (cap > 0 && !out))
         return set_global_error(LAYA_E_INVALID, "laya_pass_plans: bad arguments");
     const PassPlans p = make_plans(*cfg, T, R);
-    const std::pair<int, int> b = plan_bucket(*cfg, T);
+    const std::pair<int, int> b = plan_segment(*cfg, T);
     *t_first = b.first;
     *t_last = b.second;
     std::vector<std::pair<const laya::GemmPlan *, int>> list = {
@@ -1009,6 +1044,16 @@ int laya_pass_plans(const laya_config *cfg, int32_t T, int32_t R, int32_t *t_fir
         ++n;
     }
     *n_out = (int32_t)list.size();
+    return LAYA_OK;
+}
+
+int laya_plan_gemm(int32_t M, int32_t N, int32_t K, int32_t epilogue, laya_gemm_plan *out) {
+    if (M < 1 || N < 1 || K < 1 || K % 64 != 0 || epilogue < 0 || epilogue > 3 || !out)
+        return set_global_error(LAYA_E_INVALID, "laya_plan_gemm: bad arguments");
+    const laya::GemmPlan g = laya::plan_gemm(M, N, K, epilogue);
+    out->config = g.config;
+    out->splits = g.splits;
+    out->fused = 0;
     return LAYA_OK;
 }
 
