@@ -99,6 +99,9 @@ def parse():
     p.add_argument("--plan-check", action="store_true",
                    help="time each projection at the first token count of every plan range, "
                         "with the range's plan and with the plan for exactly that count")
+    p.add_argument("--tile-sweep", action="store_true",
+                   help="time every whole-K tile shape for each projection over a range of "
+                        "token counts (markdown table)")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="only run a plain device-to-device copy of this many MiB three times "
                         "(the reference for scaling HBM byte counters), then exit")
@@ -479,6 +482,82 @@ def plan_check():
             del Ws
 
 
+SWEEP_T = [257, 320, 384, 448, 512, 640, 768, 896, 1024, 1152, 1280, 1344, 1536, 1715, 2048,
+           2400, 2688, 3072, 3500, 4050, 4500, 5000, 5400, 5800, 6144, 7000, 8192]
+SWEEP_CONFIGS = [2, 3, 4, 5, 6, 9]
+
+
+def tile_sweep():
+    """Every whole-K tile shape for each projection of the pass at a range of
+    token counts, timed as back-to-back launches in a captured graph with the
+    weights rotated through copies larger than the MALL.  The shapes give
+    bitwise equal outputs, so the planner may take the fastest; this is the
+    measurement it is checked against.  Prints a markdown table (µs)."""
+    import torch
+    from transformer_encoder_bf16_amd import binding as B
+    from transformer_encoder_bf16_amd.inputs import MODEL
+    torch.cuda.set_device(0)
+    dev = "cuda"
+    H, F = MODEL["hidden"], MODEL["ffn"]
+    gemms = [("qkv", 3 * H, H, 2), ("out", H, H, 0), ("up", F, H, 1), ("down", H, F, 0)]
+    cb, sb = B.rope_table(160000.0, 512, 64)
+    ct = torch.from_numpy(cb.view(np.int16)).to(dev)
+    st = torch.from_numpy(sb.view(np.int16)).to(dev)
+    tmax = max(SWEEP_T)
+    pos = torch.from_numpy((np.arange(tmax) % 512).astype(np.int32)).to(dev)
+    vtok = torch.arange(tmax, dtype=torch.int32, device=dev)
+    vt = torch.empty(H, tmax + 64, dtype=torch.bfloat16, device=dev)
+    names = [CONFIG_NAMES[c] for c in SWEEP_CONFIGS]
+    print("| GEMM | T | " + " | ".join(names) + " | fastest | planner |")
+    print("|---|---|" + "---|" * (len(names) + 2))
+    for name, N, K, epi in gemms:
+        wr = 2 * N if epi == 1 else N
+        A = (torch.randn(tmax, K, device=dev) * 0.5).bfloat16()
+        W = (torch.randn(wr, K, device=dev) * 0.03).bfloat16()
+        C = torch.empty(tmax, N, device=dev, dtype=torch.bfloat16)
+        ncopy = max(8, int(600e6 // (wr * K * 2)))
+        Ws = [W.clone() for _ in range(ncopy)]
+        del W
+        for T in SWEEP_T:
+            us = []
+            for cfg in SWEEP_CONFIGS:
+                def fn():
+                    for w in Ws:
+                        if epi == 2:
+                            B.op_gemm_qkv(A, w, C, T, N, K, pos, ct, st, 2 * H, vt, vtok, 2 * H,
+                                          config=cfg, splits=1)
+                        else:
+                            B.op_gemm_noalloc(A, w, C, T, N, K, epi, cfg, 1)
+                us.append(_graph_launch_us(fn, ncopy))
+            best = SWEEP_CONFIGS[int(np.argmin(us))]
+            plan = B.plan_gemm(T, N, K, epi)
+            print(f"| {name} | {T} | " + " | ".join(f"{u:.2f}" for u in us) +
+                  f" | {CONFIG_NAMES[best]} | {CONFIG_NAMES[plan[0]]}, {plan[1]} |", flush=True)
+        del Ws
+
+
+def _graph_launch_us(fn, n_inner, reps=5):
+    """µs per launch of `fn`'s n_inner launches, captured in one graph."""
+    import torch
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            fn()
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(reps):
+            g.replay()
+        e1.record(s)
+        torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (reps * n_inner)
+
+
 def model_config(args) -> dict:
     """The model, or with --dec-head its biased decision-head variant."""
     from transformer_encoder_bf16_amd.inputs import MODEL
@@ -657,6 +736,9 @@ def main():
         return
     if args.plan_check:
         plan_check()
+        return
+    if args.tile_sweep:
+        tile_sweep()
         return
     from transformer_encoder_bf16_amd import binding
     from transformer_encoder_bf16_amd.inputs import ALL_WORKLOADS, WEIGHT_SEED, make_batch

@@ -1343,11 +1343,38 @@ int gemm_max_splits(int config) {
     return (config <= 3 || config == 7 || config == 8) ? kMaxSplits : 1;
 }
 
+// The fastest whole-K tile shape for the pass's four projections at hidden
+// 1024 and GeGLU width 2624, measured on MI355X over 257..8192 tokens with
+// the weights streamed from HBM (every shape gives the same bits, so only
+// time decides).  Each switch point is where the faster shape's grid would
+// need one more round of the 256 CUs (two workgroups per CU for the 2-stage
+// 128x128 tile).  Other shapes use the estimate below.
+struct MeasuredTiles {
+    int32_t N, K, epilogue, n;
+    int32_t t_last[8];
+    int8_t config[8];
+};
+constexpr MeasuredTiles kMeasuredTiles[] = {
+    // QKV: 128x64 while 24 x T/64 tiles fit one round, then 128x128, the
+    // two-per-CU 128x128, 256x256, and the two-per-CU 128x128 again
+    {3072, 1024, 2, 5, {640, 1280, 2688, 5376, 1 << 30}, {2, 3, 6, 5, 6}},
+    // GeGLU up (64 or 128 output features per tile)
+    {2624, 1024, 1, 8, {384, 768, 1536, 3072, 4736, 6144, 7936, 1 << 30}, {2, 3, 6, 5, 6, 5, 6, 5}},
+    // output projection (whole K above 1024 tokens)
+    {1024, 1024, 0, 3, {2048, 4096, 1 << 30}, {2, 3, 6}},
+    // down projection (whole K above 2048 tokens)
+    {1024, 2624, 0, 2, {4096, 1 << 30}, {3, 6}},
+};
+
 GemmPlan plan_gemm_tiles(int32_t M, int32_t N, int32_t K, int epilogue) {
-    // Tile shape with the least estimated time: the tiles the busiest of the
-    // 256 compute units gets, times the per-tile cost, with each shape's
-    // relative per-CU throughput (measured on the pass's shapes, weights
-    // streamed from HBM).  The 2-stage 128x128 shape fits two workgroups per
+    for (const MeasuredTiles &m : kMeasuredTiles)
+        if (m.N == N && m.K == K && m.epilogue == epilogue)
+            for (int i = 0; i < m.n; ++i)
+                if (M <= m.t_last[i]) return GemmPlan{m.config[i], 1};
+    // Otherwise the tile shape with the least estimated time: the tiles the
+    // busiest of the 256 compute units gets, times the per-tile cost, with
+    // each shape's relative per-CU throughput (measured on the pass's shapes,
+    // weights streamed from HBM).  The 2-stage 128x128 shape fits two workgroups per
     // CU, which hide each other's waits, but its shallow ring cannot cover
     // HBM latency on its own: it pays only where every CU runs a long queue
     // of tiles (at least 4).
@@ -1367,7 +1394,6 @@ GemmPlan plan_gemm_tiles(int32_t M, int32_t N, int32_t K, int epilogue) {
             g.config = cand[i];
         }
     }
-    (void)K;
     return g;
 }
 
