@@ -7,11 +7,15 @@ graph replays on indices already resident in device memory
 (LAYA_RUN_RESIDENT), back to back, bracketed by device synchronisation.
 Reported next to it: per-call p50/p95 (device-resident inputs, synchronised
 per call), the pages' host boundary (pack + upload + replay + sync) p50, the
-first-shape capture cost, the dominant kernel's roofline fraction measured
-with HIP events on its launch stream, and the CPU oracle timed on a bounded
-sample of the same batch.
+first-shape capture cost, the same figures for the 1x48 call, the dominant
+kernel's roofline fraction measured with HIP events on its launch stream
+(back to back, and inside the pass), and the CPU oracle timed on the whole
+benchmarked batch (one warm call, then three timed).
 
-Prints ONE JSON line.  Defaults finish in well under a minute of GPU time.
+Prints ONE JSON line.  Defaults finish in a few minutes (the oracle's three
+full passes take about 30 s of that).  Other modes: --protocol (every
+workload, the pages' recipe), --plan-check and --tile-sweep (GEMM plans),
+--summarize-counters (rocprofv3 --pmc output), --copy-calibration-mib.
 """
 from __future__ import annotations
 

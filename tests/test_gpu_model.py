@@ -122,10 +122,10 @@ def test_workload_matches_oracle(binding, enc, orc, orc64, name):
     _check_batch(binding, enc, orc, orc64, make_batch(MODEL, ALL_WORKLOADS[name]), name)
 
 
-# Batch sizes B*S on either side of where the GEMM plans change (split output
-# and down projections with the fused residual + LayerNorm up to 256 and 1024
-# rows, the split down projection up to 2048, whole K above), one with
-# markers so the marker layer's fused splits run too.
+# Token counts around where the GEMM plans change (split output and down
+# projections with the fused residual + LayerNorm up to 256 and 1024 tokens,
+# the split down projection up to 2048, whole K above, and tile shapes in
+# between), one with markers so the marker layer's fused splits run too.
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("B,S,lo,mpr", [(1, 65, 65, 0), (1, 257, 257, 0), (2, 512, 400, 0),
                                         (5, 205, 150, 3), (9, 228, 180, 0)])
