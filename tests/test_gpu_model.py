@@ -12,7 +12,10 @@ it are checked for every workload:
   change of float32 summation order does that) grows until the two runs'
   rounding noise is decorrelated; the oracle against itself with a float64
   accumulator ends ~1.4% apart.  The GPU must stay within 1.1x of that floor,
-  measured in the same test.  The pages' absolute 0.005 is NOT met end to end
+  measured in the same test.  Up to 512 tokens the floor is the largest
+  distance among three valid orders (float32, float64, and 16-deep K pieces
+  added in order): a single token's distance is a noisy sample, 0.016 to
+  0.027 among those orders at 1 token.  The pages' absolute 0.005 is NOT met end to end
   (final nRMS ~0.014 on every workload); test_end_to_end_absolute_limit
   records that as an expected failure, and every report says whether a
   batch met it.
@@ -20,20 +23,23 @@ it are checked for every workload:
 The embedding must be bit-exact, graph replay must equal the eager run bit
 for bit, repeated runs must be bitwise repeatable, and the invariants the
 pages check hold bitwise: reversed row order, changed padding, and marker
-rows equal to the matching rows of the full pass.
+rows equal to the same rows of the full pass.
 """
 import numpy as np
 import pytest
 
 import oracle
 from tests.gpu_helpers import bits_of, ensure_built, report
-from transformer_encoder_bf16_amd.inputs import (ALL_WORKLOADS, MODEL, TINY, WEIGHT_SEED, WORKLOADS, make_batch,
-                                                 random_batch)
+from transformer_encoder_bf16_amd.inputs import (ALL_WORKLOADS, MODEL, TINY, WEIGHT_SEED, WORKLOADS, Batch,
+                                                 make_batch, random_batch)
 
 pytestmark = pytest.mark.gpu
 
 NRMS_LIMIT = 5e-3
 FLOOR_FACTOR = 1.1
+# Token counts up to which the end-to-end floor also takes the 16-deep K-piece
+# order (its oracle is slower, and above this the single spread is steady)
+SMALL_T = 512
 
 
 @pytest.fixture(scope="module")
@@ -170,7 +176,15 @@ def _check_batch(binding, enc, orc, orc64, batch, name):
     assert np.array_equal(bits_of(caps["emb"]), bits_of(ref_layers[0][1]))  # embedding
     e2e = {n: oracle.nrms(caps[n], y) for n, y in ref_layers}
     ref64 = orc64.forward(batch.ids, batch.lengths, markers=markers)["out"]
-    floor = oracle.nrms(ref64, ref["out"])
+    spreads = {"f32_vs_f64": oracle.nrms(ref64, ref["out"])}
+    if batch.T <= SMALL_T:
+        # one token's 1024 values give a noisy estimate of the spread, so
+        # small calls take the largest distance among three valid orders
+        r16 = oracle.Oracle(MODEL, orc.w, accumulate="chunk16").forward(
+            batch.ids, batch.lengths, markers=markers)["out"]
+        spreads["f32_vs_chunk16"] = oracle.nrms(r16, ref["out"])
+        spreads["chunk16_vs_f64"] = oracle.nrms(r16, ref64)
+    floor = max(spreads.values())
     final = e2e["out"]
     final64 = oracle.nrms(caps["out"], ref64)
     max_abs = float(np.abs(caps["out"] - ref["out"]).max())
@@ -179,7 +193,9 @@ def _check_batch(binding, enc, orc, orc64, batch, name):
           flush=True)
     report("workload", {"workload": name, "T": batch.T, "per_layer_nrms": per_layer,
                         "end_to_end_nrms": e2e, "final_nrms": final, "max_abs": max_abs,
-                        "oracle_f32_vs_f64_final_nrms": floor, "final_nrms_vs_f64_oracle": final64,
+                        "oracle_f32_vs_f64_final_nrms": spreads["f32_vs_f64"],
+                        "oracle_spreads": spreads, "floor": floor,
+                        "final_nrms_vs_f64_oracle": final64,
                         "final_over_floor": final / floor if floor else None,
                         "end_to_end_within_0.005": bool(final <= NRMS_LIMIT)})
     for n, e in per_layer.items():
@@ -204,6 +220,37 @@ def _check_batch(binding, enc, orc, orc64, batch, name):
         e = oracle.nrms(to_f(eager), to_f(full[rows]))
         report("marker_subset_vs_full", {"rows": int(len(rows)), "bitwise": bitwise, "nrms": e})
         assert bitwise, e
+
+
+def _batch_of(B, S, lengths, seed, markers=None):
+    """A batch with the given row lengths (ids drawn as in the workloads)."""
+    b = random_batch(MODEL, B, S, seed=seed)
+    lengths = np.asarray(lengths, np.int32)
+    ids = b.ids.copy()
+    for r in range(B):
+        ids[r, lengths[r]:] = 0
+    mk = None if markers is None else np.asarray(markers, np.int32).reshape(-1, 2)
+    return Batch(ids=ids, lengths=lengths, markers=mk)
+
+
+# Degenerate shapes: a single token, single-token rows beside a full one,
+# many tiny rows, every token a marker, and markers out of order with
+# duplicates (the output follows the list).
+DEGENERATE = {
+    "1x1": (1, 1, [1], None),
+    "3x512_1_512_2": (3, 512, [1, 512, 2], None),
+    "16x8_tiny_rows": (16, 8, [1, 2, 3, 4, 5, 6, 7, 8, 8, 7, 6, 5, 4, 3, 2, 1], None),
+    "2x20_all_markers": (2, 20, [20, 13], [(r, p) for r, n in ((0, 20), (1, 13)) for p in range(n)]),
+    "4x30_markers_unordered": (4, 30, [30, 1, 17, 5],
+                               [(2, 16), (0, 3), (1, 0), (0, 3), (3, 4), (2, 0), (0, 29), (3, 0)]),
+}
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", list(DEGENERATE))
+def test_degenerate_shapes_match_oracle(binding, enc, orc, orc64, name):
+    B, S, lengths, markers = DEGENERATE[name]
+    _check_batch(binding, enc, orc, orc64, _batch_of(B, S, lengths, 7 + B * S, markers), name)
 
 
 @pytest.mark.xfail(strict=True, reason=(
