@@ -15,7 +15,8 @@ benchmarked batch (one warm call, then three timed).
 Prints ONE JSON line.  Defaults finish in a few minutes (the oracle's three
 full passes take about 30 s of that).  Other modes: --protocol (every
 workload, the pages' recipe), --plan-check and --tile-sweep (GEMM plans),
---summarize-counters (rocprofv3 --pmc output), --copy-calibration-mib.
+--summarize-counters (rocprofv3 --pmc output), --copy-calibration-mib,
+--chip-peaks (the chip probe).
 """
 from __future__ import annotations
 
@@ -106,6 +107,9 @@ def parse():
     p.add_argument("--tile-sweep", action="store_true",
                    help="time every whole-K tile shape for each projection over a range of "
                         "token counts (markdown table)")
+    p.add_argument("--chip-peaks", action="store_true",
+                   help="run the chip probe (matrix-core issue rate, LDS read bandwidth, one "
+                        "workgroup's HBM stream) and print its figures")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="only run a plain device-to-device copy of this many MiB three times "
                         "(the reference for scaling HBM byte counters), then exit")
@@ -401,6 +405,41 @@ def protocol(args):
                                         "calls_per_s": v["graph_host"]["calls_per_s"],
                                         "roofline_ms": v["roofline_time_ms"]}
                                     for k, v in results["workloads"].items()}}), flush=True)
+
+
+def chip_peaks():
+    """Run the chip probe built next to the library (a child process: this
+    process touches no GPU first) and print its figures as markdown."""
+    import subprocess
+    from transformer_encoder_bf16_amd import build_lib
+    if not os.path.exists(build_lib.PROBE):
+        build_lib.build()
+    r = subprocess.run([build_lib.PROBE], capture_output=True, text=True, timeout=300)
+    if r.returncode != 0:
+        print(r.stdout, r.stderr, file=sys.stderr)
+        sys.exit(r.returncode)
+    recs = [json.loads(line) for line in r.stdout.splitlines() if line.startswith("{")]
+    dev = next(x for x in recs if x["probe"] == "device")
+    print(f"Device: {dev['name']} ({dev['arch']}), {dev['cus']} CUs.\n")
+    print("| Matrix cores (4 independent 32x32x16 BF16 chains per wave) | µs | TFLOP/s | of 2500 |")
+    print("|---|---|---|---|")
+    for x in recs:
+        if x["probe"] == "mfma_bf16_32x32x16":
+            print(f"| {x['workgroups_per_cu']} four-wave workgroups per CU | {x['us']} | {x['tflops']} | "
+                  f"{x['tflops'] / PEAK_BF16_TFLOPS:.2f} |")
+    print("\n| LDS reads (ds_read_b128, no bank conflicts) | µs | TB/s (chip) | B/clk per CU at 2.1 GHz |")
+    print("|---|---|---|---|")
+    for x in recs:
+        if x["probe"] == "lds_read_b128":
+            print(f"| {x['workgroups_per_cu']} workgroups of 512 threads per CU | {x['us']} | {x['tb_per_s']} | "
+                  f"{x['bytes_per_clk_per_cu_at_2.1ghz']} |")
+    print("\n| One workgroup streaming HBM -> LDS (16 workgroups) | KB per workgroup | empty launch µs | µs, 8 waves "
+          "| µs, 16 waves | GB/s per workgroup above the empty launch, 8 / 16 waves |")
+    print("|---|---|---|---|---|---|")
+    for x in recs:
+        if x["probe"] == "one_workgroup_stream":
+            print(f"| | {x['kb_per_workgroup']} | {x['empty_launch_us']} | {x['us_8_waves']} | {x['us_16_waves']} | "
+                  f"{x['gb_per_s_per_workgroup_8_waves']} / {x['gb_per_s_per_workgroup_16_waves']} |")
 
 
 CONFIG_NAMES = ["XS", "XSG", "S", "M", "L", "XL", "M2", "XS2", "XSG2", "PP"]
@@ -725,6 +764,9 @@ def main():
     if args.summarize_counters:
         summarize_counters(args.summarize_counters, args.copy_fetch_per_byte,
                            args.copy_write_per_byte)
+        return
+    if args.chip_peaks:
+        chip_peaks()
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the pass has no "

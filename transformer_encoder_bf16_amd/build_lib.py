@@ -17,6 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "liblaya_encoder.so")
+PROBE = os.path.join(HERE, "chip_probe")
 
 SOURCES = ["k_elementwise.hip", "k_gemm.hip", "k_attention.hip", "engine.cpp", "queue.cpp"]
 
@@ -61,6 +62,13 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    # the chip probe (bench.py --chip-peaks): a program of its own
+    tmp = PROBE + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, *FLAGS, os.path.join(CSRC, "chip_probe.hip"), "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for chip_probe.hip:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, PROBE)
     if verbose:
         print("built", LIB)
     return LIB
