@@ -450,7 +450,7 @@ int laya_op_layernorm(void *stream, void *x, const void *r, void *n, const float
  * 256x256 with two wave groups alternating between multiplying and loading;
  * weight rows x tokens) with
  * `splits` K ranges forces one (split K only on shapes 0..3, 7 and 8; GeGLU
- * not on shapes 0 and 7).  Each output is the sum, in
+ * not on shape 0).  Each output is the sum, in
  * order, of one MFMA chain per K range, so results depend only on `splits`.
  * With splits > 1 the call allocates its scratch and synchronises the
  * stream.
