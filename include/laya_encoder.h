@@ -236,12 +236,12 @@ int laya_encoder_create(const laya_config *cfg, uint64_t weight_seed, int device
  * queries, attention, output projection and FFN only for the R marker rows;
  * out->hidden is [R][hidden] in marker-list order (duplicates allowed).
  *
- * Without LAYA_RUN_EAGER the launch sequence for the shape key (B, S, R and
- * the LAYA_RUN_ROPE_STANDALONE choice) is
- * captured once into a hipGraph (two eager warmups, then capture; the cost is
- * reported by laya_encoder_stats) and replayed on `stream` afterwards; the
- * kernels read T and the row layout from device memory, so one graph serves
- * every length pattern of its key.  Eager and graph runs give bitwise equal
+ * Without LAYA_RUN_EAGER the launch sequence for the shape key (B, S, R, the
+ * RoPE variant flag, and the run of live token counts T whose GEMM plans are
+ * equal, see laya_pass_plans) is captured once into a hipGraph (two eager
+ * warmups, then capture; the cost is reported by laya_encoder_stats) and
+ * replayed on `stream` afterwards; the kernels read T and the row layout
+ * from device memory, so one graph serves every length pattern of its key.  Eager and graph runs give bitwise equal
  * outputs.  B == 0 returns LAYA_OK with out->rows == 0 and launches nothing.
  *
  * With LAYA_RUN_RESIDENT the pass reruns on the device copy of the previous
