@@ -488,13 +488,17 @@ int laya_op_gemm_noalloc(void *stream, const void *A, int32_t lda, const void *W
  * Rust/CUDA Laya inference #66", section Implementation priorities):
  *   f = bf16(A W^T) (with a bias: bf16(bf16(A W^T) + bias)),
  *   x <- bf16(x + f),  n <- bf16((x - mean) / sqrt(var + eps) * gamma),
- * computed with `splits` >= 2 K ranges on tile shape `config` (0..3, 7, 8),
- * the split's reduce launch doing the residual and the LayerNorm: bitwise
- * laya_op_gemm(config, splits) into r followed by laya_op_layernorm(x, r, n).
- * A device BF16 [M][lda], W device BF16 [N][ldw] (N <= 1024, a multiple of
- * 64), x device BF16 [M][N] (updated in place), n device BF16 [M][N] (not
- * aliasing x), gamma device float32 [N], bias device BF16 [N] 16-byte aligned
- * or NULL.  The call allocates its scratch and synchronises the stream. */
+ * bitwise laya_op_gemm(config, splits) into r followed by
+ * laya_op_layernorm(x, r, n).  With `splits` >= 2 K ranges on tile shape
+ * `config` (0..3, 7, 8) the split's reduce launch does the residual and the
+ * LayerNorm; with splits == 1 (whole K, any tile shape but 9) the GEMM's
+ * store does the residual add into x and a LayerNorm launch reading x alone
+ * follows.  A device BF16 [M][lda], W device BF16 [N][ldw] (N <= 1024, a
+ * multiple of 64), x device BF16 [M][N] (updated in place, 16-byte aligned),
+ * n device BF16 [M][N] (not aliasing x), gamma device float32 [N], bias
+ * device BF16 [N] 16-byte aligned or NULL.  The call allocates its scratch
+ * (a K split only) and synchronises the stream; LAYA_E_INVALID for any other
+ * argument. */
 int laya_op_gemm_layernorm(void *stream, const void *A, int32_t lda, const void *W, int32_t ldw,
                            void *x, void *n, const float *gamma, int32_t M, int32_t N, int32_t K,
                            int32_t config, int32_t splits, const void *bias, float eps);

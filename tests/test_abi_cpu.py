@@ -232,15 +232,16 @@ def test_queue_and_health_reject_null_handles(lib):
 
 
 def test_gemm_layernorm_rejects_bad_arguments(lib):
-    """The fused split projection + LayerNorm validates on the host before any
-    device call (dummy aligned addresses are never dereferenced)."""
+    """The fused projection + residual + LayerNorm validates on the host before
+    any device call (dummy aligned addresses are never dereferenced)."""
     P = ctypes.c_void_p
     A, W, x, n, g = P(0x1000), P(0x2000), P(0x3000), P(0x4000), P(0x5000)
 
     def call(M=48, N=1024, K=1024, config=7, splits=4, bias=None, x_=x, n_=n, eps=1e-5):
         return lib.laya_op_gemm_layernorm(None, A, K, W, K, x_, n_, g, M, N, K, config, splits,
                                           bias, eps)
-    assert call(splits=1) == b.LAYA_E_INVALID          # needs a K split
+    assert call(config=9, splits=1) == b.LAYA_E_INVALID  # whole K: not the ping-pong shape
+    assert call(config=10, splits=1) == b.LAYA_E_INVALID  # no such shape
     assert call(splits=17) == b.LAYA_E_INVALID         # more ranges than 64-wide K pieces
     assert call(N=2048) == b.LAYA_E_INVALID            # one wave per row: N <= 1024
     assert call(config=4) == b.LAYA_E_INVALID          # whole-K-only tile shape

@@ -407,10 +407,17 @@ def test_gemm_every_tile_shape_and_split(B, M, N, K, epi):
 @pytest.mark.parametrize("M,N,K,cfg,splits,bias", [
     (48, 1024, 1024, 7, 4, False), (48, 1024, 2624, 7, 8, False), (64, 1024, 2624, 0, 8, False),
     (200, 1024, 2624, 2, 4, False), (97, 1024, 4096, 8, 8, True), (33, 512, 1024, 3, 2, True),
-    (1, 1024, 1024, 1, 3, False)])
+    (1, 1024, 1024, 1, 3, False),
+    # whole K: the residual add in the GEMM's store, every one-kernel tile shape
+    (300, 1024, 1024, 3, 1, False), (300, 1024, 2624, 6, 1, False), (130, 512, 1024, 2, 1, True),
+    (257, 1024, 1024, 5, 1, False), (100, 1024, 1024, 4, 1, True), (65, 1024, 1024, 0, 1, False),
+    (48, 1024, 1024, 7, 1, False), (20, 1024, 1024, 8, 1, True), (5, 1024, 1024, 1, 1, False),
+    (517, 1024, 2624, 6, 1, True)])
 def test_gemm_layernorm_equals_gemm_then_layernorm(B, M, N, K, cfg, splits, bias):
-    """The split reduce with the residual add and LayerNorm fused in is bitwise
-    the split GEMM followed by the LayerNorm kernel, and matches the oracle."""
+    """The projection with the residual add and LayerNorm fused in (in the split's
+    reduce launch, or in the whole-K GEMM's store followed by a LayerNorm of x
+    alone) is bitwise the GEMM followed by the LayerNorm kernel, and matches the
+    oracle."""
     import torch
     a_h = oracle.bf16_round(random_normal((M, K), 11 * M + K))
     w_h = oracle.bf16_round(random_normal((N, K), 5 * N + K, 0.03))
@@ -419,7 +426,7 @@ def test_gemm_layernorm_equals_gemm_then_layernorm(B, M, N, K, cfg, splits, bias
     b_h = oracle.bf16_round(random_normal((N,), N + 7, 0.5)) if bias else None
     a, w, g = to_dev(a_h), to_dev(w_h), torch.from_numpy(g_h).cuda()
     bb = to_dev(b_h) if bias else None
-    # reference: split GEMM into r, then the LayerNorm kernel on a copy of x
+    # reference: the GEMM into r, then the LayerNorm kernel on a copy of x
     r = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
     B.op_gemm(a, w, r, M, N, K, 0, config=cfg, splits=splits, bias=bb)
     x_ref, n_ref = to_dev(x_h), torch.empty((M, N), dtype=torch.bfloat16, device="cuda")

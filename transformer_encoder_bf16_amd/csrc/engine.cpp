@@ -357,7 +357,7 @@ struct laya_encoder {
     size_t ws_bytes = 0;
     int64_t tcap = 0;
     bf16_t *xa = nullptr, *xb = nullptr, *nrm = nullptr, *qkv = nullptr, *att = nullptr,
-           *proj = nullptr, *hid = nullptr, *out = nullptr;
+           *hid = nullptr, *out = nullptr;
     bf16_t *x_sub = nullptr, *n_sub = nullptr, *q_sub = nullptr;
     bf16_t *vt = nullptr;  // transposed V [n_heads*64][ldvt], rows start 64-aligned
     int32_t ldvt = 0;
@@ -741,7 +741,7 @@ int record(laya_encoder *enc, hipStream_t s, const RunShape &rs, Profiler *prof 
     auto gemm_by = [&](double M, double Nw, double N, double K) {
         return b2 * (M * K + Nw * K + M * N);
     };
-    const double ln_res_by = 4 * T * H * b2, ln_by = 2 * T * H * b2;
+    const double ln_by = 2 * T * H * b2;
     // a projection onto H whose split reduce also does the residual and the
     // LayerNorm: reads A, W and x, writes x and n (f is never stored)
     auto proj_ln_by = [&](double M, double K) { return b2 * (M * K + H * K + 3 * M * H); };
@@ -758,8 +758,8 @@ int record(laya_encoder *enc, hipStream_t s, const RunShape &rs, Profiler *prof 
     L_OP(OP_GATHER, 0, 2 * T * H * b2 + 4 * T,
          laya::launch_gather(s, enc->emb, ids, T_dev, Tmax, H, xr));
     C_CHK(cap("emb", xr, rs.T));
-    bool pending = false;   // the down projection of the previous layer waits in proj
-    bool ln_ready = false;  // ... or was fused with the residual and the next LayerNorm
+    bool prev = false;      // xr holds the previous layer's output (residual added)
+    bool ln_ready = false;  // ... and its down projection's reduce made the next LayerNorm
     char name[32];
     for (int L = 0; L < NL; ++L) {
         const bool is_enc = L < c.n_enc_layers;
@@ -778,11 +778,11 @@ int record(laya_encoder *enc, hipStream_t s, const RunShape &rs, Profiler *prof 
         const bool head = c.dec_head && !is_enc;
         const bf16_t *Bqkv = enc->bqkv[L], *Bo = enc->bo[L], *B1 = enc->b1[L], *B2 = enc->b2[L];
         const int FW = head ? 4 * H : F;  // width of the FFN's inner activation
-        // up + activation and down projection into enc->proj (M rows, T_dev or
-        // Mmax rows when T_dev is null)
-        // With a K split, the down projection's reduce launch also does the
-        // residual add into x_res and the LayerNorm that follows it, into
-        // n_next (*fused set); otherwise f is left in enc->proj.
+        // up + activation and down projection (M rows, T_dev or Mmax rows when
+        // T_dev is null), with the residual add into x_res.  With a K split
+        // the down projection's reduce launch also does the LayerNorm that
+        // follows, into n_next (*fused set); with whole K the GEMM's store
+        // adds f to x_res and the LayerNorm is left to the caller.
         auto ffn = [&](const bf16_t *n_in, const int32_t *M_dev, int Mmax, double Mf,
                        const laya::GemmPlan &pu, const laya::GemmPlan &pd, bf16_t *x_res,
                        bf16_t *n_next, bool *fused) -> int {
@@ -803,9 +803,9 @@ int record(laya_encoder *enc, hipStream_t s, const RunShape &rs, Profiler *prof 
                      laya::launch_gemm_layernorm(s, enc->hid, FW, Wo2, FW, M_dev, Mmax, H, FW,
                                                  pd, gp, Bd, x_res, n_next, g1, c.ln_eps));
             else
-                L_OP(OP_DOWN, gemm_fl(Mf, H, FW), gemm_by(Mf, H, H, FW) + bias_by,
-                     laya::launch_gemm(s, enc->hid, FW, Wo2, FW, enc->proj, H, M_dev, Mmax, H,
-                                       FW, 0, pd, gp, nullptr, Bd));
+                L_OP(OP_DOWN, gemm_fl(Mf, H, FW), gemm_by(Mf, H, H, FW) + bias_by + Mf * H * b2,
+                     laya::launch_gemm(s, enc->hid, FW, Wo2, FW, x_res, H, M_dev, Mmax, H, FW, 0,
+                                       pd, gp, nullptr, Bd, x_res));
             return LAYA_OK;
         };
         // output projection followed by x += a, n_out = LN(x)
@@ -816,28 +816,29 @@ int record(laya_encoder *enc, hipStream_t s, const RunShape &rs, Profiler *prof 
                      laya::launch_gemm_layernorm(s, enc->att, H, Wo, H, M_dev, Mmax, H, H, po, gp,
                                                  Bo, x_res, n_out, g1, c.ln_eps));
             } else {
-                L_OP(OP_OUT_PROJ, gemm_fl(Mf, H, H), gemm_by(Mf, H, H, H),
-                     laya::launch_gemm(s, enc->att, H, Wo, H, enc->proj, H, M_dev, Mmax, H, H, 0,
-                                       po, gp, nullptr, Bo));
-                L_OP(OP_LAYERNORM, 0, 4 * Mf * H * b2,
-                     laya::launch_layernorm(s, x_res, enc->proj, n_out, g1, M_dev, Mmax, H,
+                // the GEMM's store adds the projection to x_res; the LayerNorm
+                // then reads x_res alone
+                L_OP(OP_OUT_PROJ, gemm_fl(Mf, H, H), gemm_by(Mf, H, H, H) + Mf * H * b2,
+                     laya::launch_gemm(s, enc->att, H, Wo, H, x_res, H, M_dev, Mmax, H, H, 0, po,
+                                       gp, nullptr, Bo, x_res));
+                L_OP(OP_LAYERNORM, 0, 2 * Mf * H * b2,
+                     laya::launch_layernorm(s, x_res, nullptr, n_out, g1, M_dev, Mmax, H,
                                             c.ln_eps));
             }
             return LAYA_OK;
         };
 
-        // attention sublayer: n = LN(x [+ f of the previous layer]), unless the
-        // previous layer's down projection already produced it
+        // attention sublayer: n = LN(x), unless the previous layer's down
+        // projection already produced it
         if (!ln_ready)
-            L_OP(OP_LAYERNORM, 0, pending ? ln_res_by : ln_by,
-                 laya::launch_layernorm(s, xr, pending ? enc->proj : nullptr, enc->nrm, g1,
-                                        T_dev, Tmax, H, c.ln_eps));
-        if (pending || ln_ready) {
+            L_OP(OP_LAYERNORM, 0, ln_by,
+                 laya::launch_layernorm(s, xr, nullptr, enc->nrm, g1, T_dev, Tmax, H, c.ln_eps));
+        if (prev) {
             std::snprintf(name, sizeof name, (L - 1) < c.n_enc_layers ? "enc%02d" : "dec%d",
                           (L - 1) < c.n_enc_layers ? L - 1 : L - 1 - c.n_enc_layers);
             C_CHK(cap(name, xr, rs.T));
         }
-        pending = ln_ready = false;
+        prev = ln_ready = false;
         if (!subset) {
             // Q, K rotated in the epilogue (or by the RoPE kernel after it); V
             // stored transposed for attention
@@ -862,19 +863,19 @@ int record(laya_encoder *enc, hipStream_t s, const RunShape &rs, Profiler *prof 
             bool fused = false;
             C_CHK(ffn(enc->nrm, T_dev, Mg, T, head ? plans.up4 : plans.up,
                       head ? plans.down4 : plans.down, xr, n_next, &fused));
-            pending = !fused;
+            prev = true;
             ln_ready = fused;
             if (L == c.n_enc_layers - 1) {
-                // x += f; the encoder's final LayerNorm output becomes the decision stream
+                // the encoder's final LayerNorm output becomes the decision stream
                 if (!fused)
-                    L_OP(OP_LAYERNORM, 0, ln_res_by,
-                         laya::launch_layernorm(s, xr, enc->proj, xalt, g1, T_dev, Tmax, H,
+                    L_OP(OP_LAYERNORM, 0, ln_by,
+                         laya::launch_layernorm(s, xr, nullptr, xalt, g1, T_dev, Tmax, H,
                                                 c.ln_eps));
                 std::snprintf(name, sizeof name, "enc%02d", L);
                 C_CHK(cap(name, xr, rs.T));
                 C_CHK(cap("enc_final", xalt, rs.T));
                 std::swap(xr, xalt);
-                pending = ln_ready = false;
+                prev = ln_ready = false;
             }
         } else {
             // keys/values for every token, queries only for the marker rows
@@ -911,9 +912,9 @@ int record(laya_encoder *enc, hipStream_t s, const RunShape &rs, Profiler *prof 
             C_CHK(ffn(enc->n_sub, nullptr, Ri, R, head ? plans.up4_sub : plans.up_sub,
                       head ? plans.down4_sub : plans.down_sub, enc->x_sub, enc->out, &fused));
             if (!fused)
-                L_OP(OP_LAYERNORM, 0, 4 * R * H * b2,
-                     laya::launch_layernorm(s, enc->x_sub, enc->proj, enc->out, g1, nullptr, Ri,
-                                            H, c.ln_eps));
+                L_OP(OP_LAYERNORM, 0, 2 * R * H * b2,
+                     laya::launch_layernorm(s, enc->x_sub, nullptr, enc->out, g1, nullptr, Ri, H,
+                                            c.ln_eps));
             std::snprintf(name, sizeof name, L < c.n_enc_layers ? "enc%02d" : "dec%d",
                           L < c.n_enc_layers ? L : L - c.n_enc_layers);
             C_CHK(cap(name, enc->x_sub, Ri));
@@ -924,10 +925,10 @@ int record(laya_encoder *enc, hipStream_t s, const RunShape &rs, Profiler *prof 
     // closing LayerNorm over the decision stream (already done by a fused down
     // projection)
     if (!ln_ready)
-        L_OP(OP_LAYERNORM, 0, pending ? ln_res_by : ln_by,
-             laya::launch_layernorm(s, xr, pending ? enc->proj : nullptr, enc->out,
-                                    enc->gamma_ones, T_dev, Tmax, H, c.ln_eps));
-    if (pending || ln_ready) {
+        L_OP(OP_LAYERNORM, 0, ln_by,
+             laya::launch_layernorm(s, xr, nullptr, enc->out, enc->gamma_ones, T_dev, Tmax, H,
+                                    c.ln_eps));
+    if (prev) {
         std::snprintf(name, sizeof name, (NL - 1) < c.n_enc_layers ? "enc%02d" : "dec%d",
                       (NL - 1) < c.n_enc_layers ? NL - 1 : NL - 1 - c.n_enc_layers);
         C_CHK(cap(name, xr, rs.T));
@@ -1190,7 +1191,7 @@ int laya_encoder_create(const laya_config *cfg, uint64_t seed, int device, laya_
     std::vector<std::pair<bf16_t **, size_t>> bufs = {
         {&enc->xa, (size_t)tcap * H},      {&enc->xb, (size_t)tcap * H},
         {&enc->nrm, (size_t)tcap * H},     {&enc->qkv, (size_t)tcap * 3 * H},
-        {&enc->att, (size_t)tcap * H},     {&enc->proj, (size_t)tcap * H},
+        {&enc->att, (size_t)tcap * H},
         {&enc->hid, (size_t)tcap * (c.dec_head ? std::max(F, 4 * H) : F)},
         {&enc->out, (size_t)tcap * H},
         {&enc->x_sub, (size_t)rcap * H},   {&enc->n_sub, (size_t)rcap * H},
@@ -1731,24 +1732,27 @@ int laya_op_gemm_noalloc(void *stream, const void *A, int32_t lda, const void *W
 int laya_op_gemm_layernorm(void *stream, const void *A, int32_t lda, const void *W, int32_t ldw,
                            void *x, void *n, const float *gamma, int32_t M, int32_t N, int32_t K,
                            int32_t config, int32_t splits, const void *bias, float eps) {
+    // whole K (splits == 1): any one-kernel tile shape; a K split: the small shapes
+    const bool whole = splits == 1;
     if (!gemm_args_ok(A, lda, W, ldw, x, N, M, N, K, config) || N > 1024 || !(eps > 0.f) ||
-        config < 0 || (config > 3 && config < 7) || splits < 2 || splits > K / 64 ||
-        splits > laya::gemm_max_splits(config) || (M > 0 && (!n || !gamma || n == x)) ||
-        reinterpret_cast<uintptr_t>(bias) % 16 != 0)
+        config < 0 ||
+        (whole ? config >= laya::kGemmConfigs - 1
+               : ((config > 3 && config < 7) || splits < 2 || splits > K / 64 ||
+                  splits > laya::gemm_max_splits(config))) ||
+        (M > 0 && (!n || !gamma || n == x)) || reinterpret_cast<uintptr_t>(bias) % 16 != 0)
         return set_global_error(LAYA_E_INVALID, "laya_op_gemm_layernorm: bad arguments");
     if (M == 0) return LAYA_OK;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const laya::GemmPlan plan{config, splits};
-    const size_t pb = laya::gemm_workspace_bytes(plan, M, N, 0);
     void *scratch = nullptr;
-    if (hipMalloc(&scratch, pb) != hipSuccess)
+    if (!whole && hipMalloc(&scratch, laya::gemm_workspace_bytes(plan, M, N, 0)) != hipSuccess)
         return set_global_error(LAYA_E_NOMEM, "laya_op_gemm_layernorm: scratch hipMalloc failed");
     hipError_t e = laya::launch_gemm_layernorm(
         s, static_cast<const bf16_t *>(A), lda, static_cast<const bf16_t *>(W), ldw, nullptr, M, N,
         K, plan, static_cast<float *>(scratch), static_cast<const bf16_t *>(bias),
         static_cast<bf16_t *>(x), static_cast<bf16_t *>(n), gamma, eps);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
-    hipFree(scratch);
+    if (scratch) hipFree(scratch);
     if (e != hipSuccess)
         return set_global_error(LAYA_E_DEVICE,
                                 std::string("laya_op_gemm_layernorm: ") + hipGetErrorString(e));

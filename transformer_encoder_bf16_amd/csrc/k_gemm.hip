@@ -58,6 +58,7 @@
 // takes GELU of that BF16 value, h = bf16(GELU(y)).
 #include <algorithm>
 #include <mutex>
+#include <type_traits>
 
 #include "kernels.h"
 
@@ -237,6 +238,8 @@ struct GemmParams {
     QkvEpilogue qe;      // epilogue 2 only
     const bf16_t *bias;  // [N] or null (epilogues 0 and 2; required by 3)
     int32_t split2d;     // whole K: 1 if the grid is padded for the 2-D XCD split
+    const bf16_t *res;   // whole K, epilogues 0 and 4, or null: C = bf16(res + y), with
+                         // C's row stride (the residual add; res may be C itself)
 };
 
 // MODE 0: whole K, C written.  MODE 1: one K range per blockIdx.z, its
@@ -570,6 +573,41 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
         bv[2] = bf16lo(w[1]);
         bv[3] = bf16hi(w[1]);
     };
+    // QKV tiles of whole heads: each lane's rotation-table entries (they
+    // depend only on the token's position and the pair index, so one load
+    // serves all of the wave's heads) and V^T columns, all loaded before any
+    // is used, so the epilogue waits on memory once.
+    constexpr bool QKV_FULL = EPI == 2 && !HALF;
+    [[maybe_unused]] u32x2_t rcos[QKV_FULL ? FB : 1][4], rsin[QKV_FULL ? FB : 1][4];
+    [[maybe_unused]] int32_t vtcol[QKV_FULL ? FB : 1];
+    if constexpr (QKV_FULL) {
+        const QkvEpilogue &q = p.qe;
+        bool rope = false, vt = false;  // the same for every lane of the wave
+#pragma unroll
+        for (int a = 0; a < FA; a += 2) {
+            const int32_t f0 = n0 + wrow[a];
+            if (f0 < N) {
+                rope = rope || f0 < q.rope_cols;
+                vt = vt || (f0 >= q.vt_col0 && f0 >= q.rope_cols);
+            }
+        }
+        if (compute)
+#pragma unroll
+            for (int b = 0; b < FB; ++b) {
+                const int32_t tok = t0 + wc * G::RT + 32 * b + l32;
+                const int32_t tc = tok < M ? tok : M - 1;
+                if (rope) {
+                    const uint32_t ps = (uint32_t)q.pos[tc] * 32u;
+#pragma unroll
+                    for (int g4 = 0; g4 < 4; ++g4) {
+                        const int j = 8 * g4 + 4 * lhi;
+                        rcos[b][g4] = *reinterpret_cast<const u32x2_t *>(q.cos_tab + ps + j);
+                        rsin[b][g4] = *reinterpret_cast<const u32x2_t *>(q.sin_tab + ps + j);
+                    }
+                }
+                if (vt) vtcol[b] = q.vt_tok[tc];
+            }
+    }
     if (compute)
 #pragma unroll
     for (int b = 0; b < FB; ++b) {
@@ -675,79 +713,89 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
         } else if constexpr (EPI == 2) {
             // Fragments a (dims 0..31 of a head) and a+1 (dims 32..63) sit in
             // the same lanes, so the rotation pairs (i, i+32) are in registers.
+            // The table entries and V^T columns come preloaded (below the
+            // main loop); the bias, present only in the head variant, is a
+            // compile-time case, so the encoder's tiles carry no per-element
+            // branch and no load between their stores.
             const QkvEpilogue &q = p.qe;
+            auto tile = [&](auto bias_tag) {
+                constexpr bool HB = decltype(bias_tag)::value;
 #pragma unroll
-            for (int a = 0; a < FA; a += 2) {
-                const int32_t f0 = n0 + wrow[a];  // first column of the head
-                if (f0 >= N) continue;
-                if (f0 < q.rope_cols) {
-                    const uint32_t ps = (uint32_t)q.pos[tok < M ? tok : M - 1] * 32u;
+                for (int a = 0; a < FA; a += 2) {
+                    const int32_t f0 = n0 + wrow[a];  // first column of the head
+                    if (f0 >= N) continue;
+                    if (f0 < q.rope_cols) {
 #pragma unroll
-                    for (int g4 = 0; g4 < 4; ++g4) {
-                        const int j = 8 * g4 + 4 * lhi;  // pair index of element 4*g4
-                        const u32x2_t cv = *reinterpret_cast<const u32x2_t *>(q.cos_tab + ps + j);
-                        const u32x2_t sv = *reinterpret_cast<const u32x2_t *>(q.sin_tab + ps + j);
-                        float xo[4], yo[4], bx[4] = {0, 0, 0, 0}, by[4] = {0, 0, 0, 0};
-                        if (p.bias) {
-                            bias4(f0 + j, bx);
-                            bias4(f0 + 32 + j, by);
-                        }
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            float x = bf16r(acc[a][b][4 * g4 + e]);
-                            float y = bf16r(acc[a + 1][b][4 * g4 + e]);
-                            if (p.bias) {
-                                x = bf16r(x + bx[e]);
-                                y = bf16r(y + by[e]);
+                        for (int g4 = 0; g4 < 4; ++g4) {
+                            const int j = 8 * g4 + 4 * lhi;  // pair index of element 4*g4
+                            const u32x2_t cv = rcos[b][g4], sv = rsin[b][g4];
+                            float xo[4], yo[4], bx[4] = {0, 0, 0, 0}, by[4] = {0, 0, 0, 0};
+                            if constexpr (HB) {
+                                bias4(f0 + j, bx);
+                                bias4(f0 + 32 + j, by);
                             }
-                            const float c = (e & 1) ? bf16hi(cv[e >> 1]) : bf16lo(cv[e >> 1]);
-                            const float sn = (e & 1) ? bf16hi(sv[e >> 1]) : bf16lo(sv[e >> 1]);
-                            // both products of BF16 values are exact in float32
-                            xo[e] = fmaf(x, c, -(y * sn));
-                            yo[e] = fmaf(y, c, x * sn);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                float x = bf16r(acc[a][b][4 * g4 + e]);
+                                float y = bf16r(acc[a + 1][b][4 * g4 + e]);
+                                if constexpr (HB) {
+                                    x = bf16r(x + bx[e]);
+                                    y = bf16r(y + by[e]);
+                                }
+                                const float c = (e & 1) ? bf16hi(cv[e >> 1]) : bf16lo(cv[e >> 1]);
+                                const float sn = (e & 1) ? bf16hi(sv[e >> 1]) : bf16lo(sv[e >> 1]);
+                                // both products of BF16 values are exact in float32
+                                xo[e] = fmaf(x, c, -(y * sn));
+                                yo[e] = fmaf(y, c, x * sn);
+                            }
+                            put4(tl, wrow[a] + j, pack_bf16x2(xo[0], xo[1]),
+                                 pack_bf16x2(xo[2], xo[3]));
+                            put4(tl, wrow[a] + 32 + j, pack_bf16x2(yo[0], yo[1]),
+                                 pack_bf16x2(yo[2], yo[3]));
                         }
-                        put4(tl, wrow[a] + j, pack_bf16x2(xo[0], xo[1]), pack_bf16x2(xo[2], xo[3]));
-                        put4(tl, wrow[a] + 32 + j, pack_bf16x2(yo[0], yo[1]),
-                             pack_bf16x2(yo[2], yo[3]));
-                    }
-                } else if (f0 >= q.vt_col0) {
-                    // transposed: row f - vt_col0 of vt holds this token at column
-                    // vt_tok[tok] (32 lanes write 32 consecutive tokens)
-                    if (tok < M) {
-                        bf16_t *vcol = q.vt + q.vt_tok[tok];
+                    } else if (f0 >= q.vt_col0) {
+                        // transposed: row f - vt_col0 of vt holds this token at
+                        // column vtcol[b] (32 lanes write 32 consecutive tokens)
+                        if (tok < M) {
+#pragma unroll
+                            for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                                for (int g = 0; g < 4; ++g) {
+                                    const int32_t f4 = f0 + 32 * h2 + 8 * g + 4 * lhi;
+                                    float bv[4] = {0, 0, 0, 0};
+                                    if constexpr (HB) bias4(f4, bv);
+                                    bf16_t *dst =
+                                        q.vt + (size_t)(f4 - q.vt_col0) * q.ldvt + vtcol[b];
+#pragma unroll
+                                    for (int e = 0; e < 4; ++e) {
+                                        float v = acc[a + h2][b][4 * g + e];
+                                        if constexpr (HB) v = bf16r(v) + bv[e];
+                                        dst[(size_t)e * q.ldvt] = (bf16_t)f32_to_bf16(v);
+                                    }
+                                }
+                        }
+                    } else {
 #pragma unroll
                         for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-                            for (int g = 0; g < 4; ++g) {
-                                const int32_t f4 = f0 + 32 * h2 + 8 * g + 4 * lhi;
-                                float bv[4] = {0, 0, 0, 0};
-                                if (p.bias) bias4(f4, bv);
+                            for (int g4 = 0; g4 < 4; ++g4) {
+                                const int fl = wrow[a] + 32 * h2 + 8 * g4 + 4 * lhi;
+                                float v[4], bv[4] = {0, 0, 0, 0};
+                                if constexpr (HB) bias4(n0 + fl, bv);
 #pragma unroll
                                 for (int e = 0; e < 4; ++e) {
-                                    float v = acc[a + h2][b][4 * g + e];
-                                    if (p.bias) v = bf16r(v) + bv[e];
-                                    vcol[(size_t)(f4 + e - q.vt_col0) * q.ldvt] =
-                                        (bf16_t)f32_to_bf16(v);
+                                    v[e] = acc[a + h2][b][4 * g4 + e];
+                                    if constexpr (HB) v[e] = bf16r(v[e]) + bv[e];
                                 }
+                                put4(tl, fl, pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
                             }
                     }
-                } else {
-#pragma unroll
-                    for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-                        for (int g4 = 0; g4 < 4; ++g4) {
-                            const int fl = wrow[a] + 32 * h2 + 8 * g4 + 4 * lhi;
-                            float v[4], bv[4] = {0, 0, 0, 0};
-                            if (p.bias) bias4(n0 + fl, bv);
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                v[e] = acc[a + h2][b][4 * g4 + e];
-                                if (p.bias) v[e] = bf16r(v[e]) + bv[e];
-                            }
-                            put4(tl, fl, pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-                        }
                 }
-            }
+            };
+            if (p.bias)
+                tile(std::true_type{});
+            else
+                tile(std::false_type{});
         } else {
             // epilogue 0 (plain), 4 (plain + bias) and 3 (bias, then GELU)
             constexpr bool has_bias = EPI == 3 || EPI == 4;
@@ -772,11 +820,48 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
                 }
         }
     }
-    __syncthreads();
     // columns this tile writes to C: [n0, min(N, n0 + BN), and below vt_col0)
     int32_t n_end = min(N, n0 + BN);
     if constexpr (EPI == 2) n_end = min(n_end, max(p.qe.vt_col0, n0));
     if constexpr (EPI == 2 && HALF) n_end = min(N, p.qe.vt_col0);
+    if constexpr (MODE == kWholeK && (EPI == 0 || EPI == 4)) {
+        if (p.res) {
+            // the residual add of the projections onto the hidden width:
+            // C = bf16(res + y), y the BF16 output staged above, summed in
+            // float32 and rounded once, as the LayerNorm's residual add does.
+            // This thread's chunks of res are loaded before the barrier, so
+            // their latency overlaps the other waves' staging.
+            constexpr int NIT = (BT * NCH + G::NTHR - 1) / G::NTHR;
+            u32x4_t rv[NIT];
+#pragma unroll
+            for (int i = 0; i < NIT; ++i) {
+                const int idx = tid + i * G::NTHR;
+                const int tl = idx / NCH, c = idx % NCH;
+                const int32_t f = n0 + 8 * c, tok = t0 + tl;
+                if (idx < BT * NCH && tok < M && f < n_end)
+                    rv[i] = ld16(p.res + (size_t)tok * p.ldc + f);
+            }
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < NIT; ++i) {
+                const int idx = tid + i * G::NTHR;
+                const int tl = idx / NCH, c = idx % NCH;
+                const int32_t f = n0 + 8 * c, tok = t0 + tl;
+                if (idx < BT * NCH && tok < M && f < n_end) {
+                    const u32x4_t y =
+                        *reinterpret_cast<const u32x4_t *>(&sC[tl * BN + ((c ^ (tl & (NCH - 1))) << 3)]);
+                    u32x4_t o;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        o[q] = pack_bf16x2(bf16lo(rv[i][q]) + bf16lo(y[q]),
+                                           bf16hi(rv[i][q]) + bf16hi(y[q]));
+                    st16(p.C + (size_t)tok * p.ldc + f, o);
+                }
+            }
+            return;
+        }
+    }
+    __syncthreads();
 #pragma unroll 4
     for (int idx = tid; idx < BT * NCH; idx += G::NTHR) {
         const int tl = idx / NCH, c = idx % NCH;
@@ -1491,8 +1576,14 @@ hipError_t gemm_static_scratch(float **ptr) {
 hipError_t launch_gemm(hipStream_t s, const bf16_t *A, int32_t lda, const bf16_t *W,
                        int32_t ldw, bf16_t *C, int32_t ldc, const int32_t *M_dev,
                        int32_t M_max, int32_t N, int32_t K, int epilogue, const GemmPlan &plan,
-                       float *partial, const QkvEpilogue *qe, const bf16_t *bias) {
+                       float *partial, const QkvEpilogue *qe, const bf16_t *bias,
+                       const bf16_t *res) {
     if (M_max <= 0 || N <= 0) return hipSuccess;
+    // the residual add: whole K, plain (or plain + bias) epilogue, one of the
+    // one-kernel tile shapes
+    if (res && (epilogue != 0 || plan.splits != 1 || plan.config >= kGemmConfigs - 1 ||
+                reinterpret_cast<uintptr_t>(res) % 16 != 0 || ldc % 8 != 0))
+        return hipErrorInvalidValue;
     if (epilogue < 0 || epilogue > 3 || (epilogue == 3 && !bias) || (epilogue == 1 && bias) ||
         reinterpret_cast<uintptr_t>(bias) % 8 != 0)
         return hipErrorInvalidValue;
@@ -1505,7 +1596,7 @@ hipError_t launch_gemm(hipStream_t s, const bf16_t *A, int32_t lda, const bf16_t
         return hipErrorInvalidValue;
     if (plan.splits > 1 && !partial) return hipErrorInvalidValue;
     GemmParams p{A, lda, W, ldw, C, ldc, M_dev, M_max, N, K, plan.splits, partial,
-                 epilogue == 2 ? *qe : QkvEpilogue{}, bias, 0};
+                 epilogue == 2 ? *qe : QkvEpilogue{}, bias, 0, res};
     switch (plan.config) {
         case 0: return launch_small<CfgXS>(s, p, epilogue);
         case 1: return launch_small<CfgXSG>(s, p, epilogue);
@@ -1526,13 +1617,22 @@ hipError_t launch_gemm_layernorm(hipStream_t s, const bf16_t *A, int32_t lda, co
                                  const bf16_t *bias, bf16_t *x, bf16_t *n, const float *gamma,
                                  float eps) {
     if (M_max <= 0) return hipSuccess;
+    if (plan.splits == 1) {
+        // whole K: the GEMM's store does the residual add into x, then the
+        // LayerNorm of x (no second input)
+        if (!x || !n || !gamma || N % 64 != 0 || N > 1024) return hipErrorInvalidValue;
+        const hipError_t e =
+            launch_gemm(s, A, lda, W, ldw, x, N, M_dev, M_max, N, K, 0, plan, nullptr, nullptr,
+                        bias, x);
+        return e != hipSuccess ? e : launch_layernorm(s, x, nullptr, n, gamma, M_dev, M_max, N, eps);
+    }
     // one wave per row holds 16 values per lane: widths up to 1024, multiples of 64
     if (N % 64 != 0 || N > 1024 || K % KMULT != 0 || plan.splits < 2 ||
         plan.splits > K / KMULT || plan.splits > gemm_max_splits(plan.config) || !partial ||
         !x || !n || !gamma || reinterpret_cast<uintptr_t>(bias) % 16 != 0)
         return hipErrorInvalidValue;
     GemmParams p{A, lda, W, ldw, nullptr, 0, M_dev, M_max, N, K, plan.splits, partial,
-                 QkvEpilogue{}, bias, 0};
+                 QkvEpilogue{}, bias, 0, nullptr};
     switch (plan.config) {
         case 0: return launch_split_layernorm<CfgXS>(s, p, x, n, gamma, eps);
         case 1: return launch_split_layernorm<CfgXSG>(s, p, x, n, gamma, eps);

@@ -87,18 +87,23 @@ struct QkvEpilogue {
 // C = bf16(A W^T), epilogue 0 plain, 1 GeGLU (W has 2N rows), 2 QKV (`qe`),
 // 3 bias then GELU.  `bias` ([N], BF16, optional for 0 and 2, required for 3,
 // not allowed for 1): y = bf16(bf16(A W^T) + bias).  With plan.splits > 1,
-// `partial` is required and two kernels are queued.
+// `partial` is required and two kernels are queued.  `res` (epilogue 0, whole
+// K, any tile shape but the ping-pong one; 16-byte aligned, row stride ldc, may
+// be C): C = bf16(res + y), the residual add, bitwise as launch_layernorm's.
 hipError_t launch_gemm(hipStream_t s, const bf16_t *A, int32_t lda, const bf16_t *W,
                        int32_t ldw, bf16_t *C, int32_t ldc, const int32_t *M_dev,
                        int32_t M_max, int32_t N, int32_t K, int epilogue, const GemmPlan &plan,
                        float *partial, const QkvEpilogue *qe = nullptr,
-                       const bf16_t *bias = nullptr);
+                       const bf16_t *bias = nullptr, const bf16_t *res = nullptr);
 
-// A projection onto the hidden width with a K split (plan.splits >= 2, N <=
-// 1024) whose reduce launch also does the residual add and LayerNorm that
-// follow it: x <- bf16(x + bf16(A W^T) [+ bias, rounded again]),
+// A projection onto the hidden width (N <= 1024) followed by the residual add
+// and LayerNorm: x <- bf16(x + bf16(A W^T) [+ bias, rounded again]),
 // n <- bf16(LN(x) * gamma).  Bitwise the same as launch_gemm with this plan
-// (C = r) followed by launch_layernorm(x, r, n), with one launch fewer.
+// (C = r) followed by launch_layernorm(x, r, n).  With a K split
+// (plan.splits >= 2) the reduce launch does the residual add and the
+// LayerNorm, one launch fewer; with whole K (plan.splits == 1) the GEMM's
+// store does the residual add into x and launch_layernorm(x, nullptr, n)
+// follows, so the LayerNorm reads one input instead of two.
 hipError_t launch_gemm_layernorm(hipStream_t s, const bf16_t *A, int32_t lda, const bf16_t *W,
                                  int32_t ldw, const int32_t *M_dev, int32_t M_max, int32_t N,
                                  int32_t K, const GemmPlan &plan, float *partial,
