@@ -274,6 +274,34 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
     const int split = blockIdx.z;
     const int N = p.N;
 
+    // The residual add of the whole-K plain epilogues (p.res): this thread's
+    // 16-byte chunks of res, in the store's order.  Where they fit in 32
+    // registers they are loaded before the main loop, whose waits cover them,
+    // so their latency hides behind it; otherwise at the epilogue.
+    constexpr bool RES = MODE == kWholeK && (EPI == 0 || EPI == 4);
+    constexpr int RCH = BN / 8;  // 16-byte chunks per tile row
+    constexpr int RNIT = RES ? (BT * RCH + G::NTHR - 1) / G::NTHR : 1;
+    constexpr bool RES_EARLY = RES && RNIT <= 8;
+    [[maybe_unused]] u32x4_t rv[RNIT];
+    [[maybe_unused]] auto res_chunk = [&](int i, int &tl, int &c, int32_t &tok, int32_t &f) {
+        const int idx = (int)threadIdx.x + i * G::NTHR;
+        tl = idx / RCH;
+        c = idx % RCH;
+        tok = t0 + tl;
+        f = n0 + 8 * c;
+        return idx < BT * RCH && tok < M && f < min(N, n0 + BN);
+    };
+    [[maybe_unused]] auto res_load = [&]() {
+#pragma unroll
+        for (int i = 0; i < RNIT; ++i) {
+            int tl, c;
+            int32_t tok, f;
+            if (res_chunk(i, tl, c, tok, f)) rv[i] = ld16(p.res + (size_t)tok * p.ldc + f);
+        }
+    };
+    if constexpr (RES_EARLY)
+        if (p.res) res_load();
+
     __shared__ __attribute__((aligned(16))) bf16_t smem[STAGES * G::STAGE_ELEMS];
 
     const int tid = threadIdx.x;
@@ -829,25 +857,15 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
             // the residual add of the projections onto the hidden width:
             // C = bf16(res + y), y the BF16 output staged above, summed in
             // float32 and rounded once, as the LayerNorm's residual add does.
-            // This thread's chunks of res are loaded before the barrier, so
-            // their latency overlaps the other waves' staging.
-            constexpr int NIT = (BT * NCH + G::NTHR - 1) / G::NTHR;
-            u32x4_t rv[NIT];
-#pragma unroll
-            for (int i = 0; i < NIT; ++i) {
-                const int idx = tid + i * G::NTHR;
-                const int tl = idx / NCH, c = idx % NCH;
-                const int32_t f = n0 + 8 * c, tok = t0 + tl;
-                if (idx < BT * NCH && tok < M && f < n_end)
-                    rv[i] = ld16(p.res + (size_t)tok * p.ldc + f);
-            }
+            // (Chunks not loaded early are loaded before the barrier, so their
+            // latency overlaps the other waves' staging.)
+            if constexpr (!RES_EARLY) res_load();
             __syncthreads();
 #pragma unroll
-            for (int i = 0; i < NIT; ++i) {
-                const int idx = tid + i * G::NTHR;
-                const int tl = idx / NCH, c = idx % NCH;
-                const int32_t f = n0 + 8 * c, tok = t0 + tl;
-                if (idx < BT * NCH && tok < M && f < n_end) {
+            for (int i = 0; i < RNIT; ++i) {
+                int tl, c;
+                int32_t tok, f;
+                if (res_chunk(i, tl, c, tok, f)) {
                     const u32x4_t y =
                         *reinterpret_cast<const u32x4_t *>(&sC[tl * BN + ((c ^ (tl & (NCH - 1))) << 3)]);
                     u32x4_t o;
