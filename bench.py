@@ -442,7 +442,7 @@ def chip_peaks():
                   f"{x['gb_per_s_per_workgroup_8_waves']} / {x['gb_per_s_per_workgroup_16_waves']} |")
 
 
-CONFIG_NAMES = ["XS", "XSG", "S", "M", "L", "XL", "M2", "XS2", "XSG2", "PP"]
+CONFIG_NAMES = ["XS", "XSG", "S", "M", "L", "XL", "M2", "XS2", "XSG2", "PP", "Q3", "W2"]
 
 
 def plan_check():
@@ -527,7 +527,7 @@ def plan_check():
 
 SWEEP_T = [257, 320, 384, 448, 512, 640, 768, 896, 1024, 1152, 1280, 1344, 1536, 1715, 2048,
            2400, 2688, 3072, 3500, 4050, 4500, 5000, 5400, 5800, 6144, 7000, 8192]
-SWEEP_CONFIGS = [2, 3, 4, 5, 6, 9]
+SWEEP_CONFIGS = [2, 3, 4, 5, 6, 9, 10, 11]
 
 
 def tile_sweep():

@@ -444,11 +444,11 @@ int laya_op_layernorm(void *stream, void *x, const void *r, void *n, const float
  * [M][lda], W device BF16 [N or 2N][ldw], C device BF16 [M][ldc]; K a multiple
  * of 64, N a multiple of 64, lda/ldw/ldc multiples of 8 (16-byte rows).
  * config -1 picks the tile shape and K split the pass itself would use for M
- * rows; config 0..9 (tile shapes 32x64, 64x64, 128x64, 128x128, 256x128,
+ * rows; config 0..11 (tile shapes 32x64, 64x64, 128x64, 128x128, 256x128,
  * 256x256, 128x128 with a shallower ring that fits two per compute unit,
- * 32x64 and 64x64 for short calls, two computing waves with deep rings, and
- * 256x256 with two wave groups alternating between multiplying and loading;
- * weight rows x tokens) with
+ * 32x64 and 64x64 for short calls, two computing waves with deep rings,
+ * 256x256 with two wave groups alternating between multiplying and loading,
+ * 192x256 with twelve waves, and 256x192; weight rows x tokens) with
  * `splits` K ranges forces one (split K only on shapes 0..3, 7 and 8; GeGLU
  * not on shape 0).  Each output is the sum, in
  * order, of one MFMA chain per K range, so results depend only on `splits`.

@@ -73,7 +73,7 @@ SPLIT_MAX = {0: 8, 1: 8, 2: 8, 3: 8, 7: 8, 8: 8}
 
 
 def _launchable(cfg_id, splits, K, epi, N, fused):
-    if not 0 <= cfg_id <= 9 or splits < 1 or splits > K // 64:
+    if not 0 <= cfg_id <= 11 or splits < 1 or splits > K // 64:
         return False
     if splits > SPLIT_MAX.get(cfg_id, 1):
         return False
@@ -139,7 +139,7 @@ def test_plans_are_the_planners_choice_for_the_exact_token_count(lib):
         assert [b.plan_gemm(t, N, K, e) for N, K, e in shapes] == [(p[0], p[1]) for p in plans[:4]]
     # the configs' token counts
     assert b.pass_plans(MODEL, 48)[:2] == (1, 64)
-    assert b.pass_plans(MODEL, 4050)[:2] == (3073, 4096)
+    assert b.pass_plans(MODEL, 4050)[:2] == (3585, 4096)
     with pytest.raises(b.LayaError):
         b.pass_plans(MODEL, 0)
     with pytest.raises(b.LayaError):
@@ -241,7 +241,7 @@ def test_gemm_layernorm_rejects_bad_arguments(lib):
         return lib.laya_op_gemm_layernorm(None, A, K, W, K, x_, n_, g, M, N, K, config, splits,
                                           bias, eps)
     assert call(config=9, splits=1) == b.LAYA_E_INVALID  # whole K: not the ping-pong shape
-    assert call(config=10, splits=1) == b.LAYA_E_INVALID  # no such shape
+    assert call(config=12, splits=1) == b.LAYA_E_INVALID  # no such shape
     assert call(splits=17) == b.LAYA_E_INVALID         # more ranges than 64-wide K pieces
     assert call(N=2048) == b.LAYA_E_INVALID            # one wave per row: N <= 1024
     assert call(config=4) == b.LAYA_E_INVALID          # whole-K-only tile shape

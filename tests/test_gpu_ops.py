@@ -390,8 +390,8 @@ def test_gemm_every_tile_shape_and_split(B, M, N, K, epi):
         want = oracle.bf16_round(oracle.linear(a_h, w_h))
     for splits in (1, 2, 5):
         outs = []
-        for cfg in range(10):
-            if (epi and cfg == 0) or (splits > 1 and cfg in (4, 5, 6, 9)):
+        for cfg in range(12):
+            if (epi and cfg == 0) or (splits > 1 and cfg in (4, 5, 6, 9, 10, 11)):
                 continue
             c = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
             B.op_gemm(a, w, c, M, N, K, epi, config=cfg, splits=splits)
@@ -412,7 +412,7 @@ def test_gemm_every_tile_shape_and_split(B, M, N, K, epi):
     (300, 1024, 1024, 3, 1, False), (300, 1024, 2624, 6, 1, False), (130, 512, 1024, 2, 1, True),
     (257, 1024, 1024, 5, 1, False), (100, 1024, 1024, 4, 1, True), (65, 1024, 1024, 0, 1, False),
     (48, 1024, 1024, 7, 1, False), (20, 1024, 1024, 8, 1, True), (5, 1024, 1024, 1, 1, False),
-    (517, 1024, 2624, 6, 1, True)])
+    (517, 1024, 2624, 6, 1, True), (300, 1024, 1024, 10, 1, False), (300, 1024, 1024, 11, 1, True)])
 def test_gemm_layernorm_equals_gemm_then_layernorm(B, M, N, K, cfg, splits, bias):
     """The projection with the residual add and LayerNorm fused in (in the split's
     reduce launch, or in the whole-K GEMM's store followed by a LayerNorm of x
@@ -468,7 +468,7 @@ def test_gemm_split_k_repeats_bitwise(B):
 # ------------------------------------------------------- QKV epilogue (fused) --
 
 @pytest.mark.parametrize("M,H,cfgs,splits", [(48, 128, (1, 2, 3, 7, 8), (1, 2, 5)),
-                                             (300, 1024, (2, 3, 4, 5, 6, 7, 9), (1,)),
+                                             (300, 1024, (2, 3, 4, 5, 6, 7, 9, 10, 11), (1,)),
                                              (97, 256, (1, 2, 3, 7), (1, 4))])
 def test_gemm_qkv_epilogue_equals_gemm_then_rope(B, M, H, cfgs, splits):
     """The QKV epilogue gives bitwise the plain GEMM followed by the RoPE
@@ -556,8 +556,8 @@ def test_gemm_bias_and_bias_gelu_every_tile_shape(B, M, N, K):
     h_tol = 1.13 * y_tol + ulp(h_or) + 2.0 ** -126
     worst = {"y": 0.0, "h": 0.0}
     for splits in (1, 2, 4):
-        for cfg in range(10):
-            if (splits > 1 and cfg in (4, 5, 6, 9)) or splits > K // 64:
+        for cfg in range(12):
+            if (splits > 1 and cfg in (4, 5, 6, 9, 10, 11)) or splits > K // 64:
                 continue
             outs = {}
             for epi, bb in ((0, None), (0, bias), (3, bias)):
@@ -593,7 +593,7 @@ def test_gemm_bias_rules(B):
 
 
 @pytest.mark.parametrize("M,H,cfgs,splits", [(48, 128, (1, 2, 3, 7), (1, 2)),
-                                             (300, 1024, (2, 3, 4, 5, 7), (1,))])
+                                             (300, 1024, (2, 3, 4, 5, 7, 10), (1,))])
 def test_gemm_qkv_bias_equals_biased_gemm_then_rope(B, M, H, cfgs, splits):
     """With a bias the QKV epilogue equals the biased plain GEMM followed by
     the RoPE kernel, and V^T holds the biased V columns, bitwise."""
@@ -639,8 +639,8 @@ def test_gemm_qkv_bias_equals_biased_gemm_then_rope(B, M, H, cfgs, splits):
 
 # ------------------------------------------- 2-D XCD split of large grids --
 
-@pytest.mark.parametrize("M,N,K,epi,cfgs", [(4049, 2624, 1024, 1, (3, 4, 5, 6, 9)),
-                                            (4050, 3072, 1024, 0, (3, 5, 6, 9)),
+@pytest.mark.parametrize("M,N,K,epi,cfgs", [(4049, 2624, 1024, 1, (3, 4, 5, 6, 9, 11, 10)),
+                                            (4050, 3072, 1024, 0, (3, 5, 6, 9, 10, 11)),
                                             (2049, 4096, 1024, 0, (3, 6, 9)),
                                             (8192, 2624, 1024, 1, (6, 9))])
 def test_gemm_two_dimensional_xcd_split_writes_every_tile(B, M, N, K, epi, cfgs):

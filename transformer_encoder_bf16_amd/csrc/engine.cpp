@@ -1736,7 +1736,7 @@ int laya_op_gemm_layernorm(void *stream, const void *A, int32_t lda, const void 
     const bool whole = splits == 1;
     if (!gemm_args_ok(A, lda, W, ldw, x, N, M, N, K, config) || N > 1024 || !(eps > 0.f) ||
         config < 0 ||
-        (whole ? config >= laya::kGemmConfigs - 1
+        (whole ? config == laya::kPingPongConfig
                : ((config > 3 && config < 7) || splits < 2 || splits > K / 64 ||
                   splits > laya::gemm_max_splits(config))) ||
         (M > 0 && (!n || !gamma || n == x)) || reinterpret_cast<uintptr_t>(bias) % 16 != 0)

@@ -212,17 +212,23 @@ struct Cfg {
     static constexpr int OCC = (160 * 1024) / (STAGES * STAGE_ELEMS * 2) >= 2 ? 2 : 1;
     static constexpr int CH = BK / 8;                      // 16-byte chunks per row
     static constexpr int RPL = 64 / CH;                    // rows per 1 KB DMA load
-    static constexpr int LOADS = (BW + BT) / RPL / NWAVE;  // DMA loads per wave per stage
+    static constexpr int BLOCKS = (BW + BT) / RPL;         // 1 KB DMA loads per stage
+    // DMA loads per wave per stage: LOADS_MIN for every wave, one more for
+    // the first BLOCKS % NWAVE waves (token rows only)
+    static constexpr int LOADS = (BLOCKS + NWAVE - 1) / NWAVE, LOADS_MIN = BLOCKS / NWAVE;
     static constexpr int WLOADS = BW / RPL / NWAVE;        // the first WLOADS are weight rows
     static_assert(BK == 32 || BK == 64, "K step");
-    static_assert((BW / RPL) % NWAVE == 0 && (BT / RPL) % NWAVE == 0, "even split of loads");
+    static_assert((BW / RPL) % NWAVE == 0 && BT % RPL == 0, "weight loads split evenly");
     static_assert(RW % 32 == 0 && RT % 32 == 0, "32x32 fragments");
     static_assert(STAGES >= 2 && (STAGES - 1) * LOADS < 64, "vmcnt range");
     static_assert(STAGES * STAGE_ELEMS * 2 <= 160 * 1024, "LDS");
     static_assert(FA + FB <= 15, "lgkmcnt range");
-    static_assert((BW & (BW - 1)) == 0 && (BT & (BT - 1)) == 0,
-                  "power-of-two tiles (the output staging swizzles 16-byte chunks by XOR)");
 };
+
+// XOR mask of the output staging's 16-byte chunk swizzle for rows of n
+// chunks: the largest power of two dividing n, minus one, so a chunk stays
+// inside its row (all of it for power-of-two rows).
+constexpr int chunk_swizzle(int n) { return (n & -n) - 1; }
 
 struct GemmParams {
     const bf16_t *A;
@@ -336,6 +342,10 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
 #pragma unroll
     for (int j = 0; j < G::LOADS; ++j) {
         const int jj = j * G::NWAVE + wave;
+        if (j >= G::LOADS_MIN && jj >= G::BLOCKS) {  // past the stage's last block: no load
+            off[j] = a_bytes;
+            continue;
+        }
         const int r = RPL * jj + rr;      // stage row
         const int c = pchunk<BK>(r, pc);  // logical chunk stored at physical chunk pc
         if (j < G::WLOADS) {
@@ -368,6 +378,7 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
         const int k0b = kt * BK * 2;
 #pragma unroll
         for (int j = 0; j < G::LOADS; ++j) {
+            if (j >= G::LOADS_MIN && j * G::NWAVE + wave_u >= G::BLOCKS) continue;
             if (j < G::WLOADS)
                 dma16(p.W, w_bytes, (lds_ptr_t)(base + j * G::NWAVE * 512), off[j], k0b);
             else
@@ -431,7 +442,7 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
       for (int st = 0; st < STAGES; ++st)
           if (st < nk) issue(st, st);
       if (nk >= STAGES)
-          wait_vmcnt<(STAGES - 1) * G::LOADS>();
+          wait_vmcnt<(STAGES - 1) * G::LOADS_MIN>();
       else
           wait_vmcnt<0>();
       wait_lgkmcnt<0>();  // no scalar loads left in flight, so
@@ -441,7 +452,7 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
           // the same waits, barriers and refills as the computing waves
           for (int i = 0; i < nk; ++i) {
               if (i + STAGES <= nk)
-                  wait_vmcnt<(STAGES - 2) * G::LOADS>();
+                  wait_vmcnt<(STAGES - 2) * G::LOADS_MIN>();
               else
                   wait_vmcnt<0>();
               ring_barrier();
@@ -459,7 +470,7 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
               } else {
                   // outstanding loads after stage i+1: stages i+2 .. min(i+STAGES-1, nk-1)
                   if (i + STAGES <= nk)
-                      wait_vmcnt<(STAGES - 2) * G::LOADS>();
+                      wait_vmcnt<(STAGES - 2) * G::LOADS_MIN>();
                   else
                       wait_vmcnt<0>();
                   wait_lgkmcnt<0>();  // this stage fully read
@@ -498,7 +509,7 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4) {
                     const int c = (wrow[a] + 8 * g4 + 4 * lhi) >> 2;
-                    *reinterpret_cast<f32x4_t *>(&sP[tl * BW + ((c ^ (tl & (NC4 - 1))) << 2)]) =
+                    *reinterpret_cast<f32x4_t *>(&sP[tl * BW + ((c ^ (tl & chunk_swizzle(NC4))) << 2)]) =
                         f32x4_t{acc[a][b][4 * g4], acc[a][b][4 * g4 + 1], acc[a][b][4 * g4 + 2],
                                 acc[a][b][4 * g4 + 3]};
                 }
@@ -511,7 +522,7 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
             const int32_t tok = t0 + tl, f = n0 + 4 * c;
             if (tok < M && f < N)
                 *reinterpret_cast<f32x4_t *>(dst + (size_t)tok * N + f) =
-                    *reinterpret_cast<const f32x4_t *>(&sP[tl * BW + ((c ^ (tl & (NC4 - 1))) << 2)]);
+                    *reinterpret_cast<const f32x4_t *>(&sP[tl * BW + ((c ^ (tl & chunk_swizzle(NC4))) << 2)]);
         }
         return;
     }
@@ -590,7 +601,7 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
     auto put4 = [&](int tl, int fl, uint32_t lo, uint32_t hi) {
         const int c = fl >> 3;
         *reinterpret_cast<u32x2_t *>(
-            &sC[tl * BN + ((c ^ (tl & (NCH - 1))) << 3) + (fl & 4)]) = u32x2_t{lo, hi};
+            &sC[tl * BN + ((c ^ (tl & chunk_swizzle(NCH))) << 3) + (fl & 4)]) = u32x2_t{lo, hi};
     };
     auto bf16r = [](float v) { return bf16_to_f32(f32_to_bf16(v)); };
     // four consecutive bias values (f a multiple of 4; the bias is 8-byte aligned)
@@ -867,7 +878,7 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
                 int32_t tok, f;
                 if (res_chunk(i, tl, c, tok, f)) {
                     const u32x4_t y =
-                        *reinterpret_cast<const u32x4_t *>(&sC[tl * BN + ((c ^ (tl & (NCH - 1))) << 3)]);
+                        *reinterpret_cast<const u32x4_t *>(&sC[tl * BN + ((c ^ (tl & chunk_swizzle(NCH))) << 3)]);
                     u32x4_t o;
 #pragma unroll
                     for (int q = 0; q < 4; ++q)
@@ -890,7 +901,7 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
         const int32_t tok = t0 + tl;
         if (tok < M && f < n_end)
             st16(p.C + (size_t)tok * p.ldc + f,
-                 *reinterpret_cast<const u32x4_t *>(&sC[tl * BN + ((c ^ (tl & (NCH - 1))) << 3)]));
+                 *reinterpret_cast<const u32x4_t *>(&sC[tl * BN + ((c ^ (tl & chunk_swizzle(NCH))) << 3)]));
     }
 }
 
@@ -1340,6 +1351,10 @@ using CfgXL = Cfg<256, 256, 2, 4, 64, 2>;  // 8 waves of 128 x 64
 using CfgM2 = Cfg<128, 128, 2, 2, 64, 2>;   // M with a 2-stage ring: 64 KB, two per CU
 using CfgXS2 = Cfg<32, 64, 1, 2, 64, 13, 2>;  // small M, 2 waves of 32 x 32 + 2 loading, deep ring
 using CfgXSG2 = Cfg<64, 64, 1, 2, 64, 8>;  // small M, 2 waves of 64 x 32, deep ring
+// 3 heads x 256 tokens: twelve waves of 64 x 64, three per SIMD (16 x 16 tiles
+// cover the QKV projection of 4096 tokens in one round of the 256 CUs)
+using CfgQ3 = Cfg<192, 256, 3, 4, 64, 2>;
+using CfgW2 = Cfg<256, 192, 4, 2, 64, 2>;  // 8 waves of 64 x 96
 
 struct CfgInfo {
     int bw, bt;
@@ -1348,7 +1363,8 @@ constexpr CfgInfo kCfgs[kGemmConfigs] = {{CfgXS::BW, CfgXS::BT}, {CfgXSG::BW, Cf
                                          {CfgS::BW, CfgS::BT},   {CfgM::BW, CfgM::BT},
                                          {CfgL::BW, CfgL::BT},   {CfgXL::BW, CfgXL::BT},
                                          {CfgM2::BW, CfgM2::BT}, {CfgXS2::BW, CfgXS2::BT},
-                                         {CfgXSG2::BW, CfgXSG2::BT}, {pp::BW, pp::BT}};
+                                         {CfgXSG2::BW, CfgXSG2::BT}, {pp::BW, pp::BT},
+                                         {CfgQ3::BW, CfgQ3::BT}, {CfgW2::BW, CfgW2::BT}};
 
 // Whole-K grids of at least 512 tiles may take the 2-D XCD split (on smaller
 // grids it gained nothing and the padding cost a little): the grid rows
@@ -1449,20 +1465,25 @@ int gemm_max_splits(int config) {
 // The fastest whole-K tile shape for the pass's four projections at hidden
 // 1024 and GeGLU width 2624, measured on MI355X over 257..8192 tokens with
 // the weights streamed from HBM (every shape gives the same bits, so only
-// time decides).  Each switch point is where the faster shape's grid would
+// time decides).  Most switch points are where the faster shape's grid would
 // need one more round of the 256 CUs (two workgroups per CU for the 2-stage
-// 128x128 tile).  Other shapes use the estimate below.
+// 128x128 tile); between 3072 and 4608 tokens the up projection's 192x256 and
+// 256x192 shapes are within a few percent of each other, and the table
+// follows the measurement.  Other shapes use the estimate below.
 struct MeasuredTiles {
     int32_t N, K, epilogue, n;
-    int32_t t_last[8];
-    int8_t config[8];
+    int32_t t_last[12];
+    int8_t config[12];
 };
 constexpr MeasuredTiles kMeasuredTiles[] = {
     // QKV: 128x64 while 24 x T/64 tiles fit one round, then 128x128, the
-    // two-per-CU 128x128, 256x256, and the two-per-CU 128x128 again
-    {3072, 1024, 2, 5, {640, 1280, 2688, 5376, 1 << 30}, {2, 3, 6, 5, 6}},
-    // GeGLU up (64 or 128 output features per tile)
-    {2624, 1024, 1, 8, {384, 768, 1536, 3072, 4736, 6144, 7936, 1 << 30}, {2, 3, 6, 5, 6, 5, 6, 5}},
+    // two-per-CU 128x128, 192x256 (16 x T/256 tiles: one round up to 4096
+    // tokens), 256x256, and 192x256 again
+    {3072, 1024, 2, 6, {640, 1280, 2688, 4096, 5376, 1 << 30}, {2, 3, 6, 10, 5, 10}},
+    // GeGLU up (64, 96 or 128 output features per tile); 192x256 and 256x192
+    // fit one round up to 2304 tokens and two up to 4608
+    {2624, 1024, 1, 12, {384, 768, 1536, 2304, 3072, 3584, 4352, 4608, 4736, 6144, 7936, 1 << 30},
+     {2, 3, 6, 10, 5, 10, 11, 10, 6, 5, 6, 5}},
     // output projection (whole K above 1024 tokens)
     {1024, 1024, 0, 3, {2048, 4096, 1 << 30}, {2, 3, 6}},
     // down projection (whole K above 2048 tokens)
@@ -1599,7 +1620,7 @@ hipError_t launch_gemm(hipStream_t s, const bf16_t *A, int32_t lda, const bf16_t
     if (M_max <= 0 || N <= 0) return hipSuccess;
     // the residual add: whole K, plain (or plain + bias) epilogue, one of the
     // one-kernel tile shapes
-    if (res && (epilogue != 0 || plan.splits != 1 || plan.config >= kGemmConfigs - 1 ||
+    if (res && (epilogue != 0 || plan.splits != 1 || plan.config == kPingPongConfig ||
                 reinterpret_cast<uintptr_t>(res) % 16 != 0 || ldc % 8 != 0))
         return hipErrorInvalidValue;
     if (epilogue < 0 || epilogue > 3 || (epilogue == 3 && !bias) || (epilogue == 1 && bias) ||
@@ -1625,6 +1646,8 @@ hipError_t launch_gemm(hipStream_t s, const bf16_t *A, int32_t lda, const bf16_t
         case 6: return launch_large<CfgM2>(s, p, epilogue);
         case 7: return launch_small<CfgXS2>(s, p, epilogue);
         case 8: return launch_small<CfgXSG2>(s, p, epilogue);
+        case 10: return launch_large<CfgQ3>(s, p, epilogue);
+        case 11: return launch_large<CfgW2>(s, p, epilogue);
         default: return launch_pp(s, p, epilogue);
     }
 }

@@ -45,13 +45,16 @@ hipError_t launch_layernorm(hipStream_t s, bf16_t *x, const bf16_t *r, bf16_t *n
 // GEMM tile configuration and K split.  Every output element is one MFMA
 // chain per K range, the ranges summed in order, so a result depends only on
 // `splits` (never on the tile shape).
-constexpr int kGemmConfigs = 10;
+constexpr int kGemmConfigs = 12;
+constexpr int kPingPongConfig = 9;
 struct GemmPlan {
     int config;  // 0 XS 32x64, 1 XSG 64x64, 2 S 128x64, 3 M 128x128, 4 L 256x128, 5 XL 256x256,
                  // 6 M2 128x128 with a 2-stage ring (two workgroups per CU),
                  // 7 XS2 32x64 and 8 XSG2 64x64 (two computing waves each, deep
                  // rings; XS2 with two more waves that only load),
-                 // 9 P 256x256 with two wave groups in ping-pong (whole K)
+                 // 9 P 256x256 with two wave groups in ping-pong (whole K),
+                 // 10 Q3 192x256 (three heads, twelve waves, three per SIMD),
+                 // 11 W2 256x192 (eight waves of 64x96); whole K for 4..6, 9..11
     int splits;  // K ranges (>= 1)
 };
 // plan for a GEMM of up to M_max rows (its K split and tile shape; the split
