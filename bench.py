@@ -107,6 +107,10 @@ def parse():
     p.add_argument("--tile-sweep", action="store_true",
                    help="time every whole-K tile shape for each projection over a range of "
                         "token counts (markdown table)")
+    p.add_argument("--gemm-phases", action="store_true",
+                   help="per-workgroup phases (prologue, main loop, epilogue) of the pass's four "
+                        "projections at the workload's token count, from the library's "
+                        "diagnostic build (markdown table)")
     p.add_argument("--chip-peaks", action="store_true",
                    help="run the chip probe (matrix-core issue rate, LDS read bandwidth, one "
                         "workgroup's HBM stream) and print its figures")
@@ -579,6 +583,95 @@ def tile_sweep():
         del Ws
 
 
+# whole-K tile shapes: weight rows, tokens, workgroups one CU holds
+PHASE_TILES = {2: (128, 64, 1), 3: (128, 128, 1), 4: (256, 128, 1), 5: (256, 256, 1),
+               6: (128, 128, 2), 10: (192, 256, 1), 11: (256, 192, 1)}
+
+
+def gemm_phases(workload):
+    """The pass's four projections at the workload's token count, with the
+    planner's whole-K tile shapes, run through the library's diagnostic build,
+    whose GEMM workgroups record the shader clock at their start, when their
+    ring is first full, at the end of their main loop, before and after the
+    barrier ahead of their stores, and at their end (plus the 100 MHz clock at
+    start and end, from which the shader clock's rate is fitted).  One launch
+    per projection after three warm ones, weights rotated beyond the MALL.
+    Prints the medians over the workgroups as markdown."""
+    import ctypes
+    import torch
+    from transformer_encoder_bf16_amd import binding as B
+    from transformer_encoder_bf16_amd import build_lib
+    from transformer_encoder_bf16_amd.inputs import ALL_WORKLOADS, MODEL, make_batch
+    if not os.path.exists(build_lib.PHASES_LIB):
+        build_lib.build()
+    B.LIB_PATH = build_lib.PHASES_LIB
+    lib = B.load()
+    lib.laya_gemm_phases_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    torch.cuda.set_device(0)
+    dev = "cuda"
+    T = make_batch(MODEL, ALL_WORKLOADS[workload]).T
+    H, F = MODEL["hidden"], MODEL["ffn"]
+    cb, sb = B.rope_table(160000.0, 512, 64)
+    ct = torch.from_numpy(cb.view(np.int16)).to(dev)
+    st = torch.from_numpy(sb.view(np.int16)).to(dev)
+    pos = torch.from_numpy((np.arange(T) % 512).astype(np.int32)).to(dev)
+    vtok = torch.arange(T, dtype=torch.int32, device=dev)
+    vt = torch.empty(H, T + 64, dtype=torch.bfloat16, device=dev)
+    print(f"Workload {workload}: T = {T} tokens.\n")
+    print("| GEMM | Tile | Workgroups | Clock GHz | Span µs | Prologue µs | Main loop µs "
+          "| µs per 64-wide K step | Loop at MFMA rate | Epilogue: compute + staging µs "
+          "| barrier µs | stores µs |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|---|")
+    for name, N, K, epi in [("qkv", 3 * H, H, 2), ("out", H, H, 0), ("up", F, H, 1),
+                            ("down", H, F, 0)]:
+        cfg, splits = B.plan_gemm(T, N, K, epi)
+        if splits != 1 or cfg not in PHASE_TILES:
+            print(f"| {name} | {CONFIG_NAMES[cfg]}, {splits} K ranges | (split K: not recorded) "
+                  "| | | | | | | | | |")
+            continue
+        wr = 2 * N if epi == 1 else N
+        A = (torch.randn(T, K, device=dev) * 0.5).bfloat16()
+        W = (torch.randn(wr, K, device=dev) * 0.03).bfloat16()
+        C = torch.empty(T, N, device=dev, dtype=torch.bfloat16)
+        Ws = [W.clone() for _ in range(max(8, int(600e6 // (wr * K * 2))))]
+        del W
+
+        def one(w):
+            if epi == 2:
+                B.op_gemm_qkv(A, w, C, T, N, K, pos, ct, st, 2 * H, vt, vtok, 2 * H,
+                              config=cfg, splits=1)
+            else:
+                B.op_gemm_noalloc(A, w, C, T, N, K, epi, cfg, 1)
+        for i in range(3):
+            one(Ws[i])
+        torch.cuda.synchronize()
+        if lib.laya_gemm_phases_clear() != 0:
+            raise RuntimeError("laya_gemm_phases_clear failed")
+        one(Ws[3])
+        torch.cuda.synchronize()
+        buf = np.zeros(65536 * 10, dtype=np.uint64)
+        if lib.laya_gemm_phases_read(buf.ctypes.data, buf.nbytes) != 0:
+            raise RuntimeError("laya_gemm_phases_read failed")
+        rec = buf.reshape(-1, 10)
+        rec = rec[rec[:, 9] == 1].astype(np.int64)
+        c, r0, r1 = rec[:, :6], rec[:, 6], rec[:, 7]
+        clock = float(np.median((c[:, 5] - c[:, 0]) / np.maximum(r1 - r0, 1))) * 100e6
+        us = lambda cyc: float(np.median(cyc)) / clock * 1e6
+        bw, bt, occ = PHASE_TILES[cfg]
+        steps = K // 64
+        # one MFMA-bound K step: the tile's 2*bw*bt*64 FLOP at 4 SIMDs x 1024 FLOP
+        # per clock, shared with the other workgroups the CU holds
+        conc = min(occ, -(-len(rec) // 256))
+        ideal = 2.0 * bw * bt * 64 * conc / (4 * 1024) / clock * 1e6
+        step = us(c[:, 2] - c[:, 1]) / steps
+        print(f"| {name} | {CONFIG_NAMES[cfg]} {bw}x{bt} | {len(rec)} | {clock / 1e9:.2f} | "
+              f"{(r1.max() - r0.min()) / 100.0:.1f} | {us(c[:, 1] - c[:, 0]):.2f} | "
+              f"{us(c[:, 2] - c[:, 1]):.2f} | {step:.3f} | {ideal / step:.2f} | "
+              f"{us(c[:, 3] - c[:, 2]):.2f} | {us(c[:, 4] - c[:, 3]):.2f} | "
+              f"{us(c[:, 5] - c[:, 4]):.2f} |", flush=True)
+        del Ws
+
+
 def _graph_launch_us(fn, n_inner, reps=5):
     """µs per launch of `fn`'s n_inner launches, captured in one graph."""
     import torch
@@ -785,6 +878,9 @@ def main():
         return
     if args.tile_sweep:
         tile_sweep()
+        return
+    if args.gemm_phases:
+        gemm_phases(args.workload)
         return
     from transformer_encoder_bf16_amd import binding
     from transformer_encoder_bf16_amd.inputs import ALL_WORKLOADS, WEIGHT_SEED, make_batch

@@ -18,6 +18,9 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "liblaya_encoder.so")
 PROBE = os.path.join(HERE, "chip_probe")
+# diagnostic build: the same library with the GEMMs' per-workgroup phase
+# timestamps compiled in (bench.py --gemm-phases); never loaded by the pass
+PHASES_LIB = os.path.join(HERE, "liblaya_encoder_phases.so")
 
 SOURCES = ["k_elementwise.hip", "k_gemm.hip", "k_attention.hip", "engine.cpp", "queue.cpp"]
 
@@ -41,9 +44,9 @@ FLAGS = [
 FILE_FLAGS = {"k_attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"]}
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, extra: tuple = (), suffix: str = "") -> str:
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + suffix + ".o")
+    cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(src, []), *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
@@ -54,14 +57,18 @@ def build(verbose: bool = False) -> str:
     if not os.path.exists(HIPCC) and shutil.which(HIPCC) is None:
         raise RuntimeError(f"hipcc not found at {HIPCC}")
     os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES) + 1)) as ex:
+        phases = ex.submit(_compile, "k_gemm.hip", ("-DLAYA_GEMM_PHASES",), "_phases")
         objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+        phases_obj = phases.result()
+    for lib, lib_objs in ((LIB, objs), (PHASES_LIB, [phases_obj if o.endswith("k_gemm.o") else o
+                                                      for o in objs])):
+        tmp = lib + ".tmp%d" % os.getpid()
+        cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *lib_objs]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+        os.replace(tmp, lib)
     # the chip probe (bench.py --chip-peaks): a program of its own
     tmp = PROBE + ".tmp%d" % os.getpid()
     cmd = [HIPCC, *FLAGS, os.path.join(CSRC, "chip_probe.hip"), "-o", tmp]

@@ -62,6 +62,22 @@
 
 #include "kernels.h"
 
+// Diagnostic build (LAYA_GEMM_PHASES, a separate library next to the product
+// one): every whole-K workgroup of gemm_kernel records the shader clock when
+// its tile is known, when its ring is first full, when its main loop ends,
+// before and after the barrier ahead of its stores, and at its end, plus the
+// 100 MHz real-time clock at its start and end and its tile, into
+// gemm_phases[workgroup][10] (first 65536 workgroups of a launch).
+#ifdef LAYA_GEMM_PHASES
+namespace {
+constexpr int kPhaseWorkgroups = 65536;
+__device__ unsigned long long gemm_phases[kPhaseWorkgroups * 10];
+}  // namespace
+#define LAYA_PHASE(var) (var) = __builtin_readcyclecounter()
+#else
+#define LAYA_PHASE(var) (void)0
+#endif
+
 // Split-K partials of the allocation-free GEMM entry point: device memory the
 // library holds for the life of the process on each GPU it runs on, shared by
 // every such call on that GPU.
@@ -279,6 +295,27 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
     const int32_t n0 = bx * BN;
     const int split = blockIdx.z;
     const int N = p.N;
+    [[maybe_unused]] uint64_t ph[6] = {0, 0, 0, 0, 0, 0};
+    [[maybe_unused]] uint64_t ph_r0 = 0;
+    LAYA_PHASE(ph[0]);
+#ifdef LAYA_GEMM_PHASES
+    ph_r0 = wall_clock64();
+#endif
+    // the phase record of this workgroup (diagnostic build, whole K)
+    [[maybe_unused]] auto phase_store = [&]() {
+#ifdef LAYA_GEMM_PHASES
+        LAYA_PHASE(ph[5]);
+        const int wg = blockIdx.y * gridDim.x + blockIdx.x;
+        if (MODE == kWholeK && threadIdx.x == 0 && wg < kPhaseWorkgroups) {
+            unsigned long long *d = gemm_phases + (size_t)wg * 10;
+            for (int i = 0; i < 6; ++i) d[i] = ph[i];
+            d[6] = ph_r0;
+            d[7] = wall_clock64();
+            d[8] = ((uint64_t)(uint32_t)bx << 32) | (uint32_t)by;
+            d[9] = 1;
+        }
+#endif
+    };
 
     // The residual add of the whole-K plain epilogues (p.res): this thread's
     // 16-byte chunks of res, in the store's order.  Where they fit in 32
@@ -448,6 +485,7 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
       wait_lgkmcnt<0>();  // no scalar loads left in flight, so
                                            // the loop's LDS reads can be waited on in order
       ring_barrier();
+      LAYA_PHASE(ph[1]);
       if (!compute) {
           // the same waits, barriers and refills as the computing waves
           for (int i = 0; i < nk; ++i) {
@@ -594,6 +632,7 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
     // XOR-swizzled by token), then written with 16-byte stores along whole
     // row segments: direct stores would touch 32 token rows per instruction.
     // Columns bound for the transposed V (epilogue 2) are stored directly.
+    LAYA_PHASE(ph[2]);
     constexpr int NCH = BN / 8;  // 16-byte chunks per tile row
     static_assert(BT * BN * 2 <= STAGES * G::STAGE_ELEMS * 2, "output tile fits the ring");
     __syncthreads();  // every wave is done with the ring
@@ -871,7 +910,9 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
             // (Chunks not loaded early are loaded before the barrier, so their
             // latency overlaps the other waves' staging.)
             if constexpr (!RES_EARLY) res_load();
+            LAYA_PHASE(ph[3]);
             __syncthreads();
+            LAYA_PHASE(ph[4]);
 #pragma unroll
             for (int i = 0; i < RNIT; ++i) {
                 int tl, c;
@@ -887,10 +928,13 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
                     st16(p.C + (size_t)tok * p.ldc + f, o);
                 }
             }
+            phase_store();
             return;
         }
     }
+    LAYA_PHASE(ph[3]);
     __syncthreads();
+    LAYA_PHASE(ph[4]);
 #pragma unroll 4
     for (int idx = tid; idx < BT * NCH; idx += G::NTHR) {
         const int tl = idx / NCH, c = idx % NCH;
@@ -903,6 +947,7 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
             st16(p.C + (size_t)tok * p.ldc + f,
                  *reinterpret_cast<const u32x4_t *>(&sC[tl * BN + ((c ^ (tl & chunk_swizzle(NCH))) << 3)]));
     }
+    phase_store();
 }
 
 // Split-K reduce fused with the residual add and LayerNorm that follow a
@@ -1686,3 +1731,20 @@ hipError_t launch_gemm_layernorm(hipStream_t s, const bf16_t *A, int32_t lda, co
 }
 
 }  // namespace laya
+
+#ifdef LAYA_GEMM_PHASES
+// Host access to the diagnostic build's phase records (not part of the
+// product library's interface): copy out the first `bytes` bytes, or clear
+// them all.
+extern "C" int laya_gemm_phases_read(void *dst, size_t bytes) {
+    return (int)hipMemcpyFromSymbol(dst, HIP_SYMBOL(gemm_phases), bytes, 0,
+                                    hipMemcpyDeviceToHost);
+}
+extern "C" int laya_gemm_phases_clear() {
+    void *ptr = nullptr;
+    hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(gemm_phases));
+    if (e == hipSuccess) e = hipMemset(ptr, 0, sizeof(unsigned long long) * kPhaseWorkgroups * 10);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    return (int)e;
+}
+#endif
