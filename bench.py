@@ -117,7 +117,10 @@ def parse():
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="only run a plain device-to-device copy of this many MiB three times "
                         "(the reference for scaling HBM byte counters), then exit")
-    return p.parse_args()
+    args = p.parse_args()
+    if args.profile_passes < 1:
+        p.error("--profile-passes must be at least 1: the roofline figure comes from the per-op table")
+    return args
 
 
 def copy_calibration(mib):

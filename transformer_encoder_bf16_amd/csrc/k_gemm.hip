@@ -473,11 +473,39 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
                                                                     acc[a][b], 0, 0, 0);
     };
 
+    // Half-head QKV tiles (short calls): the lane's token position is loaded
+    // ahead of the ring's first loads and its rotation-table entries right
+    // after them, so their latency hides behind the main loop (whose waits,
+    // counted in order, then cover them as well).
+    constexpr bool QKV_HALF = EPI == 2 && HALF;
+    [[maybe_unused]] u32x2_t hcos[2] = {}, hsin[2] = {};
+    [[maybe_unused]] uint32_t hps = 0;
+    [[maybe_unused]] bool half_rope = false;
+    [[maybe_unused]] auto half_tables = [&]() {
+#pragma unroll
+        for (int g4 = 0; g4 < 2; ++g4) {
+            const int j = (bx & 1) * 16 + 8 * g4 + 4 * lhi;  // pair index of element 4*g4
+            hcos[g4] = *reinterpret_cast<const u32x2_t *>(p.qe.cos_tab + hps + j);
+            hsin[g4] = *reinterpret_cast<const u32x2_t *>(p.qe.sin_tab + hps + j);
+        }
+    };
+    if constexpr (QKV_HALF) {
+        half_rope = compute && (bx >> 1) * 64 < p.qe.rope_cols;
+        if (half_rope) {
+            const int32_t tok = t0 + wc * G::RT + l32;
+            hps = (uint32_t)p.qe.pos[tok < M ? tok : M - 1] * 32u;
+        }
+        if constexpr (MODE == kReduce)
+            if (half_rope) half_tables();
+    }
+
     if constexpr (MODE != kReduce) {
     // prologue: every stage of the ring in flight, then stage 0 published
   #pragma unroll
       for (int st = 0; st < STAGES; ++st)
           if (st < nk) issue(st, st);
+      if constexpr (QKV_HALF)
+          if (half_rope) half_tables();
       if (nk >= STAGES)
           wait_vmcnt<(STAGES - 1) * G::LOADS_MIN>();
       else
@@ -719,75 +747,82 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
             // dimension 16p + 8 g4 + 4 lhi + e, element 4 (g4 + 2) + e the
             // dimension 32 above it, so each rotation pair is in one lane.  The
             // staged tile holds the 16 low dimensions, then the 16 high ones.
+            // (Rotation tables preloaded above; the bias, head variant only,
+            // a compile-time case.)
             const QkvEpilogue &q = p.qe;
             const int32_t hcol = (bx >> 1) * 64;  // first column of the head
             const int p16 = (bx & 1) * 16;
-            if (hcol < q.rope_cols) {
-                const uint32_t ps = (uint32_t)q.pos[tok < M ? tok : M - 1] * 32u;
+            auto tile = [&](auto bias_tag) {
+                constexpr bool HB = decltype(bias_tag)::value;
+                if (hcol < q.rope_cols) {
 #pragma unroll
-                for (int g4 = 0; g4 < 2; ++g4) {
-                    const int j = p16 + 8 * g4 + 4 * lhi;  // pair index of element 4*g4
-                    const u32x2_t cv = *reinterpret_cast<const u32x2_t *>(q.cos_tab + ps + j);
-                    const u32x2_t sv = *reinterpret_cast<const u32x2_t *>(q.sin_tab + ps + j);
-                    float xo[4], yo[4], bx4[4] = {0, 0, 0, 0}, by4[4] = {0, 0, 0, 0};
-                    if (p.bias) {
-                        bias4(hcol + j, bx4);
-                        bias4(hcol + 32 + j, by4);
-                    }
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        float x = bf16r(acc[0][b][4 * g4 + e]);
-                        float y = bf16r(acc[0][b][4 * (g4 + 2) + e]);
-                        if (p.bias) {
-                            x = bf16r(x + bx4[e]);
-                            y = bf16r(y + by4[e]);
+                    for (int g4 = 0; g4 < 2; ++g4) {
+                        const int j = p16 + 8 * g4 + 4 * lhi;  // pair index of element 4*g4
+                        const u32x2_t cv = hcos[g4], sv = hsin[g4];
+                        float xo[4], yo[4], bx4[4] = {0, 0, 0, 0}, by4[4] = {0, 0, 0, 0};
+                        if constexpr (HB) {
+                            bias4(hcol + j, bx4);
+                            bias4(hcol + 32 + j, by4);
                         }
-                        const float c = (e & 1) ? bf16hi(cv[e >> 1]) : bf16lo(cv[e >> 1]);
-                        const float sn = (e & 1) ? bf16hi(sv[e >> 1]) : bf16lo(sv[e >> 1]);
-                        // both products of BF16 values are exact in float32
-                        xo[e] = fmaf(x, c, -(y * sn));
-                        yo[e] = fmaf(y, c, x * sn);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            float x = bf16r(acc[0][b][4 * g4 + e]);
+                            float y = bf16r(acc[0][b][4 * (g4 + 2) + e]);
+                            if constexpr (HB) {
+                                x = bf16r(x + bx4[e]);
+                                y = bf16r(y + by4[e]);
+                            }
+                            const float c = (e & 1) ? bf16hi(cv[e >> 1]) : bf16lo(cv[e >> 1]);
+                            const float sn = (e & 1) ? bf16hi(sv[e >> 1]) : bf16lo(sv[e >> 1]);
+                            // both products of BF16 values are exact in float32
+                            xo[e] = fmaf(x, c, -(y * sn));
+                            yo[e] = fmaf(y, c, x * sn);
+                        }
+                        put4(tl, 8 * g4 + 4 * lhi, pack_bf16x2(xo[0], xo[1]),
+                             pack_bf16x2(xo[2], xo[3]));
+                        put4(tl, 16 + 8 * g4 + 4 * lhi, pack_bf16x2(yo[0], yo[1]),
+                             pack_bf16x2(yo[2], yo[3]));
                     }
-                    put4(tl, 8 * g4 + 4 * lhi, pack_bf16x2(xo[0], xo[1]),
-                         pack_bf16x2(xo[2], xo[3]));
-                    put4(tl, 16 + 8 * g4 + 4 * lhi, pack_bf16x2(yo[0], yo[1]),
-                         pack_bf16x2(yo[2], yo[3]));
-                }
-            } else if (hcol >= q.vt_col0) {
-                if (tok < M) {
-                    bf16_t *vcol = q.vt + q.vt_tok[tok];
+                } else if (hcol >= q.vt_col0) {
+                    if (tok < M) {
+                        bf16_t *vcol = q.vt + q.vt_tok[tok];
+#pragma unroll
+                        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                            for (int g = 0; g < 2; ++g) {
+                                const int32_t f4 = hcol + 32 * h2 + p16 + 8 * g + 4 * lhi;
+                                float bv[4] = {0, 0, 0, 0};
+                                if constexpr (HB) bias4(f4, bv);
+                                bf16_t *dst = vcol + (size_t)(f4 - q.vt_col0) * q.ldvt;
+#pragma unroll
+                                for (int e = 0; e < 4; ++e) {
+                                    float v = acc[0][b][4 * (g + 2 * h2) + e];
+                                    if constexpr (HB) v = bf16r(v) + bv[e];
+                                    dst[(size_t)e * q.ldvt] = (bf16_t)f32_to_bf16(v);
+                                }
+                            }
+                    }
+                } else {
 #pragma unroll
                     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-                        for (int g = 0; g < 2; ++g) {
-                            const int32_t f4 = hcol + 32 * h2 + p16 + 8 * g + 4 * lhi;
-                            float bv[4] = {0, 0, 0, 0};
-                            if (p.bias) bias4(f4, bv);
+                        for (int g4 = 0; g4 < 2; ++g4) {
+                            float v[4], bv[4] = {0, 0, 0, 0};
+                            if constexpr (HB) bias4(hcol + 32 * h2 + p16 + 8 * g4 + 4 * lhi, bv);
 #pragma unroll
                             for (int e = 0; e < 4; ++e) {
-                                float v = acc[0][b][4 * (g + 2 * h2) + e];
-                                if (p.bias) v = bf16r(v) + bv[e];
-                                vcol[(size_t)(f4 + e - q.vt_col0) * q.ldvt] =
-                                    (bf16_t)f32_to_bf16(v);
+                                v[e] = acc[0][b][4 * (g4 + 2 * h2) + e];
+                                if constexpr (HB) v[e] = bf16r(v[e]) + bv[e];
                             }
+                            put4(tl, 16 * h2 + 8 * g4 + 4 * lhi, pack_bf16x2(v[0], v[1]),
+                                 pack_bf16x2(v[2], v[3]));
                         }
                 }
-            } else {
-#pragma unroll
-                for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-                    for (int g4 = 0; g4 < 2; ++g4) {
-                        float v[4], bv[4] = {0, 0, 0, 0};
-                        if (p.bias) bias4(hcol + 32 * h2 + p16 + 8 * g4 + 4 * lhi, bv);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            v[e] = acc[0][b][4 * (g4 + 2 * h2) + e];
-                            if (p.bias) v[e] = bf16r(v[e]) + bv[e];
-                        }
-                        put4(tl, 16 * h2 + 8 * g4 + 4 * lhi, pack_bf16x2(v[0], v[1]),
-                             pack_bf16x2(v[2], v[3]));
-                    }
-            }
+            };
+            if (p.bias)
+                tile(std::true_type{});
+            else
+                tile(std::false_type{});
         } else if constexpr (EPI == 2) {
             // Fragments a (dims 0..31 of a head) and a+1 (dims 32..63) sit in
             // the same lanes, so the rotation pairs (i, i+32) are in registers.
