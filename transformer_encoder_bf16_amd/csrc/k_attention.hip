@@ -201,11 +201,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void a
         }
         // this tile's maximum in raw score units (the scale is positive),
         // reduced over the 4 lanes of a query (rows of 16 lanes swapped
-        // pairwise, then the two halves of the wave)
-        float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                         fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-        mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(s[2][0], s[2][1]), fmaxf(s[2][2], s[2][3])),
-                             fmaxf(fmaxf(s[3][0], s[3][1]), fmaxf(s[3][2], s[3][3]))));
+        // pairwise, then the two halves of the wave).  Two chains of
+        // max(max(a, b), c), which the compiler fuses into three-input
+        // v_max3_f32: 8 instructions for the 16 scores instead of 12.
+        float mx = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
+        mx = fmaxf(fmaxf(mx, s[0][3]), s[1][0]);
+        mx = fmaxf(fmaxf(mx, s[1][1]), s[1][2]);
+        mx = fmaxf(fmaxf(mx, s[1][3]), s[2][0]);
+        float my = fmaxf(fmaxf(s[2][1], s[2][2]), s[2][3]);
+        my = fmaxf(fmaxf(my, s[3][0]), s[3][1]);
+        my = fmaxf(fmaxf(my, s[3][2]), s[3][3]);
+        mx = fmaxf(mx, my);
         {
             const uint32_t xb = __float_as_uint(mx);
             const auto r16 = __builtin_amdgcn_permlane16_swap(xb, xb, false, false);

@@ -510,6 +510,17 @@ __global__ __launch_bounds__(G::NTHR) void gemm_kernel(GemmParams p) {
           wait_vmcnt<(STAGES - 1) * G::LOADS_MIN>();
       else
           wait_vmcnt<0>();
+      // The output, bias, residual, partial and QKV table pointers are needed
+      // only after the main loop (or just before it), but left to itself the
+      // compiler may issue their scalar loads just before the loop.
+      // Scalar and LDS loads share one wait counter and the scalar ones can
+      // return out of order, so a scalar load still in flight at the loop's
+      // entry turns the loop's first fragment wait into a wait for every LDS
+      // read.  Using the pointers here puts their loads under the wait below.
+      asm volatile("" ::"s"(p.C), "s"(p.bias), "s"(p.res), "s"(p.partial));
+      if constexpr (EPI == 2)
+          asm volatile("" ::"s"(p.qe.pos), "s"(p.qe.cos_tab), "s"(p.qe.sin_tab), "s"(p.qe.vt),
+                       "s"(p.qe.vt_tok));
       wait_lgkmcnt<0>();  // no scalar loads left in flight, so
                                            // the loop's LDS reads can be waited on in order
       ring_barrier();
